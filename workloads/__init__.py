@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the selective scan (shared by tests and bench).
+
+This module holds no arithmetic of the method itself: it only draws the
+seeded random inputs, rounds them to bfloat16 where a workload asks for it,
+and describes the workload shapes.  Both the GPU library's tests and the
+float64 oracle receive exactly the bits produced here.
+
+Every tensor is drawn with ``numpy.random.default_rng([workload_id,
+tensor_id, b])`` in float32 (one stream per batch row), or with key
+``[workload_id, tensor_id, b, d]`` per (b, d) row when ``per_row`` is set so
+that a single channel of a very long sequence can be regenerated alone.
+Tensor ids: u=0, delta=1, B=2, C=3, z=4, D=5, delta_bias=6, dout=7.
+
+Distributions: u, z, B, C, delta (before bias/softplus), dout ~ N(0, 1);
+D ~ N(0, 1); A[d, n] = -(n + 1) (S4D-Real, described in the paper summary's
+section 3.4 "Additional Model Details"); delta_bias either the constant -2 or
+Uniform(log(e^0.001 - 1), log(e^0.1 - 1)) drawn uniformly in bias space (the
+bias range corresponds to softplus values 0.001..0.1, the initialisation the
+same section describes).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+TENSOR_IDS = dict(u=0, delta=1, B=2, C=3, z=4, D=5, delta_bias=6, dout=7)
+BIAS_LO = math.log(math.expm1(0.001))   # -6.907255...
+BIAS_HI = math.log(math.expm1(0.1))     # -2.252168...
+
+
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+    Inputs here are finite, so NaN handling is not needed."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))
+    return ((bits + rounding) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
+        np.float32)
+
+
+@dataclass
+class Workload:
+    wid: int
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    seqlen: int
+    dtype: str            # "f32" or "bf16" for u, delta, B, C, z, out, dout
+    bias: str             # "const" (-2) or "uniform"
+    discs: tuple = ("zoh",)
+    backward: bool = False
+    per_row: bool = False
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def channel_tokens(self) -> int:
+        return self.batch * self.dim * self.seqlen
+
+
+# The five workloads the library is specified on, numbered 1..5.
+WORKLOADS = {
+    1: Workload(1, "tiny-fwd-f32", 1, 16, 4, 128, "f32", "const"),
+    2: Workload(2, "mamba130m-layer-fwd-f32", 8, 1536, 16, 2048, "f32", "uniform"),
+    3: Workload(3, "mamba1.4b-layer-fwd-bf16", 4, 4096, 16, 4096, "bf16", "const",
+                discs=("zoh", "euler")),
+    4: Workload(4, "long-seq-fwd-bf16", 1, 1536, 16, 1048576, "bf16", "const", per_row=True),
+    5: Workload(5, "bwd-recompute-bf16", 2, 5120, 16, 2048, "bf16", "const", backward=True),
+}
+
+
+def _normal(key, shape):
+    return np.random.default_rng(key).standard_normal(shape, dtype=np.float32)
+
+
+def _seq_tensor(wid, tid, batch, rows, seqlen, per_row=False, row_subset=None):
+    """(batch, rows, seqlen) float32 standard normals, one stream per batch
+    row (or per (b, row) when per_row)."""
+    if per_row:
+        rsel = range(rows) if row_subset is None else row_subset
+        out = np.empty((batch, len(rsel), seqlen), np.float32)
+        for b in range(batch):
+            for i, r in enumerate(rsel):
+                out[b, i] = _normal([wid, tid, b, r], seqlen)
+        return out
+    out = np.empty((batch, rows, seqlen), np.float32)
+    for b in range(batch):
+        out[b] = _normal([wid, tid, b], (rows, seqlen))
+    if row_subset is not None:
+        out = out[:, list(row_subset)]
+    return out
+
+
+def make_inputs(wid: int, batch: int, dim: int, dstate: int, seqlen: int, *, dtype="f32",
+                bias="const", with_D=True, with_z=True, with_bias=True, with_dout=False,
+                per_row=False, dim_subset=None, A_mode="s4d_real"):
+    """Returns a dict of numpy arrays.
+
+    Sequence tensors (u, delta, B, C, z, dout) are float32 for dtype "f32" and
+    uint16 bfloat16 bit patterns for "bf16"; A, D, delta_bias are float32.
+    ``dim_subset`` (with per_row) draws only the listed channels, bit-identical
+    to the same rows of the full tensor.
+    """
+    rows = list(dim_subset) if dim_subset is not None else None
+    ndim = len(rows) if rows is not None else dim
+    res = {}
+    res["u"] = _seq_tensor(wid, 0, batch, dim, seqlen, per_row, rows)
+    res["delta"] = _seq_tensor(wid, 1, batch, dim, seqlen, per_row, rows)
+    res["B"] = _seq_tensor(wid, 2, batch, dstate, seqlen, False)
+    res["C"] = _seq_tensor(wid, 3, batch, dstate, seqlen, False)
+    if with_z:
+        res["z"] = _seq_tensor(wid, 4, batch, dim, seqlen, per_row, rows)
+    if with_dout:
+        res["dout"] = _seq_tensor(wid, 7, batch, dim, seqlen, per_row, rows)
+    if A_mode == "s4d_real":
+        A = -np.broadcast_to(np.arange(1, dstate + 1, dtype=np.float32), (dim, dstate)).copy()
+    elif A_mode == "random_neg":
+        A = -np.exp(_normal([wid, 8], (dim, dstate)))
+    else:
+        raise ValueError(A_mode)
+    Dv = _normal([wid, 5], dim)
+    if bias == "const":
+        bv = np.full(dim, -2.0, np.float32)
+    elif bias == "uniform":
+        bv = np.random.default_rng([wid, 6]).uniform(BIAS_LO, BIAS_HI, dim).astype(np.float32)
+    elif bias == "normal":
+        bv = _normal([wid, 6], dim)
+    else:
+        raise ValueError(bias)
+    if rows is not None:
+        A, Dv, bv = A[rows], Dv[rows], bv[rows]
+    res["A"] = np.ascontiguousarray(A, dtype=np.float32)
+    if with_D:
+        res["D"] = Dv.astype(np.float32)
+    if with_bias:
+        res["delta_bias"] = bv.astype(np.float32)
+    if dtype == "bf16":
+        for k in ("u", "delta", "B", "C", "z", "dout"):
+            if k in res:
+                res[k] = bf16_round_bits(res[k])
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    assert all(v.shape[0] == (ndim if k in ("A", "D", "delta_bias") else batch)
+               for k, v in res.items())
+    return res
+
+
+def workload_inputs(wid: int, **kw):
+    w = WORKLOADS[wid]
+    args = dict(dtype=w.dtype, bias=w.bias, with_dout=w.backward, per_row=w.per_row)
+    args.update(kw)
+    return make_inputs(wid, w.batch, w.dim, w.dstate, w.seqlen, **args)
+
+
+def as_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """The exact float64 values of a generated array (bf16 bits widened)."""
+    if dtype == "bf16" and arr.dtype == np.uint16:
+        return bf16_bits_to_f32(arr).astype(np.float64)
+    return np.asarray(arr, dtype=np.float64)
+
+
+def inputs_f64(inp: dict, dtype: str) -> dict:
+    return {k: as_f64(v, dtype) if k in ("u", "delta", "B", "C", "z", "dout") else
+            np.asarray(v, np.float64) for k, v in inp.items()}
