@@ -1,0 +1,192 @@
+/*
+ * mamba_scan.h -- C ABI of the MI355X (gfx950) selective-scan (S6) library.
+ *
+ * The library computes, for every channel (b, d) independently, the selective
+ * state space recurrence of Mamba (Gu & Dao, "Mamba: Linear-Time Sequence
+ * Modeling with Selective State Spaces"):
+ *
+ *   delta_t = softplus(delta_raw_t + delta_bias[d])        (or without softplus)
+ *   Abar_t[n] = exp(delta_t * A[d,n])
+ *   Bbar_t[n] = (exp(delta_t*A[d,n]) - 1) / A[d,n] * B[b,n,t]    (ZOH)
+ *             =  delta_t * B[b,n,t]                             (EULER)
+ *   h_t[n]  = Abar_t[n] * h_{t-1}[n] + Bbar_t[n] * u_t,   h_{-1} = h0 (or 0)
+ *   y_t     = sum_n C[b,n,t] * h_t[n] + D[d] * u_t
+ *   out_t   = y_t * z_t * sigmoid(z_t)                      (when z is given)
+ *
+ * Definitions on the pages this follows:
+ *   - ZOH rule and recurrence: chapterpal.com page of the paper, Knowl 1
+ *     "Selective State Space Layer (S6)", steps 3 and 4 (diagonal A, so the
+ *     matrix exponential is elementwise).
+ *   - delta = tau_Delta(Parameter + s_Delta(x)) with tau_Delta = softplus:
+ *     same Knowl, step 2; delta_bias is that Parameter.
+ *   - B and C shared by all D channels, shape (B, L, N); A of shape (D, N):
+ *     trishampatil.com essay, Part II §6 "S6: the selective SSM", Algorithm 2.
+ *   - h_0 = 0: same essay, Part II §4.
+ *   - Fused scan, chunks carrying the scan state across chunk boundaries,
+ *     recomputation of the states in the backward: paper-graph-ui.vercel.app
+ *     summary, section 3.4, "Hardware-Aware Scan Algorithm (Section 3.3)".
+ *   - SiLU gate: chapterpal page, Knowl 3 "Mamba Block Architecture" items
+ *     4-5 (the gate branch multiplies the SSM output).
+ * The D skip term, the gate fused into the scan, the Euler variant of Bbar
+ * and the initial state h0 are part of this library's specification, not of
+ * the pages.
+ *
+ * Layouts: every array is dense, row-major, with no strides.
+ *   u, delta, z, out, dout, du, ddelta, dz   (batch, dim, seqlen)
+ *   B, C, dB, dC                             (batch, dstate, seqlen)
+ *   A, dA                                    (dim, dstate)
+ *   D, dD, delta_bias, ddelta_bias           (dim)
+ *   h0, dh0, last_state, state               (batch, dim, dstate)
+ *   state_update per-step tensors: u, delta, z, out (batch, dim);
+ *                                  B, C (batch, dstate)
+ * Dtypes: `dt` selects the element type of u, delta, B, C, z, out and dout
+ * (MAMBA_F32 or MAMBA_BF16, bfloat16 stored as 16-bit words).  A, D,
+ * delta_bias, h0, last_state, state and every gradient are float32.  All
+ * arithmetic is float32; bf16 inputs are widened exactly, bf16 outputs are
+ * rounded to nearest even.
+ *
+ * Pointers: every array pointer is a DEVICE pointer (hipMalloc'ed or
+ * equivalent memory visible to the GPU) with at least 16-byte alignment.
+ * `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *
+ * Ownership: the caller allocates and frees every buffer, including the
+ * workspace sized by the *_workspace_size queries.  The library never
+ * allocates, frees or synchronizes, keeps no global mutable state, and only
+ * enqueues work on `stream`.  Inputs are read only.  Outputs are fully
+ * overwritten (gradients are never accumulated into caller memory); the
+ * library clears whatever it accumulates into on `stream` itself.  Calls on
+ * distinct streams with distinct output and workspace buffers may run
+ * concurrently.
+ *
+ * Errors: functions return a mamba_status and never abort.  Arguments are
+ * checked before anything is enqueued; on any error nothing is enqueued and
+ * outputs are untouched.  A failed kernel launch returns MAMBA_ERR_HIP.
+ * Faults inside kernels surface at the caller's next synchronization, as
+ * for any HIP call.  Limits: batch >= 1, dim >= 1, 1 <= dstate <= 64,
+ * seqlen >= 1, batch*dim*seqlen < 2^62; otherwise MAMBA_ERR_UNSUPPORTED
+ * (MAMBA_ERR_SHAPE for non-positive sizes).
+ */
+#ifndef MAMBA_SCAN_H_
+#define MAMBA_SCAN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAMBA_SCAN_ABI_VERSION 1
+
+typedef enum {
+  MAMBA_OK = 0,
+  MAMBA_ERR_NULL_PTR = 1,     /* a required pointer is NULL                 */
+  MAMBA_ERR_SHAPE = 2,        /* a size is zero or negative                 */
+  MAMBA_ERR_DTYPE = 3,        /* unknown dtype or discretization value      */
+  MAMBA_ERR_ALIGNMENT = 4,    /* a pointer is not 16-byte aligned           */
+  MAMBA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required    */
+  MAMBA_ERR_UNSUPPORTED = 6,  /* sizes outside the supported limits         */
+  MAMBA_ERR_HIP = 7,          /* a HIP runtime call or launch failed        */
+  MAMBA_ERR_INVALID = 8       /* inconsistent optional arguments            */
+} mamba_status;
+
+typedef enum { MAMBA_F32 = 0, MAMBA_BF16 = 1 } mamba_dtype;
+
+typedef enum { MAMBA_DISC_ZOH = 0, MAMBA_DISC_EULER = 1 } mamba_disc;
+
+/* Version of this ABI (MAMBA_SCAN_ABI_VERSION). */
+int mamba_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* mamba_status_string(mamba_status status);
+
+/* Bytes of device workspace mamba_scan_fwd needs for these sizes (may be 0;
+ * then workspace may be NULL).  Returns SIZE_MAX for unsupported sizes. */
+size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                     mamba_dtype dt);
+
+/* Bytes of device workspace mamba_scan_bwd needs (SIZE_MAX if unsupported). */
+size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                     mamba_dtype dt);
+
+/*
+ * Forward scan: writes out (batch, dim, seqlen) and, when last_state is not
+ * NULL, the final state h_{seqlen-1} (batch, dim, dstate) in float32.
+ * D, z, delta_bias, h0, last_state may be NULL (no skip term, no gate, zero
+ * bias, zero initial state, no final state).  The expanded (B, L, D, N)
+ * tensors are never written to memory: only out and last_state are.
+ */
+mamba_status mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z,
+                            const float* delta_bias, const float* h0, int delta_softplus,
+                            mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
+                            int64_t dstate, int64_t seqlen, void* out, float* last_state,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of mamba_scan_fwd for the loss sum(dout * out): recomputes the
+ * states from the inputs (none are saved by the forward) and writes float32
+ * gradients du, ddelta (w.r.t. the raw delta), dA, dB, dC, and, exactly when
+ * the matching input is given, dD, dz, ddelta_bias, dh0 (each must be NULL
+ * when its input is NULL, else MAMBA_ERR_INVALID; dh0 may also be NULL when
+ * h0 is given, to skip it).  No gradient flows into last_state.  Reductions
+ * (dA, dB, dC, dD, ddelta_bias) use float32 atomics or partial sums, so the
+ * backward is deterministic only up to float32 rounding order.
+ */
+mamba_status mamba_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z,
+                            const float* delta_bias, const float* h0, const void* dout,
+                            int delta_softplus, mamba_disc disc, mamba_dtype dt, int64_t batch,
+                            int64_t dim, int64_t dstate, int64_t seqlen, float* du,
+                            float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz,
+                            float* ddelta_bias, float* dh0, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent (decode) step for every (b, d): state (batch, dim, dstate)
+ * float32 is updated IN PLACE (h <- Abar*h + Bbar*u) and out (batch, dim)
+ * receives y * SiLU(z).  Constant time and memory per step (the pages'
+ * recurrent inference mode: paper-graph-ui.vercel.app summary, section 3.4,
+ * the recurrent form "ideal for autoregressive inference").
+ * D, z, delta_bias may be NULL.
+ */
+mamba_status mamba_state_update(float* state, const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                const float* delta_bias, int delta_softplus, mamba_disc disc,
+                                mamba_dtype dt, int64_t batch, int64_t dim, int64_t dstate,
+                                void* out, void* stream);
+
+/*
+ * Tuning variants.  Identical to the calls above except for an explicit
+ * number of lanes each channel's scan is spread over (16, 32 or 64; 0 picks
+ * the default the plain calls use).  The result does not depend on the
+ * choice beyond float32 rounding order; tests and launch-shape sweeps use
+ * them.  mamba_scan_bwd_ex needs the workspace reported by
+ * mamba_scan_bwd_workspace_size_ex for the same lanes value.
+ */
+mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                               const void* C, const float* D, const void* z,
+                               const float* delta_bias, const float* h0, int delta_softplus,
+                               mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
+                               int64_t dstate, int64_t seqlen, void* out, float* last_state,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               int lanes_per_channel);
+
+size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
+                                        int64_t seqlen, mamba_dtype dt, int lanes_per_channel);
+
+mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                               const void* C, const float* D, const void* z,
+                               const float* delta_bias, const float* h0, const void* dout,
+                               int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                               int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                               float* du, float* ddelta, float* dA, float* dB, float* dC,
+                               float* dD, float* dz, float* ddelta_bias, float* dh0,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               int lanes_per_channel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H_ */

@@ -1,0 +1,214 @@
+"""Selective scan (Mamba S6) for MI355X: thin PyTorch binding of libmamba_scan.
+
+Every computation runs in the HIP kernels behind the C ABI of
+include/mamba_scan.h; this module only checks tensor metadata, passes device
+pointers and the current HIP stream, and allocates outputs and workspace
+with PyTorch.  Names and argument order follow the C ABI:
+
+    scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, ...)
+    scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, ...)
+    state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, ...)
+
+Layouts: u, delta, z, out (batch, dim, L); B, C (batch, N, L); A (dim, N);
+D, delta_bias (dim,); h0 / states (batch, dim, N).  Sequence tensors are
+float32 or bfloat16 (all the same); A, D, delta_bias and states are float32.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import BF16, EULER, F32, ZOH, MambaScanError
+
+__all__ = ["scan_fwd", "scan_bwd", "state_update", "SelectiveScanFn", "selective_scan",
+           "MambaScanError", "lib", "abi_version"]
+
+
+def lib():
+    return _lib.load()
+
+
+def abi_version() -> int:
+    return int(lib().mamba_abi_version())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"sequence tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _disc_code(disc) -> int:
+    if disc in ("zoh", ZOH):
+        return ZOH
+    if disc in ("euler", EULER):
+        return EULER
+    raise ValueError(f"disc must be 'zoh' or 'euler', got {disc!r}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _req(t, name, dtype, shape, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
+             delta_softplus=True, disc="zoh", return_last_state=False, out=None, last_state=None,
+             lanes=0):
+    """Fused selective-scan forward.  Returns out, or (out, last_state)."""
+    L_ = lib()
+    if not u.is_cuda:
+        raise ValueError("u must be a GPU tensor (no CPU path exists)")
+    dev = u.device
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    sdt = u.dtype
+    dt = _dtype_code(u)
+    _req(u, "u", sdt, (batch, dim, L), dev)
+    _req(delta, "delta", sdt, (batch, dim, L), dev)
+    _req(A, "A", torch.float32, (dim, N), dev)
+    _req(B, "B", sdt, (batch, N, L), dev)
+    _req(C, "C", sdt, (batch, N, L), dev)
+    _req(D, "D", torch.float32, (dim,), dev)
+    _req(z, "z", sdt, (batch, dim, L), dev)
+    _req(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _req(h0, "h0", torch.float32, (batch, dim, N), dev)
+    if out is None:
+        out = torch.empty((batch, dim, L), dtype=sdt, device=dev)
+    _req(out, "out", sdt, (batch, dim, L), dev)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _req(last_state, "last_state", torch.float32, (batch, dim, N), dev)
+    st = L_.mamba_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                              _ptr(delta_bias), _ptr(h0), int(bool(delta_softplus)),
+                              _disc_code(disc), dt, batch, dim, N, L, _ptr(out),
+                              _ptr(last_state), None, 0, _stream(dev), int(lanes))
+    _lib.check(st, "mamba_scan_fwd")
+    return (out, last_state) if return_last_state else out
+
+
+def bwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0) -> int:
+    code = F32 if dtype == torch.float32 else BF16
+    n = lib().mamba_scan_bwd_workspace_size_ex(batch, dim, N, L, code, int(lanes))
+    if n >= 2 ** 63:
+        raise MambaScanError(6, "mamba_scan_bwd_workspace_size")
+    return int(n)
+
+
+def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softplus=True,
+             disc="zoh", lanes=0, workspace=None, want_dh0=True):
+    """Backward with state recomputation.  Returns a dict of float32 gradients:
+    du, ddelta, dA, dB, dC and, when the input is given, dD, dz, ddelta_bias, dh0."""
+    L_ = lib()
+    dev = u.device
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    sdt = u.dtype
+    dt = _dtype_code(u)
+    for t, name, shp, ty in ((u, "u", (batch, dim, L), sdt), (delta, "delta", (batch, dim, L), sdt),
+                             (A, "A", (dim, N), torch.float32), (B, "B", (batch, N, L), sdt),
+                             (C, "C", (batch, N, L), sdt), (D, "D", (dim,), torch.float32),
+                             (z, "z", (batch, dim, L), sdt),
+                             (delta_bias, "delta_bias", (dim,), torch.float32),
+                             (h0, "h0", (batch, dim, N), torch.float32),
+                             (dout, "dout", (batch, dim, L), sdt)):
+        _req(t, name, ty, shp, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(du=torch.empty((batch, dim, L), **f32), ddelta=torch.empty((batch, dim, L), **f32),
+             dA=torch.empty((dim, N), **f32), dB=torch.empty((batch, N, L), **f32),
+             dC=torch.empty((batch, N, L), **f32))
+    if D is not None:
+        g["dD"] = torch.empty((dim,), **f32)
+    if z is not None:
+        g["dz"] = torch.empty((batch, dim, L), **f32)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty((dim,), **f32)
+    if h0 is not None and want_dh0:
+        g["dh0"] = torch.empty((batch, dim, N), **f32)
+    nbytes = bwd_workspace_bytes(batch, dim, N, L, sdt, lanes)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = L_.mamba_scan_bwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                              _ptr(delta_bias), _ptr(h0), _ptr(dout), int(bool(delta_softplus)),
+                              _disc_code(disc), dt, batch, dim, N, L, _ptr(g["du"]),
+                              _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                              _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
+                              _ptr(g.get("dh0")), workspace.data_ptr(), workspace.numel(),
+                              _stream(dev), int(lanes))
+    _lib.check(st, "mamba_scan_bwd")
+    return g
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
+                 delta_softplus=True, disc="zoh", out=None):
+    """One recurrent step; `state` (batch, dim, N) float32 is updated in place.
+    Per-step tensors: u, delta, z (batch, dim); B, C (batch, N).  Returns out."""
+    L_ = lib()
+    dev = state.device
+    batch, dim, N = state.shape
+    sdt = u.dtype
+    dt = _dtype_code(u)
+    _req(state, "state", torch.float32, (batch, dim, N), dev)
+    for t, name, shp, ty in ((u, "u", (batch, dim), sdt), (delta, "delta", (batch, dim), sdt),
+                             (A, "A", (dim, N), torch.float32), (B, "B", (batch, N), sdt),
+                             (C, "C", (batch, N), sdt), (D, "D", (dim,), torch.float32),
+                             (z, "z", (batch, dim), sdt),
+                             (delta_bias, "delta_bias", (dim,), torch.float32)):
+        _req(t, name, ty, shp, dev)
+    if out is None:
+        out = torch.empty((batch, dim), dtype=sdt, device=dev)
+    _req(out, "out", sdt, (batch, dim), dev)
+    st = L_.mamba_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                               _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
+                               _disc_code(disc), dt, batch, dim, N, _ptr(out), _stream(dev))
+    _lib.check(st, "mamba_state_update")
+    return out
+
+
+class SelectiveScanFn(torch.autograd.Function):
+    """Autograd wrapper: forward = scan_fwd, backward = scan_bwd (states are
+    recomputed, only the inputs are saved)."""
+
+    @staticmethod
+    def forward(ctx, u, delta, A, B, C, D, z, delta_bias, delta_softplus, disc):
+        out = scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus=delta_softplus,
+                       disc=disc)
+        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias)
+        ctx.flags = (delta_softplus, disc)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        u, delta, A, B, C, D, z, delta_bias = ctx.saved_tensors
+        sp, disc = ctx.flags
+        g = scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout.contiguous().to(u.dtype),
+                     delta_softplus=sp, disc=disc)
+        cast = lambda t, like: None if t is None else t.to(like.dtype)
+        return (cast(g["du"], u), cast(g["ddelta"], delta), g["dA"], cast(g["dB"], B),
+                cast(g["dC"], C), g.get("dD"), cast(g.get("dz"), z) if z is not None else None,
+                g.get("ddelta_bias"), None, None)
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                   disc="zoh"):
+    return SelectiveScanFn.apply(u, delta, A, B, C, D, z, delta_bias, delta_softplus, disc)

@@ -1,0 +1,62 @@
+"""Builds the HIP library libmamba_scan.so for gfx950 with hipcc.
+
+Every source under csrc/ is compiled to an object in parallel, then linked
+into scan_selective_fwd_amd/libmamba_scan.so.  HIP code is built with packed
+FP32 instructions disabled (`-Xclang -target-feature -Xclang -packed-fp32-ops`).
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libmamba_scan.so")
+ARCH = os.environ.get("MAMBA_SCAN_ARCH", "gfx950")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = ["-O3", f"--offload-arch={ARCH}", "-std=c++17", "-fPIC",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith((".hip", ".cpp")))
+
+
+def _compile(src, verbose):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [HIPCC] + [f for f in COMMON if f not in ("-Xclang", "-target-feature",
+                                                        "-packed-fp32-ops")] + ["-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed for {src}")
+    return obj
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    with ThreadPoolExecutor(max(1, min(jobs, len(srcs)))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    t = __import__("time").time()
+    print(build(verbose="-v" in sys.argv))
+    print(f"built in {__import__('time').time() - t:.1f}s")

@@ -1,0 +1,260 @@
+// C ABI of the selective-scan library: argument checks, launch-shape choice,
+// workspace carving and dispatch to the HIP kernels.  Nothing here allocates,
+// frees or synchronizes; every launch goes on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kernels.hpp"
+#include "mamba_scan.h"
+
+namespace {
+
+using mscan::kItems;
+using mscan::kItemsBwd;
+
+constexpr int64_t kMaxState = 64;
+constexpr size_t kAlignWs = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(mamba_dtype dt) { return dt == MAMBA_F32 ? 4 : 2; }
+
+size_t round_up(size_t x) { return (x + kAlignWs - 1) / kAlignWs * kAlignWs; }
+
+// Lanes per channel: enough waves to cover the 1024 SIMDs of the chip a few
+// times over, without chunks much longer than the sequence.
+int choose_lanes(int64_t nchannels, int64_t L, int items) {
+  int r_par = 64;
+  if (nchannels * 16 / 64 >= 2048) r_par = 16;
+  else if (nchannels * 32 / 64 >= 2048) r_par = 32;
+  int r_len = 64;
+  if (L <= 16 * items) r_len = 16;
+  else if (L <= 32 * items) r_len = 32;
+  return r_par < r_len ? r_par : r_len;
+}
+
+bool valid_lanes(int r) { return r == 16 || r == 32 || r == 64; }
+
+mamba_status check_sizes(mamba_dtype dt, int disc, int64_t batch, int64_t dim, int64_t dstate,
+                         int64_t seqlen) {
+  if (dt != MAMBA_F32 && dt != MAMBA_BF16) return MAMBA_ERR_DTYPE;
+  if (disc != MAMBA_DISC_ZOH && disc != MAMBA_DISC_EULER) return MAMBA_ERR_DTYPE;
+  if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return MAMBA_ERR_SHAPE;
+  if (dstate > kMaxState) return MAMBA_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 62;
+  if (batch > lim / dim) return MAMBA_ERR_UNSUPPORTED;
+  const int64_t nch = batch * dim;
+  if (nch > lim / seqlen || nch > lim / kMaxState) return MAMBA_ERR_UNSUPPORTED;
+  if (batch > lim / (dstate * seqlen)) return MAMBA_ERR_UNSUPPORTED;
+  // grid sizes must fit the 32-bit grid dimension
+  if (nch / 4 + 1 > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
+  return MAMBA_OK;
+}
+
+struct BwdLayout {
+  int lanes;
+  int64_t nchunks, groups;
+  size_t off_states, off_bc, off_a, off_d, total;
+};
+
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int lanes) {
+  BwdLayout w;
+  w.lanes = lanes;
+  w.nchunks = (seqlen + (int64_t)lanes * kItemsBwd - 1) / ((int64_t)lanes * kItemsBwd);
+  w.groups = mscan::bwd_groups(dim, lanes);
+  const int64_t nch = batch * dim;
+  size_t off = 0;
+  w.off_states = off;
+  off += round_up((size_t)nch * (size_t)w.nchunks * (size_t)dstate * 4);
+  w.off_bc = off;
+  off += round_up((size_t)batch * (size_t)w.groups * 2 * (size_t)dstate * (size_t)seqlen * 4);
+  w.off_a = off;
+  off += round_up((size_t)nch * (size_t)dstate * 4);
+  w.off_d = off;
+  off += round_up((size_t)nch * 2 * 4);
+  w.total = off;
+  return w;
+}
+
+inline mamba_status hip_status(hipError_t e) { return e == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int mamba_abi_version(void) { return MAMBA_SCAN_ABI_VERSION; }
+
+const char* mamba_status_string(mamba_status s) {
+  switch (s) {
+    case MAMBA_OK: return "ok";
+    case MAMBA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case MAMBA_ERR_SHAPE: return "a size is zero or negative";
+    case MAMBA_ERR_DTYPE: return "unknown dtype or discretization";
+    case MAMBA_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
+    case MAMBA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MAMBA_ERR_UNSUPPORTED: return "sizes outside the supported limits";
+    case MAMBA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case MAMBA_ERR_INVALID: return "inconsistent optional arguments";
+  }
+  return "unknown status";
+}
+
+size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                     mamba_dtype dt) {
+  if (check_sizes(dt, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK) return SIZE_MAX;
+  return 0;
+}
+
+// Workspace of mamba_scan_bwd_ex for a given lanes-per-channel choice (0 = the
+// choice mamba_scan_bwd makes).
+size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                        mamba_dtype dt, int lanes_per_channel) {
+  if (check_sizes(dt, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK) return SIZE_MAX;
+  int lanes = lanes_per_channel;
+  if (lanes == 0) lanes = choose_lanes(batch * dim, seqlen, kItemsBwd);
+  if (!valid_lanes(lanes)) return SIZE_MAX;
+  return bwd_layout(batch, dim, dstate, seqlen, lanes).total;
+}
+
+size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                     mamba_dtype dt) {
+  return mamba_scan_bwd_workspace_size_ex(batch, dim, dstate, seqlen, dt, 0);
+}
+
+// Same as mamba_scan_fwd with an explicit lanes-per-channel choice (16, 32 or
+// 64; 0 = automatic).  For tests and tuning.
+mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                               const void* C, const float* D, const void* z,
+                               const float* delta_bias, const float* h0, int delta_softplus,
+                               mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
+                               int64_t dstate, int64_t seqlen, void* out, float* last_state,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               int lanes_per_channel) {
+  (void)workspace;
+  (void)workspace_bytes;
+  mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
+  if (st != MAMBA_OK) return st;
+  if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL_PTR;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, out, last_state};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MAMBA_ERR_ALIGNMENT;
+  int lanes = lanes_per_channel;
+  if (lanes == 0) lanes = choose_lanes(batch * dim, seqlen, kItems);
+  if (!valid_lanes(lanes)) return MAMBA_ERR_UNSUPPORTED;
+
+  mscan::FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.bias = delta_bias;
+  p.h0 = h0; p.out = out; p.last_state = last_state; p.chunk_states = nullptr;
+  p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
+  p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
+  const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  return hip_status(mscan::dispatch_scan_fwd(p, dt == MAMBA_F32 ? 0 : 1, (int)disc, lanes, vec,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+mamba_status mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z,
+                            const float* delta_bias, const float* h0, int delta_softplus,
+                            mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
+                            int64_t dstate, int64_t seqlen, void* out, float* last_state,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return mamba_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, disc, dt,
+                           batch, dim, dstate, seqlen, out, last_state, workspace,
+                           workspace_bytes, stream, 0);
+}
+
+mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                               const void* C, const float* D, const void* z,
+                               const float* delta_bias, const float* h0, const void* dout,
+                               int delta_softplus, mamba_disc disc, mamba_dtype dt, int64_t batch,
+                               int64_t dim, int64_t dstate, int64_t seqlen, float* du,
+                               float* ddelta, float* dA, float* dB, float* dC, float* dD,
+                               float* dz, float* ddelta_bias, float* dh0, void* workspace,
+                               size_t workspace_bytes, void* stream, int lanes_per_channel) {
+  mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
+  if (st != MAMBA_OK) return st;
+  if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
+    return MAMBA_ERR_NULL_PTR;
+  if ((D == nullptr) != (dD == nullptr) || (z == nullptr) != (dz == nullptr) ||
+      (delta_bias == nullptr) != (ddelta_bias == nullptr) || (h0 == nullptr && dh0 != nullptr))
+    return MAMBA_ERR_INVALID;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, dout, du, ddelta, dA, dB, dC,
+                        dD, dz, ddelta_bias, dh0, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MAMBA_ERR_ALIGNMENT;
+  int lanes = lanes_per_channel;
+  if (lanes == 0) lanes = choose_lanes(batch * dim, seqlen, kItemsBwd);
+  if (!valid_lanes(lanes)) return MAMBA_ERR_UNSUPPORTED;
+  const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen, lanes);
+  if (!workspace || workspace_bytes < w.total) return MAMBA_ERR_WORKSPACE;
+  if (batch * w.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
+
+  char* ws = static_cast<char*>(workspace);
+  float* states = reinterpret_cast<float*>(ws + w.off_states);
+  const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  const int dti = dt == MAMBA_F32 ? 0 : 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  mscan::FwdParams fp;
+  memset(&fp, 0, sizeof(fp));
+  fp.u = u; fp.delta = delta; fp.A = A; fp.B = B; fp.C = C; fp.D = D; fp.z = z;
+  fp.bias = delta_bias; fp.h0 = h0; fp.out = nullptr; fp.last_state = nullptr;
+  fp.chunk_states = states;
+  fp.batch = batch; fp.dim = dim; fp.L = seqlen; fp.nchannels = batch * dim;
+  fp.N = (int)dstate; fp.softplus = delta_softplus ? 1 : 0;
+  hipError_t e = mscan::dispatch_chunk_states(fp, dti, (int)disc, lanes, vec, s);
+  if (e != hipSuccess) return MAMBA_ERR_HIP;
+
+  mscan::BwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.bias = delta_bias;
+  p.h0 = h0; p.dout = dout; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB; p.dC = dC;
+  p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0;
+  p.chunk_states = states;
+  p.part_bc = reinterpret_cast<float*>(ws + w.off_bc);
+  p.part_a = reinterpret_cast<float*>(ws + w.off_a);
+  p.part_d = reinterpret_cast<float*>(ws + w.off_d);
+  p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
+  p.nchunks = w.nchunks; p.groups = w.groups; p.N = (int)dstate;
+  p.softplus = delta_softplus ? 1 : 0;
+  e = mscan::dispatch_scan_bwd(p, dti, (int)disc, lanes, vec, s);
+  if (e != hipSuccess) return MAMBA_ERR_HIP;
+  return hip_status(mscan::launch_bwd_reduce(p, s));
+}
+
+mamba_status mamba_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z,
+                            const float* delta_bias, const float* h0, const void* dout,
+                            int delta_softplus, mamba_disc disc, mamba_dtype dt, int64_t batch,
+                            int64_t dim, int64_t dstate, int64_t seqlen, float* du,
+                            float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz,
+                            float* ddelta_bias, float* dh0, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return mamba_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout, delta_softplus, disc,
+                           dt, batch, dim, dstate, seqlen, du, ddelta, dA, dB, dC, dD, dz,
+                           ddelta_bias, dh0, workspace, workspace_bytes, stream, 0);
+}
+
+mamba_status mamba_state_update(float* state, const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                const float* delta_bias, int delta_softplus, mamba_disc disc,
+                                mamba_dtype dt, int64_t batch, int64_t dim, int64_t dstate,
+                                void* out, void* stream) {
+  mamba_status st = check_sizes(dt, disc, batch, dim, dstate, 1);
+  if (st != MAMBA_OK) return st;
+  if (!state || !u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL_PTR;
+  const void* ptrs[] = {state, u, delta, A, B, C, D, z, delta_bias, out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MAMBA_ERR_ALIGNMENT;
+  mscan::StepParams p;
+  memset(&p, 0, sizeof(p));
+  p.state = state; p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
+  p.bias = delta_bias; p.out = out; p.batch = batch; p.dim = dim; p.nchannels = batch * dim;
+  p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
+  return hip_status(mscan::dispatch_state_update(p, dt == MAMBA_F32 ? 0 : 1, (int)disc,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,300 @@
+// Device helpers shared by the selective-scan kernels (gfx950 / CDNA4, wave64).
+//
+// Lane layout used by the scan kernels: a channel (one (b, d) pair) owns R
+// consecutive lanes of a wave (R = 16, 32 or 64), each lane owning K
+// consecutive time steps of the current chunk, so a chunk covers R*K steps.
+// The recurrence h_t = a_t h_{t-1} + b_t composes affine maps h -> a h + b;
+// composition is associative ((a1,b1) then (a2,b2) = (a2 a1, a2 b1 + b2)),
+// which is what lets the scan run as a tree across lanes (paper-graph-ui
+// summary of the Mamba paper, section 3.4, "The parallel scan"; trishampatil
+// essay, Part III §2).  The cross-lane steps use DPP row shifts/broadcasts,
+// which move data between lanes inside the VALU without touching LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mscan {
+
+typedef uint16_t bf16_t;  // bfloat16 stored as its 16-bit pattern
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// DPP moves.  With bound_ctrl off, a lane whose source lane is invalid (or
+// whose row is masked off) keeps `old`: the scans pass the identity element
+// of the operation there.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ float dpp_mov(float old, float src) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, src),
+                                         CTRL, ROW_MASK, BANK_MASK, false));
+}
+
+enum : int {
+  kRowShr1 = 0x111,
+  kRowShr2 = 0x112,
+  kRowShr4 = 0x114,
+  kRowShr8 = 0x118,
+  kWaveShr1 = 0x138,
+  kRowBcast15 = 0x142,
+  kRowBcast31 = 0x143,
+};
+
+// One step of the inclusive scan: combine with the pair held by the source
+// lane of the DPP pattern (the earlier segment).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ void affine_step(float& A, float& B) {
+  float Ap = dpp_mov<CTRL, ROW_MASK>(1.0f, A);
+  float Bp = dpp_mov<CTRL, ROW_MASK>(0.0f, B);
+  B = __builtin_fmaf(A, Bp, B);
+  A = A * Ap;
+}
+
+// Inclusive scan of affine pairs over groups of R lanes (R = 16, 32, 64).
+// On return lane i of a group holds the composition of lanes 0..i.
+template <int R>
+__device__ __forceinline__ void affine_scan_inclusive(float& A, float& B) {
+  static_assert(R == 16 || R == 32 || R == 64, "R");
+  affine_step<kRowShr1>(A, B);
+  affine_step<kRowShr2>(A, B);
+  affine_step<kRowShr4>(A, B);
+  affine_step<kRowShr8>(A, B);
+  if constexpr (R >= 32) affine_step<kRowBcast15, 0xA>(A, B);
+  if constexpr (R == 64) affine_step<kRowBcast31, 0xC>(A, B);
+}
+
+// Value of lane R-1 of this lane's group, broadcast to the whole group.
+template <int R>
+__device__ __forceinline__ float group_last(float v) {
+  if constexpr (R == 16) {
+    // ds_swizzle bit mode: lane reads ((lane & 0x10) | 0x0F) within 32 lanes.
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x1F0));
+  } else if constexpr (R == 32) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x3E0));
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  }
+}
+
+// Value of lane 0 of this lane's group, broadcast to the whole group.
+template <int R>
+__device__ __forceinline__ float group_first(float v) {
+  if constexpr (R == 16) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x010));
+  } else if constexpr (R == 32) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x000));
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  }
+}
+
+// Lane i receives lane i-1 of its group; lane 0 of the group receives `first`.
+template <int R>
+__device__ __forceinline__ float group_shift_right(float v, float first) {
+  if constexpr (R == 16) {
+    return dpp_mov<kRowShr1>(first, v);
+  } else {
+    float s = dpp_mov<kWaveShr1>(first, v);
+    if constexpr (R == 32) s = ((__lane_id() & 31) == 0) ? first : s;
+    return s;
+  }
+}
+
+// Sum over the R lanes of a group, result in every lane of the group.
+template <int R>
+__device__ __forceinline__ float group_sum(float v) {
+  // butterfly with ds_swizzle xor (within 32) and a readlane/permute above.
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                             (0x1F) | (1 << 10)));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                             (0x1F) | (2 << 10)));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                             (0x1F) | (4 << 10)));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                             (0x1F) | (8 << 10)));
+  if constexpr (R >= 32)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                               (0x1F) | (16 << 10)));
+  if constexpr (R == 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Math.  exp and log use the hardware base-2 instructions (v_exp_f32,
+// v_log_f32); softplus uses an accurate log1p.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// log1p(e) for e in [0, 1]: with w = 1 + e rounded, log1p(e) = log(w) * e /
+// (w - 1) when w != 1, and e otherwise.  The quotient e / (w - 1) cancels the
+// rounding of w (Goldberg, "What Every Computer Scientist Should Know About
+// Floating-Point Arithmetic", 1991, Theorem 4).
+__device__ __forceinline__ float log1p_unit(float e) {
+  float w = 1.0f + e;
+  float den = w - 1.0f;
+  float lg = __builtin_amdgcn_logf(w) * kLn2;
+  return den == 0.0f ? e : lg * (e * fast_rcp(den));
+}
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}).
+__device__ __forceinline__ float softplus(float x) {
+  float e = fast_exp(-__builtin_fabsf(x));
+  return __builtin_fmaxf(x, 0.0f) + log1p_unit(e);
+}
+
+__device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + fast_exp(-x)); }
+__device__ __forceinline__ float silu(float x) { return x * sigmoid(x); }
+
+// ---------------------------------------------------------------------------
+// Element I/O for float and bfloat16 rows.  `load_k` reads K consecutive
+// elements starting at p (16-byte aligned when VEC), `load_k_guarded` reads
+// only the first `nvalid` of them (others are 0).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bfloat16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (f != f) ? ((u >> 16) | 0x40u) : r;
+}
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  template <int K>
+  __device__ __forceinline__ static void load_k(const float* __restrict__ p, float (&v)[K]) {
+    static_assert(K % 4 == 0, "K");
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) {
+      float4 x = reinterpret_cast<const float4*>(p)[i];
+      v[4 * i + 0] = x.x;
+      v[4 * i + 1] = x.y;
+      v[4 * i + 2] = x.z;
+      v[4 * i + 3] = x.w;
+    }
+  }
+  template <int K>
+  __device__ __forceinline__ static void load_k_guarded(const float* __restrict__ p, int nvalid,
+                                                        float (&v)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = (k < nvalid) ? p[k] : 0.0f;
+  }
+  template <int K>
+  __device__ __forceinline__ static void store_k(float* __restrict__ p, const float (&v)[K]) {
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i)
+      reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  }
+  template <int K>
+  __device__ __forceinline__ static void store_k_guarded(float* __restrict__ p, int nvalid,
+                                                         const float (&v)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (k < nvalid) p[k] = v[k];
+  }
+  __device__ __forceinline__ static float load1(const float* p) { return *p; }
+  __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
+};
+
+template <>
+struct Elem<bf16_t> {
+  template <int K>
+  __device__ __forceinline__ static void load_k(const bf16_t* __restrict__ p, float (&v)[K]) {
+    static_assert(K % 8 == 0, "K");
+#pragma unroll
+    for (int i = 0; i < K / 8; ++i) {
+      uint4 x = reinterpret_cast<const uint4*>(p)[i];
+      v[8 * i + 0] = bf16_lo(x.x);
+      v[8 * i + 1] = bf16_hi(x.x);
+      v[8 * i + 2] = bf16_lo(x.y);
+      v[8 * i + 3] = bf16_hi(x.y);
+      v[8 * i + 4] = bf16_lo(x.z);
+      v[8 * i + 5] = bf16_hi(x.z);
+      v[8 * i + 6] = bf16_lo(x.w);
+      v[8 * i + 7] = bf16_hi(x.w);
+    }
+  }
+  template <int K>
+  __device__ __forceinline__ static void load_k_guarded(const bf16_t* __restrict__ p, int nvalid,
+                                                        float (&v)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = (k < nvalid) ? bf16_to_f32(p[k]) : 0.0f;
+  }
+  template <int K>
+  __device__ __forceinline__ static void store_k(bf16_t* __restrict__ p, const float (&v)[K]) {
+#pragma unroll
+    for (int i = 0; i < K / 8; ++i) {
+      uint4 x;
+      x.x = f32_to_bf16_bits(v[8 * i + 0]) | (f32_to_bf16_bits(v[8 * i + 1]) << 16);
+      x.y = f32_to_bf16_bits(v[8 * i + 2]) | (f32_to_bf16_bits(v[8 * i + 3]) << 16);
+      x.z = f32_to_bf16_bits(v[8 * i + 4]) | (f32_to_bf16_bits(v[8 * i + 5]) << 16);
+      x.w = f32_to_bf16_bits(v[8 * i + 6]) | (f32_to_bf16_bits(v[8 * i + 7]) << 16);
+      reinterpret_cast<uint4*>(p)[i] = x;
+    }
+  }
+  template <int K>
+  __device__ __forceinline__ static void store_k_guarded(bf16_t* __restrict__ p, int nvalid,
+                                                         const float (&v)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (k < nvalid) p[k] = (bf16_t)f32_to_bf16_bits(v[k]);
+  }
+  __device__ __forceinline__ static float load1(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store1(bf16_t* p, float v) {
+    *p = (bf16_t)f32_to_bf16_bits(v);
+  }
+};
+
+// Load K elements of a row starting at element offset `t` of a row with
+// `L` valid elements; vector loads when the whole run is in range.
+template <typename T, int K, bool VEC>
+__device__ __forceinline__ void load_run(const T* __restrict__ row, int64_t t, int64_t L,
+                                         float (&v)[K]) {
+  int64_t rem = L - t;
+  int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
+  if (VEC && nvalid == K) {
+    Elem<T>::template load_k<K>(row + t, v);
+  } else {
+    Elem<T>::template load_k_guarded<K>(row + t, nvalid, v);
+  }
+}
+
+template <typename T, int K, bool VEC>
+__device__ __forceinline__ void store_run(T* __restrict__ row, int64_t t, int64_t L,
+                                          const float (&v)[K]) {
+  int64_t rem = L - t;
+  int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
+  if (VEC && nvalid == K) {
+    Elem<T>::template store_k<K>(row + t, v);
+  } else if (nvalid > 0) {
+    Elem<T>::template store_k_guarded<K>(row + t, nvalid, v);
+  }
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of the chip (each
+// XCD has its own L2).  Remap so that XCD x runs a contiguous range of
+// logical blocks; neighbouring channels (which share B and C rows of the same
+// batch) then share one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  int xcd = bid % kXcd;
+  int idx = bid / kXcd;
+  int q = nblocks / kXcd, r = nblocks % kXcd;
+  return xcd * q + (xcd < r ? xcd : r) + idx;
+}
+
+}  // namespace mscan

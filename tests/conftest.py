@@ -9,3 +9,15 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running (full-size workloads)")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _name_gpu_case(request):
+    """Print (and flush) the test id before a GPU test runs, so a run that
+    ends abruptly still names the case it was in."""
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu-test] {request.node.nodeid}", flush=True)
+    yield

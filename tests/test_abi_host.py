@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/mamba_scan.h declares,
+and reject bad arguments with the documented status before enqueuing any
+work (so these calls never reach the device).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from scan_selective_fwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba_scan.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(mamba_[a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for required in ("mamba_scan_fwd", "mamba_scan_bwd", "mamba_state_update",
+                     "mamba_scan_fwd_workspace_size", "mamba_scan_bwd_workspace_size",
+                     "mamba_status_string", "mamba_abi_version"):
+        assert required in names
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mamba_abi_version() == 1
+    for code in range(0, 9):
+        s = lib.mamba_status_string(code)
+        assert s and isinstance(s, bytes)
+    assert lib.mamba_status_string(0) == b"ok"
+    assert b"unknown" in lib.mamba_status_string(99)
+
+
+def test_workspace_queries(lib):
+    assert lib.mamba_scan_fwd_workspace_size(8, 1536, 16, 2048, 0) == 0
+    n = lib.mamba_scan_bwd_workspace_size(2, 5120, 16, 2048, 1)
+    assert 0 < n < 2 ** 31
+    assert n % 256 == 0
+    assert lib.mamba_scan_bwd_workspace_size(2, 5120, 65, 2048, 1) == 2 ** 64 - 1
+    assert lib.mamba_scan_bwd_workspace_size(0, 5120, 16, 2048, 1) == 2 ** 64 - 1
+    for lanes in (16, 32, 64):
+        assert lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, lanes) > 0
+    assert lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 8) == 2 ** 64 - 1
+
+
+P = 4096  # a 16-byte aligned fake address; never dereferenced (calls fail first)
+
+
+def fwd(lib, **kw):
+    a = dict(u=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, h0=None, sp=1, disc=0, dt=0,
+             batch=1, dim=16, N=4, L=128, out=P, last=None, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.mamba_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                              a["bias"], a["h0"], a["sp"], a["disc"], a["dt"], a["batch"],
+                              a["dim"], a["N"], a["L"], a["out"], a["last"], a["ws"], a["wsb"],
+                              a["stream"])
+
+
+def bwd(lib, **kw):
+    a = dict(u=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, h0=None, dout=P, sp=1,
+             disc=0, dt=0, batch=1, dim=16, N=4, L=128, du=P, ddelta=P, dA=P, dB=P, dC=P,
+             dD=None, dz=None, dbias=None, dh0=None, ws=P, wsb=0, stream=None)
+    a.update(kw)
+    return lib.mamba_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                              a["bias"], a["h0"], a["dout"], a["sp"], a["disc"], a["dt"],
+                              a["batch"], a["dim"], a["N"], a["L"], a["du"], a["ddelta"], a["dA"],
+                              a["dB"], a["dC"], a["dD"], a["dz"], a["dbias"], a["dh0"], a["ws"],
+                              a["wsb"], a["stream"])
+
+
+def step(lib, **kw):
+    a = dict(state=P, u=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=1, disc=0, dt=0,
+             batch=1, dim=16, N=4, out=P, stream=None)
+    a.update(kw)
+    return lib.mamba_state_update(a["state"], a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"],
+                                  a["z"], a["bias"], a["sp"], a["disc"], a["dt"], a["batch"],
+                                  a["dim"], a["N"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(u=None), 1), (dict(delta=None), 1), (dict(A=None), 1), (dict(B=None), 1),
+    (dict(C=None), 1), (dict(out=None), 1),
+    (dict(batch=0), 2), (dict(dim=-1), 2), (dict(N=0), 2), (dict(L=0), 2),
+    (dict(dt=2), 3), (dict(disc=7), 3),
+    (dict(u=P + 4), 4), (dict(z=P + 8), 4), (dict(last=P + 2), 4), (dict(h0=P + 12), 4),
+    (dict(N=65), 6), (dict(batch=2 ** 40, dim=2 ** 30), 6),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=None), 1), (dict(du=None), 1), (dict(dC=None), 1),
+    (dict(D=P), 8), (dict(dz=P), 8), (dict(bias=P), 8), (dict(dh0=P), 8),
+    (dict(ws=None), 5), (dict(wsb=16), 5),
+    (dict(ws=P + 4, wsb=1 << 30), 4), (dict(dt=9), 3), (dict(N=100), 6),
+])
+def test_bwd_rejects_bad_arguments(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), 1), (dict(out=None), 1), (dict(N=0), 2), (dict(N=65), 6),
+    (dict(state=P + 4), 4), (dict(disc=3), 3),
+])
+def test_state_update_rejects_bad_arguments(lib, kw, code):
+    assert step(lib, **kw) == code
+
+
+def test_binding_has_no_cpu_path():
+    import torch
+    import scan_selective_fwd_amd as ms
+    x = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):
+        ms.scan_fwd(x, x, torch.zeros(2, 4), torch.zeros(1, 4, 8), torch.zeros(1, 4, 8))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        _lib._lib_saved = _lib._lib
+        try:
+            _lib._lib = None
+            _lib.load(str(tmp_path / "nope.so"))
+        finally:
+            _lib._lib = _lib._lib_saved

@@ -1,0 +1,275 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle
+on identical seeded inputs.  Small shapes span several chunks and a ragged
+tail in every launch variant (lanes per channel 16/32/64, vector and scalar
+loads, N <= 16 and N > 16, ZOH and Euler, float32 and bfloat16, optional
+inputs present or absent, initial state, A = 0)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scan_selective_fwd_amd as ms
+import workloads as W
+from parity_utils import RTOL, announce, assert_match, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_fwd(f, disc, softplus=True, h0=None):
+    return oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"), f.get("z"),
+                           f.get("delta_bias"), h0, delta_softplus=softplus,
+                           disc=oracle.ZOH if disc == "zoh" else oracle.EULER)
+
+
+def _make(wid, batch, dim, N, L, dtype, bias="uniform", **kw):
+    inp = W.make_inputs(wid, batch, dim, N, L, dtype=dtype, bias=bias, **kw)
+    return inp, W.inputs_f64(inp, dtype)
+
+
+def _positive_steps(inp, dtype):
+    """Without the softplus the raw step is used as is: make it positive
+    (0.01 + 0.05|raw| plus a small positive bias) so the recurrence decays."""
+    raw = np.abs(W.bf16_bits_to_f32(inp["delta"]) if dtype == "bf16" else inp["delta"])
+    raw = raw * 0.05 + 0.01
+    inp["delta"] = W.bf16_round_bits(raw) if dtype == "bf16" else raw.astype(np.float32)
+    if "delta_bias" in inp:
+        inp["delta_bias"] = (np.abs(inp["delta_bias"]) * 0.01).astype(np.float32)
+    return inp, W.inputs_f64(inp, dtype)
+
+
+def run_fwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=False, opts=None,
+                 zero_A=False, A_mode="s4d_real", rtol=None):
+    opts = opts or {}
+    announce(f"fwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} lanes={lanes} "
+             f"softplus={softplus} h0={h0} opts={opts} zero_A={zero_A}")
+    inp, f = _make(wid, batch, dim, N, L, dtype, A_mode=A_mode, **opts)
+    if not softplus:
+        inp, f = _positive_steps(inp, dtype)
+    if zero_A:
+        inp["A"][::3, 0] = 0.0
+        f["A"] = inp["A"].astype(np.float64)
+    h0v = None
+    if h0:
+        h0v = np.random.default_rng(wid).standard_normal((batch, dim, N)).astype(np.float32)
+    g = to_device(inp, dtype)
+    h0t = torch.from_numpy(h0v).cuda() if h0v is not None else None
+    out, last = ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g.get("D"), g.get("z"),
+                            g.get("delta_bias"), h0t, delta_softplus=softplus, disc=disc,
+                            return_last_state=True, lanes=lanes)
+    torch.cuda.synchronize()
+    ref, ref_last = _oracle_fwd(f, disc, softplus, None if h0v is None else h0v.astype(np.float64))
+    rt = rtol or RTOL[dtype]
+    assert_match(to_f64(out), ref, rt, "out")
+    # the state is float32 in both dtypes: hold it to the float32 tolerance
+    # unless the inputs are bf16 (same values, so the same bound applies)
+    assert_match(to_f64(last), ref_last, rt, "last_state")
+    return out, last
+
+
+# --------------------------------------------------------------------------
+# forward
+# --------------------------------------------------------------------------
+def test_fwd_workload1_exact_config():
+    run_fwd_case(1, 1, 16, 4, 128, "f32", "zoh", opts=dict(bias="const"))
+
+
+@pytest.mark.parametrize("lanes", [16, 32, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_fwd_lanes_dtypes_discs(lanes, dtype, disc):
+    # 1000 steps: several chunks of 16*16/32*16/64*16 and a ragged tail;
+    # 37 channels: partial last block and partial last wave.
+    run_fwd_case(11, 2, 37, 16, 1000, dtype, disc, lanes=lanes)
+
+
+@pytest.mark.parametrize("L", [1, 3, 999, 1001])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fwd_ragged_and_unaligned_lengths(L, dtype):
+    for lanes in (16, 64):
+        run_fwd_case(12, 1, 5, 16, L, dtype, "zoh", lanes=lanes)
+
+
+@pytest.mark.parametrize("N", [1, 5, 16, 17, 33, 64])
+def test_fwd_state_sizes(N):
+    run_fwd_case(13, 2, 9, N, 700, "f32", "zoh", lanes=32, A_mode="random_neg")
+
+
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_fwd_without_optional_inputs_and_softplus_off(disc):
+    run_fwd_case(14, 2, 21, 16, 513, "f32", disc, softplus=False,
+                 opts=dict(with_D=False, with_z=False, with_bias=False))
+    run_fwd_case(15, 2, 21, 16, 513, "f32", disc, softplus=False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fwd_initial_state(dtype):
+    run_fwd_case(16, 3, 10, 16, 600, dtype, "zoh", h0=True)
+    run_fwd_case(16, 3, 10, 7, 600, dtype, "euler", h0=True, lanes=64)
+
+
+def test_fwd_zero_A_limit():
+    run_fwd_case(17, 2, 12, 16, 400, "f32", "zoh", zero_A=True)
+    run_fwd_case(17, 2, 12, 16, 400, "f32", "zoh", zero_A=True, lanes=64)
+
+
+def test_fwd_is_deterministic_and_lane_choice_independent():
+    inp, f = _make(18, 2, 40, 16, 2048, "f32")
+    g = to_device(inp, "f32")
+    outs = []
+    for lanes in (16, 16, 32, 64):
+        outs.append(ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                                g["delta_bias"], lanes=lanes))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    for o in outs[2:]:
+        assert_match(to_f64(o), to_f64(outs[0]), 1e-5, "lanes")
+
+
+def test_fwd_reset_by_large_step():
+    # a large raw step resets the state: outputs after it do not depend on
+    # the prefix (Knowl 4 of the chapterpal page: large step resets).
+    inp, _ = _make(19, 1, 8, 16, 512, "f32")
+    inp2 = {k: v.copy() for k, v in inp.items()}
+    rng = np.random.default_rng(5)
+    inp2["u"][..., :200] = rng.standard_normal((1, 8, 200)).astype(np.float32)
+    for x in (inp, inp2):
+        x["delta"][..., 200] = 60.0
+    o = []
+    for x in (inp, inp2):
+        g = to_device(x, "f32")
+        o.append(to_f64(ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                                    g["delta_bias"])))
+    assert not np.allclose(o[0][..., :200], o[1][..., :200])
+    np.testing.assert_allclose(o[0][..., 200:], o[1][..., 200:], rtol=1e-6, atol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# state update (decode step)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+@pytest.mark.parametrize("N", [16, 40])
+def test_state_update_matches_oracle_and_continues_forward(dtype, disc, N):
+    announce(f"state_update {dtype} {disc} N={N}")
+    batch, dim, L, k = 3, 50, 300, 6
+    inp, f = _make(21, batch, dim, N, L + k, dtype, A_mode="random_neg")
+    g = to_device(inp, dtype)
+    sl = lambda t, a, b: t[..., a:b].contiguous()
+    # GPU prefill of the first L steps, then k decode steps
+    _, state = ms.scan_fwd(sl(g["u"], 0, L), sl(g["delta"], 0, L), g["A"], sl(g["B"], 0, L),
+                           sl(g["C"], 0, L), g["D"], sl(g["z"], 0, L), g["delta_bias"],
+                           disc=disc, return_last_state=True)
+    ref_full, ref_last = _oracle_fwd(f, disc)
+    outs = []
+    for t in range(L, L + k):
+        outs.append(to_f64(ms.state_update(state, g["u"][..., t].contiguous(),
+                                           g["delta"][..., t].contiguous(), g["A"],
+                                           g["B"][..., t].contiguous(), g["C"][..., t].contiguous(),
+                                           g["D"], g["z"][..., t].contiguous(), g["delta_bias"],
+                                           disc=disc)))
+    torch.cuda.synchronize()
+    rt = RTOL[dtype]
+    assert_match(np.stack(outs, -1), ref_full[..., L:], rt, "decode out")
+    assert_match(to_f64(state), ref_last, rt, "decode state")
+    # one step from an arbitrary state against the oracle's step
+    st0 = np.random.default_rng(3).standard_normal((batch, dim, N)).astype(np.float32)
+    stt = torch.from_numpy(st0).cuda()
+    t = 17
+    y = ms.state_update(stt, g["u"][..., t].contiguous(), g["delta"][..., t].contiguous(), g["A"],
+                        g["B"][..., t].contiguous(), g["C"][..., t].contiguous(), g["D"],
+                        g["z"][..., t].contiguous(), g["delta_bias"], disc=disc)
+    yr, sr = oracle.state_update(st0.astype(np.float64), f["u"][..., t], f["delta"][..., t], f["A"],
+                                 f["B"][..., t], f["C"][..., t], f["D"], f["z"][..., t],
+                                 f["delta_bias"],
+                                 disc=oracle.ZOH if disc == "zoh" else oracle.EULER)
+    assert_match(to_f64(y), yr, rt, "step out")
+    assert_match(to_f64(stt), sr, rt, "step state")
+
+
+def test_state_update_without_optionals():
+    batch, dim, N = 2, 33, 16
+    inp, f = _make(22, batch, dim, N, 4, "f32", with_D=False, with_z=False, with_bias=False)
+    g = to_device(inp, "f32")
+    st0 = np.random.default_rng(4).standard_normal((batch, dim, N)).astype(np.float32)
+    stt = torch.from_numpy(st0).cuda()
+    y = ms.state_update(stt, g["u"][..., 1].contiguous(), g["delta"][..., 1].contiguous(), g["A"],
+                        g["B"][..., 1].contiguous(), g["C"][..., 1].contiguous())
+    yr, sr = oracle.state_update(st0.astype(np.float64), f["u"][..., 1], f["delta"][..., 1],
+                                 f["A"], f["B"][..., 1], f["C"][..., 1])
+    assert_match(to_f64(y), yr, 1e-4, "out")
+    assert_match(to_f64(stt), sr, 1e-4, "state")
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def run_bwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=False,
+                 opts=None, zero_A=False, A_mode="s4d_real", rtol=None):
+    opts = opts or {}
+    announce(f"bwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} lanes={lanes} "
+             f"h0={h0} opts={opts} zero_A={zero_A}")
+    inp, f = _make(wid, batch, dim, N, L, dtype, with_dout=True, A_mode=A_mode, **opts)
+    if not softplus:
+        inp, f = _positive_steps(inp, dtype)
+    if zero_A:
+        inp["A"][::4, 1] = 0.0
+        f["A"] = inp["A"].astype(np.float64)
+    h0v = np.random.default_rng(wid).standard_normal((batch, dim, N)).astype(np.float32) \
+        if h0 else None
+    g = to_device(inp, dtype)
+    h0t = torch.from_numpy(h0v).cuda() if h0v is not None else None
+    res = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g.get("D"), g.get("z"),
+                      g.get("delta_bias"), g["dout"], h0t, delta_softplus=softplus, disc=disc,
+                      lanes=lanes)
+    torch.cuda.synchronize()
+    ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"), f.get("z"),
+                          f.get("delta_bias"), f["dout"],
+                          None if h0v is None else h0v.astype(np.float64),
+                          delta_softplus=softplus,
+                          disc=oracle.ZOH if disc == "zoh" else oracle.EULER)
+    rt = rtol or RTOL[dtype]
+    assert set(res) == set(ref), (set(res), set(ref))
+    for k in ref:
+        assert_match(to_f64(res[k]), ref[k], rt, k)
+    return res
+
+
+@pytest.mark.parametrize("lanes", [16, 32, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_bwd_lanes_dtypes_discs(lanes, dtype, disc):
+    run_bwd_case(31, 2, 19, 16, 700, dtype, disc, lanes=lanes, h0=True)
+
+
+@pytest.mark.parametrize("L", [1, 77, 1000])
+def test_bwd_ragged_lengths(L):
+    run_bwd_case(32, 2, 7, 16, L, "f32", "zoh", lanes=16)
+    run_bwd_case(32, 2, 7, 16, L, "bf16", "zoh", lanes=64)
+
+
+@pytest.mark.parametrize("N", [1, 5, 17, 64])
+def test_bwd_state_sizes(N):
+    run_bwd_case(33, 2, 9, N, 300, "f32", "zoh", lanes=16, A_mode="random_neg")
+
+
+def test_bwd_optionals_absent_softplus_off_zero_A():
+    run_bwd_case(34, 2, 13, 16, 400, "f32", "zoh",
+                 opts=dict(with_D=False, with_z=False, with_bias=False))
+    run_bwd_case(35, 2, 13, 16, 400, "f32", "euler", softplus=False, opts=dict(bias="normal"))
+    run_bwd_case(36, 2, 13, 16, 400, "f32", "zoh", zero_A=True)
+
+
+def test_autograd_function_matches_bwd():
+    inp, f = _make(37, 2, 8, 16, 256, "f32", with_dout=True)
+    g = to_device(inp, "f32")
+    leaves = {k: g[k].clone().requires_grad_(True)
+              for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    out = ms.selective_scan(leaves["u"], leaves["delta"], leaves["A"], leaves["B"], leaves["C"],
+                            leaves["D"], leaves["z"], leaves["delta_bias"])
+    out.backward(g["dout"])
+    ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                          f["delta_bias"], f["dout"])
+    names = dict(u="du", delta="ddelta", A="dA", B="dB", C="dC", D="dD", z="dz",
+                 delta_bias="ddelta_bias")
+    for k, gk in names.items():
+        assert_match(to_f64(leaves[k].grad), ref[gk], 1e-4, gk)

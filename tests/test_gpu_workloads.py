@@ -1,0 +1,102 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (the default lanes-per-channel choice of the C ABI).
+
+Workloads 2, 3 and 5 are compared element by element with the float64 oracle
+over every channel (the oracle is threaded over channels).  Workload 4
+(L = 1,048,576) is compared on sampled channels, which the oracle
+regenerates row by row from the same seeds, including their final states.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scan_selective_fwd_amd as ms
+import workloads as W
+from parity_utils import RTOL, announce, assert_match, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _disc(d):
+    return oracle.ZOH if d == "zoh" else oracle.EULER
+
+
+def test_workload2_fwd_f32_full():
+    announce("workload 2: fwd f32 (8,1536,16,2048) full compare")
+    inp = W.workload_inputs(2)
+    g = to_device(inp, "f32")
+    out, last = ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                            g["delta_bias"], return_last_state=True)
+    torch.cuda.synchronize()
+    out2 = ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                       g["delta_bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "forward must be bitwise deterministic"
+    f = W.inputs_f64(inp, "f32")
+    del g
+    ref, ref_last = oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                                    f["delta_bias"])
+    e = assert_match(to_f64(out), ref, RTOL["f32"], "out")
+    assert_match(to_f64(last), ref_last, RTOL["f32"], "last_state")
+    print(f"workload 2 rel errors (max, l2): {e}", flush=True)
+
+
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_workload3_fwd_bf16_full(disc):
+    announce(f"workload 3: fwd bf16 (4,4096,16,4096) {disc} full compare")
+    inp = W.workload_inputs(3)
+    g = to_device(inp, "bf16")
+    out, last = ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                            g["delta_bias"], disc=disc, return_last_state=True)
+    torch.cuda.synchronize()
+    f = W.inputs_f64(inp, "bf16")
+    del g
+    ref, ref_last = oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                                    f["delta_bias"], disc=_disc(disc))
+    e = assert_match(to_f64(out), ref, RTOL["bf16"], "out")
+    e2 = assert_match(to_f64(last), ref_last, RTOL["bf16"], "last_state")
+    # the state never passes through bf16: it must also meet the float32 bound
+    assert e2[0] <= 1e-4, e2
+    print(f"workload 3 {disc} rel errors out {e} state {e2}", flush=True)
+
+
+def test_workload4_long_sequence_sampled_channels():
+    announce("workload 4: fwd bf16 (1,1536,16,1048576) sampled channels")
+    w = W.WORKLOADS[4]
+    inp = W.workload_inputs(4)
+    g = to_device(inp, "bf16")
+    del inp
+    out, last = ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                            g["delta_bias"], return_last_state=True)
+    torch.cuda.synchronize()
+    chans = [0, 1, 511, 1024, 1534, 1535]
+    got = to_f64(out[0, chans])
+    got_last = to_f64(last[0, chans])
+    del g, out
+    sub = W.inputs_f64(W.make_inputs(4, w.batch, w.dim, w.dstate, w.seqlen, dtype="bf16",
+                                     bias=w.bias, per_row=True, dim_subset=chans), "bf16")
+    ref, ref_last = oracle.scan_fwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"],
+                                    sub["D"], sub["z"], sub["delta_bias"])
+    e = assert_match(got, ref[0], RTOL["bf16"], "out")
+    e2 = assert_match(got_last, ref_last[0], 1e-4, "last_state")
+    print(f"workload 4 rel errors out {e} state {e2}", flush=True)
+
+
+def test_workload5_bwd_full():
+    announce("workload 5: bwd bf16 inputs, f32 grads (2,5120,16,2048) full compare")
+    inp = W.workload_inputs(5)
+    g = to_device(inp, "bf16")
+    res = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                      g["delta_bias"], g["dout"])
+    torch.cuda.synchronize()
+    got = {k: to_f64(v) for k, v in res.items()}
+    del g, res
+    f = W.inputs_f64(inp, "bf16")
+    ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                          f["delta_bias"], f["dout"])
+    assert set(got) == set(ref)
+    errs = {}
+    for k in ref:
+        errs[k] = assert_match(got[k], ref[k], RTOL["bf16"], k)
+    print(f"workload 5 rel errors {errs}", flush=True)

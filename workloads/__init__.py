@@ -21,6 +21,7 @@ same section describes).
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -79,22 +80,34 @@ def _normal(key, shape):
     return np.random.default_rng(key).standard_normal(shape, dtype=np.float32)
 
 
-def _seq_tensor(wid, tid, batch, rows, seqlen, per_row=False, row_subset=None):
-    """(batch, rows, seqlen) float32 standard normals, one stream per batch
-    row (or per (b, row) when per_row)."""
+def _seq_tensor(wid, tid, batch, rows, seqlen, per_row=False, row_subset=None, bf16=False):
+    """(batch, rows, seqlen) standard normals, one stream per batch row (or
+    per (b, row) when per_row).  float32, or bfloat16 bit patterns when bf16
+    (per-row tensors are rounded row by row, in threads)."""
     if per_row:
-        rsel = range(rows) if row_subset is None else row_subset
-        out = np.empty((batch, len(rsel), seqlen), np.float32)
-        for b in range(batch):
-            for i, r in enumerate(rsel):
-                out[b, i] = _normal([wid, tid, b, r], seqlen)
+        rsel = list(range(rows)) if row_subset is None else list(row_subset)
+        out = np.empty((batch, len(rsel), seqlen), np.uint16 if bf16 else np.float32)
+
+        def fill(bi):
+            b, i = divmod(bi, len(rsel))
+            x = _normal([wid, tid, b, rsel[i]], seqlen)
+            out[b, i] = bf16_round_bits(x) if bf16 else x
+
+        jobs = batch * len(rsel)
+        if jobs >= 64:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+                list(ex.map(fill, range(jobs)))
+        else:
+            for bi in range(jobs):
+                fill(bi)
         return out
     out = np.empty((batch, rows, seqlen), np.float32)
     for b in range(batch):
         out[b] = _normal([wid, tid, b], (rows, seqlen))
     if row_subset is not None:
         out = out[:, list(row_subset)]
-    return out
+    return bf16_round_bits(out) if bf16 else out
 
 
 def make_inputs(wid: int, batch: int, dim: int, dstate: int, seqlen: int, *, dtype="f32",
@@ -109,15 +122,18 @@ def make_inputs(wid: int, batch: int, dim: int, dstate: int, seqlen: int, *, dty
     """
     rows = list(dim_subset) if dim_subset is not None else None
     ndim = len(rows) if rows is not None else dim
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(dtype)
+    bf = dtype == "bf16"
     res = {}
-    res["u"] = _seq_tensor(wid, 0, batch, dim, seqlen, per_row, rows)
-    res["delta"] = _seq_tensor(wid, 1, batch, dim, seqlen, per_row, rows)
-    res["B"] = _seq_tensor(wid, 2, batch, dstate, seqlen, False)
-    res["C"] = _seq_tensor(wid, 3, batch, dstate, seqlen, False)
+    res["u"] = _seq_tensor(wid, 0, batch, dim, seqlen, per_row, rows, bf)
+    res["delta"] = _seq_tensor(wid, 1, batch, dim, seqlen, per_row, rows, bf)
+    res["B"] = _seq_tensor(wid, 2, batch, dstate, seqlen, False, None, bf)
+    res["C"] = _seq_tensor(wid, 3, batch, dstate, seqlen, False, None, bf)
     if with_z:
-        res["z"] = _seq_tensor(wid, 4, batch, dim, seqlen, per_row, rows)
+        res["z"] = _seq_tensor(wid, 4, batch, dim, seqlen, per_row, rows, bf)
     if with_dout:
-        res["dout"] = _seq_tensor(wid, 7, batch, dim, seqlen, per_row, rows)
+        res["dout"] = _seq_tensor(wid, 7, batch, dim, seqlen, per_row, rows, bf)
     if A_mode == "s4d_real":
         A = -np.broadcast_to(np.arange(1, dstate + 1, dtype=np.float32), (dim, dstate)).copy()
     elif A_mode == "random_neg":
@@ -140,12 +156,6 @@ def make_inputs(wid: int, batch: int, dim: int, dstate: int, seqlen: int, *, dty
         res["D"] = Dv.astype(np.float32)
     if with_bias:
         res["delta_bias"] = bv.astype(np.float32)
-    if dtype == "bf16":
-        for k in ("u", "delta", "B", "C", "z", "dout"):
-            if k in res:
-                res[k] = bf16_round_bits(res[k])
-    elif dtype != "f32":
-        raise ValueError(dtype)
     assert all(v.shape[0] == (ndim if k in ("A", "D", "delta_bias") else batch)
                for k, v in res.items())
     return res
