@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--disc", default="zoh", choices=["zoh", "euler"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calls", default=None,
+                    help="comma list of calls to time instead of the full step (fwd,bwd,step)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the selective scan shards over channels with no "
@@ -117,6 +119,8 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     calls = {2: ["fwd", "bwd", "step"], 3: ["fwd"], 4: ["fwd"], 5: ["bwd"]}[w.wid]
+    if args.calls:
+        calls = args.calls.split(",")
     g = gpu_inputs(w, torch, "bwd" in calls)
     ws = None
     if "bwd" in calls:

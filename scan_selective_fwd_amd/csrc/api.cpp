@@ -53,27 +53,16 @@ mamba_status check_sizes(mamba_dtype dt, int disc, int64_t batch, int64_t dim, i
 }
 
 struct BwdLayout {
-  int lanes;
   int64_t nchunks, groups;
-  size_t off_states, off_bc, off_a, off_d, total;
+  size_t total;   // bytes: the chunk-start states (nchannels, nchunks, dstate) float32
 };
 
-BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int lanes) {
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
   BwdLayout w;
-  w.lanes = lanes;
-  w.nchunks = (seqlen + (int64_t)lanes * kItemsBwd - 1) / ((int64_t)lanes * kItemsBwd);
-  w.groups = mscan::bwd_groups(dim, lanes);
-  const int64_t nch = batch * dim;
-  size_t off = 0;
-  w.off_states = off;
-  off += round_up((size_t)nch * (size_t)w.nchunks * (size_t)dstate * 4);
-  w.off_bc = off;
-  off += round_up((size_t)batch * (size_t)w.groups * 2 * (size_t)dstate * (size_t)seqlen * 4);
-  w.off_a = off;
-  off += round_up((size_t)nch * (size_t)dstate * 4);
-  w.off_d = off;
-  off += round_up((size_t)nch * 2 * 4);
-  w.total = off;
+  const int64_t tch = (int64_t)mscan::kBwdLanes * kItemsBwd;
+  w.nchunks = (seqlen + tch - 1) / tch;
+  w.groups = mscan::channel_groups(dim, mscan::kBwdLanes);
+  w.total = round_up((size_t)(batch * dim) * (size_t)w.nchunks * (size_t)dstate * 4);
   return w;
 }
 
@@ -106,15 +95,13 @@ size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
   return 0;
 }
 
-// Workspace of mamba_scan_bwd_ex for a given lanes-per-channel choice (0 = the
-// choice mamba_scan_bwd makes).
+// Workspace of mamba_scan_bwd_ex for a lanes-per-channel choice.  The
+// backward always spreads a channel over 16 lanes: 0 and 16 are accepted.
 size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                         mamba_dtype dt, int lanes_per_channel) {
   if (check_sizes(dt, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK) return SIZE_MAX;
-  int lanes = lanes_per_channel;
-  if (lanes == 0) lanes = choose_lanes(batch * dim, seqlen, kItemsBwd);
-  if (!valid_lanes(lanes)) return SIZE_MAX;
-  return bwd_layout(batch, dim, dstate, seqlen, lanes).total;
+  if (lanes_per_channel != 0 && lanes_per_channel != mscan::kBwdLanes) return SIZE_MAX;
+  return bwd_layout(batch, dim, dstate, seqlen).total;
 }
 
 size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
@@ -148,7 +135,9 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.bias = delta_bias;
   p.h0 = h0; p.out = out; p.last_state = last_state; p.chunk_states = nullptr;
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
+  p.groups = mscan::channel_groups(dim, lanes);
   p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
+  if (batch * p.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
   const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
   return hip_status(mscan::dispatch_scan_fwd(p, dt == MAMBA_F32 ? 0 : 1, (int)disc, lanes, vec,
                                              static_cast<hipStream_t>(stream)));
@@ -184,15 +173,13 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
                         dD, dz, ddelta_bias, dh0, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MAMBA_ERR_ALIGNMENT;
-  int lanes = lanes_per_channel;
-  if (lanes == 0) lanes = choose_lanes(batch * dim, seqlen, kItemsBwd);
-  if (!valid_lanes(lanes)) return MAMBA_ERR_UNSUPPORTED;
-  const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen, lanes);
+  if (lanes_per_channel != 0 && lanes_per_channel != mscan::kBwdLanes) return MAMBA_ERR_UNSUPPORTED;
+  const int lanes = mscan::kBwdLanes;
+  const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
   if (!workspace || workspace_bytes < w.total) return MAMBA_ERR_WORKSPACE;
   if (batch * w.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
 
-  char* ws = static_cast<char*>(workspace);
-  float* states = reinterpret_cast<float*>(ws + w.off_states);
+  float* states = static_cast<float*>(workspace);
   const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
   const int dti = dt == MAMBA_F32 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -203,6 +190,7 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   fp.bias = delta_bias; fp.h0 = h0; fp.out = nullptr; fp.last_state = nullptr;
   fp.chunk_states = states;
   fp.batch = batch; fp.dim = dim; fp.L = seqlen; fp.nchannels = batch * dim;
+  fp.groups = w.groups;
   fp.N = (int)dstate; fp.softplus = delta_softplus ? 1 : 0;
   hipError_t e = mscan::dispatch_chunk_states(fp, dti, (int)disc, lanes, vec, s);
   if (e != hipSuccess) return MAMBA_ERR_HIP;
@@ -213,15 +201,10 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   p.h0 = h0; p.dout = dout; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB; p.dC = dC;
   p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0;
   p.chunk_states = states;
-  p.part_bc = reinterpret_cast<float*>(ws + w.off_bc);
-  p.part_a = reinterpret_cast<float*>(ws + w.off_a);
-  p.part_d = reinterpret_cast<float*>(ws + w.off_d);
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.nchunks = w.nchunks; p.groups = w.groups; p.N = (int)dstate;
   p.softplus = delta_softplus ? 1 : 0;
-  e = mscan::dispatch_scan_bwd(p, dti, (int)disc, lanes, vec, s);
-  if (e != hipSuccess) return MAMBA_ERR_HIP;
-  return hip_status(mscan::launch_bwd_reduce(p, s));
+  return hip_status(mscan::dispatch_scan_bwd(p, dti, (int)disc, vec, s));
 }
 
 mamba_status mamba_scan_bwd(const void* u, const void* delta, const float* A, const void* B,

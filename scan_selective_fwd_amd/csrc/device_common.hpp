@@ -66,6 +66,99 @@ __device__ __forceinline__ void affine_scan_inclusive(float& A, float& B) {
   if constexpr (R == 64) affine_step<kRowBcast31, 0xC>(A, B);
 }
 
+// The same inclusive scan written with DPP-modified VOP2 instructions: each
+// step is one v_fmac_f32_dpp and one v_mul_f32_dpp.  A lane whose DPP source
+// is outside its row (or in a row masked off) is not written, which leaves
+// it holding its own pair -- the identity of the combine -- without the
+// separate identity moves the builtin form needs.  Two wait states separate
+// a VALU write from a DPP read of the same register (s_nop 1).  Requires all
+// 64 lanes active (it is only used outside divergent code).
+template <int R>
+__device__ __forceinline__ void affine_scan_inclusive_fused(float& A, float& B) {
+  static_assert(R == 16 || R == 32 || R == 64, "R");
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      : "+v"(A), "+v"(B));
+  if constexpr (R >= 32)
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        : "+v"(A), "+v"(B));
+  if constexpr (R == 64)
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+        : "+v"(A), "+v"(B));
+}
+
+// Suffix counterpart over 16-lane rows: lane i ends with the composition of
+// lanes i..15 of its row, later lanes applied first (row_shl sources).
+__device__ __forceinline__ void affine_suffix_scan_row_fused(float& A, float& B) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+      : "+v"(A), "+v"(B));
+}
+
+// Compiler-level fence: memory operations are not moved across it.  Used
+// between the iterations of unrolled loops so that each iteration's loads
+// stay with it instead of being hoisted en masse.
+__device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
+
+// Reduce-scatter over the 4 rows of a wave: v[k] (K = 8 items) of the four
+// 16-lane rows are summed so that lane (row r, j) returns out[m] = sum over
+// rows of v[4m + r] at position j (m = 0, 1).  Uses gfx950's
+// v_permlane16_swap (odd rows of one register <-> even rows of another) and
+// v_permlane32_swap (upper half <-> lower half): 6 swaps and 6 adds.
+__device__ __forceinline__ void reduce_scatter_rows8(const float (&v)[8], float (&out)[2]) {
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2 * i]),
+                                              __float_as_uint(v[2 * i + 1]), false, false);
+    s[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);   // rows 0,2: item 2i; rows 1,3: 2i+1
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s[2 * m]),
+                                              __float_as_uint(s[2 * m + 1]), false, false);
+    out[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // row r: item 4m + r
+  }
+}
+
+// LDS tile of fp32 rows in which lane j of a 16..64-lane group reads its K
+// consecutive elements [j*K, j*K+K) as K/4 16-byte granules.  Granule g of a
+// row is stored at g ^ ((g >> 4) & (K/4 - 1)): within every 16 consecutive
+// lanes the granules a ds_read_b128 touches then cover all 64 banks once.
+template <int K>
+__device__ __forceinline__ int tile_granule(int g) {
+  constexpr int GPL = K / 4;
+  return g ^ ((g >> 4) & (GPL - 1));
+}
+
 // Value of lane R-1 of this lane's group, broadcast to the whole group.
 template <int R>
 __device__ __forceinline__ float group_last(float v) {

@@ -8,7 +8,7 @@
 namespace mscan {
 
 // Items (time steps) each lane owns per chunk: forward and backward.
-constexpr int kItems = 16;
+constexpr int kItems = 8;
 constexpr int kItemsBwd = 8;
 // Threads per workgroup of the scan kernels (4 waves of 64).
 constexpr int kBlock = 256;
@@ -28,6 +28,7 @@ struct FwdParams {
   float* chunk_states;     // states-only mode: (nchannels, nchunks, N) state at each chunk start
   int64_t batch, dim, L;
   int64_t nchannels;       // batch * dim
+  int64_t groups;          // channel groups per batch row (one block each)
   int N;
   int softplus;
 };
@@ -53,12 +54,9 @@ struct BwdParams {
   float* dbias;            // nullable
   float* dh0;              // nullable
   const float* chunk_states;  // workspace: (nchannels, nchunks, N) states at chunk starts
-  float* part_bc;          // workspace: (batch, groups, 2, N, L) partial dB / dC per channel group
-  float* part_a;           // workspace: (batch, dim, N) partial dA per batch row
-  float* part_d;           // workspace: (batch, dim, 2) partial dD, ddelta_bias per batch row
   int64_t batch, dim, L;
   int64_t nchannels;
-  int64_t nchunks;         // chunks of R*kItemsBwd steps
+  int64_t nchunks;         // chunks of 16*kItemsBwd steps
   int64_t groups;          // channel groups per batch row (ceil(dim / channels per block))
   int N;
   int softplus;
@@ -81,16 +79,40 @@ struct StepParams {
   int softplus;
 };
 
+// Channels a block of kBlock threads serves when each channel owns `lanes`
+// lanes, and the number of such groups per batch row.
+inline int channels_per_block(int lanes) { return (kBlock / 64) * (64 / lanes); }
+inline int64_t channel_groups(int64_t dim, int lanes) {
+  const int64_t cpb = channels_per_block(lanes);
+  return (dim + cpb - 1) / cpb;
+}
+
 // dtype: 0 = f32, 1 = bf16.  disc: 0 = ZOH, 1 = Euler.  lanes: 16/32/64.
-hipError_t dispatch_scan_fwd(const FwdParams& p, int dtype, int disc, int lanes, bool vec,
-                             hipStream_t stream);
+hipError_t dispatch_scan_fwd_f32(const FwdParams& p, int disc, int lanes, bool vec, hipStream_t s);
+hipError_t dispatch_scan_fwd_bf16(const FwdParams& p, int disc, int lanes, bool vec, hipStream_t s);
+hipError_t dispatch_chunk_states_f32(const FwdParams& p, int disc, int lanes, bool vec,
+                                     hipStream_t s);
+hipError_t dispatch_chunk_states_bf16(const FwdParams& p, int disc, int lanes, bool vec,
+                                      hipStream_t s);
+inline hipError_t dispatch_scan_fwd(const FwdParams& p, int dtype, int disc, int lanes, bool vec,
+                                    hipStream_t s) {
+  return dtype == 0 ? dispatch_scan_fwd_f32(p, disc, lanes, vec, s)
+                    : dispatch_scan_fwd_bf16(p, disc, lanes, vec, s);
+}
 // Backward: chunk-state recompute, reverse adjoint scan, then reductions.
-hipError_t dispatch_chunk_states(const FwdParams& p, int dtype, int disc, int lanes, bool vec,
-                                 hipStream_t stream);
-hipError_t dispatch_scan_bwd(const BwdParams& p, int dtype, int disc, int lanes, bool vec,
-                             hipStream_t stream);
-hipError_t launch_bwd_reduce(const BwdParams& p, hipStream_t stream);
-int64_t bwd_groups(int64_t dim, int lanes);
+inline hipError_t dispatch_chunk_states(const FwdParams& p, int dtype, int disc, int lanes,
+                                        bool vec, hipStream_t s) {
+  return dtype == 0 ? dispatch_chunk_states_f32(p, disc, lanes, vec, s)
+                    : dispatch_chunk_states_bf16(p, disc, lanes, vec, s);
+}
+// The backward always spreads a channel over 16 lanes (kBwdLanes).
+constexpr int kBwdLanes = 16;
+hipError_t dispatch_scan_bwd_f32(const BwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_scan_bwd_bf16(const BwdParams& p, int disc, bool vec, hipStream_t s);
+inline hipError_t dispatch_scan_bwd(const BwdParams& p, int dtype, int disc, bool vec,
+                                    hipStream_t s) {
+  return dtype == 0 ? dispatch_scan_bwd_f32(p, disc, vec, s) : dispatch_scan_bwd_bf16(p, disc, vec, s);
+}
 hipError_t dispatch_state_update(const StepParams& p, int dtype, int disc, hipStream_t stream);
 
 }  // namespace mscan

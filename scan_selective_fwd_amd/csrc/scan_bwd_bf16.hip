@@ -1,0 +1,10 @@
+// Backward kernels for bf16 sequences (see scan_bwd_impl.hpp).
+#include "scan_bwd_impl.hpp"
+
+namespace mscan {
+
+hipError_t dispatch_scan_bwd_bf16(const BwdParams& p, int disc, bool vec, hipStream_t stream) {
+  return dispatch_bwd_t<bf16_t>(p, disc, vec, stream);
+}
+
+}  // namespace mscan

@@ -1,0 +1,10 @@
+// Backward kernels for f32 sequences (see scan_bwd_impl.hpp).
+#include "scan_bwd_impl.hpp"
+
+namespace mscan {
+
+hipError_t dispatch_scan_bwd_f32(const BwdParams& p, int disc, bool vec, hipStream_t stream) {
+  return dispatch_bwd_t<float>(p, disc, vec, stream);
+}
+
+}  // namespace mscan

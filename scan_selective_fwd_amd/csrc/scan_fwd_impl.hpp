@@ -1,0 +1,287 @@
+// Fused selective-scan forward for gfx950 (kernel template; instantiated per
+// element type in scan_fwd_{f32,bf16}.hip and, in states-only mode, in
+// scan_states_{f32,bf16}.hip).
+//
+// What is computed (chapterpal.com page on the Mamba paper, Knowl 1
+// "Selective State Space Layer (S6)", steps 3-4, with diagonal A):
+//   Abar_t = exp(delta_t A), Bbar_t = (exp(delta_t A) - 1)/A * B_t  (ZOH)
+//   h_t = Abar_t h_{t-1} + Bbar_t u_t,  y_t = C_t . h_t
+// plus the library's additions y += D u, out = y * SiLU(z), Euler Bbar.
+//
+// How (MI355X-first; the pages' fused-kernel outline -- load the parameters
+// once, discretize and scan on chip, write only y -- is the paper-graph-ui
+// summary's section 3.4 "Kernel fusion" and its chunking paragraph):
+//   * A block serves CPB channels of ONE batch row; a channel (b, d) owns R
+//     lanes of a wave and lane j owns K consecutive steps of each chunk of
+//     R*K steps.  u, delta, z are read once per lane with 16-byte loads; the
+//     B and C chunk, shared by all the block's channels, is staged once per
+//     block into an LDS tile (tile_stage.hpp); out is written once.  The
+//     expanded (B, L, D, N) Abar/Bbar/h never leave registers.
+//   * Per state index n: pass 1 discretizes the lane's K steps in registers
+//     (one v_exp_f32 per step) and folds them into the lane's affine summary
+//     (A_lane, B_lane); A_lane is exp(A * sum(delta)), one exponential per
+//     lane instead of K multiplies.  A DPP scan over the channel's R lanes
+//     (fused v_fmac/v_mul with row_shr / row_bcast sources, no LDS) turns the
+//     summaries into each lane's starting state, composed with the state
+//     carried in from the previous chunk.  Pass 2 replays the K steps from
+//     that state and accumulates y_t += C_t[n] h_t[n].
+//   * Chunks follow each other inside the block; the carried state is a
+//     register per n (the pages' "chunk boundary" carry).  The next chunk's
+//     u/delta and B/C loads are in flight while the current one computes.
+// No atomics, no workspace: the result is bitwise deterministic.
+#pragma once
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "tile_stage.hpp"
+
+namespace mscan {
+
+// K elements of a row from step t: vector loads when `full` (the whole
+// chunk lies inside the sequence and rows are 16-byte aligned), else
+// element loads with steps past L reading 0.
+template <typename T, int K>
+__device__ __forceinline__ void load_items(const T* __restrict__ row, int64_t t, int64_t L,
+                                           bool full, float (&v)[K]) {
+  if (full) {
+    Elem<T>::template load_k<K>(row + t, v);
+  } else {
+    const int64_t rem = L - t;
+    const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
+    Elem<T>::template load_k_guarded<K>(row + t, nvalid, v);
+  }
+}
+
+template <typename T, int K>
+__device__ __forceinline__ void store_items(T* __restrict__ row, int64_t t, int64_t L, bool full,
+                                            const float (&v)[K]) {
+  if (full) {
+    Elem<T>::template store_k<K>(row + t, v);
+  } else {
+    const int64_t rem = L - t;
+    const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
+    if (nvalid > 0) Elem<T>::template store_k_guarded<K>(row + t, nvalid, v);
+  }
+}
+
+// STATES = true is the backward's recompute pass: it only writes the state
+// at the start of every chunk (to p.chunk_states) and skips C, z, y and out.
+template <typename T, int R, int K, int NT, bool ZOH, bool VEC, bool STATES>
+__global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
+  constexpr int CPW = 64 / R;   // channels per wave
+  constexpr int CPB = (kBlock / 64) * CPW;
+  constexpr int TCH = R * K;    // steps per chunk
+  constexpr int TROWS = STATES ? NT : 2 * NT;
+  // The LDS tile holds two chunks of B/C rows (2 * TROWS * TCH floats): it is
+  // used for R = 16, N <= 16 (32 KB at K = 8); wider lane groups or larger N
+  // read B/C per lane from global memory (L1/L2 cached) instead.
+  constexpr bool TILE = (R == 16 && NT == 16);
+  __shared__ float4 tile_mem[2][TILE ? TROWS * TCH / 4 : 1];
+  __shared__ float a2s[CPB][NT], ias[CPB][NT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j = lane % R;
+  const int cl = wave * CPW + lane / R;       // channel slot in the block
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = blk / p.groups;
+  const int64_t grp = blk - b * p.groups;
+  const int64_t d_raw = grp * CPB + cl;
+  const bool active = d_raw < p.dim;
+  const int64_t d = active ? d_raw : p.dim - 1;
+  const int64_t c = b * p.dim + d;
+  const int N = p.N;
+  const int64_t L = p.L;
+
+  const T* __restrict__ u_row = static_cast<const T*>(p.u) + c * L;
+  const T* __restrict__ dl_row = static_cast<const T*>(p.delta) + c * L;
+  const T* __restrict__ z_row = p.z ? static_cast<const T*>(p.z) + c * L : nullptr;
+  T* __restrict__ out_row = static_cast<T*>(p.out) + c * L;
+  const T* __restrict__ B_b = static_cast<const T*>(p.B) + b * N * L;
+  const T* __restrict__ C_b = static_cast<const T*>(p.C) + b * N * L;
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const float Dd = p.D ? p.D[d] : 0.0f;
+
+  // per-channel constants: A * log2(e) and 1/A (0 where A is ~0, the ZOH limit)
+  for (int i = tid; i < CPB * NT; i += kBlock) {
+    const int ci = i / NT, n = i - ci * NT;
+    const int64_t dd = grp * CPB + ci;
+    const float a = (dd < p.dim && n < N) ? p.A[dd * N + n] : -1.0f;
+    a2s[ci][n] = a * kLog2e;
+    ias[ci][n] = __builtin_fabsf(a) < 1e-30f ? 0.0f : 1.0f / a;
+  }
+
+  float carry[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) carry[n] = (n < N && p.h0) ? p.h0[c * N + n] : 0.0f;
+
+  const int64_t nchunks = (L + TCH - 1) / TCH;
+  TileStager<T, TCH, K, NT, TILE ? TROWS : 1, kBlock> stage;
+  float nu[K], nd[K];
+  {
+    const bool full0 = VEC && TCH <= L;
+    if constexpr (TILE) {
+      stage.load(B_b, C_b, N, L, 0, full0, tid);
+      stage.store(reinterpret_cast<float*>(tile_mem[0]), N, tid);
+    }
+    load_items<T, K>(u_row, (int64_t)j * K, L, full0, nu);
+    load_items<T, K>(dl_row, (int64_t)j * K, L, full0, nd);
+  }
+  __syncthreads();
+
+  for (int64_t ch = 0; ch < nchunks; ++ch) {
+    const int buf = (int)(ch & 1);
+    const int64_t t0 = ch * TCH;
+    const int64_t tl = t0 + (int64_t)j * K;   // this lane's first step
+    const bool full = VEC && t0 + TCH <= L;
+    const bool more = ch + 1 < nchunks;
+    const bool full_next = VEC && t0 + 2 * TCH <= L;
+    const int64_t rem = L - tl;
+    const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
+    if constexpr (STATES) {
+      if (active && j == 0) {
+        float* dst = p.chunk_states + (c * nchunks + ch) * N;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          if (n < N) dst[n] = carry[n];
+      }
+    }
+    if constexpr (TILE) {
+      if (more) stage.load(B_b, C_b, N, L, t0 + TCH, full_next, tid);
+    }
+
+    float uv[K], dt[K], y[K], zv[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      uv[k] = nu[k];
+      dt[k] = nd[k];
+    }
+    if (more) {
+      load_items<T, K>(u_row, tl + TCH, L, full_next, nu);
+      load_items<T, K>(dl_row, tl + TCH, L, full_next, nd);
+    }
+    if constexpr (!STATES) {
+      if (z_row) load_items<T, K>(z_row, tl, L, full, zv);
+    }
+    float dsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float r = dt[k] + bias;
+      float s = p.softplus ? softplus(r) : r;
+      s = (k < nvalid) ? s : 0.0f;     // steps past L are the identity map
+      dt[k] = s;
+      dsum += s;
+      y[k] = Dd * uv[k];
+      if constexpr (!ZOH) uv[k] = s * uv[k];   // Euler: Bbar u = B (delta u)
+    }
+
+    const float* tB = reinterpret_cast<const float*>(tile_mem[buf]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (n < N) {
+        const float a2 = a2s[cl][n];
+        float Bv[K], a[K], beta[K];
+        if constexpr (TILE) tile_read<K>(tB + n * TCH, j, Bv);
+        else load_items<T, K>(B_b + (int64_t)n * L, tl, L, full, Bv);
+        float agg = 0.0f;
+        if constexpr (ZOH) {
+          const float ia = ias[cl][n];
+          if (__builtin_amdgcn_ballot_w64(ia == 0.0f) == 0) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+              a[k] = fast_exp2(dt[k] * a2);
+              const float q = Bv[k] * (uv[k] * ia);
+              beta[k] = __builtin_fmaf(a[k], q, -q);     // (Abar - 1)/A * B * u
+              agg = __builtin_fmaf(a[k], agg, beta[k]);
+            }
+          } else {
+            // some channel of this wave has A == 0: (e^{dA}-1)/A -> delta
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+              a[k] = fast_exp2(dt[k] * a2);
+              const float coef = ia == 0.0f ? dt[k] : (a[k] - 1.0f) * ia;
+              beta[k] = coef * Bv[k] * uv[k];
+              agg = __builtin_fmaf(a[k], agg, beta[k]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            a[k] = fast_exp2(dt[k] * a2);
+            beta[k] = Bv[k] * uv[k];
+            agg = __builtin_fmaf(a[k], agg, beta[k]);
+          }
+        }
+        float Ag = fast_exp2(a2 * dsum);
+        affine_scan_inclusive_fused<R>(Ag, agg);
+        const float hend = __builtin_fmaf(Ag, carry[n], agg);   // state after this lane's steps
+        if constexpr (!STATES) {
+          float Cv[K];
+          if constexpr (TILE) tile_read<K>(tB + (NT + n) * TCH, j, Cv);
+          else load_items<T, K>(C_b + (int64_t)n * L, tl, L, full, Cv);
+          float h = group_shift_right<R>(hend, carry[n]);       // state before them
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            h = __builtin_fmaf(a[k], h, beta[k]);
+            y[k] = __builtin_fmaf(Cv[k], h, y[k]);
+          }
+        }
+        carry[n] = group_last<R>(hend);                         // state after the chunk
+      }
+      mem_fence_compiler();
+    }
+
+    if constexpr (!STATES) {
+      if (z_row) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) y[k] *= silu(zv[k]);
+      }
+      if (active) store_items<T, K>(out_row, tl, L, full, y);
+    }
+    if constexpr (TILE) {
+      if (more) stage.store(reinterpret_cast<float*>(tile_mem[buf ^ 1]), N, tid);
+      __syncthreads();
+    }
+  }
+
+  if (!STATES && active && j == 0 && p.last_state) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      if (n < N) p.last_state[c * N + n] = carry[n];
+  }
+}
+
+template <typename T, int R, int K, int NT, bool ZOH, bool VEC, bool STATES>
+static hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
+  const int64_t nblocks = p.batch * p.groups;
+  hipLaunchKernelGGL((scan_fwd_kernel<T, R, K, NT, ZOH, VEC, STATES>), dim3((unsigned)nblocks),
+                     dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+// N <= 16 takes the NT = 16 kernel, 16 < N <= 64 the NT = 64 kernel.
+template <typename T, int R, int K, bool ZOH, bool STATES>
+static hipError_t fwd_nv(const FwdParams& p, bool vec, hipStream_t s) {
+  if (p.N <= 16)
+    return vec ? launch_fwd<T, R, K, 16, ZOH, true, STATES>(p, s)
+               : launch_fwd<T, R, K, 16, ZOH, false, STATES>(p, s);
+  return vec ? launch_fwd<T, R, K, 64, ZOH, true, STATES>(p, s)
+             : launch_fwd<T, R, K, 64, ZOH, false, STATES>(p, s);
+}
+
+template <typename T, int K, bool STATES>
+static hipError_t dispatch_fwd_t(const FwdParams& p, int disc, int lanes, bool vec,
+                                 hipStream_t s) {
+  const bool zoh = disc == 0;
+  switch (lanes) {
+    case 16:
+      return zoh ? fwd_nv<T, 16, K, true, STATES>(p, vec, s) : fwd_nv<T, 16, K, false, STATES>(p, vec, s);
+    case 32:
+      return zoh ? fwd_nv<T, 32, K, true, STATES>(p, vec, s) : fwd_nv<T, 32, K, false, STATES>(p, vec, s);
+    default:
+      return zoh ? fwd_nv<T, 64, K, true, STATES>(p, vec, s) : fwd_nv<T, 64, K, false, STATES>(p, vec, s);
+  }
+}
+
+}  // namespace mscan

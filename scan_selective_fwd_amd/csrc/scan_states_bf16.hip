@@ -1,0 +1,12 @@
+// The backward's state-recompute pass for bf16 sequences: the forward kernel
+// template in states-only mode with the backward's chunk length.
+#include "scan_fwd_impl.hpp"
+
+namespace mscan {
+
+hipError_t dispatch_chunk_states_bf16(const FwdParams& p, int disc, int lanes, bool vec,
+                                      hipStream_t stream) {
+  return dispatch_fwd_t<bf16_t, kItemsBwd, true>(p, disc, lanes, vec, stream);
+}
+
+}  // namespace mscan

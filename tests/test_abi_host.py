@@ -60,9 +60,13 @@ def test_workspace_queries(lib):
     assert n % 256 == 0
     assert lib.mamba_scan_bwd_workspace_size(2, 5120, 65, 2048, 1) == 2 ** 64 - 1
     assert lib.mamba_scan_bwd_workspace_size(0, 5120, 16, 2048, 1) == 2 ** 64 - 1
-    for lanes in (16, 32, 64):
-        assert lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, lanes) > 0
-    assert lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 8) == 2 ** 64 - 1
+    # the backward spreads a channel over 16 lanes: 0 (default) and 16 only
+    n16 = lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 16)
+    assert n16 > 0 and n16 == lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 0)
+    # the workspace holds the state at each 128-step chunk start: (2*64) * 4 * 16 floats
+    assert n16 == 2 * 64 * 4 * 16 * 4
+    for lanes in (8, 32, 64):
+        assert lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, lanes) == 2 ** 64 - 1
 
 
 P = 4096  # a 16-byte aligned fake address; never dereferenced (calls fail first)
