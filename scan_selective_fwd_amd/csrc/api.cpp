@@ -52,9 +52,11 @@ mamba_status check_sizes(mamba_dtype dt, int disc, int64_t batch, int64_t dim, i
   return MAMBA_OK;
 }
 
+// Backward workspace: the chunk-start states (nchannels, nchunks, dstate)
+// float32, then one int flag per block.
 struct BwdLayout {
   int64_t nchunks, groups;
-  size_t total;   // bytes: the chunk-start states (nchannels, nchunks, dstate) float32
+  size_t off_flags, total;
 };
 
 BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
@@ -62,7 +64,8 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen)
   const int64_t tch = (int64_t)mscan::kBwdLanes * kItemsBwd;
   w.nchunks = (seqlen + tch - 1) / tch;
   w.groups = mscan::channel_groups(dim, mscan::kBwdLanes);
-  w.total = round_up((size_t)(batch * dim) * (size_t)w.nchunks * (size_t)dstate * 4);
+  w.off_flags = round_up((size_t)(batch * dim) * (size_t)w.nchunks * (size_t)dstate * 4);
+  w.total = w.off_flags + round_up((size_t)(batch * w.groups) * 4);
   return w;
 }
 
@@ -201,6 +204,7 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   p.h0 = h0; p.dout = dout; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB; p.dC = dC;
   p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0;
   p.chunk_states = states;
+  p.deferred = reinterpret_cast<int*>(static_cast<char*>(workspace) + w.off_flags);
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.nchunks = w.nchunks; p.groups = w.groups; p.N = (int)dstate;
   p.softplus = delta_softplus ? 1 : 0;

@@ -123,6 +123,36 @@ __device__ __forceinline__ void affine_suffix_scan_row_fused(float& A, float& B)
       : "+v"(A), "+v"(B));
 }
 
+// Sum over each 16-lane row, result in the row's lane 15 (the other lanes
+// hold partial sums): an inclusive DPP add-scan with row_shr sources.
+__device__ __forceinline__ float row_sum_to_last(float v) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      : "+v"(v));
+  return v;
+}
+
+// One stage-1 exchange of the row reduce-scatter: for items (x, y) of the
+// four 16-lane rows returns, in rows 0 and 2, x summed over the row pair
+// (0,1) or (2,3), and in rows 1 and 3 the same for y.
+__device__ __forceinline__ float rs_pair16(float x, float y) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Stage 2: from two stage-1 results, rows 0/1 get the first summed over all
+// four rows, rows 2/3 the second.
+__device__ __forceinline__ float rs_pair32(float x, float y) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Compiler-level fence: memory operations are not moved across it.  Used
 // between the iterations of unrolled loops so that each iteration's loads
 // stay with it instead of being hoisted en masse.
@@ -157,6 +187,28 @@ template <int K>
 __device__ __forceinline__ int tile_granule(int g) {
   constexpr int GPL = K / 4;
   return g ^ ((g >> 4) & (GPL - 1));
+}
+
+// Carry hand-off between chunks without a broadcast: the state leaving the
+// last lane of a channel's group is moved to the group's FIRST lane (the only
+// lane that uses it: it is folded into lane 0's summary before the next
+// scan).  R = 16: DPP row_ror:1; R = 64: wave_ror:1; R = 32: two readlanes.
+template <int R>
+__device__ __forceinline__ float last_to_first(float v) {
+  if constexpr (R == 16) {
+    return dpp_mov<0x121 /*row_ror:1*/>(v, v);
+  } else if constexpr (R == 64) {
+    return dpp_mov<0x13C /*wave_ror:1*/>(v, v);
+  } else {
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    return (__lane_id() & 32) ? hi : lo;
+  }
+}
+
+// Reverse hand-off for 16-lane rows: lane 0's value moves to lane 15.
+__device__ __forceinline__ float row_first_to_last(float v) {
+  return dpp_mov<0x12F /*row_ror:15*/>(v, v);
 }
 
 // Value of lane R-1 of this lane's group, broadcast to the whole group.

@@ -54,6 +54,7 @@ struct BwdParams {
   float* dbias;            // nullable
   float* dh0;              // nullable
   const float* chunk_states;  // workspace: (nchannels, nchunks, N) states at chunk starts
+  int* deferred;           // workspace: one flag per block (blocks with A ~ 0, ZOH)
   int64_t batch, dim, L;
   int64_t nchannels;
   int64_t nchunks;         // chunks of 16*kItemsBwd steps

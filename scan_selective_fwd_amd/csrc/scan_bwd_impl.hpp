@@ -45,7 +45,11 @@ __device__ __forceinline__ float row_shift_left(float v, float last) {
   return dpp_mov<0x101 /*row_shl:1*/>(last, v);
 }
 
-template <typename T, int NT, bool ZOH, bool VEC>
+// TINY = false: the fast kernel.  A block in which some channel has A ~ 0
+// (ZOH only) sets its flag in p.deferred and exits without computing; the
+// TINY = true kernel, launched right after on the same stream, computes
+// exactly the flagged blocks with the A = 0 limits of the ZOH coefficients.
+template <typename T, int NT, bool ZOH, bool VEC, bool TINY>
 __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
   constexpr int R = 16;
   constexpr int K = kItemsBwd;
@@ -54,10 +58,14 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
   constexpr int CPB = (kBlock / 64) * CPW;
   constexpr int TCH = R * K;
   constexpr bool TILE = (NT == 16);
-  __shared__ float4 tile_mem[2][TILE ? 2 * NT * TCH / 4 : 1];
-  __shared__ float hst[2][CPB][NT];          // chunk-start states
-  __shared__ float acc[2][NT][TCH];          // dB, dC summed over the block's channels
-  __shared__ float a2s[CPB][NT], ias[CPB][NT];
+  constexpr int SREG = (CPB * NT + kBlock - 1) / kBlock;
+  // single-buffered: refilled between the two barriers that close a chunk
+  __shared__ float4 tile_mem[TILE ? 2 * NT * TCH / 4 : 1];   // B, C rows of the chunk
+  __shared__ float hst[CPB][NT];        // forward state at the chunk start
+  __shared__ float gcs[CPB][NT];        // adjoint carried from the later chunk
+  __shared__ float dAs[CPB][NT];        // dA of each channel, this batch row
+  __shared__ float acc[2][NT][TCH];     // dB, dC of the chunk summed over the block
+  __shared__ float as_[CPB][NT], a2s[CPB][NT], ias[CPB][NT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,19 +93,26 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
 
+  bool my_tiny = false;
   for (int i = tid; i < CPB * NT; i += kBlock) {
     const int ci = i / NT, n = i - ci * NT;
     const int64_t dd = grp * CPB + ci;
-    const float a = (dd < p.dim && n < N) ? p.A[dd * N + n] : -1.0f;
+    const bool real = dd < p.dim && n < N;
+    const float a = real ? p.A[dd * N + n] : -1.0f;
+    const bool tiny = __builtin_fabsf(a) < 1e-30f;
+    my_tiny |= real && tiny;
+    as_[ci][n] = a;
     a2s[ci][n] = a * kLog2e;
-    ias[ci][n] = __builtin_fabsf(a) < 1e-30f ? 0.0f : 1.0f / a;
+    ias[ci][n] = tiny ? 0.0f : 1.0f / a;
+    gcs[ci][n] = 0.0f;     // no gradient flows into the final state
+    dAs[ci][n] = 0.0f;
   }
   for (int i = tid; i < 2 * NT * TCH; i += kBlock) (&acc[0][0][0])[i] = 0.0f;
 
   // chunk-start states of this block's channels for chunk `ch`
-  auto load_states = [&](int64_t ch, float (&dst)[(CPB * NT + kBlock - 1) / kBlock]) {
+  auto load_states = [&](int64_t ch, float (&dst)[SREG]) {
 #pragma unroll
-    for (int r = 0; r < (CPB * NT + kBlock - 1) / kBlock; ++r) {
+    for (int r = 0; r < SREG; ++r) {
       const int i = r * kBlock + tid;
       const int ci = i / NT, n = i - ci * NT;
       const int64_t dd = grp * CPB + ci;
@@ -105,47 +120,46 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
                    ? p.chunk_states[((b * p.dim + dd) * nchunks + ch) * N + n] : 0.0f;
     }
   };
-  auto store_states = [&](int bufi, const float (&src)[(CPB * NT + kBlock - 1) / kBlock]) {
+  auto store_states = [&](const float (&src)[SREG]) {
 #pragma unroll
-    for (int r = 0; r < (CPB * NT + kBlock - 1) / kBlock; ++r) {
+    for (int r = 0; r < SREG; ++r) {
       const int i = r * kBlock + tid;
-      if (i < CPB * NT) (&hst[bufi][0][0])[i] = src[r];
+      if (i < CPB * NT) (&hst[0][0])[i] = src[r];
     }
   };
 
   TileStager<T, TCH, K, NT, TILE ? 2 * NT : 1, kBlock> stage;
-  float hreg[(CPB * NT + kBlock - 1) / kBlock];
+  float hreg[SREG];
   {
     const int64_t last = nchunks - 1;
     const bool full_last = VEC && last * TCH + TCH <= L;
     if constexpr (TILE) {
       stage.load(B_b, C_b, N, L, last * TCH, full_last, tid);
-      stage.store(reinterpret_cast<float*>(tile_mem[0]), N, tid);
+      stage.store(reinterpret_cast<float*>(tile_mem), N, tid);
     }
     load_states(last, hreg);
-    store_states(0, hreg);
+    store_states(hreg);
   }
-  __syncthreads();
+  // barrier for the LDS fills; also: does any channel of the block have A ~ 0?
+  const bool any_tiny = __syncthreads_or(my_tiny);
+  if constexpr (ZOH) {
+    if constexpr (!TINY) {
+      if (tid == 0) p.deferred[blockIdx.x] = any_tiny ? 1 : 0;
+      if (any_tiny) return;            // block-uniform: the TINY kernel takes it
+    } else {
+      if (p.deferred[blockIdx.x] == 0) return;
+    }
+  }
 
-  float gcarry[NT];   // adjoint entering each chunk from the later one
-  float dA1[NT];      // this lane's share of dA[d, n]
-#pragma unroll
-  for (int n = 0; n < NT; ++n) gcarry[n] = dA1[n] = 0.0f;
   float dD_acc = 0.0f, db_acc = 0.0f;
 
   for (int64_t ch = nchunks - 1; ch >= 0; --ch) {
-    const int buf = (int)((nchunks - 1 - ch) & 1);
     const int64_t t0 = ch * TCH;
     const int64_t tl = t0 + (int64_t)j * K;
     const bool full = VEC && t0 + TCH <= L;
     const int64_t rem = L - tl;
     const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
-    if (ch > 0) {
-      if constexpr (TILE) stage.load(B_b, C_b, N, L, t0 - TCH, VEC, tid);   // earlier chunks are full
-      load_states(ch - 1, hreg);
-    }
-
-    float uv[K], dt[K], gy[K], yv[K], du[K], gdt[K], sig[K];
+    float uv[K], dt[K], gy[K], yv[K], du[K], gdt[K];
     {
       float raw[K], dov[K];
       load_items<T, K>(u_row, tl, L, full, uv);
@@ -155,7 +169,6 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
       for (int k = 0; k < K; ++k) {
         const float r = raw[k] + bias;
         const float s = p.softplus ? softplus(r) : r;
-        sig[k] = p.softplus ? sigmoid(r) : 1.0f;
         dt[k] = (k < nvalid) ? s : 0.0f;
         gy[k] = dov[k];
       }
@@ -169,6 +182,9 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
     float dsum = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
+      // a channel slot past `dim` contributes nothing to the reduced gradients
+      uv[k] = active ? uv[k] : 0.0f;
+      gy[k] = active ? gy[k] : 0.0f;
       dsum += dt[k];
       yv[k] = Dd * uv[k];
       du[k] = Dd * gy[k];
@@ -176,15 +192,13 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
       dD_acc = __builtin_fmaf(gy[k], uv[k], dD_acc);
     }
 
-    const float* tB = reinterpret_cast<const float*>(tile_mem[buf]);
+    const float* tB = reinterpret_cast<const float*>(tile_mem);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       if (n < N) {
-        const float An = p.A[d * N + n];
-        const float a2 = a2s[cl][n];
-        const float ia = ias[cl][n];
-        const bool tiny = ZOH && ia == 0.0f;
-        const bool any_tiny = __builtin_amdgcn_ballot_w64(tiny) != 0;
+        const float An = as_[cl][n], a2 = a2s[cl][n], ia = ias[cl][n];
+        const float h_in = hst[cl][n];
+        const float gc = gcs[cl][n];
         float Bv[K], Cv[K];
         if constexpr (TILE) {
           tile_read<K>(tB + n * TCH, j, Bv);
@@ -193,6 +207,9 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
           load_items<T, K>(B_b + (int64_t)n * L, tl, L, full, Bv);
           load_items<T, K>(C_b + (int64_t)n * L, tl, L, full, Cv);
         }
+        // TINY: where A ~ 0 (1/A stored as 0) the ZOH coefficient
+        // (e^{dA}-1)/A takes its limit delta
+        const bool tiny = TINY && ia == 0.0f;
 
         // ---- forward replay of this chunk for state index n ----
         float a[K], beta[K], hv[K];
@@ -200,14 +217,12 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           a[k] = fast_exp2(dt[k] * a2);
-          if constexpr (ZOH) {
-            if (!any_tiny) {
-              const float q = Bv[k] * (uv[k] * ia);
-              beta[k] = __builtin_fmaf(a[k], q, -q);
-            } else {
-              const float coef = tiny ? dt[k] : (a[k] - 1.0f) * ia;
-              beta[k] = coef * Bv[k] * uv[k];
-            }
+          if constexpr (ZOH && !TINY) {
+            const float q = Bv[k] * (uv[k] * ia);
+            beta[k] = __builtin_fmaf(a[k], q, -q);
+          } else if constexpr (ZOH) {
+            const float coef = tiny ? dt[k] : (a[k] - 1.0f) * ia;
+            beta[k] = coef * Bv[k] * uv[k];
           } else {
             beta[k] = dt[k] * Bv[k] * uv[k];
           }
@@ -215,10 +230,9 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
         }
         const float Alane = fast_exp2(a2 * dsum);
         float Ag = Alane;
+        agg = (j == 0) ? __builtin_fmaf(Ag, h_in, agg) : agg;   // chunk-start state enters lane 0
         affine_scan_inclusive_fused<R>(Ag, agg);
-        const float h_in = hst[buf][cl][n];
-        const float hend = __builtin_fmaf(Ag, h_in, agg);
-        const float hstart = group_shift_right<R>(hend, h_in);
+        const float hstart = group_shift_right<R>(agg, h_in);
         {
           float h = hstart;
 #pragma unroll
@@ -230,80 +244,102 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
         }
 
         // ---- reverse adjoint: g_t = Abar_t (g_{t+1} + C_t gy_t) ----
-        float e[K];
         float gagg = 0.0f;
 #pragma unroll
-        for (int k = K - 1; k >= 0; --k) {
-          e[k] = Cv[k] * gy[k];
-          gagg = a[k] * (e[k] + gagg);
-        }
+        for (int k = K - 1; k >= 0; --k) gagg = a[k] * __builtin_fmaf(Cv[k], gy[k], gagg);
         float As = Alane;
+        gagg = (j == R - 1) ? __builtin_fmaf(As, gc, gagg) : gagg;   // later chunk enters lane 15
         affine_suffix_scan_row_fused(As, gagg);
-        const float gstart = __builtin_fmaf(As, gcarry[n], gagg);   // leaving this lane leftwards
-        float g = row_shift_left(gstart, gcarry[n]);                 // entering from the right
-        gcarry[n] = group_first<R>(gstart);
+        float g = row_shift_left(gagg, gc);                 // adjoint entering each lane from the right
+        const float gc_new = row_first_to_last(gagg);       // leaving lane 0, now in lane 15
+        if (j == R - 1) gcs[cl][n] = gc_new;
 
-        float dBv[K], dCv[K];
-        float dA2 = 0.0f;
+        // ---- gradient terms, with dB/dC summed over the wave's 4 channels
+        //      as soon as each pair of steps is done ----
+        float dAp = 0.0f, dA2 = 0.0f;
+        float pB = 0.0f, pC = 0.0f, sB[4], sC[4], TB[2], TC[2];
 #pragma unroll
         for (int k = K - 1; k >= 0; --k) {
-          const float gh = e[k] + g;                      // dL/dh_t
+          const float gh = __builtin_fmaf(Cv[k], gy[k], g);   // dL/dh_t
           const float hprev = (k == 0) ? hstart : hv[k - 1];
           const float P = gh * a[k];
           const float gu = gh * uv[k];
           float coef, dbdd;
           if constexpr (ZOH) {
-            coef = __builtin_fmaf(a[k], ia, -ia);                  // (Abar - 1)/A
-            if (any_tiny && tiny) coef = dt[k];                    // its limit at A = 0
-            dbdd = a[k] * Bv[k];                                   // dBbar/ddelta
+            coef = __builtin_fmaf(a[k], ia, -ia);         // (Abar - 1)/A
+            if constexpr (TINY) coef = tiny ? dt[k] : coef;
+            dbdd = a[k] * Bv[k];                          // dBbar/ddelta
           } else {
             coef = dt[k];
             dbdd = Bv[k];
           }
+          const float Ph = P * hprev;
           // ddelta: gh * (hprev * A * Abar + u * dBbar/ddelta)
-          gdt[k] = __builtin_fmaf(P * hprev, An, gdt[k]);
-          gdt[k] = __builtin_fmaf(gu, dbdd, gdt[k]);
-          // dA: gh * hprev * delta * Abar + gh * u * dBbar/dA, where the ZOH
-          // dBbar/dA = (delta*Abar*B - Bbar)/A (limit delta^2 B / 2 at A = 0)
-          // (1/A is stored as 0 where A ~ 0, which drops the non-limit terms there)
-          dA1[n] = __builtin_fmaf(dt[k], P * hprev, dA1[n]);
+          gdt[k] = __builtin_fmaf(Ph, An, __builtin_fmaf(gu, dbdd, gdt[k]));
+          // dA: gh * hprev * delta * Abar + gh * u * dBbar/dA with the ZOH
+          // dBbar/dA = (delta*Abar*B - Bbar)/A, limit delta^2 B / 2 at A = 0
+          // (1/A = 0 there drops the other terms)
+          dAp = __builtin_fmaf(dt[k], Ph, dAp);
           if constexpr (ZOH) {
-            dA1[n] = __builtin_fmaf(gu * dt[k], dbdd * ia, dA1[n]);
+            float t = dbdd * ia;
+            if constexpr (TINY) t = tiny ? 0.5f * dt[k] * Bv[k] : t;
+            dAp = __builtin_fmaf(gu * dt[k], t, dAp);
             dA2 = __builtin_fmaf(gh, beta[k], dA2);
-            if (any_tiny && tiny) dA1[n] = __builtin_fmaf(gu, 0.5f * dt[k] * dt[k] * Bv[k], dA1[n]);
           }
           const float s = gh * coef;
           du[k] = __builtin_fmaf(s, Bv[k], du[k]);
-          dBv[k] = active ? s * uv[k] : 0.0f;
-          dCv[k] = active ? gy[k] * hv[k] : 0.0f;
+          const float vB = s * uv[k];
+          const float vC = gy[k] * hv[k];
+          if (k & 1) {
+            pB = vB;
+            pC = vC;
+          } else {
+            sB[k / 2] = rs_pair16(vB, pB);
+            sC[k / 2] = rs_pair16(vC, pC);
+            if (k == 4) {
+              TB[1] = rs_pair32(sB[2], sB[3]);
+              TC[1] = rs_pair32(sC[2], sC[3]);
+            } else if (k == 0) {
+              TB[0] = rs_pair32(sB[0], sB[1]);
+              TC[0] = rs_pair32(sC[0], sC[1]);
+            }
+          }
           g = P;
         }
-        if constexpr (ZOH) dA1[n] = __builtin_fmaf(-dA2, ia, dA1[n]);
-
-        // ---- dB/dC: sum over the wave's 4 channels, then over the block ----
-        float rb[2], rc[2];
-        reduce_scatter_rows8(dBv, rb);
-        reduce_scatter_rows8(dCv, rc);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < 2; ++m) {   // lane (row r, j) owns step j*K + 4m + r
           const int tt = j * K + 4 * m + row;
-          atomicAdd(&acc[0][n][tt], rb[m]);
-          atomicAdd(&acc[1][n][tt], rc[m]);
+          atomicAdd(&acc[0][n][tt], TB[m]);
+          atomicAdd(&acc[1][n][tt], TC[m]);
         }
+        if constexpr (ZOH) dAp = __builtin_fmaf(-dA2, ia, dAp);
+        dAp = row_sum_to_last(dAp);
+        if (j == R - 1) dAs[cl][n] += dAp;
       }
       mem_fence_compiler();
     }
 
-    // ---- per-step outputs ----
-    float ddl[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      ddl[k] = (k < nvalid) ? gdt[k] * sig[k] : 0.0f;
-      db_acc += ddl[k];
+    // the earlier chunk's B/C rows and states: issued here (not at the chunk
+    // start) so their registers are not live across the state-index loop
+    if (ch > 0) {
+      if constexpr (TILE) stage.load(B_b, C_b, N, L, t0 - TCH, VEC, tid);   // earlier chunks are full
+      load_states(ch - 1, hreg);
     }
-    if (active) {
-      store_items<float, K>(p.du + c * L, tl, L, full, du);
-      store_items<float, K>(p.ddelta + c * L, tl, L, full, ddl);
+
+    // ---- per-step outputs ----
+    {
+      float raw[K], ddl[K];
+      load_items<T, K>(dl_row, tl, L, full, raw);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float sg = p.softplus ? sigmoid(raw[k] + bias) : 1.0f;   // softplus'
+        ddl[k] = (k < nvalid) ? gdt[k] * sg : 0.0f;
+        db_acc += ddl[k];
+      }
+      if (active) {
+        store_items<float, K>(p.du + c * L, tl, L, full, du);
+        store_items<float, K>(p.ddelta + c * L, tl, L, full, ddl);
+      }
     }
     if (z_row) {
       float zv[K], dov[K], dzv[K];
@@ -316,12 +352,9 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
       }
       if (active) store_items<float, K>(p.dz + c * L, tl, L, full, dzv);
     }
-    if (ch > 0) {
-      if constexpr (TILE) stage.store(reinterpret_cast<float*>(tile_mem[buf ^ 1]), N, tid);
-      store_states(buf ^ 1, hreg);
-    }
     __syncthreads();
-    // flush this chunk's dB/dC sums (all waves have added them) and clear
+    // all waves are done with this chunk: flush its dB/dC sums, clear them,
+    // and refill the tile and the chunk-start states with the earlier chunk
     for (int i = tid; i < 2 * NT * TCH; i += kBlock) {
       const int which = i / (NT * TCH);
       const int rest = i - which * NT * TCH;
@@ -332,21 +365,25 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
       const int64_t t = t0 + tt;
       if (n < N && t < L) unsafeAtomicAdd((which ? p.dC : p.dB) + (b * N + n) * L + t, v);
     }
+    if (ch > 0) {
+      if constexpr (TILE) stage.store(reinterpret_cast<float*>(tile_mem), N, tid);
+      store_states(hreg);
+    }
     __syncthreads();
   }
 
-  // ---- per-channel reductions over the channel's lanes ----
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    if (n < N) {
-      const float s = group_sum<R>(dA1[n]);
-      if (active && j == 0) unsafeAtomicAdd(p.dA + d * N + n, s);
-      if (active && j == 0 && p.dh0) p.dh0[c * N + n] = gcarry[n];
+  // ---- per-channel results: dh0, dA (over batch rows), dD, ddelta_bias ----
+  for (int i = tid; i < CPB * NT; i += kBlock) {
+    const int ci = i / NT, n = i - ci * NT;
+    const int64_t dd = grp * CPB + ci;
+    if (dd < p.dim && n < N) {
+      if (p.dh0) p.dh0[(b * p.dim + dd) * N + n] = gcs[ci][n];
+      unsafeAtomicAdd(p.dA + dd * N + n, dAs[ci][n]);
     }
   }
-  const float sD = group_sum<R>(dD_acc);
-  const float sb = group_sum<R>(db_acc);
-  if (active && j == 0) {
+  const float sD = row_sum_to_last(dD_acc);
+  const float sb = row_sum_to_last(db_acc);
+  if (active && j == R - 1) {
     if (p.dD) unsafeAtomicAdd(p.dD + d, sD);
     if (p.dbias) unsafeAtomicAdd(p.dbias + d, sb);
   }
@@ -374,8 +411,12 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(const BwdParams p)
 template <typename T, int NT, bool ZOH, bool VEC>
 static hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   const int64_t nblocks = p.batch * p.groups;
-  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC>), dim3((unsigned)nblocks), dim3(kBlock), 0,
-                     s, p);
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, false>), dim3((unsigned)nblocks),
+                     dim3(kBlock), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !ZOH) return e;
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, true>), dim3((unsigned)nblocks),
+                     dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 

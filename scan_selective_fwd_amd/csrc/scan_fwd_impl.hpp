@@ -35,6 +35,8 @@
 #include "kernels.hpp"
 #include "tile_stage.hpp"
 
+#include <type_traits>
+
 namespace mscan {
 
 // K elements of a row from step t: vector loads when `full` (the whole
@@ -104,17 +106,23 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
   const float Dd = p.D ? p.D[d] : 0.0f;
 
   // per-channel constants: A * log2(e) and 1/A (0 where A is ~0, the ZOH limit)
+  bool my_tiny = false;
   for (int i = tid; i < CPB * NT; i += kBlock) {
     const int ci = i / NT, n = i - ci * NT;
     const int64_t dd = grp * CPB + ci;
-    const float a = (dd < p.dim && n < N) ? p.A[dd * N + n] : -1.0f;
+    const bool real = dd < p.dim && n < N;
+    const float a = real ? p.A[dd * N + n] : -1.0f;
+    const bool tiny = __builtin_fabsf(a) < 1e-30f;
+    my_tiny |= real && tiny;
     a2s[ci][n] = a * kLog2e;
-    ias[ci][n] = __builtin_fabsf(a) < 1e-30f ? 0.0f : 1.0f / a;
+    ias[ci][n] = tiny ? 0.0f : 1.0f / a;
   }
 
-  float carry[NT];
+  // Carried state per n.  Only the FIRST lane of each channel's group holds
+  // it (it is folded into that lane's summary before the scan).
+  float cr[NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) carry[n] = (n < N && p.h0) ? p.h0[c * N + n] : 0.0f;
+  for (int n = 0; n < NT; ++n) cr[n] = (n < N && p.h0) ? p.h0[c * N + n] : 0.0f;
 
   const int64_t nchunks = (L + TCH - 1) / TCH;
   TileStager<T, TCH, K, NT, TILE ? TROWS : 1, kBlock> stage;
@@ -128,75 +136,98 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
     load_items<T, K>(u_row, (int64_t)j * K, L, full0, nu);
     load_items<T, K>(dl_row, (int64_t)j * K, L, full0, nd);
   }
-  __syncthreads();
+  // barrier for the LDS fills; also: does any channel of the block have A ~ 0?
+  const bool any_tiny = __syncthreads_or(my_tiny);
 
-  for (int64_t ch = 0; ch < nchunks; ++ch) {
-    const int buf = (int)(ch & 1);
-    const int64_t t0 = ch * TCH;
-    const int64_t tl = t0 + (int64_t)j * K;   // this lane's first step
-    const bool full = VEC && t0 + TCH <= L;
-    const bool more = ch + 1 < nchunks;
-    const bool full_next = VEC && t0 + 2 * TCH <= L;
-    const int64_t rem = L - tl;
-    const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
-    if constexpr (STATES) {
-      if (active && j == 0) {
-        float* dst = p.chunk_states + (c * nchunks + ch) * N;
+  {
+    for (int64_t ch = 0; ch < nchunks; ++ch) {
+      const int buf = (int)(ch & 1);
+      const int64_t t0 = ch * TCH;
+      const int64_t tl = t0 + (int64_t)j * K;   // this lane's first step
+      const bool full = VEC && t0 + TCH <= L;
+      const bool more = ch + 1 < nchunks;
+      const bool full_next = VEC && t0 + 2 * TCH <= L;
+      const int64_t rem = L - tl;
+      const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
+      if constexpr (STATES) {
+        if (active && j == 0) {
+          float* dst = p.chunk_states + (c * nchunks + ch) * N;
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-          if (n < N) dst[n] = carry[n];
+          for (int n = 0; n < NT; ++n)
+            if (n < N) dst[n] = cr[n];
+        }
       }
-    }
-    if constexpr (TILE) {
-      if (more) stage.load(B_b, C_b, N, L, t0 + TCH, full_next, tid);
-    }
+      if constexpr (TILE) {
+        if (more) stage.load(B_b, C_b, N, L, t0 + TCH, full_next, tid);
+      }
 
-    float uv[K], dt[K], y[K], zv[K];
+      float uv[K], dt[K], y[K], zv[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      uv[k] = nu[k];
-      dt[k] = nd[k];
-    }
-    if (more) {
-      load_items<T, K>(u_row, tl + TCH, L, full_next, nu);
-      load_items<T, K>(dl_row, tl + TCH, L, full_next, nd);
-    }
-    if constexpr (!STATES) {
-      if (z_row) load_items<T, K>(z_row, tl, L, full, zv);
-    }
-    float dsum = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        uv[k] = nu[k];
+        dt[k] = nd[k];
+      }
+      if (more) {
+        load_items<T, K>(u_row, tl + TCH, L, full_next, nu);
+        load_items<T, K>(dl_row, tl + TCH, L, full_next, nd);
+      }
+      if constexpr (!STATES) {
+        if (z_row) load_items<T, K>(z_row, tl, L, full, zv);
+      }
+      float dsum = 0.0f;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const float r = dt[k] + bias;
-      float s = p.softplus ? softplus(r) : r;
-      s = (k < nvalid) ? s : 0.0f;     // steps past L are the identity map
-      dt[k] = s;
-      dsum += s;
-      y[k] = Dd * uv[k];
-      if constexpr (!ZOH) uv[k] = s * uv[k];   // Euler: Bbar u = B (delta u)
-    }
+      for (int k = 0; k < K; ++k) {
+        const float r = dt[k] + bias;
+        float s = p.softplus ? softplus(r) : r;
+        s = (k < nvalid) ? s : 0.0f;     // steps past L are the identity map
+        dt[k] = s;
+        dsum += s;
+        y[k] = Dd * uv[k];
+        if constexpr (!ZOH) uv[k] = s * uv[k];   // Euler: Bbar u = B (delta u)
+      }
 
-    const float* tB = reinterpret_cast<const float*>(tile_mem[buf]);
+      const float* tB = reinterpret_cast<const float*>(tile_mem[buf]);
+      // operands of state index n + 1 are read while n is computed
+      // B of state index n + 1 is read while n is computed; C of n is read
+      // at the start of n (it is first needed after pass 1 and the scan)
+      float a2n = a2s[cl][0], ian = ias[cl][0];
+      float Bn[K];
+      if constexpr (TILE) tile_read<K>(tB, j, Bn);
+      else load_items<T, K>(B_b, tl, L, full, Bn);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      if (n < N) {
-        const float a2 = a2s[cl][n];
-        float Bv[K], a[K], beta[K];
-        if constexpr (TILE) tile_read<K>(tB + n * TCH, j, Bv);
-        else load_items<T, K>(B_b + (int64_t)n * L, tl, L, full, Bv);
-        float agg = 0.0f;
-        if constexpr (ZOH) {
-          const float ia = ias[cl][n];
-          if (__builtin_amdgcn_ballot_w64(ia == 0.0f) == 0) {
+      for (int n = 0; n < NT; ++n) {
+        if (n < N) {
+          const float a2 = a2n, ia = ian;
+          float Bv[K], Cv[K];
+#pragma unroll
+          for (int k = 0; k < K; ++k) Bv[k] = Bn[k];
+          if constexpr (!STATES) {
+            if constexpr (TILE) tile_read<K>(tB + (NT + n) * TCH, j, Cv);
+            else load_items<T, K>(C_b + (int64_t)n * L, tl, L, full, Cv);
+          }
+          if (n + 1 < N) {
+            a2n = a2s[cl][n + 1];
+            ian = ias[cl][n + 1];
+            if constexpr (TILE) tile_read<K>(tB + (n + 1) * TCH, j, Bn);
+            else load_items<T, K>(B_b + (int64_t)(n + 1) * L, tl, L, full, Bn);
+          }
+          float a[K], beta[K];
+          float agg = 0.0f;
+          if (!ZOH || !any_tiny || __builtin_amdgcn_ballot_w64(ia == 0.0f) == 0) {
 #pragma unroll
             for (int k = 0; k < K; ++k) {
               a[k] = fast_exp2(dt[k] * a2);
-              const float q = Bv[k] * (uv[k] * ia);
-              beta[k] = __builtin_fmaf(a[k], q, -q);     // (Abar - 1)/A * B * u
+              if constexpr (ZOH) {
+                const float q = Bv[k] * (uv[k] * ia);
+                beta[k] = __builtin_fmaf(a[k], q, -q);     // (Abar - 1)/A * B * u
+              } else {
+                beta[k] = Bv[k] * uv[k];
+              }
               agg = __builtin_fmaf(a[k], agg, beta[k]);
             }
           } else {
-            // some channel of this wave has A == 0: (e^{dA}-1)/A -> delta
+            // a channel of this wave has A ~ 0 (stored as 1/A = 0):
+            // (e^{dA}-1)/A -> delta there
 #pragma unroll
             for (int k = 0; k < K; ++k) {
               a[k] = fast_exp2(dt[k] * a2);
@@ -205,50 +236,42 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
               agg = __builtin_fmaf(a[k], agg, beta[k]);
             }
           }
-        } else {
+          float Ag = fast_exp2(a2 * dsum);
+          // the carried state enters through the first lane's summary
+          agg = (j == 0) ? __builtin_fmaf(Ag, cr[n], agg) : agg;
+          affine_scan_inclusive_fused<R>(Ag, agg);
+          const float hend = agg;                        // state after this lane's steps
+          if constexpr (!STATES) {
+            float h = group_shift_right<R>(hend, cr[n]);  // state before them
 #pragma unroll
-          for (int k = 0; k < K; ++k) {
-            a[k] = fast_exp2(dt[k] * a2);
-            beta[k] = Bv[k] * uv[k];
-            agg = __builtin_fmaf(a[k], agg, beta[k]);
+            for (int k = 0; k < K; ++k) {
+              h = __builtin_fmaf(a[k], h, beta[k]);
+              y[k] = __builtin_fmaf(Cv[k], h, y[k]);
+            }
           }
+          cr[n] = last_to_first<R>(hend);                // state after the chunk
         }
-        float Ag = fast_exp2(a2 * dsum);
-        affine_scan_inclusive_fused<R>(Ag, agg);
-        const float hend = __builtin_fmaf(Ag, carry[n], agg);   // state after this lane's steps
-        if constexpr (!STATES) {
-          float Cv[K];
-          if constexpr (TILE) tile_read<K>(tB + (NT + n) * TCH, j, Cv);
-          else load_items<T, K>(C_b + (int64_t)n * L, tl, L, full, Cv);
-          float h = group_shift_right<R>(hend, carry[n]);       // state before them
-#pragma unroll
-          for (int k = 0; k < K; ++k) {
-            h = __builtin_fmaf(a[k], h, beta[k]);
-            y[k] = __builtin_fmaf(Cv[k], h, y[k]);
-          }
-        }
-        carry[n] = group_last<R>(hend);                         // state after the chunk
+        mem_fence_compiler();
       }
-      mem_fence_compiler();
-    }
 
-    if constexpr (!STATES) {
-      if (z_row) {
+      if constexpr (!STATES) {
+        if (z_row) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) y[k] *= silu(zv[k]);
+          for (int k = 0; k < K; ++k) y[k] *= silu(zv[k]);
+        }
+        if (active) store_items<T, K>(out_row, tl, L, full, y);
       }
-      if (active) store_items<T, K>(out_row, tl, L, full, y);
-    }
-    if constexpr (TILE) {
-      if (more) stage.store(reinterpret_cast<float*>(tile_mem[buf ^ 1]), N, tid);
-      __syncthreads();
+      if constexpr (TILE) {
+        if (more) stage.store(reinterpret_cast<float*>(tile_mem[buf ^ 1]), N, tid);
+        __syncthreads();
+      }
     }
   }
 
   if (!STATES && active && j == 0 && p.last_state) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
-      if (n < N) p.last_state[c * N + n] = carry[n];
+      if (n < N) p.last_state[c * N + n] = cr[n];
   }
 }
 

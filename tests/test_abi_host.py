@@ -63,8 +63,9 @@ def test_workspace_queries(lib):
     # the backward spreads a channel over 16 lanes: 0 (default) and 16 only
     n16 = lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 16)
     assert n16 > 0 and n16 == lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 0)
-    # the workspace holds the state at each 128-step chunk start: (2*64) * 4 * 16 floats
-    assert n16 == 2 * 64 * 4 * 16 * 4
+    # the workspace holds the state at each 128-step chunk start, (2*64) * 4 * 16
+    # floats, then one flag per block of 16 channels (8 blocks), 256-byte rounded
+    assert n16 == 2 * 64 * 4 * 16 * 4 + 256
     for lanes in (8, 32, 64):
         assert lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, lanes) == 2 ** 64 - 1
 
