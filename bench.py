@@ -8,16 +8,23 @@ mamba_state_update decode step continuing from the final state.
 
 Prints ONE JSON line.  `value` is the achieved algorithmic HBM throughput of
 the step (bytes every call must move at least once, divided by the step
-time), in GB/s; the roofline object is for the dominant call, timed live with
-HIP events on the stream the kernels run on; cpu_baseline is the float64 CPU
-oracle on a bounded sample of the same workload.
+time), in GB/s.  `roofline` is for the kernel that takes most of the step,
+timed alone with HIP events that the library records around it on the
+stream it runs on; its `traffic` comes from the committed counter summary of
+that kernel when the kernel's sources are unchanged since it was taken.
+`cpu_baseline` is the float64 CPU oracle on a bounded sample of the same
+workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4|5]
-                       [--no-cpu-baseline]
+                       [--disc zoh|euler] [--calls fwd,bwd,step] [--no-cpu-baseline]
+                       [--copy-calibration]
+       python bench.py --summarize-counters counter_collection.csv [...]
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +36,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+CSRC = os.path.join(ROOT, "scan_selective_fwd_amd", "csrc")
+# Sources each timed kernel is compiled from (its counter summary is void
+# once any of them changes).
+KERNEL_SOURCES = {
+    "scan_fwd_kernel": ["scan_fwd_impl.hpp", "tile_stage.hpp", "device_common.hpp",
+                        "kernels.hpp", "scan_fwd_f32.hip", "scan_fwd_bf16.hip"],
+    "scan_bwd_kernel": ["scan_bwd_impl.hpp", "tile_stage.hpp", "device_common.hpp",
+                        "kernels.hpp", "scan_bwd_f32.hip", "scan_bwd_bf16.hip"],
+}
+COPY_BYTES = 1 << 30   # calibration copy: reads and writes 1 GiB
 
 
 def algorithmic_bytes(w, call: str) -> float:
@@ -48,6 +65,52 @@ def algorithmic_bytes(w, call: str) -> float:
     raise ValueError(call)
 
 
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.txt, or
+    None when there is no such summary or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_counters(paths):
+    """Per-kernel mean of every counter in rocprofv3 counter_collection.csv
+    files (one row per dispatch and counter)."""
+    acc = {}
+    for p in paths:
+        with open(p) as f:
+            for row in csv.DictReader(f):
+                name = row.get("Kernel_Name", "?")
+                key = (name.split("(")[0][:120], row["Counter_Name"])
+                d = acc.setdefault(key, {})
+                d.setdefault(row["Dispatch_Id"], 0.0)
+                d[row["Dispatch_Id"]] += float(row["Counter_Value"])
+    for (name, counter), per_dispatch in sorted(acc.items()):
+        v = list(per_dispatch.values())
+        print(f"{counter:14s} dispatches={len(v):4d} mean={np.mean(v):16.1f} "
+              f"min={np.min(v):16.1f} max={np.max(v):16.1f}  {name}")
+
+
 def gpu_inputs(w, torch, with_dout):
     import workloads as W
     inp = W.workload_inputs(w.wid, with_dout=with_dout)
@@ -62,39 +125,58 @@ def gpu_inputs(w, torch, with_dout):
     return out
 
 
-def cpu_baseline(w, calls):
-    """The float64 oracle on a bounded sample of the same workload: the first
-    `nb` batch rows (all D channels of each), running the same calls."""
+def cpu_baseline(w, calls, disc, budget_s=10.0):
+    """The float64 oracle on a bounded sample of the same workload, on the
+    host cores available to the process.  The sample is the whole batch at
+    the full sequence length (a 65536-step prefix of every channel for the
+    1M-step workload); passes repeat until `budget_s` seconds have elapsed."""
     import oracle
     import workloads as W
-    nb = 2 if w.batch >= 2 else 1
-    L = w.seqlen
-    if w.wid == 4:
-        L = 65536   # a prefix of the long sequence keeps the sample ~10 s
+    L = min(w.seqlen, 65536)
+    nb = w.batch
     inp = W.make_inputs(w.wid, nb, w.dim, w.dstate, L, dtype=w.dtype, bias=w.bias,
                         with_dout=True, per_row=w.per_row)
     f = W.inputs_f64(inp, w.dtype)
+    dcode = oracle.ZOH if disc == "zoh" else oracle.EULER
     threads = oracle.default_threads()
+    passes = 0
     t0 = time.perf_counter()
-    if "fwd" in calls:
-        oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
-                        f["delta_bias"], threads=threads)
-    if "bwd" in calls:
-        oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
-                        f["delta_bias"], f["dout"], threads=threads)
-    if "step" in calls:
-        st = np.zeros((nb, w.dim, w.dstate))
-        oracle.state_update(st, f["u"][..., 0], f["delta"][..., 0], f["A"], f["B"][..., 0],
-                            f["C"][..., 0], f["D"], f["z"][..., 0], f["delta_bias"])
-    dt = time.perf_counter() - t0
+    while True:
+        if "fwd" in calls:
+            oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                            f["delta_bias"], disc=dcode, threads=threads)
+        if "bwd" in calls:
+            oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                            f["delta_bias"], f["dout"], disc=dcode, threads=threads)
+        if "step" in calls:
+            st = np.zeros((nb, w.dim, w.dstate))
+            oracle.state_update(st, f["u"][..., 0], f["delta"][..., 0], f["A"], f["B"][..., 0],
+                                f["C"][..., 0], f["D"], f["z"][..., 0], f["delta_bias"],
+                                disc=dcode)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or passes >= 20:
+            break
     import copy
     ws = copy.copy(w)
     ws.batch, ws.seqlen = nb, L
-    nbytes = sum(algorithmic_bytes(ws, c) for c in calls)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nb} of {w.batch} batch rows x {w.dim} channels x {L} steps "
-                      f"({'+'.join(calls)}), {dt:.2f} s wall",
-            "channel_tokens_per_s": round(nb * w.dim * L / dt, 1)}
+    nbytes = passes * sum(algorithmic_bytes(ws, c) for c in calls)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) over {nb} batch rows x {w.dim} channels x {L} steps "
+                      f"({'+'.join(calls)}, float64), {dt:.2f} s wall",
+            "channel_tokens_per_s": round(passes * nb * w.dim * L / dt, 1)}
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size, so that counter runs over this
+    process can scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def main():
@@ -105,12 +187,19 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--disc", default="zoh", choices=["zoh", "euler"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy first (for counter calibration)")
     ap.add_argument("--calls", default=None,
                     help="comma list of calls to time instead of the full step (fwd,bwd,step)")
+    ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="CSV")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the selective scan shards over channels with no "
-              "communication (see DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: every (batch, channel) recurrence is "
+              "independent, so the scan shards over channels or batch rows with no exchange "
+              "in the forward; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -121,6 +210,8 @@ def main():
     calls = {2: ["fwd", "bwd", "step"], 3: ["fwd"], 4: ["fwd"], 5: ["bwd"]}[w.wid]
     if args.calls:
         calls = args.calls.split(",")
+    if args.copy_calibration:
+        copy_calibration(torch)
     g = gpu_inputs(w, torch, "bwd" in calls)
     ws = None
     if "bwd" in calls:
@@ -132,14 +223,14 @@ def main():
     step_args = {k: g[k][..., 0].contiguous() for k in ("u", "delta", "B", "C", "z")}
     step_out = torch.empty((w.batch, w.dim), dtype=sdt, device="cuda")
 
-    def run_call(c):
+    def run_call(c, timing=None):
         if c == "fwd":
             ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
                         g["delta_bias"], disc=args.disc, out=t_out, last_state=t_last,
-                        return_last_state=True)
+                        return_last_state=True, timing=timing)
         elif c == "bwd":
             ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
-                        g["delta_bias"], g["dout"], disc=args.disc, workspace=ws)
+                        g["delta_bias"], g["dout"], disc=args.disc, workspace=ws, timing=timing)
         else:   # decode step continuing from the forward's final state, in place
             ms.state_update(t_last, step_args["u"], step_args["delta"], g["A"], step_args["B"],
                             step_args["C"], g["D"], step_args["z"], g["delta_bias"],
@@ -151,37 +242,42 @@ def main():
             run_call(c)
     torch.cuda.synchronize()
 
-    ev = {c: [] for c in calls}
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)      # creates the underlying event
+        return e
+
+    # events: per call (whole call) and per timed kernel (fwd / bwd scan kernel)
+    ev = {c: [(new_event(), new_event()) for _ in range(args.steps)] for c in calls}
+    kev = {c: [(new_event(), new_event()) for _ in range(args.steps)]
+           for c in calls if c in ("fwd", "bwd")}
+    start, end = new_event(), new_event()
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         for c in calls:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
+            e0, e1 = ev[c][i]
             e0.record(stream)
-            run_call(c)
+            run_call(c, kev[c][i] if c in kev else None)
             e1.record(stream)
-            ev[c].append((e0, e1))
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     call_ms = {c: float(np.mean([a.elapsed_time(b) for a, b in ev[c]])) for c in calls}
+    kern_ms = {c: float(np.mean([a.elapsed_time(b) for a, b in kev[c]])) for c in kev}
 
     step_bytes = sum(algorithmic_bytes(w, c) for c in calls)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     ct = w.batch * w.dim * w.seqlen
-    dom = max((c for c in calls if c != "step"), key=lambda c: call_ms[c])
-    dom_bytes = algorithmic_bytes(w, dom)
-    achieved = dom_bytes / (call_ms[dom] * 1e-3) / 1e9
-    kernels = {"fwd": "scan_fwd_kernel", "bwd": "scan_fwd_kernel(states) + scan_bwd_kernel + "
-               "bwd_reduce kernels", "step": "state_update_kernel"}
+    kernel_names = {"fwd": "scan_fwd_kernel", "bwd": "scan_bwd_kernel"}
     per_call = {c: {"ms": round(call_ms[c], 5),
                     "algorithmic_MB": round(algorithmic_bytes(w, c) / 1e6, 3),
                     "GB/s": round(algorithmic_bytes(w, c) / (call_ms[c] * 1e-3) / 1e9, 1)}
                 for c in calls}
+    for c in kern_ms:
+        per_call[c]["kernel"] = kernel_names[c]
+        per_call[c]["kernel_ms"] = round(kern_ms[c], 5)
     res = {
         "metric": "selective-scan fwd/bwd achieved HBM GB/s (% peak); channel-tokens/s, "
                   "D=1536 L=2048",
@@ -203,14 +299,22 @@ def main():
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "channel_tokens_per_s": round(ct / (ms_per_step * 1e-3), 1),
         "per_call": per_call,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": kernels[dom], "call": f"mamba_scan_{dom}",
-                     "algorithmic_bytes_per_launch": int(dom_bytes),
-                     "avg_launch_ms": round(call_ms[dom], 5)},
     }
+    if kern_ms:
+        dom = max(kern_ms, key=lambda c: kern_ms[c])
+        kname = kernel_names[dom]
+        dom_bytes = algorithmic_bytes(w, dom)
+        achieved = dom_bytes / (kern_ms[dom] * 1e-3) / 1e9
+        wl_tag = f"w{w.wid}_{args.disc}"
+        res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                           "traffic": committed_traffic(kname, wl_tag),
+                           "kernel": kname, "call": f"mamba_scan_{dom}",
+                           "algorithmic_bytes_per_launch": int(dom_bytes),
+                           "avg_launch_ms": round(kern_ms[dom], 5),
+                           "kernel_source_sha256": kernel_source_hash(kname)}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, calls)
+        res["cpu_baseline"] = cpu_baseline(w, calls, args.disc)
     print(json.dumps(res), flush=True)
 
 

@@ -157,12 +157,20 @@ mamba_status mamba_state_update(float* state, const void* u, const void* delta, 
                                 void* out, void* stream);
 
 /*
- * Tuning variants.  Identical to the calls above except for an explicit
- * number of lanes each channel's scan is spread over (16, 32 or 64; 0 picks
- * the default the plain calls use).  The result does not depend on the
- * choice beyond float32 rounding order; tests and launch-shape sweeps use
- * them.  mamba_scan_bwd_ex needs the workspace reported by
- * mamba_scan_bwd_workspace_size_ex for the same lanes value.
+ * Tuning and timing variants.  Identical to the calls above except for:
+ *  - lanes_per_channel: the number of lanes each channel's scan is spread
+ *    over (16, 32 or 64 for the forward; 0 picks the default the plain calls
+ *    use; the backward accepts 0 and 16 only).  The result does not depend on
+ *    the choice beyond float32 rounding order; tests and launch-shape sweeps
+ *    use it.  mamba_scan_bwd_ex needs the workspace reported by
+ *    mamba_scan_bwd_workspace_size_ex for the same lanes value.
+ *  - timing_begin, timing_end: hipEvent_t handles (NULL = none).  When given,
+ *    they are recorded on `stream` immediately before and after the main
+ *    scan kernel of the call (the forward's only kernel; the backward's
+ *    reverse-scan kernel, after its state-recompute and zeroing kernels have
+ *    been enqueued), so a caller can time that kernel alone with
+ *    hipEventElapsedTime.  The caller owns the events; failure to record one
+ *    returns MAMBA_ERR_HIP.
  */
 mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
                                const void* C, const float* D, const void* z,
@@ -170,7 +178,7 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
                                mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
                                int64_t dstate, int64_t seqlen, void* out, float* last_state,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel);
+                               int lanes_per_channel, void* timing_begin, void* timing_end);
 
 size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
                                         int64_t seqlen, mamba_dtype dt, int lanes_per_channel);
@@ -183,7 +191,7 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
                                float* du, float* ddelta, float* dA, float* dB, float* dC,
                                float* dD, float* dz, float* ddelta_bias, float* dh0,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel);
+                               int lanes_per_channel, void* timing_begin, void* timing_end);
 
 #ifdef __cplusplus
 }

@@ -87,10 +87,17 @@ def _split(n_items: int, threads: int):
 
 
 def default_threads() -> int:
+    """Host cores available to this process, capped by OMP_NUM_THREADS when
+    the environment sets it (a machine's share of cores may be smaller than
+    what the affinity mask shows)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = max(1, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return n
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,

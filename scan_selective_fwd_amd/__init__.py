@@ -72,10 +72,25 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _events(timing):
+    """Raw hipEvent_t handles of a (begin, end) pair of torch.cuda.Event
+    created with enable_timing=True, or (None, None)."""
+    if timing is None:
+        return None, None
+    handles = []
+    for ev in timing:
+        if not ev.cuda_event:       # torch creates the event on its first record
+            ev.record()
+        handles.append(ev.cuda_event)
+    return handles[0], handles[1]
+
+
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
              delta_softplus=True, disc="zoh", return_last_state=False, out=None, last_state=None,
-             lanes=0):
-    """Fused selective-scan forward.  Returns out, or (out, last_state)."""
+             lanes=0, timing=None):
+    """Fused selective-scan forward.  Returns out, or (out, last_state).
+    `timing`: optional (begin, end) torch.cuda.Event pair recorded around the
+    scan kernel on the current stream."""
     L_ = lib()
     if not u.is_cuda:
         raise ValueError("u must be a GPU tensor (no CPU path exists)")
@@ -102,7 +117,8 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
     st = L_.mamba_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                               _ptr(delta_bias), _ptr(h0), int(bool(delta_softplus)),
                               _disc_code(disc), dt, batch, dim, N, L, _ptr(out),
-                              _ptr(last_state), None, 0, _stream(dev), int(lanes))
+                              _ptr(last_state), None, 0, _stream(dev), int(lanes),
+                              *_events(timing))
     _lib.check(st, "mamba_scan_fwd")
     return (out, last_state) if return_last_state else out
 
@@ -116,9 +132,11 @@ def bwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0) -> int:
 
 
 def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softplus=True,
-             disc="zoh", lanes=0, workspace=None, want_dh0=True):
+             disc="zoh", lanes=0, workspace=None, want_dh0=True, timing=None):
     """Backward with state recomputation.  Returns a dict of float32 gradients:
-    du, ddelta, dA, dB, dC and, when the input is given, dD, dz, ddelta_bias, dh0."""
+    du, ddelta, dA, dB, dC and, when the input is given, dD, dz, ddelta_bias, dh0.
+    `timing`: optional (begin, end) torch.cuda.Event pair recorded around the
+    reverse-scan kernel on the current stream."""
     L_ = lib()
     dev = u.device
     batch, dim, L = u.shape
@@ -154,7 +172,7 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
                               _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
                               _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
                               _ptr(g.get("dh0")), workspace.data_ptr(), workspace.numel(),
-                              _stream(dev), int(lanes))
+                              _stream(dev), int(lanes), *_events(timing))
     _lib.check(st, "mamba_scan_bwd")
     return g
 

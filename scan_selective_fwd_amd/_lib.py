@@ -65,12 +65,12 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_fwd.restype = _int
     lib.mamba_scan_fwd.argtypes = fwd_args
     lib.mamba_scan_fwd_ex.restype = _int
-    lib.mamba_scan_fwd_ex.argtypes = fwd_args + [_int]
+    lib.mamba_scan_fwd_ex.argtypes = fwd_args + [_int, _vp, _vp]
     bwd_args = [_vp] * 10 + [_int, _int, _int] + [_i64] * 4 + [_vp] * 10 + [_sz, _vp]
     lib.mamba_scan_bwd.restype = _int
     lib.mamba_scan_bwd.argtypes = bwd_args
     lib.mamba_scan_bwd_ex.restype = _int
-    lib.mamba_scan_bwd_ex.argtypes = bwd_args + [_int]
+    lib.mamba_scan_bwd_ex.argtypes = bwd_args + [_int, _vp, _vp]
     lib.mamba_state_update.restype = _int
     lib.mamba_state_update.argtypes = [_vp] * 9 + [_int, _int, _int] + [_i64] * 3 + [_vp, _vp]
     _lib = lib

@@ -120,7 +120,7 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
                                mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
                                int64_t dstate, int64_t seqlen, void* out, float* last_state,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel) {
+                               int lanes_per_channel, void* timing_begin, void* timing_end) {
   (void)workspace;
   (void)workspace_bytes;
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
@@ -142,8 +142,14 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
   p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
   if (batch * p.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
   const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
-  return hip_status(mscan::dispatch_scan_fwd(p, dt == MAMBA_F32 ? 0 : 1, (int)disc, lanes, vec,
-                                             static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (timing_begin && hipEventRecord(static_cast<hipEvent_t>(timing_begin), s) != hipSuccess)
+    return MAMBA_ERR_HIP;
+  if (mscan::dispatch_scan_fwd(p, dt == MAMBA_F32 ? 0 : 1, (int)disc, lanes, vec, s) != hipSuccess)
+    return MAMBA_ERR_HIP;
+  if (timing_end && hipEventRecord(static_cast<hipEvent_t>(timing_end), s) != hipSuccess)
+    return MAMBA_ERR_HIP;
+  return MAMBA_OK;
 }
 
 mamba_status mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
@@ -154,7 +160,7 @@ mamba_status mamba_scan_fwd(const void* u, const void* delta, const float* A, co
                             void* workspace, size_t workspace_bytes, void* stream) {
   return mamba_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, disc, dt,
                            batch, dim, dstate, seqlen, out, last_state, workspace,
-                           workspace_bytes, stream, 0);
+                           workspace_bytes, stream, 0, nullptr, nullptr);
 }
 
 mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
@@ -164,7 +170,8 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
                                int64_t dim, int64_t dstate, int64_t seqlen, float* du,
                                float* ddelta, float* dA, float* dB, float* dC, float* dD,
                                float* dz, float* ddelta_bias, float* dh0, void* workspace,
-                               size_t workspace_bytes, void* stream, int lanes_per_channel) {
+                               size_t workspace_bytes, void* stream, int lanes_per_channel,
+                               void* timing_begin, void* timing_end) {
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
   if (st != MAMBA_OK) return st;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
@@ -208,7 +215,9 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.nchunks = w.nchunks; p.groups = w.groups; p.N = (int)dstate;
   p.softplus = delta_softplus ? 1 : 0;
-  return hip_status(mscan::dispatch_scan_bwd(p, dti, (int)disc, vec, s));
+  return hip_status(mscan::dispatch_scan_bwd(p, dti, (int)disc, vec, s,
+                                             static_cast<hipEvent_t>(timing_begin),
+                                             static_cast<hipEvent_t>(timing_end)));
 }
 
 mamba_status mamba_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
@@ -221,7 +230,8 @@ mamba_status mamba_scan_bwd(const void* u, const void* delta, const float* A, co
                             size_t workspace_bytes, void* stream) {
   return mamba_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout, delta_softplus, disc,
                            dt, batch, dim, dstate, seqlen, du, ddelta, dA, dB, dC, dD, dz,
-                           ddelta_bias, dh0, workspace, workspace_bytes, stream, 0);
+                           ddelta_bias, dh0, workspace, workspace_bytes, stream, 0, nullptr,
+                           nullptr);
 }
 
 mamba_status mamba_state_update(float* state, const void* u, const void* delta, const float* A,

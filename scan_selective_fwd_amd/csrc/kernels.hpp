@@ -108,11 +108,16 @@ inline hipError_t dispatch_chunk_states(const FwdParams& p, int dtype, int disc,
 }
 // The backward always spreads a channel over 16 lanes (kBwdLanes).
 constexpr int kBwdLanes = 16;
-hipError_t dispatch_scan_bwd_f32(const BwdParams& p, int disc, bool vec, hipStream_t s);
-hipError_t dispatch_scan_bwd_bf16(const BwdParams& p, int disc, bool vec, hipStream_t s);
+// ev_begin / ev_end (nullable) are recorded on the stream right before and
+// after the main backward kernel, for timing it alone.
+hipError_t dispatch_scan_bwd_f32(const BwdParams& p, int disc, bool vec, hipStream_t s,
+                                 hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t dispatch_scan_bwd_bf16(const BwdParams& p, int disc, bool vec, hipStream_t s,
+                                  hipEvent_t ev_begin, hipEvent_t ev_end);
 inline hipError_t dispatch_scan_bwd(const BwdParams& p, int dtype, int disc, bool vec,
-                                    hipStream_t s) {
-  return dtype == 0 ? dispatch_scan_bwd_f32(p, disc, vec, s) : dispatch_scan_bwd_bf16(p, disc, vec, s);
+                                    hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  return dtype == 0 ? dispatch_scan_bwd_f32(p, disc, vec, s, ev_begin, ev_end)
+                    : dispatch_scan_bwd_bf16(p, disc, vec, s, ev_begin, ev_end);
 }
 hipError_t dispatch_state_update(const StepParams& p, int dtype, int disc, hipStream_t stream);
 

@@ -3,8 +3,9 @@
 
 namespace mscan {
 
-hipError_t dispatch_scan_bwd_bf16(const BwdParams& p, int disc, bool vec, hipStream_t stream) {
-  return dispatch_bwd_t<bf16_t>(p, disc, vec, stream);
+hipError_t dispatch_scan_bwd_bf16(const BwdParams& p, int disc, bool vec, hipStream_t stream,
+                                 hipEvent_t ev_begin, hipEvent_t ev_end) {
+  return dispatch_bwd_t<bf16_t>(p, disc, vec, stream, ev_begin, ev_end);
 }
 
 }  // namespace mscan

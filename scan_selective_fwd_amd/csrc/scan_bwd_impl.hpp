@@ -409,19 +409,25 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(const BwdParams p)
 }
 
 template <typename T, int NT, bool ZOH, bool VEC>
-static hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
+static hipError_t launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin,
+                             hipEvent_t ev_end) {
   const int64_t nblocks = p.batch * p.groups;
+  hipError_t e;
+  if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
   hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, false>), dim3((unsigned)nblocks),
                      dim3(kBlock), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !ZOH) return e;
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
+  if (!ZOH) return e;
   hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, true>), dim3((unsigned)nblocks),
                      dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t dispatch_bwd_t(const BwdParams& p, int disc, bool vec, hipStream_t s) {
+static hipError_t dispatch_bwd_t(const BwdParams& p, int disc, bool vec, hipStream_t s,
+                                 hipEvent_t ev_begin, hipEvent_t ev_end) {
   {
     const int64_t total = 2 * p.batch * p.N * p.L + p.dim * p.N + 2 * p.dim;
     int64_t blocks = (total + 255) / 256;
@@ -431,12 +437,17 @@ static hipError_t dispatch_bwd_t(const BwdParams& p, int disc, bool vec, hipStre
     if (e != hipSuccess) return e;
   }
   const bool zoh = disc == 0;
+  const hipEvent_t b = ev_begin, e = ev_end;
   if (p.N <= 16) {
-    if (zoh) return vec ? launch_bwd<T, 16, true, true>(p, s) : launch_bwd<T, 16, true, false>(p, s);
-    return vec ? launch_bwd<T, 16, false, true>(p, s) : launch_bwd<T, 16, false, false>(p, s);
+    if (zoh) return vec ? launch_bwd<T, 16, true, true>(p, s, b, e)
+                        : launch_bwd<T, 16, true, false>(p, s, b, e);
+    return vec ? launch_bwd<T, 16, false, true>(p, s, b, e)
+               : launch_bwd<T, 16, false, false>(p, s, b, e);
   }
-  if (zoh) return vec ? launch_bwd<T, 64, true, true>(p, s) : launch_bwd<T, 64, true, false>(p, s);
-  return vec ? launch_bwd<T, 64, false, true>(p, s) : launch_bwd<T, 64, false, false>(p, s);
+  if (zoh) return vec ? launch_bwd<T, 64, true, true>(p, s, b, e)
+                      : launch_bwd<T, 64, true, false>(p, s, b, e);
+  return vec ? launch_bwd<T, 64, false, true>(p, s, b, e)
+             : launch_bwd<T, 64, false, false>(p, s, b, e);
 }
 
 }  // namespace mscan
