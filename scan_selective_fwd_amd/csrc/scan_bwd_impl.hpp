@@ -33,6 +33,8 @@
 // deterministic only up to float32 rounding order.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "scan_fwd_impl.hpp"
@@ -45,27 +47,60 @@ __device__ __forceinline__ float row_shift_left(float v, float last) {
   return dpp_mov<0x101 /*row_shl:1*/>(last, v);
 }
 
+// Moves between fixed lanes of every 16-lane row (other lanes: unspecified).
+template <int k>   // lane k -> lane 0 (row_shl:k)
+__device__ __forceinline__ float row_lane_to_first(float v) {
+  if constexpr (k == 0) return v;
+  else return dpp_mov<0x100 + k>(v, v);
+}
+template <int k>   // lane k -> lane 15 (row_shr:15-k)
+__device__ __forceinline__ float row_lane_to_last(float v) {
+  if constexpr (k == 15) return v;
+  else return dpp_mov<0x110 + (15 - k)>(v, v);
+}
+template <int k>   // lane 0 -> lane k (row_shr:k)
+__device__ __forceinline__ float row_first_to_lane(float v) {
+  if constexpr (k == 0) return v;
+  else return dpp_mov<0x110 + k>(v, v);
+}
+template <int k>   // lane 15 -> lane k (row_shl:15-k)
+__device__ __forceinline__ float row_last_to_lane(float v) {
+  if constexpr (k == 15) return v;
+  else return dpp_mov<0x100 + (15 - k)>(v, v);
+}
+
+template <int I, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, E>(f);
+  }
+}
+
 // TINY = false: the fast kernel.  A block in which some channel has A ~ 0
 // (ZOH only) sets its flag in p.deferred and exits without computing; the
 // TINY = true kernel, launched right after on the same stream, computes
 // exactly the flagged blocks with the A = 0 limits of the ZOH coefficients.
+//
+// Per-state values that live across state indices (the chunk-start state,
+// the adjoint carried from the later chunk, the dA sum) are kept in
+// registers "lane n holds state n": a channel's 16 lanes hold 16 states per
+// register, and DPP row shifts bring state n to lane 0 or lane 15 and back.
 template <typename T, int NT, bool ZOH, bool VEC, bool TINY>
-__global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(const BwdParams p) {
   constexpr int R = 16;
   constexpr int K = kItemsBwd;
   static_assert(K == 8, "the row reduce-scatter assumes 8 steps per lane");
+  static_assert(NT % 16 == 0, "states are spread over the 16 lanes of a channel");
   constexpr int CPW = 64 / R;
   constexpr int CPB = (kBlock / 64) * CPW;
   constexpr int TCH = R * K;
   constexpr bool TILE = (NT == 16);
-  constexpr int SREG = (CPB * NT + kBlock - 1) / kBlock;
+  constexpr int NQ = NT / 16;
   // single-buffered: refilled between the two barriers that close a chunk
   __shared__ float4 tile_mem[TILE ? 2 * NT * TCH / 4 : 1];   // B, C rows of the chunk
-  __shared__ float hst[CPB][NT];        // forward state at the chunk start
-  __shared__ float gcs[CPB][NT];        // adjoint carried from the later chunk
-  __shared__ float dAs[CPB][NT];        // dA of each channel, this batch row
+  __shared__ float4 prm[CPB][NT];       // {A log2(e), 1/A (0 where A ~ 0), A, 0}
   __shared__ float acc[2][NT][TCH];     // dB, dC of the chunk summed over the block
-  __shared__ float as_[CPB][NT], a2s[CPB][NT], ias[CPB][NT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -101,35 +136,27 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
     const float a = real ? p.A[dd * N + n] : -1.0f;
     const bool tiny = __builtin_fabsf(a) < 1e-30f;
     my_tiny |= real && tiny;
-    as_[ci][n] = a;
-    a2s[ci][n] = a * kLog2e;
-    ias[ci][n] = tiny ? 0.0f : 1.0f / a;
-    gcs[ci][n] = 0.0f;     // no gradient flows into the final state
-    dAs[ci][n] = 0.0f;
+    prm[ci][n] = make_float4(a * kLog2e, tiny ? 0.0f : 1.0f / a, a, 0.0f);
   }
   for (int i = tid; i < 2 * NT * TCH; i += kBlock) (&acc[0][0][0])[i] = 0.0f;
 
-  // chunk-start states of this block's channels for chunk `ch`
-  auto load_states = [&](int64_t ch, float (&dst)[SREG]) {
+  // chunk-start states of this lane's channel: lane j holds state 16 q + j
+  const float* __restrict__ st_row = p.chunk_states + c * nchunks * N;
+  auto load_states = [&](int64_t ch, float (&dst)[NQ]) {
 #pragma unroll
-    for (int r = 0; r < SREG; ++r) {
-      const int i = r * kBlock + tid;
-      const int ci = i / NT, n = i - ci * NT;
-      const int64_t dd = grp * CPB + ci;
-      dst[r] = (i < CPB * NT && dd < p.dim && n < N)
-                   ? p.chunk_states[((b * p.dim + dd) * nchunks + ch) * N + n] : 0.0f;
-    }
-  };
-  auto store_states = [&](const float (&src)[SREG]) {
-#pragma unroll
-    for (int r = 0; r < SREG; ++r) {
-      const int i = r * kBlock + tid;
-      if (i < CPB * NT) (&hst[0][0])[i] = src[r];
+    for (int q = 0; q < NQ; ++q) {
+      const int n = 16 * q + j;
+      dst[q] = (active && n < N) ? st_row[ch * N + n] : 0.0f;
     }
   };
 
   TileStager<T, TCH, K, NT, TILE ? 2 * NT : 1, kBlock> stage;
-  float hreg[SREG];
+  float hreg[NQ], gcreg[NQ], dAreg[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    gcreg[q] = 0.0f;     // no gradient flows into the final state
+    dAreg[q] = 0.0f;
+  }
   {
     const int64_t last = nchunks - 1;
     const bool full_last = VEC && last * TCH + TCH <= L;
@@ -138,7 +165,6 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
       stage.store(reinterpret_cast<float*>(tile_mem), N, tid);
     }
     load_states(last, hreg);
-    store_states(hreg);
   }
   // barrier for the LDS fills; also: does any channel of the block have A ~ 0?
   const bool any_tiny = __syncthreads_or(my_tiny);
@@ -193,12 +219,16 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
     }
 
     const float* tB = reinterpret_cast<const float*>(tile_mem);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
+    float4 pr_next = prm[cl][0];
+    static_for<0, NT>([&](auto nc) {
+      constexpr int n = decltype(nc)::value;
+      constexpr int q = n / 16, nl = n % 16;
+      const float4 pr = pr_next;
+      if constexpr (n + 1 < NT) pr_next = prm[cl][n + 1];
       if (n < N) {
-        const float An = as_[cl][n], a2 = a2s[cl][n], ia = ias[cl][n];
-        const float h_in = hst[cl][n];
-        const float gc = gcs[cl][n];
+        const float a2 = pr.x, ia = pr.y, An = pr.z;
+        const float h_in = row_lane_to_first<nl>(hreg[q]);   // state n, in lane 0
+        const float gc = row_lane_to_last<nl>(gcreg[q]);     // carry n, in lane 15
         float Bv[K], Cv[K];
         if constexpr (TILE) {
           tile_read<K>(tB + n * TCH, j, Bv);
@@ -218,8 +248,8 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
         for (int k = 0; k < K; ++k) {
           a[k] = fast_exp2(dt[k] * a2);
           if constexpr (ZOH && !TINY) {
-            const float q = Bv[k] * (uv[k] * ia);
-            beta[k] = __builtin_fmaf(a[k], q, -q);
+            const float qv = Bv[k] * (uv[k] * ia);
+            beta[k] = __builtin_fmaf(a[k], qv, -qv);
           } else if constexpr (ZOH) {
             const float coef = tiny ? dt[k] : (a[k] - 1.0f) * ia;
             beta[k] = coef * Bv[k] * uv[k];
@@ -251,8 +281,8 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
         gagg = (j == R - 1) ? __builtin_fmaf(As, gc, gagg) : gagg;   // later chunk enters lane 15
         affine_suffix_scan_row_fused(As, gagg);
         float g = row_shift_left(gagg, gc);                 // adjoint entering each lane from the right
-        const float gc_new = row_first_to_last(gagg);       // leaving lane 0, now in lane 15
-        if (j == R - 1) gcs[cl][n] = gc_new;
+        const float gc_new = row_first_to_lane<nl>(gagg);   // leaving lane 0, now in lane n
+        gcreg[q] = (j == nl) ? gc_new : gcreg[q];
 
         // ---- gradient terms, with dB/dC summed over the wave's 4 channels
         //      as soon as each pair of steps is done ----
@@ -263,28 +293,38 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
           const float gh = __builtin_fmaf(Cv[k], gy[k], g);   // dL/dh_t
           const float hprev = (k == 0) ? hstart : hv[k - 1];
           const float P = gh * a[k];
-          const float gu = gh * uv[k];
-          float coef, dbdd;
-          if constexpr (ZOH) {
-            coef = __builtin_fmaf(a[k], ia, -ia);         // (Abar - 1)/A
-            if constexpr (TINY) coef = tiny ? dt[k] : coef;
-            dbdd = a[k] * Bv[k];                          // dBbar/ddelta
-          } else {
-            coef = dt[k];
-            dbdd = Bv[k];
-          }
-          const float Ph = P * hprev;
-          // ddelta: gh * (hprev * A * Abar + u * dBbar/ddelta)
-          gdt[k] = __builtin_fmaf(Ph, An, __builtin_fmaf(gu, dbdd, gdt[k]));
-          // dA: gh * hprev * delta * Abar + gh * u * dBbar/dA with the ZOH
-          // dBbar/dA = (delta*Abar*B - Bbar)/A, limit delta^2 B / 2 at A = 0
-          // (1/A = 0 there drops the other terms)
-          dAp = __builtin_fmaf(dt[k], Ph, dAp);
-          if constexpr (ZOH) {
-            float t = dbdd * ia;
-            if constexpr (TINY) t = tiny ? 0.5f * dt[k] * Bv[k] : t;
-            dAp = __builtin_fmaf(gu * dt[k], t, dAp);
+          float coef;
+          if constexpr (ZOH && !TINY) {
+            // with Y = A h_{t-1} + B u:  ddelta += gh Abar Y;
+            // dA += (delta gh Abar Y - gh Bbar u) / A  (1/A applied once below)
+            const float Y = __builtin_fmaf(An, hprev, Bv[k] * uv[k]);
+            gdt[k] = __builtin_fmaf(P, Y, gdt[k]);
+            dAp = __builtin_fmaf(dt[k] * P, Y, dAp);
             dA2 = __builtin_fmaf(gh, beta[k], dA2);
+            coef = __builtin_fmaf(a[k], ia, -ia);           // (Abar - 1)/A
+          } else {
+            const float gu = gh * uv[k];
+            float dbdd;
+            if constexpr (ZOH) {
+              coef = __builtin_fmaf(a[k], ia, -ia);
+              coef = tiny ? dt[k] : coef;
+              dbdd = a[k] * Bv[k];                          // dBbar/ddelta
+            } else {
+              coef = dt[k];
+              dbdd = Bv[k];
+            }
+            const float Ph = P * hprev;
+            // ddelta: gh * (hprev * A * Abar + u * dBbar/ddelta)
+            gdt[k] = __builtin_fmaf(Ph, An, __builtin_fmaf(gu, dbdd, gdt[k]));
+            // dA: gh * hprev * delta * Abar + gh * u * dBbar/dA with the ZOH
+            // dBbar/dA = (delta*Abar*B - Bbar)/A, limit delta^2 B / 2 at A = 0
+            // (1/A = 0 there drops the other terms)
+            dAp = __builtin_fmaf(dt[k], Ph, dAp);
+            if constexpr (ZOH) {
+              const float t = tiny ? 0.5f * dt[k] * Bv[k] : dbdd * ia;
+              dAp = __builtin_fmaf(gu * dt[k], t, dAp);
+              dA2 = __builtin_fmaf(gh, beta[k], dA2);
+            }
           }
           const float s = gh * coef;
           du[k] = __builtin_fmaf(s, Bv[k], du[k]);
@@ -312,12 +352,13 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
           atomicAdd(&acc[0][n][tt], TB[m]);
           atomicAdd(&acc[1][n][tt], TC[m]);
         }
-        if constexpr (ZOH) dAp = __builtin_fmaf(-dA2, ia, dAp);
-        dAp = row_sum_to_last(dAp);
-        if (j == R - 1) dAs[cl][n] += dAp;
+        if constexpr (ZOH && !TINY) dAp = (dAp - dA2) * ia;
+        else if constexpr (ZOH) dAp = __builtin_fmaf(-dA2, ia, dAp);
+        const float dAn = row_last_to_lane<nl>(row_sum_to_last(dAp));
+        dAreg[q] += (j == nl) ? dAn : 0.0f;
       }
       mem_fence_compiler();
-    }
+    });
 
     // the earlier chunk's B/C rows and states: issued here (not at the chunk
     // start) so their registers are not live across the state-index loop
@@ -354,7 +395,7 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
     }
     __syncthreads();
     // all waves are done with this chunk: flush its dB/dC sums, clear them,
-    // and refill the tile and the chunk-start states with the earlier chunk
+    // and refill the tile with the earlier chunk
     for (int i = tid; i < 2 * NT * TCH; i += kBlock) {
       const int which = i / (NT * TCH);
       const int rest = i - which * NT * TCH;
@@ -365,20 +406,19 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_kernel(const BwdParams p) {
       const int64_t t = t0 + tt;
       if (n < N && t < L) unsafeAtomicAdd((which ? p.dC : p.dB) + (b * N + n) * L + t, v);
     }
-    if (ch > 0) {
-      if constexpr (TILE) stage.store(reinterpret_cast<float*>(tile_mem), N, tid);
-      store_states(hreg);
+    if constexpr (TILE) {
+      if (ch > 0) stage.store(reinterpret_cast<float*>(tile_mem), N, tid);
     }
     __syncthreads();
   }
 
   // ---- per-channel results: dh0, dA (over batch rows), dD, ddelta_bias ----
-  for (int i = tid; i < CPB * NT; i += kBlock) {
-    const int ci = i / NT, n = i - ci * NT;
-    const int64_t dd = grp * CPB + ci;
-    if (dd < p.dim && n < N) {
-      if (p.dh0) p.dh0[(b * p.dim + dd) * N + n] = gcs[ci][n];
-      unsafeAtomicAdd(p.dA + dd * N + n, dAs[ci][n]);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int n = 16 * q + j;
+    if (active && n < N) {
+      if (p.dh0) p.dh0[c * N + n] = gcreg[q];
+      unsafeAtomicAdd(p.dA + d * N + n, dAreg[q]);
     }
   }
   const float sD = row_sum_to_last(dD_acc);
