@@ -27,8 +27,9 @@
 // with the carry from the later chunk, reverse pass 2) and the gradient
 // terms.  The B/C chunk and the chunk-start states are staged in LDS once per
 // block.  dB/dC are summed over the wave's 4 channels with gfx950 permlane
-// swaps, over the block's waves with LDS float adds, and once per chunk into
-// global memory with float atomics.  dA, dD, ddelta_bias are summed over the
+// swaps, over the block's waves through per-wave LDS slices (plain stores,
+// summed after a barrier every 4 state indices), and into global memory with
+// one float atomic per (n, t) per block.  dA, dD, ddelta_bias are summed over the
 // channel's lanes and atomically over batch rows.  Atomics make the result
 // deterministic only up to float32 rounding order.
 #pragma once
@@ -100,7 +101,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   // single-buffered: refilled between the two barriers that close a chunk
   __shared__ float4 tile_mem[TILE ? 2 * NT * TCH / 4 : 1];   // B, C rows of the chunk
   __shared__ float4 prm[CPB][NT];       // {A log2(e), 1/A (0 where A ~ 0), A, 0}
-  __shared__ float acc[2][NT][TCH];     // dB, dC of the chunk summed over the block
+  // dB, dC partial sums of each wave for a group of 4 state indices, double
+  // buffered: written with plain stores, summed over the waves and flushed
+  // to global memory after the group's barrier.  (LDS float atomics are far
+  // slower than stores on this chip.)  Step tt of the chunk sits at
+  // position (tt % 8) * 16 + tt / 8, which makes each wave's 64 stores hit
+  // 64 consecutive words.
+  constexpr int G = 4;
+  constexpr int NW = kBlock / 64;
+  __shared__ float red[2][NW][2][G][TCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -138,7 +147,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     my_tiny |= real && tiny;
     prm[ci][n] = make_float4(a * kLog2e, tiny ? 0.0f : 1.0f / a, a, 0.0f);
   }
-  for (int i = tid; i < 2 * NT * TCH; i += kBlock) (&acc[0][0][0])[i] = 0.0f;
 
   // chunk-start states of this lane's channel: lane j holds state 16 q + j
   const float* __restrict__ st_row = p.chunk_states + c * nchunks * N;
@@ -346,16 +354,39 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           }
           g = P;
         }
+        constexpr int buf = (n / G) & 1;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {   // lane (row r, j) owns step j*K + 4m + r
-          const int tt = j * K + 4 * m + row;
-          atomicAdd(&acc[0][n][tt], TB[m]);
-          atomicAdd(&acc[1][n][tt], TC[m]);
+          const int pos = (4 * m + row) * 16 + j;
+          red[buf][wave][0][n % G][pos] = TB[m];
+          red[buf][wave][1][n % G][pos] = TC[m];
         }
         if constexpr (ZOH && !TINY) dAp = (dAp - dA2) * ia;
         else if constexpr (ZOH) dAp = __builtin_fmaf(-dA2, ia, dAp);
         const float dAn = row_last_to_lane<nl>(row_sum_to_last(dAp));
         dAreg[q] += (j == nl) ? dAn : 0.0f;
+      }
+      if constexpr (n % G == G - 1) {
+        // end of a group of G states: sum the waves' partials and add them
+        // to dB, dC (block-uniform condition: N is the same for all threads)
+        constexpr int n0 = n - (G - 1);
+        constexpr int buf = (n / G) & 1;
+        if (n0 < N) {
+          __syncthreads();
+#pragma unroll 1
+          for (int s = 0; s < 2 * G * TCH / kBlock; ++s) {
+            const int i = s * kBlock + tid;
+            const int which = i / (G * TCH);
+            const int nn = (i / TCH) % G;
+            const int pos = i % TCH;
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v += red[buf][w][which][nn][pos];
+            const int tt = (pos % 16) * K + pos / 16;
+            if (n0 + nn < N && t0 + tt < L)
+              unsafeAtomicAdd((which ? p.dC : p.dB) + (b * N + n0 + nn) * L + t0 + tt, v);
+          }
+        }
       }
       mem_fence_compiler();
     });
@@ -393,23 +424,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       }
       if (active) store_items<float, K>(p.dz + c * L, tl, L, full, dzv);
     }
-    __syncthreads();
-    // all waves are done with this chunk: flush its dB/dC sums, clear them,
-    // and refill the tile with the earlier chunk
-    for (int i = tid; i < 2 * NT * TCH; i += kBlock) {
-      const int which = i / (NT * TCH);
-      const int rest = i - which * NT * TCH;
-      const int n = rest / TCH, tt = rest - n * TCH;
-      float* slot = &acc[which][n][tt];
-      const float v = *slot;
-      *slot = 0.0f;
-      const int64_t t = t0 + tt;
-      if (n < N && t < L) unsafeAtomicAdd((which ? p.dC : p.dB) + (b * N + n) * L + t, v);
+    // every wave is past the last group barrier, so no wave still reads the
+    // tile: refill it with the earlier chunk.  The barrier also keeps the
+    // next chunk's slice stores behind this chunk's last flush.
+    if (ch > 0) {
+      if constexpr (TILE) stage.store(reinterpret_cast<float*>(tile_mem), N, tid);
+      __syncthreads();
     }
-    if constexpr (TILE) {
-      if (ch > 0) stage.store(reinterpret_cast<float*>(tile_mem), N, tid);
-    }
-    __syncthreads();
   }
 
   // ---- per-channel results: dh0, dA (over batch rows), dD, ddelta_bias ----
