@@ -36,6 +36,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+# float32 vector peak without packed math: 256 CUs x 64 lanes x 2 flops (FMA)
+# x 2.4 GHz.  The chip's published 157.3 TFLOP/s counts packed FP32, which
+# these kernels do not use.
+PEAK_F32_TFLOPS = 78.6
+PEAK_F32_PACKED_TFLOPS = 157.3
+# Algorithmic float32 work per (t, n) (an exp counts as one flop):
+#   forward : dA 1, exp 1, ZOH Bbar*u 4, h update 2, y accumulate 2       = 10
+#   backward: forward replay incl. y 10, adjoint 3, ddelta 6, dA 5, du 5,
+#             dB 2, dC 2                                                  = 33 (+1 exp)
+FLOPS_PER_TN = {"fwd": 10, "bwd": 34}
 CSRC = os.path.join(ROOT, "scan_selective_fwd_amd", "csrc")
 # Sources each timed kernel is compiled from (its counter summary is void
 # once any of them changes).
@@ -218,6 +228,10 @@ def main():
         ws = torch.empty(ms.bwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen,
                                                 g["u"].dtype), dtype=torch.uint8, device="cuda")
     sdt = g["u"].dtype
+    fws = None
+    nfws = ms.fwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen, sdt)
+    if nfws:
+        fws = torch.empty(nfws, dtype=torch.uint8, device="cuda")
     t_last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device="cuda")
     t_out = torch.empty_like(g["u"])
     step_args = {k: g[k][..., 0].contiguous() for k in ("u", "delta", "B", "C", "z")}
@@ -227,7 +241,7 @@ def main():
         if c == "fwd":
             ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
                         g["delta_bias"], disc=args.disc, out=t_out, last_state=t_last,
-                        return_last_state=True, timing=timing)
+                        return_last_state=True, workspace=fws, timing=timing)
         elif c == "bwd":
             ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
                         g["delta_bias"], g["dout"], disc=args.disc, workspace=ws, timing=timing)
@@ -301,16 +315,27 @@ def main():
         "per_call": per_call,
     }
     if kern_ms:
+        # The scan kernels are bound by float32 vector arithmetic (their VALU
+        # issue rate is the limit; HBM runs far below its peak), so the roofline
+        # is the ALU one; the HBM view of the same launch is reported beside it.
         dom = max(kern_ms, key=lambda c: kern_ms[c])
         kname = kernel_names[dom]
         dom_bytes = algorithmic_bytes(w, dom)
-        achieved = dom_bytes / (kern_ms[dom] * 1e-3) / 1e9
+        dom_flops = FLOPS_PER_TN[dom] * w.batch * w.dim * w.seqlen * w.dstate
+        secs = kern_ms[dom] * 1e-3
+        tflops = dom_flops / secs / 1e12
+        gbs = dom_bytes / secs / 1e9
         wl_tag = f"w{w.wid}_{args.disc}"
-        res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                           "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+        res["roofline"] = {"bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_F32_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_F32_TFLOPS, 4),
                            "traffic": committed_traffic(kname, wl_tag),
                            "kernel": kname, "call": f"mamba_scan_{dom}",
-                           "algorithmic_bytes_per_launch": int(dom_bytes),
+                           "algorithmic_flops_per_launch": int(dom_flops),
+                           "flops_per_state_step": FLOPS_PER_TN[dom],
+                           "peak_with_packed_fp32": PEAK_F32_PACKED_TFLOPS,
+                           "hbm": {"achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS,
+                                   "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                   "algorithmic_bytes_per_launch": int(dom_bytes)},
                            "avg_launch_ms": round(kern_ms[dom], 5),
                            "kernel_source_sha256": kernel_source_hash(kname)}
     if not args.no_cpu_baseline:

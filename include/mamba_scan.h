@@ -101,7 +101,15 @@ int mamba_abi_version(void);
 const char* mamba_status_string(mamba_status status);
 
 /* Bytes of device workspace mamba_scan_fwd needs for these sizes (may be 0;
- * then workspace may be NULL).  Returns SIZE_MAX for unsupported sizes. */
+ * then workspace may be NULL).  Returns SIZE_MAX for unsupported sizes.
+ * It is non-zero when the sequence is long and the channels alone would give
+ * too few workgroups to fill the GPU: the forward then splits the sequence
+ * into segments that run in parallel, joined by an exact carry of the state
+ * (the associative scan composition of trishampatil essay, Part III §2, with
+ * the chunking of its Part III §4).  The workspace holds, per channel and
+ * segment, the segment's end state, its entering state (float32, dstate
+ * each) and its delta sum.  mamba_scan_fwd given a smaller workspace (or
+ * NULL) still works, in one pass over the sequence (slower for such shapes). */
 size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                      mamba_dtype dt);
 
@@ -164,21 +172,31 @@ mamba_status mamba_state_update(float* state, const void* u, const void* delta, 
  *    the choice beyond float32 rounding order; tests and launch-shape sweeps
  *    use it.  mamba_scan_bwd_ex needs the workspace reported by
  *    mamba_scan_bwd_workspace_size_ex for the same lanes value.
+ *  - segments (forward only): 0 = automatic (as mamba_scan_fwd), 1 = one pass
+ *    over the sequence, k >= 2 = split the sequence into k segments (at most
+ *    one per 128-step chunk).  Segmented runs need the workspace reported by
+ *    mamba_scan_fwd_workspace_size_ex for the same lanes and segments values
+ *    (MAMBA_ERR_WORKSPACE otherwise) and 16 lanes per channel.
  *  - timing_begin, timing_end: hipEvent_t handles (NULL = none).  When given,
  *    they are recorded on `stream` immediately before and after the main
- *    scan kernel of the call (the forward's only kernel; the backward's
- *    reverse-scan kernel, after its state-recompute and zeroing kernels have
- *    been enqueued), so a caller can time that kernel alone with
- *    hipEventElapsedTime.  The caller owns the events; failure to record one
- *    returns MAMBA_ERR_HIP.
+ *    scan kernel of the call (the forward's output kernel, after a segmented
+ *    run's summary and carry kernels; the backward's reverse-scan kernel,
+ *    after its state-recompute and zeroing kernels have been enqueued), so a
+ *    caller can time that kernel alone with hipEventElapsedTime.  The caller
+ *    owns the events; failure to record one returns MAMBA_ERR_HIP.
  */
+size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
+                                        int64_t seqlen, mamba_dtype dt, int lanes_per_channel,
+                                        int segments);
+
 mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
                                const void* C, const float* D, const void* z,
                                const float* delta_bias, const float* h0, int delta_softplus,
                                mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
                                int64_t dstate, int64_t seqlen, void* out, float* last_state,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel, void* timing_begin, void* timing_end);
+                               int lanes_per_channel, int segments, void* timing_begin,
+                               void* timing_end);
 
 size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
                                         int64_t seqlen, mamba_dtype dt, int lanes_per_channel);

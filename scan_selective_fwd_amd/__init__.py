@@ -87,10 +87,12 @@ def _events(timing):
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
              delta_softplus=True, disc="zoh", return_last_state=False, out=None, last_state=None,
-             lanes=0, timing=None):
+             lanes=0, segments=0, workspace=None, timing=None):
     """Fused selective-scan forward.  Returns out, or (out, last_state).
+    `segments`: 0 automatic, 1 one pass, k >= 2 that many sequence segments.
+    `workspace`: optional uint8 device tensor reused across calls.
     `timing`: optional (begin, end) torch.cuda.Event pair recorded around the
-    scan kernel on the current stream."""
+    output kernel on the current stream."""
     L_ = lib()
     if not u.is_cuda:
         raise ValueError("u must be a GPU tensor (no CPU path exists)")
@@ -114,13 +116,25 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
     if return_last_state and last_state is None:
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _req(last_state, "last_state", torch.float32, (batch, dim, N), dev)
+    nbytes = fwd_workspace_bytes(batch, dim, N, L, sdt, lanes, segments)
+    if nbytes and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if nbytes else None
     st = L_.mamba_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                               _ptr(delta_bias), _ptr(h0), int(bool(delta_softplus)),
                               _disc_code(disc), dt, batch, dim, N, L, _ptr(out),
-                              _ptr(last_state), None, 0, _stream(dev), int(lanes),
-                              *_events(timing))
+                              _ptr(last_state), ws_ptr, nbytes, _stream(dev), int(lanes),
+                              int(segments), *_events(timing))
     _lib.check(st, "mamba_scan_fwd")
     return (out, last_state) if return_last_state else out
+
+
+def fwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0, segments=0) -> int:
+    code = F32 if dtype == torch.float32 else BF16
+    n = lib().mamba_scan_fwd_workspace_size_ex(batch, dim, N, L, code, int(lanes), int(segments))
+    if n >= 2 ** 63:
+        raise MambaScanError(6, "mamba_scan_fwd_workspace_size")
+    return int(n)
 
 
 def bwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0) -> int:

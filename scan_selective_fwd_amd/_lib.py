@@ -23,7 +23,8 @@ ZOH, EULER = 0, 1
 EXPORTS = (
     "mamba_abi_version", "mamba_status_string", "mamba_scan_fwd_workspace_size",
     "mamba_scan_bwd_workspace_size", "mamba_scan_fwd", "mamba_scan_bwd", "mamba_state_update",
-    "mamba_scan_fwd_ex", "mamba_scan_bwd_workspace_size_ex", "mamba_scan_bwd_ex",
+    "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size_ex", "mamba_scan_bwd_workspace_size_ex",
+    "mamba_scan_bwd_ex",
 )
 
 
@@ -59,13 +60,15 @@ def load(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.restype = _sz
         f.argtypes = [_i64, _i64, _i64, _i64, _int]
+    lib.mamba_scan_fwd_workspace_size_ex.restype = _sz
+    lib.mamba_scan_fwd_workspace_size_ex.argtypes = [_i64, _i64, _i64, _i64, _int, _int, _int]
     lib.mamba_scan_bwd_workspace_size_ex.restype = _sz
     lib.mamba_scan_bwd_workspace_size_ex.argtypes = [_i64, _i64, _i64, _i64, _int, _int]
     fwd_args = [_vp] * 9 + [_int, _int, _int] + [_i64] * 4 + [_vp, _vp, _vp, _sz, _vp]
     lib.mamba_scan_fwd.restype = _int
     lib.mamba_scan_fwd.argtypes = fwd_args
     lib.mamba_scan_fwd_ex.restype = _int
-    lib.mamba_scan_fwd_ex.argtypes = fwd_args + [_int, _vp, _vp]
+    lib.mamba_scan_fwd_ex.argtypes = fwd_args + [_int, _int, _vp, _vp]
     bwd_args = [_vp] * 10 + [_int, _int, _int] + [_i64] * 4 + [_vp] * 10 + [_sz, _vp]
     lib.mamba_scan_bwd.restype = _int
     lib.mamba_scan_bwd.argtypes = bwd_args

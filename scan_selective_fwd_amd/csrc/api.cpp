@@ -52,6 +52,47 @@ mamba_status check_sizes(mamba_dtype dt, int disc, int64_t batch, int64_t dim, i
   return MAMBA_OK;
 }
 
+// Forward segmentation.  When a sequence is long and its channels alone give
+// too few blocks to fill the chip, the sequence is split into segments run in
+// parallel: a summary launch (each segment's end state from zero and its
+// delta sum), a carry launch (the state entering each segment) and the
+// output launch.  Segments are whole chunks of 16 lanes x kItems steps.
+constexpr int64_t kFwdChunk = 16 * kItems;
+
+int64_t auto_segments(int64_t batch, int64_t dim, int64_t seqlen) {
+  const int64_t blocks = batch * mscan::channel_groups(dim, 16);
+  if (blocks >= 1024) return 1;
+  const int64_t nchunks = (seqlen + kFwdChunk - 1) / kFwdChunk;
+  int64_t nseg = (3072 + blocks - 1) / blocks;
+  const int64_t cap = nchunks / 16;   // segments of at least 16 chunks
+  if (nseg > cap) nseg = cap;
+  return nseg < 1 ? 1 : nseg;
+}
+
+// Forward workspace (segmented only): the segment end states and the
+// entering states (nchannels, nseg, dstate) float32, then the delta sums
+// (nchannels, nseg).
+struct FwdLayout {
+  int64_t nseg, seg_chunks;
+  size_t off_h0, off_dsum, total;
+};
+
+FwdLayout fwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                     int64_t segments) {
+  FwdLayout w = {1, 0, 0, 0, 0};
+  const int64_t nchunks = (seqlen + kFwdChunk - 1) / kFwdChunk;
+  int64_t nseg = segments < nchunks ? segments : nchunks;
+  if (nseg <= 1) return w;
+  w.seg_chunks = (nchunks + nseg - 1) / nseg;
+  w.nseg = (nchunks + w.seg_chunks - 1) / w.seg_chunks;
+  if (w.nseg <= 1) return FwdLayout{1, 0, 0, 0, 0};
+  const size_t nst = (size_t)(batch * dim) * (size_t)w.nseg * (size_t)dstate * 4;
+  w.off_h0 = round_up(nst);
+  w.off_dsum = w.off_h0 + round_up(nst);
+  w.total = w.off_dsum + round_up((size_t)(batch * dim) * (size_t)w.nseg * 4);
+  return w;
+}
+
 // Backward workspace: the chunk-start states (nchannels, nchunks, dstate)
 // float32, then one int flag per block.
 struct BwdLayout {
@@ -92,10 +133,23 @@ const char* mamba_status_string(mamba_status s) {
   return "unknown status";
 }
 
+size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
+                                        int64_t seqlen, mamba_dtype dt, int lanes_per_channel,
+                                        int segments) {
+  if (check_sizes(dt, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK) return SIZE_MAX;
+  if (segments < 0) return SIZE_MAX;
+  const int64_t want = segments != 0 ? segments
+                       : (lanes_per_channel != 0 && lanes_per_channel != 16)
+                           ? 1   // an explicit wider lane layout runs in one pass
+                           : auto_segments(batch, dim, seqlen);
+  const FwdLayout w = fwd_layout(batch, dim, dstate, seqlen, want);
+  if (w.nseg > 1 && lanes_per_channel != 0 && lanes_per_channel != 16) return SIZE_MAX;
+  return w.total;
+}
+
 size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                      mamba_dtype dt) {
-  if (check_sizes(dt, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK) return SIZE_MAX;
-  return 0;
+  return mamba_scan_fwd_workspace_size_ex(batch, dim, dstate, seqlen, dt, 0, 0);
 }
 
 // Workspace of mamba_scan_bwd_ex for a lanes-per-channel choice.  The
@@ -120,16 +174,29 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
                                mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
                                int64_t dstate, int64_t seqlen, void* out, float* last_state,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel, void* timing_begin, void* timing_end) {
-  (void)workspace;
-  (void)workspace_bytes;
+                               int lanes_per_channel, int segments, void* timing_begin,
+                               void* timing_end) {
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
   if (st != MAMBA_OK) return st;
   if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL_PTR;
-  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, out, last_state};
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, out, last_state, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MAMBA_ERR_ALIGNMENT;
-  int lanes = lanes_per_channel;
+  if (segments < 0) return MAMBA_ERR_UNSUPPORTED;
+  const int64_t want = segments != 0 ? segments
+                       : (lanes_per_channel != 0 && lanes_per_channel != 16)
+                           ? 1   // an explicit wider lane layout runs in one pass
+                           : auto_segments(batch, dim, seqlen);
+  const FwdLayout w = fwd_layout(batch, dim, dstate, seqlen, want);
+  bool segmented = w.nseg > 1;
+  if (segmented) {
+    if (lanes_per_channel != 0 && lanes_per_channel != 16) return MAMBA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < w.total) {
+      if (segments != 0) return MAMBA_ERR_WORKSPACE;
+      segmented = false;   // automatic choice without the workspace: one pass
+    }
+  }
+  int lanes = segmented ? 16 : lanes_per_channel;
   if (lanes == 0) lanes = choose_lanes(batch * dim, seqlen, kItems);
   if (!valid_lanes(lanes)) return MAMBA_ERR_UNSUPPORTED;
 
@@ -140,12 +207,25 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.groups = mscan::channel_groups(dim, lanes);
   p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
-  if (batch * p.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
+  p.nseg = 1;
+  p.seg_chunks = 0;
+  if (batch * p.groups * w.nseg > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
   const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  const int dti = dt == MAMBA_F32 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (segmented) {
+    char* ws = static_cast<char*>(workspace);
+    p.nseg = w.nseg;
+    p.seg_chunks = w.seg_chunks;
+    p.seg_state = reinterpret_cast<float*>(ws);
+    p.seg_h0 = reinterpret_cast<float*>(ws + w.off_h0);
+    p.seg_dsum = reinterpret_cast<float*>(ws + w.off_dsum);
+    if (mscan::dispatch_seg_summary(p, dti, (int)disc, vec, s) != hipSuccess) return MAMBA_ERR_HIP;
+    if (mscan::dispatch_seg_carry(p, s) != hipSuccess) return MAMBA_ERR_HIP;
+  }
   if (timing_begin && hipEventRecord(static_cast<hipEvent_t>(timing_begin), s) != hipSuccess)
     return MAMBA_ERR_HIP;
-  if (mscan::dispatch_scan_fwd(p, dt == MAMBA_F32 ? 0 : 1, (int)disc, lanes, vec, s) != hipSuccess)
+  if (mscan::dispatch_scan_fwd(p, dti, (int)disc, lanes, vec, s) != hipSuccess)
     return MAMBA_ERR_HIP;
   if (timing_end && hipEventRecord(static_cast<hipEvent_t>(timing_end), s) != hipSuccess)
     return MAMBA_ERR_HIP;
@@ -160,7 +240,7 @@ mamba_status mamba_scan_fwd(const void* u, const void* delta, const float* A, co
                             void* workspace, size_t workspace_bytes, void* stream) {
   return mamba_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, disc, dt,
                            batch, dim, dstate, seqlen, out, last_state, workspace,
-                           workspace_bytes, stream, 0, nullptr, nullptr);
+                           workspace_bytes, stream, 0, 0, nullptr, nullptr);
 }
 
 mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
@@ -201,6 +281,8 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   fp.chunk_states = states;
   fp.batch = batch; fp.dim = dim; fp.L = seqlen; fp.nchannels = batch * dim;
   fp.groups = w.groups;
+  fp.nseg = 1;
+  fp.seg_chunks = 0;
   fp.N = (int)dstate; fp.softplus = delta_softplus ? 1 : 0;
   hipError_t e = mscan::dispatch_chunk_states(fp, dti, (int)disc, lanes, vec, s);
   if (e != hipSuccess) return MAMBA_ERR_HIP;

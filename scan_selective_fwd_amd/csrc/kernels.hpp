@@ -29,8 +29,23 @@ struct FwdParams {
   int64_t batch, dim, L;
   int64_t nchannels;       // batch * dim
   int64_t groups;          // channel groups per batch row (one block each)
+  // Sequence segments (long sequences with few channels): each block covers
+  // seg_chunks chunks of one channel group.  seg_chunks = 0, nseg = 1: the
+  // whole sequence.
+  int64_t seg_chunks;
+  int64_t nseg;
+  float* seg_h0;           // (nchannels, nseg, N): state entering each segment
+  float* seg_state;        // summary mode: (nchannels, nseg, N) end state from a zero start
+  float* seg_dsum;         // summary mode: (nchannels, nseg) sum of delta over the segment
   int N;
   int softplus;
+};
+
+// What a forward-kernel launch computes.
+enum FwdMode : int {
+  kModeOut = 0,           // outputs (and the last state)
+  kModeChunkStates = 1,   // only the state at every chunk start (backward recompute)
+  kModeSegSummary = 2,    // only each segment's end state from zero and its delta sum
 };
 
 struct BwdParams {
@@ -95,6 +110,16 @@ hipError_t dispatch_chunk_states_f32(const FwdParams& p, int disc, int lanes, bo
                                      hipStream_t s);
 hipError_t dispatch_chunk_states_bf16(const FwdParams& p, int disc, int lanes, bool vec,
                                       hipStream_t s);
+// Segmented forward, first two launches: per-segment summaries (16 lanes per
+// channel) and the sequential carry over segments.
+hipError_t dispatch_seg_summary_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_seg_summary_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_seg_carry(const FwdParams& p, hipStream_t s);
+inline hipError_t dispatch_seg_summary(const FwdParams& p, int dtype, int disc, bool vec,
+                                       hipStream_t s) {
+  return dtype == 0 ? dispatch_seg_summary_f32(p, disc, vec, s)
+                    : dispatch_seg_summary_bf16(p, disc, vec, s);
+}
 inline hipError_t dispatch_scan_fwd(const FwdParams& p, int dtype, int disc, int lanes, bool vec,
                                     hipStream_t s) {
   return dtype == 0 ? dispatch_scan_fwd_f32(p, disc, lanes, vec, s)

@@ -66,10 +66,18 @@ __device__ __forceinline__ void store_items(T* __restrict__ row, int64_t t, int6
   }
 }
 
-// STATES = true is the backward's recompute pass: it only writes the state
-// at the start of every chunk (to p.chunk_states) and skips C, z, y and out.
-template <typename T, int R, int K, int NT, bool ZOH, bool VEC, bool STATES>
+// MODE (FwdMode): kModeOut computes the outputs.  kModeChunkStates is the
+// backward's recompute pass: it only writes the state at the start of every
+// chunk (to p.chunk_states).  kModeSegSummary runs one segment of a long
+// sequence from a zero state and writes its end state and delta sum.  The
+// two state-only modes skip C, z, y and out.
+//
+// A block serves one channel group of one batch row, for the whole sequence
+// or (p.seg_chunks > 0) for one segment of it; the segment's entering state
+// then comes from p.seg_h0, which the carry kernel filled from the summaries.
+template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE>
 __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
+  constexpr bool STATES = MODE != kModeOut;
   constexpr int CPW = 64 / R;   // channels per wave
   constexpr int CPB = (kBlock / 64) * CPW;
   constexpr int TCH = R * K;    // steps per chunk
@@ -86,9 +94,13 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
   const int wave = tid >> 6;
   const int j = lane % R;
   const int cl = wave * CPW + lane / R;       // channel slot in the block
+  // block order (b, segment, group) with the group fastest: consecutive
+  // blocks share the B/C rows of one segment
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t b = blk / p.groups;
-  const int64_t grp = blk - b * p.groups;
+  const int64_t per_b = p.groups * p.nseg;
+  const int64_t b = blk / per_b;
+  const int64_t seg = (blk - b * per_b) / p.groups;
+  const int64_t grp = blk - b * per_b - seg * p.groups;
   const int64_t d_raw = grp * CPB + cl;
   const bool active = d_raw < p.dim;
   const int64_t d = active ? d_raw : p.dim - 1;
@@ -120,36 +132,47 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
 
   // Carried state per n.  Only the FIRST lane of each channel's group holds
   // it (it is folded into that lane's summary before the scan).
+  const int64_t nchunks = (L + TCH - 1) / TCH;
+  const int64_t ch_begin = p.seg_chunks > 0 ? seg * p.seg_chunks : 0;
+  const int64_t ch_end =
+      p.seg_chunks > 0 ? (ch_begin + p.seg_chunks < nchunks ? ch_begin + p.seg_chunks : nchunks)
+                       : nchunks;
+  const float* h_enter = nullptr;
+  if constexpr (MODE == kModeOut)
+    h_enter = p.seg_h0 ? p.seg_h0 + (c * p.nseg + seg) * N : (p.h0 ? p.h0 + c * N : nullptr);
+  else if constexpr (MODE == kModeChunkStates)
+    h_enter = p.h0 ? p.h0 + c * N : nullptr;
   float cr[NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) cr[n] = (n < N && p.h0) ? p.h0[c * N + n] : 0.0f;
+  for (int n = 0; n < NT; ++n) cr[n] = (n < N && h_enter) ? h_enter[n] : 0.0f;
 
-  const int64_t nchunks = (L + TCH - 1) / TCH;
   TileStager<T, TCH, K, NT, TILE ? TROWS : 1, kBlock> stage;
   float nu[K], nd[K];
   {
-    const bool full0 = VEC && TCH <= L;
+    const int64_t tb = ch_begin * TCH;
+    const bool full0 = VEC && tb + TCH <= L;
     if constexpr (TILE) {
-      stage.load(B_b, C_b, N, L, 0, full0, tid);
+      stage.load(B_b, C_b, N, L, tb, full0, tid);
       stage.store(reinterpret_cast<float*>(tile_mem[0]), N, tid);
     }
-    load_items<T, K>(u_row, (int64_t)j * K, L, full0, nu);
-    load_items<T, K>(dl_row, (int64_t)j * K, L, full0, nd);
+    load_items<T, K>(u_row, tb + (int64_t)j * K, L, full0, nu);
+    load_items<T, K>(dl_row, tb + (int64_t)j * K, L, full0, nd);
   }
+  float dtot = 0.0f;   // this lane's delta sum over the block's chunks
   // barrier for the LDS fills; also: does any channel of the block have A ~ 0?
   const bool any_tiny = __syncthreads_or(my_tiny);
 
   {
-    for (int64_t ch = 0; ch < nchunks; ++ch) {
-      const int buf = (int)(ch & 1);
+    for (int64_t ch = ch_begin; ch < ch_end; ++ch) {
+      const int buf = (int)((ch - ch_begin) & 1);
       const int64_t t0 = ch * TCH;
       const int64_t tl = t0 + (int64_t)j * K;   // this lane's first step
       const bool full = VEC && t0 + TCH <= L;
-      const bool more = ch + 1 < nchunks;
+      const bool more = ch + 1 < ch_end;
       const bool full_next = VEC && t0 + 2 * TCH <= L;
       const int64_t rem = L - tl;
       const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
-      if constexpr (STATES) {
+      if constexpr (MODE == kModeChunkStates) {
         if (active && j == 0) {
           float* dst = p.chunk_states + (c * nchunks + ch) * N;
 #pragma unroll
@@ -185,6 +208,7 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
         y[k] = Dd * uv[k];
         if constexpr (!ZOH) uv[k] = s * uv[k];   // Euler: Bbar u = B (delta u)
       }
+      dtot += dsum;
 
       const float* tB = reinterpret_cast<const float*>(tile_mem[buf]);
       // operands of state index n + 1 are read while n is computed
@@ -268,42 +292,51 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
     }
   }
 
-  if (!STATES && active && j == 0 && p.last_state) {
+  if (MODE == kModeOut && active && j == 0 && p.last_state && seg == p.nseg - 1) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
       if (n < N) p.last_state[c * N + n] = cr[n];
   }
+  if constexpr (MODE == kModeSegSummary) {
+    const float dseg = group_sum<R>(dtot);
+    if (active && j == 0) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        if (n < N) p.seg_state[(c * p.nseg + seg) * N + n] = cr[n];
+      p.seg_dsum[c * p.nseg + seg] = dseg;
+    }
+  }
 }
 
-template <typename T, int R, int K, int NT, bool ZOH, bool VEC, bool STATES>
+template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE>
 static hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
-  const int64_t nblocks = p.batch * p.groups;
-  hipLaunchKernelGGL((scan_fwd_kernel<T, R, K, NT, ZOH, VEC, STATES>), dim3((unsigned)nblocks),
+  const int64_t nblocks = p.batch * p.groups * p.nseg;
+  hipLaunchKernelGGL((scan_fwd_kernel<T, R, K, NT, ZOH, VEC, MODE>), dim3((unsigned)nblocks),
                      dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
 // N <= 16 takes the NT = 16 kernel, 16 < N <= 64 the NT = 64 kernel.
-template <typename T, int R, int K, bool ZOH, bool STATES>
+template <typename T, int R, int K, bool ZOH, int MODE>
 static hipError_t fwd_nv(const FwdParams& p, bool vec, hipStream_t s) {
   if (p.N <= 16)
-    return vec ? launch_fwd<T, R, K, 16, ZOH, true, STATES>(p, s)
-               : launch_fwd<T, R, K, 16, ZOH, false, STATES>(p, s);
-  return vec ? launch_fwd<T, R, K, 64, ZOH, true, STATES>(p, s)
-             : launch_fwd<T, R, K, 64, ZOH, false, STATES>(p, s);
+    return vec ? launch_fwd<T, R, K, 16, ZOH, true, MODE>(p, s)
+               : launch_fwd<T, R, K, 16, ZOH, false, MODE>(p, s);
+  return vec ? launch_fwd<T, R, K, 64, ZOH, true, MODE>(p, s)
+             : launch_fwd<T, R, K, 64, ZOH, false, MODE>(p, s);
 }
 
-template <typename T, int K, bool STATES>
+template <typename T, int K, int MODE>
 static hipError_t dispatch_fwd_t(const FwdParams& p, int disc, int lanes, bool vec,
                                  hipStream_t s) {
   const bool zoh = disc == 0;
   switch (lanes) {
     case 16:
-      return zoh ? fwd_nv<T, 16, K, true, STATES>(p, vec, s) : fwd_nv<T, 16, K, false, STATES>(p, vec, s);
+      return zoh ? fwd_nv<T, 16, K, true, MODE>(p, vec, s) : fwd_nv<T, 16, K, false, MODE>(p, vec, s);
     case 32:
-      return zoh ? fwd_nv<T, 32, K, true, STATES>(p, vec, s) : fwd_nv<T, 32, K, false, STATES>(p, vec, s);
+      return zoh ? fwd_nv<T, 32, K, true, MODE>(p, vec, s) : fwd_nv<T, 32, K, false, MODE>(p, vec, s);
     default:
-      return zoh ? fwd_nv<T, 64, K, true, STATES>(p, vec, s) : fwd_nv<T, 64, K, false, STATES>(p, vec, s);
+      return zoh ? fwd_nv<T, 64, K, true, MODE>(p, vec, s) : fwd_nv<T, 64, K, false, MODE>(p, vec, s);
   }
 }
 

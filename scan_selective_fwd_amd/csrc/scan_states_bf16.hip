@@ -6,7 +6,7 @@ namespace mscan {
 
 hipError_t dispatch_chunk_states_bf16(const FwdParams& p, int disc, int lanes, bool vec,
                                       hipStream_t stream) {
-  return dispatch_fwd_t<bf16_t, kItemsBwd, true>(p, disc, lanes, vec, stream);
+  return dispatch_fwd_t<bf16_t, kItemsBwd, kModeChunkStates>(p, disc, lanes, vec, stream);
 }
 
 }  // namespace mscan

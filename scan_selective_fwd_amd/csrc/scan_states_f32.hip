@@ -6,7 +6,7 @@ namespace mscan {
 
 hipError_t dispatch_chunk_states_f32(const FwdParams& p, int disc, int lanes, bool vec,
                                       hipStream_t stream) {
-  return dispatch_fwd_t<float, kItemsBwd, true>(p, disc, lanes, vec, stream);
+  return dispatch_fwd_t<float, kItemsBwd, kModeChunkStates>(p, disc, lanes, vec, stream);
 }
 
 }  // namespace mscan

@@ -70,6 +70,39 @@ def test_workspace_queries(lib):
         assert lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, lanes) == 2 ** 64 - 1
 
 
+def test_forward_segment_workspace(lib):
+    # a long sequence over few channels is split into segments: 1536 channels
+    # are 96 blocks, so 32 segments of 256 chunks; per channel and segment two
+    # states of 16 floats and one delta sum
+    n = lib.mamba_scan_fwd_workspace_size(1, 1536, 16, 1 << 20, 1)
+    assert n == 2 * (1536 * 32 * 16 * 4) + 1536 * 32 * 4
+    assert lib.mamba_scan_fwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 0, 0) == n
+    assert lib.mamba_scan_fwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 16, 0) == n
+    # one pass: no workspace; explicit wider lanes run in one pass as well
+    assert lib.mamba_scan_fwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 0, 1) == 0
+    assert lib.mamba_scan_fwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 64, 0) == 0
+    # explicit segments need 16 lanes; more segments than chunks are capped
+    assert lib.mamba_scan_fwd_workspace_size_ex(1, 16, 4, 1024, 0, 32, 2) == 2 ** 64 - 1
+    assert (lib.mamba_scan_fwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, 100)
+            == lib.mamba_scan_fwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, 8))
+    assert lib.mamba_scan_fwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, -1) == 2 ** 64 - 1
+
+
+def fwd_ex(lib, segments, ws=None, wsb=0, lanes=0):
+    return lib.mamba_scan_fwd_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 1, 16, 4, 1024,
+                                 P, None, ws, wsb, None, lanes, segments, None, None)
+
+
+def test_forward_segment_arguments(lib):
+    need = lib.mamba_scan_fwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, 3)
+    assert need > 0
+    assert fwd_ex(lib, 3) == 5                          # explicit segments, no workspace
+    assert fwd_ex(lib, 3, ws=P, wsb=need - 1) == 5
+    assert fwd_ex(lib, 3, ws=P + 8, wsb=need) == 4      # misaligned workspace
+    assert fwd_ex(lib, 3, lanes=64) == 6                # segments need 16 lanes
+    assert fwd_ex(lib, -2) == 6
+
+
 P = 4096  # a 16-byte aligned fake address; never dereferenced (calls fail first)
 
 

@@ -38,10 +38,10 @@ def _positive_steps(inp, dtype):
 
 
 def run_fwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=False, opts=None,
-                 zero_A=False, A_mode="s4d_real", rtol=None):
+                 zero_A=False, A_mode="s4d_real", rtol=None, segments=0):
     opts = opts or {}
     announce(f"fwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} lanes={lanes} "
-             f"softplus={softplus} h0={h0} opts={opts} zero_A={zero_A}")
+             f"softplus={softplus} h0={h0} opts={opts} zero_A={zero_A} segments={segments}")
     inp, f = _make(wid, batch, dim, N, L, dtype, A_mode=A_mode, **opts)
     if not softplus:
         inp, f = _positive_steps(inp, dtype)
@@ -55,7 +55,7 @@ def run_fwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=
     h0t = torch.from_numpy(h0v).cuda() if h0v is not None else None
     out, last = ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g.get("D"), g.get("z"),
                             g.get("delta_bias"), h0t, delta_softplus=softplus, disc=disc,
-                            return_last_state=True, lanes=lanes)
+                            return_last_state=True, lanes=lanes, segments=segments)
     torch.cuda.synchronize()
     ref, ref_last = _oracle_fwd(f, disc, softplus, None if h0v is None else h0v.astype(np.float64))
     rt = rtol or RTOL[dtype]
@@ -110,6 +110,30 @@ def test_fwd_initial_state(dtype):
 def test_fwd_zero_A_limit():
     run_fwd_case(17, 2, 12, 16, 400, "f32", "zoh", zero_A=True)
     run_fwd_case(17, 2, 12, 16, 400, "f32", "zoh", zero_A=True, lanes=64)
+
+
+@pytest.mark.parametrize("segments", [2, 3, 10])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_fwd_segmented(segments, dtype, disc):
+    # the sequence split into segments joined by the carry kernel: 1189 steps
+    # are 9 full 128-step chunks and a ragged one (10 segments = one chunk
+    # each); 20 channels leave the second channel group partial
+    run_fwd_case(19, 1, 20, 16, 1189, dtype, disc, segments=segments)
+
+
+def test_fwd_segmented_state_sizes_initial_state_zero_A():
+    run_fwd_case(20, 2, 9, 5, 1300, "f32", "zoh", segments=4, h0=True)
+    run_fwd_case(20, 2, 9, 33, 1300, "f32", "zoh", segments=4, A_mode="random_neg")
+    run_fwd_case(21, 1, 12, 16, 1024, "f32", "zoh", segments=8, zero_A=True, h0=True)
+    run_fwd_case(21, 1, 12, 16, 1024, "f32", "euler", segments=5, softplus=False, h0=True)
+
+
+def test_fwd_automatic_segmentation():
+    # few channels over a long sequence: the automatic choice splits it
+    assert ms.fwd_workspace_bytes(1, 16, 16, 8192, torch.bfloat16) > 0
+    run_fwd_case(22, 1, 16, 16, 8192, "bf16", "zoh")
+    run_fwd_case(22, 1, 16, 16, 8192, "bf16", "zoh", segments=1)
 
 
 def test_fwd_is_deterministic_and_lane_choice_independent():
