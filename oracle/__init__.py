@@ -42,6 +42,7 @@ _lib = None
 _lib_lock = threading.Lock()
 
 _dp = ctypes.POINTER(ctypes.c_double)
+_u8p = ctypes.POINTER(ctypes.c_ubyte)
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
 
@@ -56,11 +57,11 @@ def _load():
 
             _build.build()
         lib = ctypes.CDLL(_LIB_PATH)
-        lib.oracle_scan_fwd.argtypes = [_dp] * 9 + [_int, _int] + [_i64] * 6 + [_dp, _dp]
+        lib.oracle_scan_fwd.argtypes = [_dp] * 9 + [_u8p, _int, _int] + [_i64] * 6 + [_dp, _dp]
         lib.oracle_scan_fwd.restype = None
         lib.oracle_state_update.argtypes = [_dp] * 9 + [_int, _int] + [_i64] * 5 + [_dp]
         lib.oracle_state_update.restype = None
-        lib.oracle_scan_bwd.argtypes = [_dp] * 10 + [_int, _int] + [_i64] * 6 + [_dp] * 9
+        lib.oracle_scan_bwd.argtypes = [_dp] * 10 + [_u8p, _int, _int] + [_i64] * 6 + [_dp] * 9
         lib.oracle_scan_bwd.restype = None
         lib.oracle_version.restype = _int
         _lib = lib
@@ -78,6 +79,19 @@ def _ptr(a):
     if a is None:
         return None
     return a.ctypes.data_as(_dp)
+
+
+def _reset(reset, batch, L):
+    """Contiguous uint8 (batch, L) copy of the reset flags (None stays None)."""
+    if reset is None:
+        return None
+    r = np.ascontiguousarray(np.asarray(reset).astype(np.uint8))
+    assert r.shape == (batch, L)
+    return r
+
+
+def _ptr8(a):
+    return None if a is None else a.ctypes.data_as(_u8p)
 
 
 def _split(n_items: int, threads: int):
@@ -101,11 +115,12 @@ def default_threads() -> int:
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
-             delta_softplus=True, disc=ZOH, threads=None, return_last_state=True):
+             delta_softplus=True, disc=ZOH, threads=None, return_last_state=True, reset=None):
     """Forward selective scan in float64.
 
     Shapes: u, delta, z (batch, dim, L); A (dim, N); B, C (batch, N, L);
-    D, delta_bias (dim,); h0 (batch, dim, N).  Returns (out, last_state).
+    D, delta_bias (dim,); h0 (batch, dim, N); reset (batch, L) flags (the
+    state is zeroed before each flagged step).  Returns (out, last_state).
     """
     lib = _load()
     u, delta, A, B, C = (_f64(t) for t in (u, delta, A, B, C))
@@ -118,9 +133,11 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
     last = np.zeros((batch, dim, N), np.float64) if return_last_state else None
     nthreads = threads or default_threads()
     args = [_ptr(t) for t in (u, delta, A, B, C, D, z, delta_bias, h0)]
+    rs = _reset(reset, batch, L)
 
     def work(rng):
-        lib.oracle_scan_fwd(*args, int(bool(delta_softplus)), int(disc), batch, dim, N, L,
+        lib.oracle_scan_fwd(*args, _ptr8(rs), int(bool(delta_softplus)), int(disc), batch, dim,
+                            N, L,
                             rng[0], rng[1], _ptr(out), _ptr(last))
 
     ranges = _split(batch * dim, nthreads)
@@ -151,7 +168,7 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
 
 
 def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softplus=True,
-             disc=ZOH, threads=None):
+             disc=ZOH, threads=None, reset=None):
     """Gradients of sum(dout * out) w.r.t. every input, in float64.
 
     Returns a dict with du, ddelta, dA, dB, dC and, when the matching input is
@@ -176,10 +193,12 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
             ddb=np.zeros(dim) if delta_bias is not None else None,
             dh0=np.zeros((batch, dim, N)) if h0 is not None else None))
     args = [_ptr(t) for t in (u, delta, A, B, C, D, z, delta_bias, h0, dout)]
+    rs = _reset(reset, batch, L)
 
     def work(i):
         a = acc[i]
-        lib.oracle_scan_bwd(*args, int(bool(delta_softplus)), int(disc), batch, dim, N, L,
+        lib.oracle_scan_bwd(*args, _ptr8(rs), int(bool(delta_softplus)), int(disc), batch, dim,
+                            N, L,
                             ranges[i][0], ranges[i][1], _ptr(du), _ptr(ddelta), _ptr(a["dA"]),
                             _ptr(a["dB"]), _ptr(a["dC"]), _ptr(a["dD"]), _ptr(dz), _ptr(a["ddb"]),
                             _ptr(a["dh0"]))

@@ -73,12 +73,16 @@ static double bbar_coef(double dt, double a_n, int disc) {
  *          h[n] = Abar*h[n] + Bbar*u_t;  y = sum_n C[b,n,t]*h[n]
  *   y += D[d]*u_t;  out = y * z*sigmoid(z)  (each when given)
  *   last_state = h after the final step (when given).
+ * reset (nullable, (batch, seqlen) bytes): where reset[b,t] != 0 the state
+ * is set to zero before step t, so several sequences packed along t run as
+ * if each started alone (boundary resetting [SUM-3.4] / [ESSAY] Part II §8,
+ * done here by the boundary flag instead of a learned Delta).
  */
 void oracle_scan_fwd(const double* u, const double* delta, const double* A, const double* B,
                      const double* C, const double* D, const double* z, const double* bias,
-                     const double* h0, int softplus_on, int disc, int64_t batch, int64_t dim,
-                     int64_t dstate, int64_t seqlen, int64_t c_begin, int64_t c_end, double* out,
-                     double* last_state) {
+                     const double* h0, const unsigned char* reset, int softplus_on, int disc,
+                     int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t c_begin,
+                     int64_t c_end, double* out, double* last_state) {
   (void)batch;
   double* h = (double*)malloc(sizeof(double) * (size_t)dstate);
   for (int64_t c = c_begin; c < c_end; ++c) {
@@ -94,6 +98,8 @@ void oracle_scan_fwd(const double* u, const double* delta, const double* A, cons
     for (int64_t t = 0; t < seqlen; ++t) {
       double dt = step_size(dl_r[t], bias, d, softplus_on);
       double y = 0.0;
+      if (reset && reset[b * seqlen + t])
+        for (int64_t n = 0; n < dstate; ++n) h[n] = 0.0;
       for (int64_t n = 0; n < dstate; ++n) {
         double abar = exp(dt * A_d[n]);
         double bbar = bbar_coef(dt, A_d[n], disc) * B_b[n * seqlen + t];
@@ -162,13 +168,16 @@ void oracle_state_update(double* state, const double* u, const double* delta, co
  *   5. ddelta_t = gdt_t * sigmoid(delta_t + bias) with softplus, else gdt_t;
  *      ddelta_bias[d] += ddelta_t;  dD[d] += gy_t*u_t;
  *   6. dh0 = Abar_0 * gh_0 (when an initial state was given).
+ * With reset flags the state entering a reset step is zero: h_{t-1} counts as
+ * zero in gA and no adjoint flows from step t to t-1.
  * dA, dB, dC, dD, ddelta_bias, dh0 are accumulated with +=; du, ddelta, dz
  * are written.  Optional outputs may be NULL.
  */
 void oracle_scan_bwd(const double* u, const double* delta, const double* A, const double* B,
                      const double* C, const double* D, const double* z, const double* bias,
-                     const double* h0, const double* dout, int softplus_on, int disc,
-                     int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t c_begin,
+                     const double* h0, const double* dout, const unsigned char* reset,
+                     int softplus_on, int disc, int64_t batch, int64_t dim, int64_t dstate,
+                     int64_t seqlen, int64_t c_begin,
                      int64_t c_end, double* du, double* ddelta, double* dA, double* dB, double* dC,
                      double* dD, double* dz, double* ddelta_bias, double* dh0) {
   (void)batch;
@@ -188,10 +197,12 @@ void oracle_scan_bwd(const double* u, const double* delta, const double* A, cons
     for (int64_t n = 0; n < dstate; ++n) hs[n] = h0 ? h0[c * dstate + n] : 0.0;
     for (int64_t t = 0; t < seqlen; ++t) {
       double dt = step_size(dl_r[t], bias, d, softplus_on);
+      int rs = reset && reset[b * seqlen + t];
       for (int64_t n = 0; n < dstate; ++n) {
         double abar = exp(dt * A_d[n]);
         double bbar = bbar_coef(dt, A_d[n], disc) * B_b[n * seqlen + t];
-        hs[(t + 1) * dstate + n] = abar * hs[t * dstate + n] + bbar * u_r[t];
+        double hprev = rs ? 0.0 : hs[t * dstate + n];
+        hs[(t + 1) * dstate + n] = abar * hprev + bbar * u_r[t];
       }
     }
     /* 3.-5. reverse sweep */
@@ -211,6 +222,7 @@ void oracle_scan_bwd(const double* u, const double* delta, const double* A, cons
       }
       double du_t = D ? gy * D[d] : 0.0;
       double gdt = 0.0;
+      int rs = reset && reset[b * seqlen + t];
       if (D) dD[d] += gy * u_r[t];
       for (int64_t n = 0; n < dstate; ++n) {
         double a_n = A_d[n];
@@ -221,7 +233,7 @@ void oracle_scan_bwd(const double* u, const double* delta, const double* A, cons
         /* gh_t = C_t*gy_t + (Abar_{t+1}*gh_{t+1}, already folded into gh[n]) */
         gh[n] = C_b[n * seqlen + t] * gy + gh[n];
         dC[b * dstate * seqlen + n * seqlen + t] += gy * hs[(t + 1) * dstate + n];
-        double gA = gh[n] * hs[t * dstate + n];
+        double gA = rs ? 0.0 : gh[n] * hs[t * dstate + n];
         double gB = gh[n] * u_r[t];
         du_t += gh[n] * bbar;
         double dbbar_ddt, dbbar_dA;
@@ -235,8 +247,8 @@ void oracle_scan_bwd(const double* u, const double* delta, const double* A, cons
         gdt += gA * a_n * abar + gB * dbbar_ddt;
         dA[d * dstate + n] += gA * dt * abar + gB * dbbar_dA;
         dB[b * dstate * seqlen + n * seqlen + t] += gB * coef;
-        /* carry to t-1: gh_{t-1} gets Abar_t * gh_t */
-        gh[n] = abar * gh[n];
+        /* carry to t-1: gh_{t-1} gets Abar_t * gh_t (nothing across a reset) */
+        gh[n] = rs ? 0.0 : abar * gh[n];
       }
       du[c * seqlen + t] = du_t;
       double gr = softplus_on ? gdt * sigmoid(r) : gdt;
@@ -251,4 +263,4 @@ void oracle_scan_bwd(const double* u, const double* delta, const double* A, cons
   free(gh);
 }
 
-int oracle_version(void) { return 1; }
+int oracle_version(void) { return 2; }

@@ -37,7 +37,7 @@ def make(seed, batch=2, dim=3, N=3, L=10, with_D=True, with_z=True, with_bias=Tr
 def loss(p, dout, softplus_on, disc):
     out, _ = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
                              p["delta_bias"], p["h0"], delta_softplus=softplus_on, disc=disc,
-                             threads=1, return_last_state=False)
+                             threads=1, return_last_state=False, reset=p.get("reset"))
     return float(np.sum(out * dout))
 
 
@@ -97,3 +97,22 @@ def test_backward_thread_split_is_consistent():
                          p["delta_bias"], dout, p["h0"], threads=5)
     for k in g1:
         np.testing.assert_allclose(g1[k], g5[k], rtol=1e-13, atol=1e-14, err_msg=k)
+
+
+@pytest.mark.parametrize("disc", [oracle.ZOH, oracle.EULER])
+def test_backward_with_resets_matches_central_differences(disc):
+    # packed sequences: flags at t = 0 (the initial state is discarded) for the
+    # first batch row, and mid-sequence (including two adjacent steps) in both
+    p, dout = make(91 + disc, L=12, with_h0=True)
+    reset = np.zeros((2, 12), np.uint8)
+    reset[0, [0, 5]] = 1
+    reset[1, [3, 4, 9]] = 1
+    p["reset"] = reset
+    g = oracle.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                        p["delta_bias"], dout, p["h0"], disc=disc, threads=2, reset=reset)
+    assert np.all(g["dh0"][0] == 0.0)       # row 0 resets before its first step
+    for name in NAMES:
+        ref = fd_grad(p, dout, name, True, disc)
+        got = g[GRAD[name]]
+        scale = max(1.0, np.abs(ref).max())
+        np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-6 * scale, err_msg=name)

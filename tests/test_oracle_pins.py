@@ -355,3 +355,79 @@ def test_bf16_rounding_is_round_to_nearest_even():
     np.testing.assert_array_equal(back[:4], [1.0, 1.0, 1.0 + 2 ** -6, 1.0])
     assert back[4] == -2.5
     assert abs(back[5] - 3.0e-3) <= 3.0e-3 * 2 ** -8
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length sequences: a reset flag zeroes the state before its
+# step, so the packed run must equal independent runs of each segment (the
+# first segment keeps the initial state unless it is itself reset).
+# ---------------------------------------------------------------------------
+def _segments(row):
+    starts = [0] + [t for t in range(1, row.size) if row[t]]
+    return list(zip(starts, starts[1:] + [row.size]))
+
+
+def _packed_inputs(seed, batch=2, dim=3, N=4, L=40):
+    g = np.random.default_rng(seed)
+    p = dict(u=g.standard_normal((batch, dim, L)), delta=g.standard_normal((batch, dim, L)),
+             A=-np.exp(g.standard_normal((dim, N))), B=g.standard_normal((batch, N, L)),
+             C=g.standard_normal((batch, N, L)), D=g.standard_normal(dim),
+             z=g.standard_normal((batch, dim, L)), delta_bias=g.standard_normal(dim) - 1.0,
+             h0=g.standard_normal((batch, dim, N)))
+    reset = np.zeros((batch, L), np.uint8)
+    reset[0, [0, 7, 8, 30]] = 1          # reset at t = 0, two adjacent flags
+    reset[1, [13, L - 1]] = 1            # a one-step final segment
+    return p, reset, g.standard_normal((batch, dim, L))
+
+
+def _slice(p, b, s, e):
+    q = {}
+    for k, v in p.items():
+        if k in ("u", "delta", "z", "B", "C"):
+            q[k] = v[b:b + 1, :, s:e]
+        elif k == "h0":
+            q[k] = v[b:b + 1]
+        else:
+            q[k] = v
+    return q
+
+
+@pytest.mark.parametrize("disc", [oracle.ZOH, oracle.EULER])
+def test_reset_forward_equals_independent_segments(disc):
+    p, reset, _ = _packed_inputs(5)
+    out, last = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                                p["delta_bias"], p["h0"], disc=disc, reset=reset)
+    for b in range(reset.shape[0]):
+        for i, (s, e) in enumerate(_segments(reset[b])):
+            q = _slice(p, b, s, e)
+            h0 = q["h0"] if (i == 0 and not reset[b, 0]) else None
+            o, l = oracle.scan_fwd(q["u"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"],
+                                   q["delta_bias"], h0, disc=disc)
+            np.testing.assert_array_equal(out[b, :, s:e], o[0])
+        np.testing.assert_array_equal(last[b], l[0])
+
+
+@pytest.mark.parametrize("disc", [oracle.ZOH, oracle.EULER])
+def test_reset_backward_equals_independent_segments(disc):
+    p, reset, dout = _packed_inputs(6)
+    g = oracle.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                        p["delta_bias"], dout, p["h0"], disc=disc, reset=reset)
+    sums = dict(dA=0.0, dD=0.0, ddelta_bias=0.0)
+    for b in range(reset.shape[0]):
+        for i, (s, e) in enumerate(_segments(reset[b])):
+            q = _slice(p, b, s, e)
+            first = i == 0 and not reset[b, 0]
+            gs = oracle.scan_bwd(q["u"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"],
+                                 q["delta_bias"], dout[b:b + 1, :, s:e],
+                                 q["h0"] if first else None, disc=disc)
+            for k in ("du", "ddelta", "dz"):
+                np.testing.assert_array_equal(g[k][b, :, s:e], gs[k][0], err_msg=k)
+            for k in ("dB", "dC"):
+                np.testing.assert_allclose(g[k][b, :, s:e], gs[k][0], rtol=1e-12, atol=1e-13)
+            for k in sums:
+                sums[k] = sums[k] + gs[k]
+            if i == 0:
+                want = gs["dh0"][0] if first else np.zeros_like(g["dh0"][b])
+                np.testing.assert_array_equal(g["dh0"][b], want)
+    for k, v in sums.items():
+        np.testing.assert_allclose(g[k], v, rtol=1e-12, atol=1e-12, err_msg=k)
