@@ -197,6 +197,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--disc", default="zoh", choices=["zoh", "euler"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--varlen", action="store_true",
+                    help="pack variable-length sequences (lengths uniform in 64..1024) into each "
+                         "row, with reset flags at their starts")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (for counter calibration)")
     ap.add_argument("--calls", default=None,
@@ -228,6 +231,9 @@ def main():
         ws = torch.empty(ms.bwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen,
                                                 g["u"].dtype), dtype=torch.uint8, device="cuda")
     sdt = g["u"].dtype
+    rst = None
+    if args.varlen:
+        rst = torch.from_numpy(W.make_resets(w.wid, w.batch, w.seqlen, 64, 1024)).cuda()
     fws = None
     nfws = ms.fwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen, sdt)
     if nfws:
@@ -241,10 +247,11 @@ def main():
         if c == "fwd":
             ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
                         g["delta_bias"], disc=args.disc, out=t_out, last_state=t_last,
-                        return_last_state=True, workspace=fws, timing=timing)
+                        return_last_state=True, workspace=fws, timing=timing, reset=rst)
         elif c == "bwd":
             ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
-                        g["delta_bias"], g["dout"], disc=args.disc, workspace=ws, timing=timing)
+                        g["delta_bias"], g["dout"], disc=args.disc, workspace=ws, timing=timing,
+                        reset=rst)
         else:   # decode step continuing from the forward's final state, in place
             ms.state_update(t_last, step_args["u"], step_args["delta"], g["A"], step_args["B"],
                             step_args["C"], g["D"], step_args["z"], g["delta_bias"],
@@ -306,7 +313,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16-in/f32-compute",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {'+'.join(calls)} ({args.disc})", "batch": w.batch,
+        "config": {"workload": f"{w.name}{' packed varlen' if args.varlen else ''}: "
+                               f"{'+'.join(calls)} ({args.disc})", "batch": w.batch,
                    "dim": w.dim, "dstate": w.dstate, "seqlen": w.seqlen, "dtype": w.dtype,
                    "disc": args.disc, "delta_softplus": True, "D": True, "z": True,
                    "delta_bias": w.bias},

@@ -165,7 +165,40 @@ mamba_status mamba_state_update(float* state, const void* u, const void* delta, 
                                 void* out, void* stream);
 
 /*
- * Tuning and timing variants.  Identical to the calls above except for:
+ * Packed variable-length sequences.  Same as mamba_scan_fwd / mamba_scan_bwd
+ * plus `reset`: (batch, seqlen) bytes, required (NULL returns
+ * MAMBA_ERR_NULL_PTR).  Where reset[b*seqlen + t] != 0 the state of every
+ * channel of batch row b is set to zero before step t, so sequences packed
+ * one after another along t run exactly as if each started alone; h0 (if
+ * given) enters only where step 0 is not flagged, and the backward sends no
+ * gradient across a flagged step (dh0 is 0 for rows flagged at t = 0).  This
+ * is the boundary resetting the pages attribute to the selection mechanism
+ * (paper-graph-ui summary, section 3.4; trishampatil essay, Part II §8),
+ * done by an explicit flag instead of a learned large Delta.  last_state is
+ * the state after the final step of each row.  Flags run with 16 lanes per
+ * channel; the workspace rules are those of the plain calls.
+ */
+mamba_status mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A,
+                                   const void* B, const void* C, const float* D, const void* z,
+                                   const float* delta_bias, const float* h0,
+                                   const uint8_t* reset, int delta_softplus, mamba_disc disc,
+                                   mamba_dtype dt, int64_t batch, int64_t dim, int64_t dstate,
+                                   int64_t seqlen, void* out, float* last_state, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+mamba_status mamba_scan_bwd_varlen(const void* u, const void* delta, const float* A,
+                                   const void* B, const void* C, const float* D, const void* z,
+                                   const float* delta_bias, const float* h0, const void* dout,
+                                   const uint8_t* reset, int delta_softplus, mamba_disc disc,
+                                   mamba_dtype dt, int64_t batch, int64_t dim, int64_t dstate,
+                                   int64_t seqlen, float* du, float* ddelta, float* dA,
+                                   float* dB, float* dC, float* dD, float* dz,
+                                   float* ddelta_bias, float* dh0, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * Tuning and timing variants.  Identical to the calls above (reset may be
+ * NULL here: no flags) except for:
  *  - lanes_per_channel: the number of lanes each channel's scan is spread
  *    over (16, 32 or 64 for the forward; 0 picks the default the plain calls
  *    use; the backward accepts 0 and 16 only).  The result does not depend on
@@ -191,12 +224,12 @@ size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dsta
 
 mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
                                const void* C, const float* D, const void* z,
-                               const float* delta_bias, const float* h0, int delta_softplus,
-                               mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
-                               int64_t dstate, int64_t seqlen, void* out, float* last_state,
-                               void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel, int segments, void* timing_begin,
-                               void* timing_end);
+                               const float* delta_bias, const float* h0, const uint8_t* reset,
+                               int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                               int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                               void* out, float* last_state, void* workspace,
+                               size_t workspace_bytes, void* stream, int lanes_per_channel,
+                               int segments, void* timing_begin, void* timing_end);
 
 size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
                                         int64_t seqlen, mamba_dtype dt, int lanes_per_channel);
@@ -204,10 +237,10 @@ size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dsta
 mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
                                const void* C, const float* D, const void* z,
                                const float* delta_bias, const float* h0, const void* dout,
-                               int delta_softplus, mamba_disc disc, mamba_dtype dt,
-                               int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                               float* du, float* ddelta, float* dA, float* dB, float* dC,
-                               float* dD, float* dz, float* ddelta_bias, float* dh0,
+                               const uint8_t* reset, int delta_softplus, mamba_disc disc,
+                               mamba_dtype dt, int64_t batch, int64_t dim, int64_t dstate,
+                               int64_t seqlen, float* du, float* ddelta, float* dA, float* dB,
+                               float* dC, float* dD, float* dz, float* ddelta_bias, float* dh0,
                                void* workspace, size_t workspace_bytes, void* stream,
                                int lanes_per_channel, void* timing_begin, void* timing_end);
 

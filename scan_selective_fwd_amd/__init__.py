@@ -68,6 +68,16 @@ def _req(t, name, dtype, shape, device):
     return t
 
 
+def _flags(reset, shape, device):
+    """Reset flags as a contiguous uint8 device tensor (None stays None)."""
+    if reset is None:
+        return None
+    if reset.dtype == torch.bool:
+        reset = reset.to(torch.uint8)
+    _req(reset, "reset", torch.uint8, shape, device)
+    return reset
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -87,8 +97,10 @@ def _events(timing):
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
              delta_softplus=True, disc="zoh", return_last_state=False, out=None, last_state=None,
-             lanes=0, segments=0, workspace=None, timing=None):
+             lanes=0, segments=0, workspace=None, timing=None, reset=None):
     """Fused selective-scan forward.  Returns out, or (out, last_state).
+    `reset`: optional (batch, L) uint8/bool device tensor; the state is zeroed
+    before every flagged step (packed variable-length sequences).
     `segments`: 0 automatic, 1 one pass, k >= 2 that many sequence segments.
     `workspace`: optional uint8 device tensor reused across calls.
     `timing`: optional (begin, end) torch.cuda.Event pair recorded around the
@@ -110,6 +122,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
     _req(z, "z", sdt, (batch, dim, L), dev)
     _req(delta_bias, "delta_bias", torch.float32, (dim,), dev)
     _req(h0, "h0", torch.float32, (batch, dim, N), dev)
+    reset = _flags(reset, (batch, L), dev)
     if out is None:
         out = torch.empty((batch, dim, L), dtype=sdt, device=dev)
     _req(out, "out", sdt, (batch, dim, L), dev)
@@ -121,7 +134,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if nbytes else None
     st = L_.mamba_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                              _ptr(delta_bias), _ptr(h0), int(bool(delta_softplus)),
+                              _ptr(delta_bias), _ptr(h0), _ptr(reset), int(bool(delta_softplus)),
                               _disc_code(disc), dt, batch, dim, N, L, _ptr(out),
                               _ptr(last_state), ws_ptr, nbytes, _stream(dev), int(lanes),
                               int(segments), *_events(timing))
@@ -146,7 +159,7 @@ def bwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0) -> int:
 
 
 def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softplus=True,
-             disc="zoh", lanes=0, workspace=None, want_dh0=True, timing=None):
+             disc="zoh", lanes=0, workspace=None, want_dh0=True, timing=None, reset=None):
     """Backward with state recomputation.  Returns a dict of float32 gradients:
     du, ddelta, dA, dB, dC and, when the input is given, dD, dz, ddelta_bias, dh0.
     `timing`: optional (begin, end) torch.cuda.Event pair recorded around the
@@ -165,6 +178,7 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
                              (h0, "h0", (batch, dim, N), torch.float32),
                              (dout, "dout", (batch, dim, L), sdt)):
         _req(t, name, ty, shp, dev)
+    reset = _flags(reset, (batch, L), dev)
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(du=torch.empty((batch, dim, L), **f32), ddelta=torch.empty((batch, dim, L), **f32),
              dA=torch.empty((dim, N), **f32), dB=torch.empty((batch, N, L), **f32),
@@ -181,7 +195,8 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     st = L_.mamba_scan_bwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                              _ptr(delta_bias), _ptr(h0), _ptr(dout), int(bool(delta_softplus)),
+                              _ptr(delta_bias), _ptr(h0), _ptr(dout), _ptr(reset),
+                              int(bool(delta_softplus)),
                               _disc_code(disc), dt, batch, dim, N, L, _ptr(g["du"]),
                               _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
                               _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),

@@ -23,6 +23,7 @@ ZOH, EULER = 0, 1
 EXPORTS = (
     "mamba_abi_version", "mamba_status_string", "mamba_scan_fwd_workspace_size",
     "mamba_scan_bwd_workspace_size", "mamba_scan_fwd", "mamba_scan_bwd", "mamba_state_update",
+    "mamba_scan_fwd_varlen", "mamba_scan_bwd_varlen",
     "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size_ex", "mamba_scan_bwd_workspace_size_ex",
     "mamba_scan_bwd_ex",
 )
@@ -67,13 +68,19 @@ def load(path: str = LIB_PATH):
     fwd_args = [_vp] * 9 + [_int, _int, _int] + [_i64] * 4 + [_vp, _vp, _vp, _sz, _vp]
     lib.mamba_scan_fwd.restype = _int
     lib.mamba_scan_fwd.argtypes = fwd_args
+    fwd_rst = [_vp] * 10 + [_int, _int, _int] + [_i64] * 4 + [_vp, _vp, _vp, _sz, _vp]
+    lib.mamba_scan_fwd_varlen.restype = _int
+    lib.mamba_scan_fwd_varlen.argtypes = fwd_rst
     lib.mamba_scan_fwd_ex.restype = _int
-    lib.mamba_scan_fwd_ex.argtypes = fwd_args + [_int, _int, _vp, _vp]
+    lib.mamba_scan_fwd_ex.argtypes = fwd_rst + [_int, _int, _vp, _vp]
     bwd_args = [_vp] * 10 + [_int, _int, _int] + [_i64] * 4 + [_vp] * 10 + [_sz, _vp]
     lib.mamba_scan_bwd.restype = _int
     lib.mamba_scan_bwd.argtypes = bwd_args
+    bwd_rst = [_vp] * 11 + [_int, _int, _int] + [_i64] * 4 + [_vp] * 10 + [_sz, _vp]
+    lib.mamba_scan_bwd_varlen.restype = _int
+    lib.mamba_scan_bwd_varlen.argtypes = bwd_rst
     lib.mamba_scan_bwd_ex.restype = _int
-    lib.mamba_scan_bwd_ex.argtypes = bwd_args + [_int, _vp, _vp]
+    lib.mamba_scan_bwd_ex.argtypes = bwd_rst + [_int, _vp, _vp]
     lib.mamba_state_update.restype = _int
     lib.mamba_state_update.argtypes = [_vp] * 9 + [_int, _int, _int] + [_i64] * 3 + [_vp, _vp]
     _lib = lib

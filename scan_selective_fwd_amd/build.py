@@ -3,6 +3,10 @@
 Every source under csrc/ is compiled to an object in parallel, then linked
 into scan_selective_fwd_amd/libmamba_scan.so.  HIP code is built with packed
 FP32 instructions disabled (`-Xclang -target-feature -Xclang -packed-fp32-ops`).
+
+`python -m scan_selective_fwd_amd.build --incremental` recompiles only the
+objects whose source or included headers changed (hipcc -MMD dependency
+files); build() without it recompiles everything.
 """
 import os
 import subprocess
@@ -27,12 +31,26 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src, verbose):
+def _up_to_date(obj):
+    dep = obj + ".d"
+    if not (os.path.exists(obj) and os.path.exists(dep)):
+        return False
+    with open(dep) as f:
+        text = f.read().replace("\\\n", " ")
+    deps = text.split(":", 1)[1].split() if ":" in text else []
+    t = os.path.getmtime(obj)
+    return all(os.path.exists(d) and os.path.getmtime(d) <= t for d in deps)
+
+
+def _compile(src, verbose, incremental=False):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+    if incremental and _up_to_date(obj):
+        return obj
+    cmd = [HIPCC] + COMMON + ["-MMD", "-MF", obj + ".d", "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + [f for f in COMMON if f not in ("-Xclang", "-target-feature",
-                                                        "-packed-fp32-ops")] + ["-c", src, "-o", obj]
+                                                        "-packed-fp32-ops")] + [
+            "-MMD", "-MF", obj + ".d", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,11 +60,11 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, incremental), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
@@ -58,5 +76,5 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
 if __name__ == "__main__":
     t = __import__("time").time()
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))
     print(f"built in {__import__('time').time() - t:.1f}s")

@@ -70,26 +70,28 @@ int64_t auto_segments(int64_t batch, int64_t dim, int64_t seqlen) {
 }
 
 // Forward workspace (segmented only): the segment end states and the
-// entering states (nchannels, nseg, dstate) float32, then the delta sums
-// (nchannels, nseg).
+// entering states (nchannels, nseg, dstate) float32, then the delta sums and
+// the reset-free factors (nchannels, nseg) float32.
 struct FwdLayout {
   int64_t nseg, seg_chunks;
-  size_t off_h0, off_dsum, total;
+  size_t off_h0, off_dsum, off_keep, total;
 };
 
 FwdLayout fwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                      int64_t segments) {
-  FwdLayout w = {1, 0, 0, 0, 0};
+  FwdLayout w = {1, 0, 0, 0, 0, 0};
   const int64_t nchunks = (seqlen + kFwdChunk - 1) / kFwdChunk;
   int64_t nseg = segments < nchunks ? segments : nchunks;
   if (nseg <= 1) return w;
   w.seg_chunks = (nchunks + nseg - 1) / nseg;
   w.nseg = (nchunks + w.seg_chunks - 1) / w.seg_chunks;
-  if (w.nseg <= 1) return FwdLayout{1, 0, 0, 0, 0};
+  if (w.nseg <= 1) return FwdLayout{1, 0, 0, 0, 0, 0};
   const size_t nst = (size_t)(batch * dim) * (size_t)w.nseg * (size_t)dstate * 4;
+  const size_t nsc = round_up((size_t)(batch * dim) * (size_t)w.nseg * 4);
   w.off_h0 = round_up(nst);
   w.off_dsum = w.off_h0 + round_up(nst);
-  w.total = w.off_dsum + round_up((size_t)(batch * dim) * (size_t)w.nseg * 4);
+  w.off_keep = w.off_dsum + nsc;
+  w.total = w.off_keep + nsc;
   return w;
 }
 
@@ -170,7 +172,8 @@ size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
 // 64; 0 = automatic).  For tests and tuning.
 mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
                                const void* C, const float* D, const void* z,
-                               const float* delta_bias, const float* h0, int delta_softplus,
+                               const float* delta_bias, const float* h0, const uint8_t* reset,
+                               int delta_softplus,
                                mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
                                int64_t dstate, int64_t seqlen, void* out, float* last_state,
                                void* workspace, size_t workspace_bytes, void* stream,
@@ -196,7 +199,9 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
       segmented = false;   // automatic choice without the workspace: one pass
     }
   }
-  int lanes = segmented ? 16 : lanes_per_channel;
+  // reset flags run with 16 lanes per channel
+  if (reset && lanes_per_channel != 0 && lanes_per_channel != 16) return MAMBA_ERR_UNSUPPORTED;
+  int lanes = (segmented || reset) ? 16 : lanes_per_channel;
   if (lanes == 0) lanes = choose_lanes(batch * dim, seqlen, kItems);
   if (!valid_lanes(lanes)) return MAMBA_ERR_UNSUPPORTED;
 
@@ -204,6 +209,7 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
   memset(&p, 0, sizeof(p));
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.bias = delta_bias;
   p.h0 = h0; p.out = out; p.last_state = last_state; p.chunk_states = nullptr;
+  p.reset = reset;
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.groups = mscan::channel_groups(dim, lanes);
   p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
@@ -220,6 +226,7 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
     p.seg_state = reinterpret_cast<float*>(ws);
     p.seg_h0 = reinterpret_cast<float*>(ws + w.off_h0);
     p.seg_dsum = reinterpret_cast<float*>(ws + w.off_dsum);
+    p.seg_keep = reinterpret_cast<float*>(ws + w.off_keep);
     if (mscan::dispatch_seg_summary(p, dti, (int)disc, vec, s) != hipSuccess) return MAMBA_ERR_HIP;
     if (mscan::dispatch_seg_carry(p, s) != hipSuccess) return MAMBA_ERR_HIP;
   }
@@ -238,20 +245,33 @@ mamba_status mamba_scan_fwd(const void* u, const void* delta, const float* A, co
                             mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
                             int64_t dstate, int64_t seqlen, void* out, float* last_state,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  return mamba_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, disc, dt,
-                           batch, dim, dstate, seqlen, out, last_state, workspace,
+  return mamba_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, nullptr, delta_softplus,
+                           disc, dt, batch, dim, dstate, seqlen, out, last_state, workspace,
+                           workspace_bytes, stream, 0, 0, nullptr, nullptr);
+}
+
+mamba_status mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A,
+                                   const void* B, const void* C, const float* D, const void* z,
+                                   const float* delta_bias, const float* h0,
+                                   const uint8_t* reset, int delta_softplus, mamba_disc disc,
+                                   mamba_dtype dt, int64_t batch, int64_t dim, int64_t dstate,
+                                   int64_t seqlen, void* out, float* last_state, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!reset) return MAMBA_ERR_NULL_PTR;
+  return mamba_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, reset, delta_softplus, disc,
+                           dt, batch, dim, dstate, seqlen, out, last_state, workspace,
                            workspace_bytes, stream, 0, 0, nullptr, nullptr);
 }
 
 mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
                                const void* C, const float* D, const void* z,
                                const float* delta_bias, const float* h0, const void* dout,
-                               int delta_softplus, mamba_disc disc, mamba_dtype dt, int64_t batch,
-                               int64_t dim, int64_t dstate, int64_t seqlen, float* du,
-                               float* ddelta, float* dA, float* dB, float* dC, float* dD,
-                               float* dz, float* ddelta_bias, float* dh0, void* workspace,
-                               size_t workspace_bytes, void* stream, int lanes_per_channel,
-                               void* timing_begin, void* timing_end) {
+                               const uint8_t* reset, int delta_softplus, mamba_disc disc,
+                               mamba_dtype dt, int64_t batch, int64_t dim, int64_t dstate,
+                               int64_t seqlen, float* du, float* ddelta, float* dA, float* dB,
+                               float* dC, float* dD, float* dz, float* ddelta_bias, float* dh0,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               int lanes_per_channel, void* timing_begin, void* timing_end) {
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
   if (st != MAMBA_OK) return st;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
@@ -279,6 +299,7 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   fp.u = u; fp.delta = delta; fp.A = A; fp.B = B; fp.C = C; fp.D = D; fp.z = z;
   fp.bias = delta_bias; fp.h0 = h0; fp.out = nullptr; fp.last_state = nullptr;
   fp.chunk_states = states;
+  fp.reset = reset;
   fp.batch = batch; fp.dim = dim; fp.L = seqlen; fp.nchannels = batch * dim;
   fp.groups = w.groups;
   fp.nseg = 1;
@@ -293,6 +314,7 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   p.h0 = h0; p.dout = dout; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB; p.dC = dC;
   p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0;
   p.chunk_states = states;
+  p.reset = reset;
   p.deferred = reinterpret_cast<int*>(static_cast<char*>(workspace) + w.off_flags);
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.nchunks = w.nchunks; p.groups = w.groups; p.N = (int)dstate;
@@ -310,8 +332,24 @@ mamba_status mamba_scan_bwd(const void* u, const void* delta, const float* A, co
                             float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz,
                             float* ddelta_bias, float* dh0, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  return mamba_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout, delta_softplus, disc,
-                           dt, batch, dim, dstate, seqlen, du, ddelta, dA, dB, dC, dD, dz,
+  return mamba_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout, nullptr,
+                           delta_softplus, disc, dt, batch, dim, dstate, seqlen, du, ddelta, dA,
+                           dB, dC, dD, dz, ddelta_bias, dh0, workspace, workspace_bytes, stream, 0,
+                           nullptr, nullptr);
+}
+
+mamba_status mamba_scan_bwd_varlen(const void* u, const void* delta, const float* A,
+                                   const void* B, const void* C, const float* D, const void* z,
+                                   const float* delta_bias, const float* h0, const void* dout,
+                                   const uint8_t* reset, int delta_softplus, mamba_disc disc,
+                                   mamba_dtype dt, int64_t batch, int64_t dim, int64_t dstate,
+                                   int64_t seqlen, float* du, float* ddelta, float* dA,
+                                   float* dB, float* dC, float* dD, float* dz,
+                                   float* ddelta_bias, float* dh0, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!reset) return MAMBA_ERR_NULL_PTR;
+  return mamba_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout, reset, delta_softplus,
+                           disc, dt, batch, dim, dstate, seqlen, du, ddelta, dA, dB, dC, dD, dz,
                            ddelta_bias, dh0, workspace, workspace_bytes, stream, 0, nullptr,
                            nullptr);
 }

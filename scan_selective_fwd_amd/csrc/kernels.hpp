@@ -37,6 +37,8 @@ struct FwdParams {
   float* seg_h0;           // (nchannels, nseg, N): state entering each segment
   float* seg_state;        // summary mode: (nchannels, nseg, N) end state from a zero start
   float* seg_dsum;         // summary mode: (nchannels, nseg) sum of delta over the segment
+  float* seg_keep;         // summary mode: (nchannels, nseg) 0 if the segment has a reset, else 1
+  const uint8_t* reset;    // nullable (batch, L): zero the state before each flagged step
   int N;
   int softplus;
 };
@@ -70,6 +72,7 @@ struct BwdParams {
   float* dh0;              // nullable
   const float* chunk_states;  // workspace: (nchannels, nchunks, N) states at chunk starts
   int* deferred;           // workspace: one flag per block (blocks with A ~ 0, ZOH)
+  const uint8_t* reset;    // nullable (batch, L): zero the state before each flagged step
   int64_t batch, dim, L;
   int64_t nchannels;
   int64_t nchunks;         // chunks of 16*kItemsBwd steps
@@ -110,6 +113,13 @@ hipError_t dispatch_chunk_states_f32(const FwdParams& p, int disc, int lanes, bo
                                      hipStream_t s);
 hipError_t dispatch_chunk_states_bf16(const FwdParams& p, int disc, int lanes, bool vec,
                                       hipStream_t s);
+// Packed sequences with reset flags (p.reset != NULL): 16 lanes per channel.
+hipError_t dispatch_scan_fwd_reset_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_scan_fwd_reset_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_seg_summary_reset_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_seg_summary_reset_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_chunk_states_reset_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_chunk_states_reset_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
 // Segmented forward, first two launches: per-segment summaries (16 lanes per
 // channel) and the sequential carry over segments.
 hipError_t dispatch_seg_summary_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
@@ -117,17 +127,26 @@ hipError_t dispatch_seg_summary_bf16(const FwdParams& p, int disc, bool vec, hip
 hipError_t dispatch_seg_carry(const FwdParams& p, hipStream_t s);
 inline hipError_t dispatch_seg_summary(const FwdParams& p, int dtype, int disc, bool vec,
                                        hipStream_t s) {
+  if (p.reset)
+    return dtype == 0 ? dispatch_seg_summary_reset_f32(p, disc, vec, s)
+                      : dispatch_seg_summary_reset_bf16(p, disc, vec, s);
   return dtype == 0 ? dispatch_seg_summary_f32(p, disc, vec, s)
                     : dispatch_seg_summary_bf16(p, disc, vec, s);
 }
 inline hipError_t dispatch_scan_fwd(const FwdParams& p, int dtype, int disc, int lanes, bool vec,
                                     hipStream_t s) {
+  if (p.reset)
+    return dtype == 0 ? dispatch_scan_fwd_reset_f32(p, disc, vec, s)
+                      : dispatch_scan_fwd_reset_bf16(p, disc, vec, s);
   return dtype == 0 ? dispatch_scan_fwd_f32(p, disc, lanes, vec, s)
                     : dispatch_scan_fwd_bf16(p, disc, lanes, vec, s);
 }
 // Backward: chunk-state recompute, reverse adjoint scan, then reductions.
 inline hipError_t dispatch_chunk_states(const FwdParams& p, int dtype, int disc, int lanes,
                                         bool vec, hipStream_t s) {
+  if (p.reset)
+    return dtype == 0 ? dispatch_chunk_states_reset_f32(p, disc, vec, s)
+                      : dispatch_chunk_states_reset_bf16(p, disc, vec, s);
   return dtype == 0 ? dispatch_chunk_states_f32(p, disc, lanes, vec, s)
                     : dispatch_chunk_states_bf16(p, disc, lanes, vec, s);
 }
@@ -139,8 +158,15 @@ hipError_t dispatch_scan_bwd_f32(const BwdParams& p, int disc, bool vec, hipStre
                                  hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t dispatch_scan_bwd_bf16(const BwdParams& p, int disc, bool vec, hipStream_t s,
                                   hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t dispatch_scan_bwd_reset_f32(const BwdParams& p, int disc, bool vec, hipStream_t s,
+                                       hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t dispatch_scan_bwd_reset_bf16(const BwdParams& p, int disc, bool vec, hipStream_t s,
+                                        hipEvent_t ev_begin, hipEvent_t ev_end);
 inline hipError_t dispatch_scan_bwd(const BwdParams& p, int dtype, int disc, bool vec,
                                     hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  if (p.reset)
+    return dtype == 0 ? dispatch_scan_bwd_reset_f32(p, disc, vec, s, ev_begin, ev_end)
+                      : dispatch_scan_bwd_reset_bf16(p, disc, vec, s, ev_begin, ev_end);
   return dtype == 0 ? dispatch_scan_bwd_f32(p, disc, vec, s, ev_begin, ev_end)
                     : dispatch_scan_bwd_bf16(p, disc, vec, s, ev_begin, ev_end);
 }

@@ -87,8 +87,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // the adjoint carried from the later chunk, the dA sum) are kept in
 // registers "lane n holds state n": a channel's 16 lanes hold 16 states per
 // register, and DPP row shifts bring state n to lane 0 or lane 15 and back.
-template <typename T, int NT, bool ZOH, bool VEC, bool TINY>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(const BwdParams p) {
+//
+// RST: packed sequences (p.reset flags).  The state entering a flagged step
+// is zero: the step's decay factor in the recurrence and in the adjoint
+// becomes 0 (Bbar keeps the true one), and its h_{t-1} counts as 0.
+template <typename T, int NT, bool ZOH, bool VEC, bool TINY, bool RST = false>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(
+    const BwdParams p) {
   constexpr int R = 16;
   constexpr int K = kItemsBwd;
   static_assert(K == 8, "the row reduce-scatter assumes 8 steps per lane");
@@ -136,6 +141,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const T* __restrict__ C_b = static_cast<const T*>(p.C) + b * N * L;
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
+  const uint8_t* __restrict__ rst_row = RST ? p.reset + b * L : nullptr;
 
   bool my_tiny = false;
   for (int i = tid; i < CPB * NT; i += kBlock) {
@@ -225,6 +231,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       gdt[k] = 0.0f;
       dD_acc = __builtin_fmaf(gy[k], uv[k], dD_acc);
     }
+    float keep[K];
+    float lane_keep = 1.0f;
+    if constexpr (RST) lane_keep = load_keep<K>(rst_row, tl, L, keep) ? 0.0f : 1.0f;
 
     const float* tB = reinterpret_cast<const float*>(tile_mem);
     float4 pr_next = prm[cl][0];
@@ -264,9 +273,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           } else {
             beta[k] = dt[k] * Bv[k] * uv[k];
           }
-          agg = __builtin_fmaf(a[k], agg, beta[k]);
+          agg = __builtin_fmaf(RST ? a[k] * keep[k] : a[k], agg, beta[k]);
         }
-        const float Alane = fast_exp2(a2 * dsum);
+        const float Alane = RST ? fast_exp2(a2 * dsum) * lane_keep : fast_exp2(a2 * dsum);
         float Ag = Alane;
         agg = (j == 0) ? __builtin_fmaf(Ag, h_in, agg) : agg;   // chunk-start state enters lane 0
         affine_scan_inclusive_fused<R>(Ag, agg);
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           float h = hstart;
 #pragma unroll
           for (int k = 0; k < K; ++k) {
-            h = __builtin_fmaf(a[k], h, beta[k]);
+            h = __builtin_fmaf(RST ? a[k] * keep[k] : a[k], h, beta[k]);
             hv[k] = h;
             yv[k] = __builtin_fmaf(Cv[k], h, yv[k]);
           }
@@ -284,7 +293,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         // ---- reverse adjoint: g_t = Abar_t (g_{t+1} + C_t gy_t) ----
         float gagg = 0.0f;
 #pragma unroll
-        for (int k = K - 1; k >= 0; --k) gagg = a[k] * __builtin_fmaf(Cv[k], gy[k], gagg);
+        for (int k = K - 1; k >= 0; --k)
+          gagg = (RST ? a[k] * keep[k] : a[k]) * __builtin_fmaf(Cv[k], gy[k], gagg);
         float As = Alane;
         gagg = (j == R - 1) ? __builtin_fmaf(As, gc, gagg) : gagg;   // later chunk enters lane 15
         affine_suffix_scan_row_fused(As, gagg);
@@ -299,7 +309,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
         for (int k = K - 1; k >= 0; --k) {
           const float gh = __builtin_fmaf(Cv[k], gy[k], g);   // dL/dh_t
-          const float hprev = (k == 0) ? hstart : hv[k - 1];
+          const float hprev = ((k == 0) ? hstart : hv[k - 1]) * (RST ? keep[k] : 1.0f);
           const float P = gh * a[k];
           float coef;
           if constexpr (ZOH && !TINY) {
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
               TC[0] = rs_pair32(sC[0], sC[1]);
             }
           }
-          g = P;
+          g = RST ? P * keep[k] : P;
         }
         constexpr int buf = (n / G) & 1;
 #pragma unroll
@@ -469,24 +479,24 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(const BwdParams p)
   }
 }
 
-template <typename T, int NT, bool ZOH, bool VEC>
+template <typename T, int NT, bool ZOH, bool VEC, bool RST>
 static hipError_t launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin,
                              hipEvent_t ev_end) {
   const int64_t nblocks = p.batch * p.groups;
   hipError_t e;
   if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, false>), dim3((unsigned)nblocks),
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, false, RST>), dim3((unsigned)nblocks),
                      dim3(kBlock), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
   if (!ZOH) return e;
-  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, true>), dim3((unsigned)nblocks),
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, true, RST>), dim3((unsigned)nblocks),
                      dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool RST = false>
 static hipError_t dispatch_bwd_t(const BwdParams& p, int disc, bool vec, hipStream_t s,
                                  hipEvent_t ev_begin, hipEvent_t ev_end) {
   {
@@ -500,15 +510,15 @@ static hipError_t dispatch_bwd_t(const BwdParams& p, int disc, bool vec, hipStre
   const bool zoh = disc == 0;
   const hipEvent_t b = ev_begin, e = ev_end;
   if (p.N <= 16) {
-    if (zoh) return vec ? launch_bwd<T, 16, true, true>(p, s, b, e)
-                        : launch_bwd<T, 16, true, false>(p, s, b, e);
-    return vec ? launch_bwd<T, 16, false, true>(p, s, b, e)
-               : launch_bwd<T, 16, false, false>(p, s, b, e);
+    if (zoh) return vec ? launch_bwd<T, 16, true, true, RST>(p, s, b, e)
+                        : launch_bwd<T, 16, true, false, RST>(p, s, b, e);
+    return vec ? launch_bwd<T, 16, false, true, RST>(p, s, b, e)
+               : launch_bwd<T, 16, false, false, RST>(p, s, b, e);
   }
-  if (zoh) return vec ? launch_bwd<T, 64, true, true>(p, s, b, e)
-                      : launch_bwd<T, 64, true, false>(p, s, b, e);
-  return vec ? launch_bwd<T, 64, false, true>(p, s, b, e)
-             : launch_bwd<T, 64, false, false>(p, s, b, e);
+  if (zoh) return vec ? launch_bwd<T, 64, true, true, RST>(p, s, b, e)
+                      : launch_bwd<T, 64, true, false, RST>(p, s, b, e);
+  return vec ? launch_bwd<T, 64, false, true, RST>(p, s, b, e)
+             : launch_bwd<T, 64, false, false, RST>(p, s, b, e);
 }
 
 }  // namespace mscan

@@ -1,0 +1,12 @@
+// Backward kernels with reset flags (packed sequences) for f32 sequences
+// (see scan_bwd_impl.hpp).
+#include "scan_bwd_impl.hpp"
+
+namespace mscan {
+
+hipError_t dispatch_scan_bwd_reset_f32(const BwdParams& p, int disc, bool vec, hipStream_t stream,
+                                       hipEvent_t ev_begin, hipEvent_t ev_end) {
+  return dispatch_bwd_t<float, true>(p, disc, vec, stream, ev_begin, ev_end);
+}
+
+}  // namespace mscan

@@ -54,6 +54,23 @@ __device__ __forceinline__ void load_items(const T* __restrict__ row, int64_t t,
   }
 }
 
+// Reset flags of a lane's K steps: keep[k] = 0 where the state is zeroed
+// before step tl + k, else 1 (steps past L keep it).  Returns whether any
+// flag is set.
+template <int K>
+__device__ __forceinline__ bool load_keep(const uint8_t* __restrict__ row, int64_t tl, int64_t L,
+                                          float (&keep)[K]) {
+  bool any = false;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t t = tl + k;
+    const bool r = t < L && row[t] != 0;
+    keep[k] = r ? 0.0f : 1.0f;
+    any |= r;
+  }
+  return any;
+}
+
 template <typename T, int K>
 __device__ __forceinline__ void store_items(T* __restrict__ row, int64_t t, int64_t L, bool full,
                                             const float (&v)[K]) {
@@ -75,7 +92,11 @@ __device__ __forceinline__ void store_items(T* __restrict__ row, int64_t t, int6
 // A block serves one channel group of one batch row, for the whole sequence
 // or (p.seg_chunks > 0) for one segment of it; the segment's entering state
 // then comes from p.seg_h0, which the carry kernel filled from the summaries.
-template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE>
+//
+// RST: packed sequences.  Where p.reset flags a step the state entering it is
+// zero: the step's decay factor in the recurrence (not in Bbar) becomes 0,
+// and so does the decay of any lane summary that contains the step.
+template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE, bool RST = false>
 __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
   constexpr bool STATES = MODE != kModeOut;
   constexpr int CPW = 64 / R;   // channels per wave
@@ -116,6 +137,7 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
   const T* __restrict__ C_b = static_cast<const T*>(p.C) + b * N * L;
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
+  const uint8_t* __restrict__ rst_row = RST ? p.reset + b * L : nullptr;
 
   // per-channel constants: A * log2(e) and 1/A (0 where A is ~0, the ZOH limit)
   bool my_tiny = false;
@@ -159,6 +181,7 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
     load_items<T, K>(dl_row, tb + (int64_t)j * K, L, full0, nd);
   }
   float dtot = 0.0f;   // this lane's delta sum over the block's chunks
+  bool seg_reset = false;   // RST: a flag in this lane's steps of the block
   // barrier for the LDS fills; also: does any channel of the block have A ~ 0?
   const bool any_tiny = __syncthreads_or(my_tiny);
 
@@ -209,6 +232,13 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
         if constexpr (!ZOH) uv[k] = s * uv[k];   // Euler: Bbar u = B (delta u)
       }
       dtot += dsum;
+      float keep[K];
+      float lane_keep = 1.0f;
+      if constexpr (RST) {
+        const bool any = load_keep<K>(rst_row, tl, L, keep);
+        lane_keep = any ? 0.0f : 1.0f;
+        seg_reset |= any;
+      }
 
       const float* tB = reinterpret_cast<const float*>(tile_mem[buf]);
       // operands of state index n + 1 are read while n is computed
@@ -247,6 +277,7 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
               } else {
                 beta[k] = Bv[k] * uv[k];
               }
+              if constexpr (RST) a[k] *= keep[k];
               agg = __builtin_fmaf(a[k], agg, beta[k]);
             }
           } else {
@@ -257,10 +288,12 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
               a[k] = fast_exp2(dt[k] * a2);
               const float coef = ia == 0.0f ? dt[k] : (a[k] - 1.0f) * ia;
               beta[k] = coef * Bv[k] * uv[k];
+              if constexpr (RST) a[k] *= keep[k];
               agg = __builtin_fmaf(a[k], agg, beta[k]);
             }
           }
           float Ag = fast_exp2(a2 * dsum);
+          if constexpr (RST) Ag *= lane_keep;
           // the carried state enters through the first lane's summary
           agg = (j == 0) ? __builtin_fmaf(Ag, cr[n], agg) : agg;
           affine_scan_inclusive_fused<R>(Ag, agg);
@@ -299,31 +332,40 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
   }
   if constexpr (MODE == kModeSegSummary) {
     const float dseg = group_sum<R>(dtot);
+    const float nreset = group_sum<R>(seg_reset ? 1.0f : 0.0f);
     if (active && j == 0) {
 #pragma unroll
       for (int n = 0; n < NT; ++n)
         if (n < N) p.seg_state[(c * p.nseg + seg) * N + n] = cr[n];
       p.seg_dsum[c * p.nseg + seg] = dseg;
+      p.seg_keep[c * p.nseg + seg] = nreset > 0.0f ? 0.0f : 1.0f;
     }
   }
 }
 
-template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE>
+template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE, bool RST = false>
 static hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
   const int64_t nblocks = p.batch * p.groups * p.nseg;
-  hipLaunchKernelGGL((scan_fwd_kernel<T, R, K, NT, ZOH, VEC, MODE>), dim3((unsigned)nblocks),
-                     dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((scan_fwd_kernel<T, R, K, NT, ZOH, VEC, MODE, RST>),
+                     dim3((unsigned)nblocks), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
 // N <= 16 takes the NT = 16 kernel, 16 < N <= 64 the NT = 64 kernel.
-template <typename T, int R, int K, bool ZOH, int MODE>
+template <typename T, int R, int K, bool ZOH, int MODE, bool RST = false>
 static hipError_t fwd_nv(const FwdParams& p, bool vec, hipStream_t s) {
   if (p.N <= 16)
-    return vec ? launch_fwd<T, R, K, 16, ZOH, true, MODE>(p, s)
-               : launch_fwd<T, R, K, 16, ZOH, false, MODE>(p, s);
-  return vec ? launch_fwd<T, R, K, 64, ZOH, true, MODE>(p, s)
-             : launch_fwd<T, R, K, 64, ZOH, false, MODE>(p, s);
+    return vec ? launch_fwd<T, R, K, 16, ZOH, true, MODE, RST>(p, s)
+               : launch_fwd<T, R, K, 16, ZOH, false, MODE, RST>(p, s);
+  return vec ? launch_fwd<T, R, K, 64, ZOH, true, MODE, RST>(p, s)
+             : launch_fwd<T, R, K, 64, ZOH, false, MODE, RST>(p, s);
+}
+
+// Reset flags: 16 lanes per channel only.
+template <typename T, int K, int MODE>
+static hipError_t dispatch_fwd_reset_t(const FwdParams& p, int disc, bool vec, hipStream_t s) {
+  return disc == 0 ? fwd_nv<T, 16, K, true, MODE, true>(p, vec, s)
+                   : fwd_nv<T, 16, K, false, MODE, true>(p, vec, s);
 }
 
 template <typename T, int K, int MODE>

@@ -1,0 +1,12 @@
+// The backward's state-recompute pass with reset flags for f32 sequences: the
+// forward kernel template in states-only mode with the backward's chunk length.
+#include "scan_fwd_impl.hpp"
+
+namespace mscan {
+
+hipError_t dispatch_chunk_states_reset_f32(const FwdParams& p, int disc, bool vec,
+                                           hipStream_t stream) {
+  return dispatch_fwd_reset_t<float, kItemsBwd, kModeChunkStates>(p, disc, vec, stream);
+}
+
+}  // namespace mscan

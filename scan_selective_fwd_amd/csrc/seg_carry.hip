@@ -9,7 +9,8 @@
 // (Abar, Bbar u) pairs the pages' parallel scan is built on (trishampatil
 // essay, Part III §2), applied to whole segments; the chunking follows the
 // same essay's Part III §4.  The forward kernel then runs every segment from
-// its entering state.
+// its entering state.  A segment that contains a reset flag passes nothing on
+// (its keep factor is 0).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -27,7 +28,9 @@ static __global__ __launch_bounds__(256) void seg_carry_kernel(const FwdParams p
   for (int64_t s = 0; s < p.nseg; ++s) {
     const int64_t k = c * p.nseg + s;
     p.seg_h0[k * p.N + n] = H;
-    H = __builtin_fmaf(exp2f(a2 * p.seg_dsum[k]), H, p.seg_state[k * p.N + n]);
+    // a reset inside segment s cuts the carry (seg_keep = 0)
+    const float decay = exp2f(a2 * p.seg_dsum[k]) * p.seg_keep[k];
+    H = __builtin_fmaf(decay, H, p.seg_state[k * p.N + n]);
   }
 }
 

@@ -73,9 +73,9 @@ def test_workspace_queries(lib):
 def test_forward_segment_workspace(lib):
     # a long sequence over few channels is split into segments: 1536 channels
     # are 96 blocks, so 32 segments of 256 chunks; per channel and segment two
-    # states of 16 floats and one delta sum
+    # states of 16 floats, the delta sum and the reset-free factor
     n = lib.mamba_scan_fwd_workspace_size(1, 1536, 16, 1 << 20, 1)
-    assert n == 2 * (1536 * 32 * 16 * 4) + 1536 * 32 * 4
+    assert n == 2 * (1536 * 32 * 16 * 4) + 2 * (1536 * 32 * 4)
     assert lib.mamba_scan_fwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 0, 0) == n
     assert lib.mamba_scan_fwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 16, 0) == n
     # one pass: no workspace; explicit wider lanes run in one pass as well
@@ -88,9 +88,9 @@ def test_forward_segment_workspace(lib):
     assert lib.mamba_scan_fwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, -1) == 2 ** 64 - 1
 
 
-def fwd_ex(lib, segments, ws=None, wsb=0, lanes=0):
-    return lib.mamba_scan_fwd_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 1, 16, 4, 1024,
-                                 P, None, ws, wsb, None, lanes, segments, None, None)
+def fwd_ex(lib, segments, ws=None, wsb=0, lanes=0, reset=None):
+    return lib.mamba_scan_fwd_ex(P, P, P, P, P, None, None, None, None, reset, 1, 0, 0, 1, 16, 4,
+                                 1024, P, None, ws, wsb, None, lanes, segments, None, None)
 
 
 def test_forward_segment_arguments(lib):
@@ -101,6 +101,15 @@ def test_forward_segment_arguments(lib):
     assert fwd_ex(lib, 3, ws=P + 8, wsb=need) == 4      # misaligned workspace
     assert fwd_ex(lib, 3, lanes=64) == 6                # segments need 16 lanes
     assert fwd_ex(lib, -2) == 6
+    assert fwd_ex(lib, 1, lanes=32, reset=P) == 6       # reset flags need 16 lanes
+
+
+def test_varlen_requires_flags(lib):
+    assert lib.mamba_scan_fwd_varlen(P, P, P, P, P, None, None, None, None, None, 1, 0, 0, 1, 16,
+                                     4, 128, P, None, None, 0, None) == 1
+    assert lib.mamba_scan_bwd_varlen(P, P, P, P, P, None, None, None, None, P, None, 1, 0, 0, 1,
+                                     16, 4, 128, P, P, P, P, P, None, None, None, None, P, 0,
+                                     None) == 1
 
 
 P = 4096  # a 16-byte aligned fake address; never dereferenced (calls fail first)

@@ -15,10 +15,10 @@ from parity_utils import RTOL, announce, assert_match, to_device, to_f64
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_fwd(f, disc, softplus=True, h0=None):
+def _oracle_fwd(f, disc, softplus=True, h0=None, reset=None):
     return oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"), f.get("z"),
                            f.get("delta_bias"), h0, delta_softplus=softplus,
-                           disc=oracle.ZOH if disc == "zoh" else oracle.EULER)
+                           disc=oracle.ZOH if disc == "zoh" else oracle.EULER, reset=reset)
 
 
 def _make(wid, batch, dim, N, L, dtype, bias="uniform", **kw):
@@ -38,10 +38,11 @@ def _positive_steps(inp, dtype):
 
 
 def run_fwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=False, opts=None,
-                 zero_A=False, A_mode="s4d_real", rtol=None, segments=0):
+                 zero_A=False, A_mode="s4d_real", rtol=None, segments=0, reset=None):
     opts = opts or {}
     announce(f"fwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} lanes={lanes} "
-             f"softplus={softplus} h0={h0} opts={opts} zero_A={zero_A} segments={segments}")
+             f"softplus={softplus} h0={h0} opts={opts} zero_A={zero_A} segments={segments} "
+             f"resets={None if reset is None else int(reset.sum())}")
     inp, f = _make(wid, batch, dim, N, L, dtype, A_mode=A_mode, **opts)
     if not softplus:
         inp, f = _positive_steps(inp, dtype)
@@ -55,9 +56,11 @@ def run_fwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=
     h0t = torch.from_numpy(h0v).cuda() if h0v is not None else None
     out, last = ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g.get("D"), g.get("z"),
                             g.get("delta_bias"), h0t, delta_softplus=softplus, disc=disc,
-                            return_last_state=True, lanes=lanes, segments=segments)
+                            return_last_state=True, lanes=lanes, segments=segments,
+                            reset=None if reset is None else torch.from_numpy(reset).cuda())
     torch.cuda.synchronize()
-    ref, ref_last = _oracle_fwd(f, disc, softplus, None if h0v is None else h0v.astype(np.float64))
+    ref, ref_last = _oracle_fwd(f, disc, softplus, None if h0v is None else h0v.astype(np.float64),
+                                reset)
     rt = rtol or RTOL[dtype]
     assert_match(to_f64(out), ref, rt, "out")
     # the state is float32 in both dtypes: hold it to the float32 tolerance
@@ -134,6 +137,34 @@ def test_fwd_automatic_segmentation():
     assert ms.fwd_workspace_bytes(1, 16, 16, 8192, torch.bfloat16) > 0
     run_fwd_case(22, 1, 16, 16, 8192, "bf16", "zoh")
     run_fwd_case(22, 1, 16, 16, 8192, "bf16", "zoh", segments=1)
+
+
+# steps flagged in every row: the first step (the initial state is dropped),
+# a lane border (8), a 128-step chunk border and the step after it, the last
+EDGE_RESETS = (0, 8, 128, 129)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_fwd_varlen(dtype, disc):
+    L = 1189
+    rs = W.make_resets(40, 2, L, 1, 300, force=EDGE_RESETS + (L - 1,))
+    rs[1, 0] = 0          # the second row keeps its initial state
+    run_fwd_case(40, 2, 20, 16, L, dtype, disc, h0=True, reset=rs)
+
+
+def test_fwd_varlen_state_sizes_and_segments():
+    L = 1300
+    rs = W.make_resets(41, 2, L, 1, 200, force=(128, 640))
+    run_fwd_case(41, 2, 9, 5, L, "f32", "zoh", h0=True, reset=rs)
+    run_fwd_case(41, 2, 9, 33, L, "f32", "zoh", A_mode="random_neg", reset=rs)
+    run_fwd_case(41, 2, 9, 16, L, "f32", "zoh", h0=True, reset=rs, segments=4)
+    run_fwd_case(42, 1, 12, 16, 1024, "f32", "zoh", zero_A=True, segments=8,
+                 reset=W.make_resets(42, 1, 1024, 50, 400))
+    # a segment boundary that is also a reset, and a segment without any
+    rs = np.zeros((1, 2048), np.uint8)
+    rs[0, [256, 1000]] = 1
+    run_fwd_case(43, 1, 16, 16, 2048, "bf16", "euler", h0=True, reset=rs, segments=8)
 
 
 def test_fwd_is_deterministic_and_lane_choice_independent():
@@ -228,10 +259,11 @@ def test_state_update_without_optionals():
 # backward
 # --------------------------------------------------------------------------
 def run_bwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=False,
-                 opts=None, zero_A=False, A_mode="s4d_real", rtol=None):
+                 opts=None, zero_A=False, A_mode="s4d_real", rtol=None, reset=None):
     opts = opts or {}
     announce(f"bwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} lanes={lanes} "
-             f"h0={h0} opts={opts} zero_A={zero_A}")
+             f"h0={h0} opts={opts} zero_A={zero_A} "
+             f"resets={None if reset is None else int(reset.sum())}")
     inp, f = _make(wid, batch, dim, N, L, dtype, with_dout=True, A_mode=A_mode, **opts)
     if not softplus:
         inp, f = _positive_steps(inp, dtype)
@@ -244,13 +276,14 @@ def run_bwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=
     h0t = torch.from_numpy(h0v).cuda() if h0v is not None else None
     res = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g.get("D"), g.get("z"),
                       g.get("delta_bias"), g["dout"], h0t, delta_softplus=softplus, disc=disc,
-                      lanes=lanes)
+                      lanes=lanes,
+                      reset=None if reset is None else torch.from_numpy(reset).cuda())
     torch.cuda.synchronize()
     ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"), f.get("z"),
                           f.get("delta_bias"), f["dout"],
                           None if h0v is None else h0v.astype(np.float64),
                           delta_softplus=softplus,
-                          disc=oracle.ZOH if disc == "zoh" else oracle.EULER)
+                          disc=oracle.ZOH if disc == "zoh" else oracle.EULER, reset=reset)
     rt = rtol or RTOL[dtype]
     assert set(res) == set(ref), (set(res), set(ref))
     for k in ref:
@@ -270,6 +303,24 @@ def test_bwd_dtypes_discs(dtype, disc):
 def test_bwd_ragged_lengths(L):
     run_bwd_case(32, 2, 7, 16, L, "f32", "zoh")
     run_bwd_case(32, 2, 7, 16, L, "bf16", "zoh")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_bwd_varlen(dtype, disc):
+    L = 700
+    rs = W.make_resets(44, 2, L, 1, 200, force=EDGE_RESETS + (L - 1,))
+    rs[1, 0] = 0
+    run_bwd_case(44, 2, 19, 16, L, dtype, disc, h0=True, reset=rs)
+
+
+def test_bwd_varlen_state_sizes_and_zero_A():
+    L = 1000
+    rs = W.make_resets(45, 2, L, 20, 300, force=(0, 384))
+    run_bwd_case(45, 2, 7, 5, L, "f32", "zoh", reset=rs)
+    run_bwd_case(45, 2, 7, 33, L, "f32", "zoh", A_mode="random_neg", h0=True, reset=rs)
+    run_bwd_case(46, 2, 8, 16, 500, "f32", "zoh", zero_A=True, h0=True,
+                 reset=W.make_resets(46, 2, 500, 10, 100))
 
 
 def test_bwd_rejects_other_lane_counts():

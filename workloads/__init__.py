@@ -178,3 +178,26 @@ def as_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
 def inputs_f64(inp: dict, dtype: str) -> dict:
     return {k: as_f64(v, dtype) if k in ("u", "delta", "B", "C", "z", "dout") else
             np.asarray(v, np.float64) for k, v in inp.items()}
+
+
+def make_resets(wid: int, batch: int, seqlen: int, min_len: int = 1, max_len: int = 300,
+                force=()) -> np.ndarray:
+    """Reset flags (batch, seqlen) uint8 for packed variable-length sequences.
+
+    Each batch row is a run of sequences whose lengths are drawn uniformly in
+    [min_len, max_len] with ``default_rng([wid, 9, b])``; a flag marks the
+    first step of every sequence except one starting at t = 0 (the row's
+    first sequence continues from the initial state).  ``force`` lists extra
+    steps flagged in every row (edge cases such as t = 0 or chunk borders).
+    """
+    r = np.zeros((batch, seqlen), np.uint8)
+    for b in range(batch):
+        g = np.random.default_rng([wid, 9, b])
+        t = int(g.integers(min_len, max_len + 1))
+        while t < seqlen:
+            r[b, t] = 1
+            t += int(g.integers(min_len, max_len + 1))
+    for t in force:
+        if 0 <= t < seqlen:
+            r[:, t] = 1
+    return r
