@@ -63,6 +63,10 @@ def _load():
         lib.oracle_state_update.restype = None
         lib.oracle_scan_bwd.argtypes = [_dp] * 10 + [_u8p, _int, _int] + [_i64] * 6 + [_dp] * 9
         lib.oracle_scan_bwd.restype = None
+        lib.oracle_conv1d_silu_fwd.argtypes = [_dp, _dp, _dp, _u8p] + [_i64] * 6 + [_dp]
+        lib.oracle_conv1d_silu_fwd.restype = None
+        lib.oracle_conv1d_silu_bwd.argtypes = [_dp, _dp, _dp, _u8p, _dp] + [_i64] * 6 + [_dp] * 3
+        lib.oracle_conv1d_silu_bwd.restype = None
         lib.oracle_version.restype = _int
         _lib = lib
         return lib
@@ -219,6 +223,40 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
         res["ddelta_bias"] = sum(a["ddb"] for a in acc)
     if h0 is not None:
         res["dh0"] = sum(a["dh0"] for a in acc)
+    return res
+
+
+def conv1d_silu_fwd(x, w, cb=None, *, reset=None):
+    """Causal depthwise convolution (W taps, x before t = 0 and before each
+    flagged sequence start counts as zero) followed by SiLU, in float64.
+    x (batch, dim, L); w (dim, W); cb (dim,).  Returns u (batch, dim, L)."""
+    lib = _load()
+    x, w, cb = _f64(x), _f64(w), _f64(cb)
+    batch, dim, L = x.shape
+    W = w.shape[1]
+    u = np.zeros_like(x)
+    rs = _reset(reset, batch, L)
+    lib.oracle_conv1d_silu_fwd(_ptr(x), _ptr(w), _ptr(cb), _ptr8(rs), batch, dim, W, L, 0,
+                               batch * dim, _ptr(u))
+    return u
+
+
+def conv1d_silu_bwd(x, w, cb, du, *, reset=None):
+    """Gradients of sum(du * u) for u = conv1d_silu_fwd(x, w, cb): returns a
+    dict with dx, dw and (when cb is given) dcb."""
+    lib = _load()
+    x, w, cb, du = _f64(x), _f64(w), _f64(cb), _f64(du)
+    batch, dim, L = x.shape
+    W = w.shape[1]
+    dx = np.zeros_like(x)
+    dw = np.zeros_like(w)
+    dcb = np.zeros(dim) if cb is not None else None
+    rs = _reset(reset, batch, L)
+    lib.oracle_conv1d_silu_bwd(_ptr(x), _ptr(w), _ptr(cb), _ptr8(rs), _ptr(du), batch, dim, W, L,
+                               0, batch * dim, _ptr(dx), _ptr(dw), _ptr(dcb))
+    res = dict(dx=dx, dw=dw)
+    if cb is not None:
+        res["dcb"] = dcb
     return res
 
 

@@ -263,4 +263,80 @@ void oracle_scan_bwd(const double* u, const double* delta, const double* A, cons
   free(gh);
 }
 
-int oracle_version(void) { return 2; }
+/*
+ * Short causal depthwise convolution + SiLU, the stage that feeds the SSM in
+ * the Mamba block ([KNOWL3]: a 1-D temporal convolution of width
+ * d_conv = 4 on the main branch, then SiLU, then the selective SSM; [ESSAY]
+ * Part II §8 draws the same block).  Per channel (b, d), with W taps:
+ *   pre_t = cb[d] + sum_{k=0}^{W-1} w[d,k] * x_{t-(W-1)+k}
+ *   u_t   = pre_t * sigmoid(pre_t)
+ * The convolution is causal: x before t = 0 counts as zero, and with reset
+ * flags (reset[b,t] != 0, a packed sequence starts at t) so does every x
+ * before the start of the current sequence.  cb may be NULL.
+ */
+static int conv_tap_valid(const unsigned char* reset_b, int64_t s, int64_t t) {
+  /* x_s contributes to step t (s <= t) iff s >= 0 and no sequence starts in (s, t] */
+  if (s < 0) return 0;
+  if (reset_b)
+    for (int64_t q = s + 1; q <= t; ++q)
+      if (reset_b[q]) return 0;
+  return 1;
+}
+
+static double conv_pre(const double* x_r, const double* w_d, double cb, int64_t W,
+                       const unsigned char* reset_b, int64_t t) {
+  double pre = cb;
+  for (int64_t k = 0; k < W; ++k) {
+    int64_t s = t - (W - 1) + k;
+    if (conv_tap_valid(reset_b, s, t)) pre += w_d[k] * x_r[s];
+  }
+  return pre;
+}
+
+void oracle_conv1d_silu_fwd(const double* x, const double* w, const double* cb,
+                            const unsigned char* reset, int64_t batch, int64_t dim, int64_t W,
+                            int64_t seqlen, int64_t c_begin, int64_t c_end, double* u) {
+  (void)batch;
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    int64_t b = c / dim, d = c % dim;
+    const unsigned char* reset_b = reset ? reset + b * seqlen : NULL;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      double pre = conv_pre(x + c * seqlen, w + d * W, cb ? cb[d] : 0.0, W, reset_b, t);
+      u[c * seqlen + t] = pre * sigmoid(pre);
+    }
+  }
+}
+
+/*
+ * Backward of the convolution stage for a gradient du at its output:
+ *   dpre_t = du_t * sigmoid(pre_t) * (1 + pre_t * (1 - sigmoid(pre_t)))
+ *   dx_s  += w[d,k] * dpre_t      for every valid tap (s = t-(W-1)+k)
+ *   dw[d,k] += dpre_t * x_s ;  dcb[d] += dpre_t
+ * dx is written; dw and dcb (nullable) are accumulated with +=.
+ */
+void oracle_conv1d_silu_bwd(const double* x, const double* w, const double* cb,
+                            const unsigned char* reset, const double* du, int64_t batch,
+                            int64_t dim, int64_t W, int64_t seqlen, int64_t c_begin,
+                            int64_t c_end, double* dx, double* dw, double* dcb) {
+  (void)batch;
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    int64_t b = c / dim, d = c % dim;
+    const unsigned char* reset_b = reset ? reset + b * seqlen : NULL;
+    const double* x_r = x + c * seqlen;
+    for (int64_t t = 0; t < seqlen; ++t) dx[c * seqlen + t] = 0.0;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      double pre = conv_pre(x_r, w + d * W, cb ? cb[d] : 0.0, W, reset_b, t);
+      double sg = sigmoid(pre);
+      double dpre = du[c * seqlen + t] * sg * (1.0 + pre * (1.0 - sg));
+      for (int64_t k = 0; k < W; ++k) {
+        int64_t s = t - (W - 1) + k;
+        if (!conv_tap_valid(reset_b, s, t)) continue;
+        dx[c * seqlen + s] += w[d * W + k] * dpre;
+        dw[d * W + k] += dpre * x_r[s];
+      }
+      if (dcb) dcb[d] += dpre;
+    }
+  }
+}
+
+int oracle_version(void) { return 3; }
