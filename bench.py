@@ -72,6 +72,10 @@ def algorithmic_bytes(w, call: str) -> float:
         return 4 * ct * es + 3 * ct * 4 + bc + 2 * w.batch * w.dstate * w.seqlen * 4 + 2 * params
     if call == "step":     # state read + write; u, delta, z, out per channel; B, C per batch row
         return 2 * state + 4 * w.batch * w.dim * es + 2 * w.batch * w.dstate * es + params
+    if call == "conv_fwd":  # read x, write u; taps and bias
+        return 2 * ct * es + 5 * w.dim * 4
+    if call == "conv_bwd":  # read x and du (f32), write dx (f32); dw, db
+        return ct * (es + 8) + 10 * w.dim * 4
     raise ValueError(call)
 
 
@@ -241,6 +245,12 @@ def main():
     t_last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device="cuda")
     t_out = torch.empty_like(g["u"])
     step_args = {k: g[k][..., 0].contiguous() for k in ("u", "delta", "B", "C", "z")}
+    conv_w = conv_b = conv_du = None
+    if any(c.startswith("conv") for c in calls):
+        cg = np.random.default_rng([w.wid, 10])
+        conv_w = torch.from_numpy((cg.standard_normal((w.dim, 4)) * 0.5).astype(np.float32)).cuda()
+        conv_b = torch.from_numpy((cg.standard_normal(w.dim) * 0.5).astype(np.float32)).cuda()
+        conv_du = g["u"].float()
     step_out = torch.empty((w.batch, w.dim), dtype=sdt, device="cuda")
 
     def run_call(c, timing=None):
@@ -252,6 +262,10 @@ def main():
             ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
                         g["delta_bias"], g["dout"], disc=args.disc, workspace=ws, timing=timing,
                         reset=rst)
+        elif c == "conv_fwd":   # x = the workload's u sequence
+            ms.conv1d_silu_fwd(g["u"], conv_w, conv_b, reset=rst, out=t_out)
+        elif c == "conv_bwd":
+            ms.conv1d_silu_bwd(g["u"], conv_w, conv_b, conv_du, reset=rst)
         else:   # decode step continuing from the forward's final state, in place
             ms.state_update(t_last, step_args["u"], step_args["delta"], g["A"], step_args["B"],
                             step_args["C"], g["D"], step_args["z"], g["delta_bias"],

@@ -197,6 +197,37 @@ mamba_status mamba_scan_bwd_varlen(const void* u, const void* delta, const float
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * Short causal depthwise convolution + SiLU, the stage that feeds the SSM
+ * in the Mamba block (chapterpal.com page, Knowl 3 "Mamba Block
+ * Architecture": a width-4 temporal convolution, then SiLU; trishampatil
+ * essay, Part II §8).  Per channel (b, d), with W = width taps (1..4):
+ *   pre_t = b[d] + sum_{k<W} w[d*W + k] * x_{t-(W-1)+k},  u_t = pre_t*sigmoid(pre_t)
+ * x before t = 0 counts as zero, and so does x before the start of the
+ * current packed sequence when `reset` (nullable, (batch, seqlen) bytes, as
+ * for mamba_scan_fwd_varlen) flags sequence starts.
+ * Layouts: x, u (batch, dim, seqlen) in `dt`; w (dim, width) and b (dim,
+ * nullable) float32.  u is overwritten.
+ *
+ * The backward takes du (float32, the gradient at u) and writes dx
+ * (float32, same layout), dw (dim, width) and db (dim; NULL iff b is NULL),
+ * recomputing pre from x rather than reading a stored copy (trishampatil
+ * essay, Part III §4: the block's cheap activations and the short
+ * convolution are recomputed in the backward, not saved).  dw and db are
+ * zeroed on the stream, then summed with float32 atomics (deterministic up to
+ * rounding order).  Errors as for the scan calls; width outside 1..4 is
+ * MAMBA_ERR_UNSUPPORTED.
+ */
+mamba_status mamba_conv1d_silu_fwd(const void* x, const float* w, const float* b,
+                                   const uint8_t* reset, int64_t width, mamba_dtype dt,
+                                   int64_t batch, int64_t dim, int64_t seqlen, void* u,
+                                   void* stream);
+
+mamba_status mamba_conv1d_silu_bwd(const void* x, const float* w, const float* b,
+                                   const uint8_t* reset, const float* du, int64_t width,
+                                   mamba_dtype dt, int64_t batch, int64_t dim, int64_t seqlen,
+                                   float* dx, float* dw, float* db, void* stream);
+
+/*
  * Tuning and timing variants.  Identical to the calls above (reset may be
  * NULL here: no flags) except for:
  *  - lanes_per_channel: the number of lanes each channel's scan is spread

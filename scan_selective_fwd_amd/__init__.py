@@ -232,6 +232,51 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
     return out
 
 
+def conv1d_silu_fwd(x, w, b=None, *, reset=None, out=None):
+    """Short causal depthwise convolution (w: (dim, W), W <= 4) followed by
+    SiLU.  x (batch, dim, L) float32 or bfloat16; returns u like x."""
+    L_ = lib()
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor (no CPU path exists)")
+    dev = x.device
+    batch, dim, L = x.shape
+    W = w.shape[1]
+    _req(x, "x", x.dtype, (batch, dim, L), dev)
+    _req(w, "w", torch.float32, (dim, W), dev)
+    _req(b, "b", torch.float32, (dim,), dev)
+    reset = _flags(reset, (batch, L), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", x.dtype, (batch, dim, L), dev)
+    st = L_.mamba_conv1d_silu_fwd(_ptr(x), _ptr(w), _ptr(b), _ptr(reset), W, _dtype_code(x),
+                                  batch, dim, L, _ptr(out), _stream(dev))
+    _lib.check(st, "mamba_conv1d_silu_fwd")
+    return out
+
+
+def conv1d_silu_bwd(x, w, b, du, *, reset=None):
+    """Backward of conv1d_silu_fwd for the gradient du (float32) at its
+    output: returns a dict with dx, dw and (when b is given) db, float32."""
+    L_ = lib()
+    dev = x.device
+    batch, dim, L = x.shape
+    W = w.shape[1]
+    _req(x, "x", x.dtype, (batch, dim, L), dev)
+    _req(w, "w", torch.float32, (dim, W), dev)
+    _req(b, "b", torch.float32, (dim,), dev)
+    _req(du, "du", torch.float32, (batch, dim, L), dev)
+    reset = _flags(reset, (batch, L), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty((batch, dim, L), **f32), dw=torch.empty((dim, W), **f32))
+    if b is not None:
+        g["db"] = torch.empty((dim,), **f32)
+    st = L_.mamba_conv1d_silu_bwd(_ptr(x), _ptr(w), _ptr(b), _ptr(reset), _ptr(du), W,
+                                  _dtype_code(x), batch, dim, L, _ptr(g["dx"]), _ptr(g["dw"]),
+                                  _ptr(g.get("db")), _stream(dev))
+    _lib.check(st, "mamba_conv1d_silu_bwd")
+    return g
+
+
 class SelectiveScanFn(torch.autograd.Function):
     """Autograd wrapper: forward = scan_fwd, backward = scan_bwd (states are
     recomputed, only the inputs are saved)."""

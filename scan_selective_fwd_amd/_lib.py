@@ -23,7 +23,8 @@ ZOH, EULER = 0, 1
 EXPORTS = (
     "mamba_abi_version", "mamba_status_string", "mamba_scan_fwd_workspace_size",
     "mamba_scan_bwd_workspace_size", "mamba_scan_fwd", "mamba_scan_bwd", "mamba_state_update",
-    "mamba_scan_fwd_varlen", "mamba_scan_bwd_varlen",
+    "mamba_scan_fwd_varlen", "mamba_scan_bwd_varlen", "mamba_conv1d_silu_fwd",
+    "mamba_conv1d_silu_bwd",
     "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size_ex", "mamba_scan_bwd_workspace_size_ex",
     "mamba_scan_bwd_ex",
 )
@@ -81,6 +82,10 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_bwd_varlen.argtypes = bwd_rst
     lib.mamba_scan_bwd_ex.restype = _int
     lib.mamba_scan_bwd_ex.argtypes = bwd_rst + [_int, _vp, _vp]
+    lib.mamba_conv1d_silu_fwd.restype = _int
+    lib.mamba_conv1d_silu_fwd.argtypes = [_vp] * 4 + [_i64, _int] + [_i64] * 3 + [_vp, _vp]
+    lib.mamba_conv1d_silu_bwd.restype = _int
+    lib.mamba_conv1d_silu_bwd.argtypes = [_vp] * 5 + [_i64, _int] + [_i64] * 3 + [_vp] * 4
     lib.mamba_state_update.restype = _int
     lib.mamba_state_update.argtypes = [_vp] * 9 + [_int, _int, _int] + [_i64] * 3 + [_vp, _vp]
     _lib = lib

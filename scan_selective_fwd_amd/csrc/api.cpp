@@ -374,4 +374,51 @@ mamba_status mamba_state_update(float* state, const void* u, const void* delta, 
                                                  static_cast<hipStream_t>(stream)));
 }
 
+// ---- short causal convolution + SiLU ----
+mamba_status mamba_conv1d_silu_fwd(const void* x, const float* w, const float* b,
+                                   const uint8_t* reset, int64_t width, mamba_dtype dt,
+                                   int64_t batch, int64_t dim, int64_t seqlen, void* u,
+                                   void* stream) {
+  mamba_status st = check_sizes(dt, MAMBA_DISC_ZOH, batch, dim, 1, seqlen);
+  if (st != MAMBA_OK) return st;
+  if (width < 1 || width > 4) return MAMBA_ERR_UNSUPPORTED;
+  if (!x || !w || !u) return MAMBA_ERR_NULL_PTR;
+  const void* ptrs[] = {x, w, b, u};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MAMBA_ERR_ALIGNMENT;
+  mscan::ConvParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x; p.w = w; p.b = b; p.reset = reset; p.u = u;
+  p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
+  p.tiles = mscan::conv_tiles(seqlen); p.W = (int)width;
+  if (p.nchannels * p.tiles > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
+  const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  return hip_status(mscan::dispatch_conv_fwd(p, dt == MAMBA_F32 ? 0 : 1, vec,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+mamba_status mamba_conv1d_silu_bwd(const void* x, const float* w, const float* b,
+                                   const uint8_t* reset, const float* du, int64_t width,
+                                   mamba_dtype dt, int64_t batch, int64_t dim, int64_t seqlen,
+                                   float* dx, float* dw, float* db, void* stream) {
+  mamba_status st = check_sizes(dt, MAMBA_DISC_ZOH, batch, dim, 1, seqlen);
+  if (st != MAMBA_OK) return st;
+  if (width < 1 || width > 4) return MAMBA_ERR_UNSUPPORTED;
+  if (!x || !w || !du || !dx || !dw) return MAMBA_ERR_NULL_PTR;
+  if ((b == nullptr) != (db == nullptr)) return MAMBA_ERR_INVALID;
+  const void* ptrs[] = {x, w, b, du, dx, dw, db};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MAMBA_ERR_ALIGNMENT;
+  mscan::ConvParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x; p.w = w; p.b = b; p.reset = reset; p.du = du; p.dx = dx; p.dw = dw; p.db = db;
+  p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
+  p.tiles = mscan::conv_tiles(seqlen); p.W = (int)width;
+  if (p.nchannels * p.tiles > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
+  // vector loads need 16-byte rows for both x and the float32 du / dx
+  const bool vec = (seqlen * elem_size(dt)) % 16 == 0 && (seqlen * 4) % 16 == 0;
+  return hip_status(mscan::dispatch_conv_bwd(p, dt == MAMBA_F32 ? 0 : 1, vec,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

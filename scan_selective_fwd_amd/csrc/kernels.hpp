@@ -98,6 +98,26 @@ struct StepParams {
   int softplus;
 };
 
+// Short causal convolution + SiLU (conv1d_silu.hip).
+struct ConvParams {
+  const void* x;           // (batch, dim, L), sequence dtype
+  const float* w;          // (dim, W)
+  const float* b;          // (dim), nullable
+  const uint8_t* reset;    // (batch, L), nullable
+  void* u;                 // forward output (batch, dim, L), sequence dtype
+  const float* du;         // backward input (batch, dim, L)
+  float* dx;               // backward outputs
+  float* dw;
+  float* db;               // nullable (iff b is)
+  int64_t batch, dim, L;
+  int64_t nchannels;
+  int64_t tiles;           // blocks per channel (conv_tiles(L))
+  int W;                   // taps, 1..4
+};
+int64_t conv_tiles(int64_t L);
+hipError_t dispatch_conv_fwd(const ConvParams& p, int dtype, bool vec, hipStream_t s);
+hipError_t dispatch_conv_bwd(const ConvParams& p, int dtype, bool vec, hipStream_t s);
+
 // Channels a block of kBlock threads serves when each channel owns `lanes`
 // lanes, and the number of such groups per batch row.
 inline int channels_per_block(int lanes) { return (kBlock / 64) * (64 / lanes); }

@@ -192,3 +192,35 @@ def test_missing_library_fails_loudly(tmp_path):
             _lib.load(str(tmp_path / "nope.so"))
         finally:
             _lib._lib = _lib._lib_saved
+
+
+def conv_fwd(lib, **kw):
+    a = dict(x=P, w=P, b=None, reset=None, width=4, dt=0, batch=1, dim=8, L=64, u=P, stream=None)
+    a.update(kw)
+    return lib.mamba_conv1d_silu_fwd(a["x"], a["w"], a["b"], a["reset"], a["width"], a["dt"],
+                                     a["batch"], a["dim"], a["L"], a["u"], a["stream"])
+
+
+def conv_bwd(lib, **kw):
+    a = dict(x=P, w=P, b=None, reset=None, du=P, width=4, dt=0, batch=1, dim=8, L=64, dx=P, dw=P,
+             db=None, stream=None)
+    a.update(kw)
+    return lib.mamba_conv1d_silu_bwd(a["x"], a["w"], a["b"], a["reset"], a["du"], a["width"],
+                                     a["dt"], a["batch"], a["dim"], a["L"], a["dx"], a["dw"],
+                                     a["db"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(u=None), 1), (dict(L=0), 2), (dict(dt=3), 3),
+    (dict(x=P + 2), 4), (dict(b=P + 4), 4), (dict(width=0), 6), (dict(width=5), 6),
+])
+def test_conv_fwd_rejects_bad_arguments(lib, kw, code):
+    assert conv_fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(du=None), 1), (dict(dx=None), 1), (dict(dw=None), 1), (dict(b=P), 8), (dict(db=P), 8),
+    (dict(dx=P + 4), 4), (dict(width=7), 6), (dict(batch=-1), 2),
+])
+def test_conv_bwd_rejects_bad_arguments(lib, kw, code):
+    assert conv_bwd(lib, **kw) == code
