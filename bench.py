@@ -2,9 +2,12 @@
 
 One step = the whole hot path over one batch of synthetic input at the
 Mamba-130M layer shape (batch 8, D = 1536, N = 16, L = 2048, float32, ZOH,
-softplus, D skip and SiLU gate): mamba_scan_fwd (with the final state), then
-mamba_scan_bwd (states recomputed from the inputs), then one
-mamba_state_update decode step continuing from the final state.
+softplus, D skip and SiLU gate), as a training framework runs it: the
+forward (with the final state, saving the state entering every 128-step
+chunk), then the backward (every state inside the chunks recomputed from
+those checkpoints and the inputs), then one decode step continuing from the
+final state.  --no-checkpoints makes the backward recompute the chunk
+states too.
 
 Prints ONE JSON line.  `value` is the achieved algorithmic HBM throughput of
 the step (bytes every call must move at least once, divided by the step
@@ -204,6 +207,8 @@ def main():
     ap.add_argument("--varlen", action="store_true",
                     help="pack variable-length sequences (lengths uniform in 64..1024) into each "
                          "row, with reset flags at their starts")
+    ap.add_argument("--no-checkpoints", action="store_true",
+                    help="the forward saves no chunk states; the backward recomputes them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (for counter calibration)")
     ap.add_argument("--calls", default=None,
@@ -243,6 +248,10 @@ def main():
     if nfws:
         fws = torch.empty(nfws, dtype=torch.uint8, device="cuda")
     t_last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device="cuda")
+    ckpt = None
+    if "fwd" in calls and "bwd" in calls and not args.no_checkpoints:
+        ckpt = torch.empty(ms.checkpoint_shape(w.batch, w.dim, w.dstate, w.seqlen),
+                           dtype=torch.float32, device="cuda")
     t_out = torch.empty_like(g["u"])
     step_args = {k: g[k][..., 0].contiguous() for k in ("u", "delta", "B", "C", "z")}
     conv_w = conv_b = conv_du = None
@@ -257,11 +266,12 @@ def main():
         if c == "fwd":
             ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
                         g["delta_bias"], disc=args.disc, out=t_out, last_state=t_last,
-                        return_last_state=True, workspace=fws, timing=timing, reset=rst)
+                        return_last_state=True, workspace=fws, timing=timing, reset=rst,
+                        checkpoints=ckpt)
         elif c == "bwd":
             ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
                         g["delta_bias"], g["dout"], disc=args.disc, workspace=ws, timing=timing,
-                        reset=rst)
+                        reset=rst, checkpoints=ckpt)
         elif c == "conv_fwd":   # x = the workload's u sequence
             ms.conv1d_silu_fwd(g["u"], conv_w, conv_b, reset=rst, out=t_out)
         elif c == "conv_bwd":
@@ -328,7 +338,9 @@ def main():
         "dtype": "f32" if w.dtype == "f32" else "bf16-in/f32-compute",
         "data": "synthetic",
         "config": {"workload": f"{w.name}{' packed varlen' if args.varlen else ''}: "
-                               f"{'+'.join(calls)} ({args.disc})", "batch": w.batch,
+                               f"{'+'.join(calls)} ({args.disc})"
+                               f"{', chunk checkpoints' if ckpt is not None else ''}",
+                   "batch": w.batch,
                    "dim": w.dim, "dstate": w.dstate, "seqlen": w.seqlen, "dtype": w.dtype,
                    "disc": args.disc, "delta_softplus": True, "D": True, "z": True,
                    "delta_bias": w.bias},

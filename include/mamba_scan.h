@@ -241,6 +241,18 @@ mamba_status mamba_conv1d_silu_bwd(const void* x, const float* w, const float* b
  *    one per 128-step chunk).  Segmented runs need the workspace reported by
  *    mamba_scan_fwd_workspace_size_ex for the same lanes and segments values
  *    (MAMBA_ERR_WORKSPACE otherwise) and 16 lanes per channel.
+ *  - checkpoints (forward: float* output, backward: const float* input;
+ *    NULL = none): the state entering every 128-step chunk, (batch, dim,
+ *    ceil(seqlen/128), dstate) float32, mamba_scan_checkpoint_size bytes.
+ *    A forward given the buffer writes it (with 16 lanes per channel); a
+ *    backward given it uses it instead of recomputing those states in a
+ *    separate pass, and then needs only the part of its workspace past the
+ *    states (the query's size still suffices).  The backward still replays
+ *    every state inside each chunk from its checkpoint: only 1/128 of the
+ *    (B, L, D, N) states is ever stored (paper-graph-ui summary, section
+ *    3.4, and trishampatil essay, Part III §4: the full states are
+ *    recomputed, not saved).  Checkpoints must come from a forward over the
+ *    same inputs.
  *  - timing_begin, timing_end: hipEvent_t handles (NULL = none).  When given,
  *    they are recorded on `stream` immediately before and after the main
  *    scan kernel of the call (the forward's output kernel, after a segmented
@@ -260,7 +272,8 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
                                int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                void* out, float* last_state, void* workspace,
                                size_t workspace_bytes, void* stream, int lanes_per_channel,
-                               int segments, void* timing_begin, void* timing_end);
+                               int segments, float* checkpoints, void* timing_begin,
+                               void* timing_end);
 
 size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
                                         int64_t seqlen, mamba_dtype dt, int lanes_per_channel);
@@ -273,7 +286,12 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
                                int64_t seqlen, float* du, float* ddelta, float* dA, float* dB,
                                float* dC, float* dD, float* dz, float* ddelta_bias, float* dh0,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel, void* timing_begin, void* timing_end);
+                               int lanes_per_channel, const float* checkpoints,
+                               void* timing_begin, void* timing_end);
+
+/* Bytes of the checkpoint buffer of the _ex calls (SIZE_MAX for unsupported
+ * sizes). */
+size_t mamba_scan_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
 
 #ifdef __cplusplus
 }

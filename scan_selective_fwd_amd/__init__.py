@@ -97,10 +97,12 @@ def _events(timing):
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
              delta_softplus=True, disc="zoh", return_last_state=False, out=None, last_state=None,
-             lanes=0, segments=0, workspace=None, timing=None, reset=None):
+             lanes=0, segments=0, workspace=None, timing=None, reset=None, checkpoints=None):
     """Fused selective-scan forward.  Returns out, or (out, last_state).
     `reset`: optional (batch, L) uint8/bool device tensor; the state is zeroed
     before every flagged step (packed variable-length sequences).
+    `checkpoints`: optional float32 tensor of checkpoint_shape(...) that
+    receives the state entering every 128-step chunk, for scan_bwd.
     `segments`: 0 automatic, 1 one pass, k >= 2 that many sequence segments.
     `workspace`: optional uint8 device tensor reused across calls.
     `timing`: optional (begin, end) torch.cuda.Event pair recorded around the
@@ -123,6 +125,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
     _req(delta_bias, "delta_bias", torch.float32, (dim,), dev)
     _req(h0, "h0", torch.float32, (batch, dim, N), dev)
     reset = _flags(reset, (batch, L), dev)
+    _req(checkpoints, "checkpoints", torch.float32, checkpoint_shape(batch, dim, N, L), dev)
     if out is None:
         out = torch.empty((batch, dim, L), dtype=sdt, device=dev)
     _req(out, "out", sdt, (batch, dim, L), dev)
@@ -137,9 +140,15 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
                               _ptr(delta_bias), _ptr(h0), _ptr(reset), int(bool(delta_softplus)),
                               _disc_code(disc), dt, batch, dim, N, L, _ptr(out),
                               _ptr(last_state), ws_ptr, nbytes, _stream(dev), int(lanes),
-                              int(segments), *_events(timing))
+                              int(segments), _ptr(checkpoints), *_events(timing))
     _lib.check(st, "mamba_scan_fwd")
     return (out, last_state) if return_last_state else out
+
+
+def checkpoint_shape(batch, dim, N, L):
+    """Shape of the forward's checkpoint buffer: the state entering every
+    128-step chunk."""
+    return (batch, dim, (L + 127) // 128, N)
 
 
 def fwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0, segments=0) -> int:
@@ -159,7 +168,8 @@ def bwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0) -> int:
 
 
 def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softplus=True,
-             disc="zoh", lanes=0, workspace=None, want_dh0=True, timing=None, reset=None):
+             disc="zoh", lanes=0, workspace=None, want_dh0=True, timing=None, reset=None,
+             checkpoints=None):
     """Backward with state recomputation.  Returns a dict of float32 gradients:
     du, ddelta, dA, dB, dC and, when the input is given, dD, dz, ddelta_bias, dh0.
     `timing`: optional (begin, end) torch.cuda.Event pair recorded around the
@@ -179,6 +189,7 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
                              (dout, "dout", (batch, dim, L), sdt)):
         _req(t, name, ty, shp, dev)
     reset = _flags(reset, (batch, L), dev)
+    _req(checkpoints, "checkpoints", torch.float32, checkpoint_shape(batch, dim, N, L), dev)
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(du=torch.empty((batch, dim, L), **f32), ddelta=torch.empty((batch, dim, L), **f32),
              dA=torch.empty((dim, N), **f32), dB=torch.empty((batch, N, L), **f32),
@@ -201,7 +212,7 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
                               _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
                               _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
                               _ptr(g.get("dh0")), workspace.data_ptr(), workspace.numel(),
-                              _stream(dev), int(lanes), *_events(timing))
+                              _stream(dev), int(lanes), _ptr(checkpoints), *_events(timing))
     _lib.check(st, "mamba_scan_bwd")
     return g
 
@@ -278,23 +289,27 @@ def conv1d_silu_bwd(x, w, b, du, *, reset=None):
 
 
 class SelectiveScanFn(torch.autograd.Function):
-    """Autograd wrapper: forward = scan_fwd, backward = scan_bwd (states are
-    recomputed, only the inputs are saved)."""
+    """Autograd wrapper: forward = scan_fwd, backward = scan_bwd.  Besides the
+    inputs, the forward saves only the state entering every 128-step chunk;
+    the backward recomputes every other state from them."""
 
     @staticmethod
     def forward(ctx, u, delta, A, B, C, D, z, delta_bias, delta_softplus, disc):
+        batch, dim, L = u.shape
+        ckpt = torch.empty(checkpoint_shape(batch, dim, A.shape[1], L), dtype=torch.float32,
+                           device=u.device)
         out = scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus=delta_softplus,
-                       disc=disc)
-        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias)
+                       disc=disc, checkpoints=ckpt)
+        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, ckpt)
         ctx.flags = (delta_softplus, disc)
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        u, delta, A, B, C, D, z, delta_bias = ctx.saved_tensors
+        u, delta, A, B, C, D, z, delta_bias, ckpt = ctx.saved_tensors
         sp, disc = ctx.flags
         g = scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout.contiguous().to(u.dtype),
-                     delta_softplus=sp, disc=disc)
+                     delta_softplus=sp, disc=disc, checkpoints=ckpt)
         cast = lambda t, like: None if t is None else t.to(like.dtype)
         return (cast(g["du"], u), cast(g["ddelta"], delta), g["dA"], cast(g["dB"], B),
                 cast(g["dC"], C), g.get("dD"), cast(g.get("dz"), z) if z is not None else None,

@@ -26,7 +26,7 @@ EXPORTS = (
     "mamba_scan_fwd_varlen", "mamba_scan_bwd_varlen", "mamba_conv1d_silu_fwd",
     "mamba_conv1d_silu_bwd",
     "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size_ex", "mamba_scan_bwd_workspace_size_ex",
-    "mamba_scan_bwd_ex",
+    "mamba_scan_bwd_ex", "mamba_scan_checkpoint_size",
 )
 
 
@@ -73,7 +73,7 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_fwd_varlen.restype = _int
     lib.mamba_scan_fwd_varlen.argtypes = fwd_rst
     lib.mamba_scan_fwd_ex.restype = _int
-    lib.mamba_scan_fwd_ex.argtypes = fwd_rst + [_int, _int, _vp, _vp]
+    lib.mamba_scan_fwd_ex.argtypes = fwd_rst + [_int, _int, _vp, _vp, _vp]
     bwd_args = [_vp] * 10 + [_int, _int, _int] + [_i64] * 4 + [_vp] * 10 + [_sz, _vp]
     lib.mamba_scan_bwd.restype = _int
     lib.mamba_scan_bwd.argtypes = bwd_args
@@ -81,7 +81,9 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_bwd_varlen.restype = _int
     lib.mamba_scan_bwd_varlen.argtypes = bwd_rst
     lib.mamba_scan_bwd_ex.restype = _int
-    lib.mamba_scan_bwd_ex.argtypes = bwd_rst + [_int, _vp, _vp]
+    lib.mamba_scan_bwd_ex.argtypes = bwd_rst + [_int, _vp, _vp, _vp]
+    lib.mamba_scan_checkpoint_size.restype = _sz
+    lib.mamba_scan_checkpoint_size.argtypes = [_i64] * 4
     lib.mamba_conv1d_silu_fwd.restype = _int
     lib.mamba_conv1d_silu_fwd.argtypes = [_vp] * 4 + [_i64, _int] + [_i64] * 3 + [_vp, _vp]
     lib.mamba_conv1d_silu_bwd.restype = _int

@@ -163,6 +163,13 @@ size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dsta
   return bwd_layout(batch, dim, dstate, seqlen).total;
 }
 
+size_t mamba_scan_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  if (check_sizes(MAMBA_F32, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK)
+    return SIZE_MAX;
+  const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
+  return (size_t)(batch * dim) * (size_t)w.nchunks * (size_t)dstate * 4;
+}
+
 size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                      mamba_dtype dt) {
   return mamba_scan_bwd_workspace_size_ex(batch, dim, dstate, seqlen, dt, 0);
@@ -177,12 +184,13 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
                                mamba_disc disc, mamba_dtype dt, int64_t batch, int64_t dim,
                                int64_t dstate, int64_t seqlen, void* out, float* last_state,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel, int segments, void* timing_begin,
-                               void* timing_end) {
+                               int lanes_per_channel, int segments, float* checkpoints,
+                               void* timing_begin, void* timing_end) {
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
   if (st != MAMBA_OK) return st;
   if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL_PTR;
-  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, out, last_state, workspace};
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, out, last_state, workspace,
+                        checkpoints};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MAMBA_ERR_ALIGNMENT;
   if (segments < 0) return MAMBA_ERR_UNSUPPORTED;
@@ -199,16 +207,17 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
       segmented = false;   // automatic choice without the workspace: one pass
     }
   }
-  // reset flags run with 16 lanes per channel
-  if (reset && lanes_per_channel != 0 && lanes_per_channel != 16) return MAMBA_ERR_UNSUPPORTED;
-  int lanes = (segmented || reset) ? 16 : lanes_per_channel;
+  // reset flags and checkpoints (128-step chunks) run with 16 lanes per channel
+  if ((reset || checkpoints) && lanes_per_channel != 0 && lanes_per_channel != 16)
+    return MAMBA_ERR_UNSUPPORTED;
+  int lanes = (segmented || reset || checkpoints) ? 16 : lanes_per_channel;
   if (lanes == 0) lanes = choose_lanes(batch * dim, seqlen, kItems);
   if (!valid_lanes(lanes)) return MAMBA_ERR_UNSUPPORTED;
 
   mscan::FwdParams p;
   memset(&p, 0, sizeof(p));
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.bias = delta_bias;
-  p.h0 = h0; p.out = out; p.last_state = last_state; p.chunk_states = nullptr;
+  p.h0 = h0; p.out = out; p.last_state = last_state; p.chunk_states = checkpoints;
   p.reset = reset;
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.groups = mscan::channel_groups(dim, lanes);
@@ -247,7 +256,7 @@ mamba_status mamba_scan_fwd(const void* u, const void* delta, const float* A, co
                             void* workspace, size_t workspace_bytes, void* stream) {
   return mamba_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, nullptr, delta_softplus,
                            disc, dt, batch, dim, dstate, seqlen, out, last_state, workspace,
-                           workspace_bytes, stream, 0, 0, nullptr, nullptr);
+                           workspace_bytes, stream, 0, 0, nullptr, nullptr, nullptr);
 }
 
 mamba_status mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A,
@@ -260,7 +269,7 @@ mamba_status mamba_scan_fwd_varlen(const void* u, const void* delta, const float
   if (!reset) return MAMBA_ERR_NULL_PTR;
   return mamba_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, reset, delta_softplus, disc,
                            dt, batch, dim, dstate, seqlen, out, last_state, workspace,
-                           workspace_bytes, stream, 0, 0, nullptr, nullptr);
+                           workspace_bytes, stream, 0, 0, nullptr, nullptr, nullptr);
 }
 
 mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
@@ -271,7 +280,8 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
                                int64_t seqlen, float* du, float* ddelta, float* dA, float* dB,
                                float* dC, float* dD, float* dz, float* ddelta_bias, float* dh0,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel, void* timing_begin, void* timing_end) {
+                               int lanes_per_channel, const float* checkpoints,
+                               void* timing_begin, void* timing_end) {
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
   if (st != MAMBA_OK) return st;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
@@ -280,16 +290,19 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
       (delta_bias == nullptr) != (ddelta_bias == nullptr) || (h0 == nullptr && dh0 != nullptr))
     return MAMBA_ERR_INVALID;
   const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, dout, du, ddelta, dA, dB, dC,
-                        dD, dz, ddelta_bias, dh0, workspace};
+                        dD, dz, ddelta_bias, dh0, workspace, checkpoints};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MAMBA_ERR_ALIGNMENT;
   if (lanes_per_channel != 0 && lanes_per_channel != mscan::kBwdLanes) return MAMBA_ERR_UNSUPPORTED;
   const int lanes = mscan::kBwdLanes;
   const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
-  if (!workspace || workspace_bytes < w.total) return MAMBA_ERR_WORKSPACE;
+  // with checkpoints from the forward only the flags live in the workspace
+  const size_t need = checkpoints ? w.total - w.off_flags : w.total;
+  if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
   if (batch * w.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
 
-  float* states = static_cast<float*>(workspace);
+  float* states = checkpoints ? const_cast<float*>(checkpoints) : static_cast<float*>(workspace);
+  const size_t off_flags = checkpoints ? 0 : w.off_flags;
   const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
   const int dti = dt == MAMBA_F32 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -305,8 +318,10 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   fp.nseg = 1;
   fp.seg_chunks = 0;
   fp.N = (int)dstate; fp.softplus = delta_softplus ? 1 : 0;
-  hipError_t e = mscan::dispatch_chunk_states(fp, dti, (int)disc, lanes, vec, s);
-  if (e != hipSuccess) return MAMBA_ERR_HIP;
+  if (!checkpoints) {
+    const hipError_t e = mscan::dispatch_chunk_states(fp, dti, (int)disc, lanes, vec, s);
+    if (e != hipSuccess) return MAMBA_ERR_HIP;
+  }
 
   mscan::BwdParams p;
   memset(&p, 0, sizeof(p));
@@ -315,7 +330,7 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0;
   p.chunk_states = states;
   p.reset = reset;
-  p.deferred = reinterpret_cast<int*>(static_cast<char*>(workspace) + w.off_flags);
+  p.deferred = reinterpret_cast<int*>(static_cast<char*>(workspace) + off_flags);
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.nchunks = w.nchunks; p.groups = w.groups; p.N = (int)dstate;
   p.softplus = delta_softplus ? 1 : 0;
@@ -335,7 +350,7 @@ mamba_status mamba_scan_bwd(const void* u, const void* delta, const float* A, co
   return mamba_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout, nullptr,
                            delta_softplus, disc, dt, batch, dim, dstate, seqlen, du, ddelta, dA,
                            dB, dC, dD, dz, ddelta_bias, dh0, workspace, workspace_bytes, stream, 0,
-                           nullptr, nullptr);
+                           nullptr, nullptr, nullptr);
 }
 
 mamba_status mamba_scan_bwd_varlen(const void* u, const void* delta, const float* A,
@@ -351,7 +366,7 @@ mamba_status mamba_scan_bwd_varlen(const void* u, const void* delta, const float
   return mamba_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout, reset, delta_softplus,
                            disc, dt, batch, dim, dstate, seqlen, du, ddelta, dA, dB, dC, dD, dz,
                            ddelta_bias, dh0, workspace, workspace_bytes, stream, 0, nullptr,
-                           nullptr);
+                           nullptr, nullptr);
 }
 
 mamba_status mamba_state_update(float* state, const void* u, const void* delta, const float* A,

@@ -25,7 +25,8 @@ struct FwdParams {
   const float* h0;         // nullable
   void* out;
   float* last_state;       // nullable
-  float* chunk_states;     // states-only mode: (nchannels, nchunks, N) state at each chunk start
+  float* chunk_states;     // (nchannels, nchunks, N) state at each 128-step chunk start: written
+                           // by the recompute mode, and by the output mode when non-null
   int64_t batch, dim, L;
   int64_t nchannels;       // batch * dim
   int64_t groups;          // channel groups per batch row (one block each)

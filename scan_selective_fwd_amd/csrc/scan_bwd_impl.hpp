@@ -388,11 +388,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             const int i = s * kBlock + tid;
             const int which = i / (G * TCH);
             const int nn = (i / TCH) % G;
-            const int pos = i % TCH;
+            // consecutive threads take consecutive steps, so that each wave's
+            // global atomics cover the fewest cache lines
+            const int tt = i % TCH;
+            const int pos = (tt % K) * 16 + tt / K;
             float v = 0.0f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) v += red[buf][w][which][nn][pos];
-            const int tt = (pos % 16) * K + pos / 16;
             if (n0 + nn < N && t0 + tt < L)
               unsafeAtomicAdd((which ? p.dC : p.dB) + (b * N + n0 + nn) * L + t0 + tt, v);
           }

@@ -83,9 +83,10 @@ __device__ __forceinline__ void store_items(T* __restrict__ row, int64_t t, int6
   }
 }
 
-// MODE (FwdMode): kModeOut computes the outputs.  kModeChunkStates is the
-// backward's recompute pass: it only writes the state at the start of every
-// chunk (to p.chunk_states).  kModeSegSummary runs one segment of a long
+// MODE (FwdMode): kModeOut computes the outputs (and, when p.chunk_states is
+// set, also saves the state at the start of every chunk as checkpoints for
+// the backward).  kModeChunkStates is the backward's recompute pass: it only
+// writes the state at the start of every chunk (to p.chunk_states).  kModeSegSummary runs one segment of a long
 // sequence from a zero state and writes its end state and delta sum.  The
 // two state-only modes skip C, z, y and out.
 //
@@ -97,7 +98,8 @@ __device__ __forceinline__ void store_items(T* __restrict__ row, int64_t t, int6
 // zero: the step's decay factor in the recurrence (not in Bbar) becomes 0,
 // and so does the decay of any lane summary that contains the step.
 template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE, bool RST = false>
-__global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_fwd_kernel(
+    const FwdParams p) {
   constexpr bool STATES = MODE != kModeOut;
   constexpr int CPW = 64 / R;   // channels per wave
   constexpr int CPB = (kBlock / 64) * CPW;
@@ -180,6 +182,22 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
     load_items<T, K>(u_row, tb + (int64_t)j * K, L, full0, nu);
     load_items<T, K>(dl_row, tb + (int64_t)j * K, L, full0, nd);
   }
+  // The state entering each chunk: the backward's recompute pass, or
+  // checkpoints a forward may save for a later backward (same 128-step
+  // chunks: 16 lanes x 8 steps).  The first chunk's is stored here, the
+  // others at the end of the chunk before them, where few registers are live.
+  constexpr bool kCkpt = R == 16 && R * K == 16 * kItemsBwd;
+  const bool save_states =
+      MODE == kModeChunkStates || (MODE == kModeOut && kCkpt && p.chunk_states != nullptr);
+  auto store_state = [&](int64_t ch) {
+    if (save_states && active && j == 0) {
+      float* dst = p.chunk_states + (c * nchunks + ch) * N;
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        if (n < N) dst[n] = cr[n];
+    }
+  };
+  store_state(ch_begin);
   float dtot = 0.0f;   // this lane's delta sum over the block's chunks
   bool seg_reset = false;   // RST: a flag in this lane's steps of the block
   // barrier for the LDS fills; also: does any channel of the block have A ~ 0?
@@ -195,14 +213,6 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
       const bool full_next = VEC && t0 + 2 * TCH <= L;
       const int64_t rem = L - tl;
       const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
-      if constexpr (MODE == kModeChunkStates) {
-        if (active && j == 0) {
-          float* dst = p.chunk_states + (c * nchunks + ch) * N;
-#pragma unroll
-          for (int n = 0; n < NT; ++n)
-            if (n < N) dst[n] = cr[n];
-        }
-      }
       if constexpr (TILE) {
         if (more) stage.load(B_b, C_b, N, L, t0 + TCH, full_next, tid);
       }
@@ -318,6 +328,7 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_kernel(const FwdParams p) {
         }
         if (active) store_items<T, K>(out_row, tl, L, full, y);
       }
+      if (more) store_state(ch + 1);
       if constexpr (TILE) {
         if (more) stage.store(reinterpret_cast<float*>(tile_mem[buf ^ 1]), N, tid);
         __syncthreads();

@@ -88,9 +88,9 @@ def test_forward_segment_workspace(lib):
     assert lib.mamba_scan_fwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, -1) == 2 ** 64 - 1
 
 
-def fwd_ex(lib, segments, ws=None, wsb=0, lanes=0, reset=None):
+def fwd_ex(lib, segments, ws=None, wsb=0, lanes=0, reset=None, ckpt=None):
     return lib.mamba_scan_fwd_ex(P, P, P, P, P, None, None, None, None, reset, 1, 0, 0, 1, 16, 4,
-                                 1024, P, None, ws, wsb, None, lanes, segments, None, None)
+                                 1024, P, None, ws, wsb, None, lanes, segments, ckpt, None, None)
 
 
 def test_forward_segment_arguments(lib):
@@ -102,6 +102,24 @@ def test_forward_segment_arguments(lib):
     assert fwd_ex(lib, 3, lanes=64) == 6                # segments need 16 lanes
     assert fwd_ex(lib, -2) == 6
     assert fwd_ex(lib, 1, lanes=32, reset=P) == 6       # reset flags need 16 lanes
+    assert fwd_ex(lib, 1, lanes=64, ckpt=P) == 6        # checkpoints need 16 lanes
+    assert fwd_ex(lib, 1, ckpt=P + 4) == 4
+
+
+def test_checkpoint_size_and_backward_workspace(lib):
+    # one state of 16 floats per channel and 128-step chunk (ragged: 17 chunks)
+    assert lib.mamba_scan_checkpoint_size(2, 64, 16, 2049) == 2 * 64 * 17 * 16 * 4
+    assert lib.mamba_scan_checkpoint_size(0, 64, 16, 2049) == 2 ** 64 - 1
+    full = lib.mamba_scan_bwd_workspace_size(2, 64, 16, 2048, 0)
+    flags = full - 2 * 64 * 16 * 16 * 4          # with checkpoints: the block flags only
+
+    def bwd_ex(ws, wsb, ckpt):
+        return lib.mamba_scan_bwd_ex(P, P, P, P, P, None, None, None, None, P, None, 1, 0, 0, 2,
+                                     64, 16, 2048, P, P, P, P, P, None, None, None, None, ws, wsb,
+                                     None, 0, ckpt, None, None)
+    assert bwd_ex(P, flags - 1, P) == 5
+    assert bwd_ex(P, flags, None) == 5               # without them the states need room
+    assert bwd_ex(P, full, P + 8) == 4
 
 
 def test_varlen_requires_flags(lib):

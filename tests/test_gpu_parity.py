@@ -323,6 +323,48 @@ def test_bwd_varlen_state_sizes_and_zero_A():
                  reset=W.make_resets(46, 2, 500, 10, 100))
 
 
+def _ckpt_case(wid, batch, dim, N, L, dtype, disc, h0=False, segments=0, reset=None):
+    # the forward saves the state entering every 128-step chunk; the backward
+    # given them must match the oracle (and the run that recomputes them)
+    announce(f"checkpoints wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} h0={h0} "
+             f"segments={segments} resets={None if reset is None else int(reset.sum())}")
+    inp, f = _make(wid, batch, dim, N, L, dtype, with_dout=True)
+    h0v = np.random.default_rng(wid).standard_normal((batch, dim, N)).astype(np.float32) \
+        if h0 else None
+    g = to_device(inp, dtype)
+    h0t = torch.from_numpy(h0v).cuda() if h0v is not None else None
+    rt = torch.from_numpy(reset).cuda() if reset is not None else None
+    ck = torch.full(ms.checkpoint_shape(batch, dim, N, L), float("nan"), device="cuda")
+    ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["delta_bias"], h0t,
+                disc=disc, segments=segments, reset=rt, checkpoints=ck)
+    res = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                      g["delta_bias"], g["dout"], h0t, disc=disc, reset=rt, checkpoints=ck)
+    res2 = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                       g["delta_bias"], g["dout"], h0t, disc=disc, reset=rt)
+    torch.cuda.synchronize()
+    assert not torch.isnan(ck).any()
+    ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                          f["delta_bias"], f["dout"],
+                          None if h0v is None else h0v.astype(np.float64),
+                          disc=oracle.ZOH if disc == "zoh" else oracle.EULER, reset=reset)
+    for k in ref:
+        assert_match(to_f64(res[k]), ref[k], RTOL[dtype], k)
+        assert_match(to_f64(res[k]), to_f64(res2[k]), RTOL["f32"], k + " vs recompute")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_bwd_from_forward_checkpoints(dtype, disc):
+    _ckpt_case(47, 2, 19, 16, 700, dtype, disc, h0=True)
+
+
+def test_bwd_from_forward_checkpoints_segmented_varlen_sizes():
+    _ckpt_case(48, 1, 16, 16, 2048, "f32", "zoh", h0=True, segments=4)
+    _ckpt_case(48, 2, 9, 5, 1000, "f32", "zoh",
+               reset=W.make_resets(48, 2, 1000, 20, 300, force=(0, 128)))
+    _ckpt_case(49, 2, 9, 33, 513, "bf16", "euler", h0=True)
+
+
 def test_bwd_rejects_other_lane_counts():
     inp, _ = _make(38, 1, 4, 16, 64, "f32", with_dout=True)
     g = to_device(inp, "f32")
