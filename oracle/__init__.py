@@ -67,6 +67,8 @@ def _load():
         lib.oracle_conv1d_silu_fwd.restype = None
         lib.oracle_conv1d_silu_bwd.argtypes = [_dp, _dp, _dp, _u8p, _dp] + [_i64] * 6 + [_dp] * 3
         lib.oracle_conv1d_silu_bwd.restype = None
+        lib.oracle_scan_fwd_complex.argtypes = [_dp] * 9 + [_int, _int] + [_i64] * 6 + [_dp, _dp]
+        lib.oracle_scan_fwd_complex.restype = None
         lib.oracle_version.restype = _int
         _lib = lib
         return lib
@@ -258,6 +260,42 @@ def conv1d_silu_bwd(x, w, cb, du, *, reset=None):
     if cb is not None:
         res["dcb"] = dcb
     return res
+
+
+def _c128(x):
+    """Complex array as contiguous interleaved float64 (re, im) pairs."""
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.complex128)).view(np.float64)
+
+
+def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
+                     delta_softplus=True, disc=ZOH, threads=None):
+    """Complex-valued forward in float64: A (dim, N), B, C (batch, N, L) and
+    h0 (batch, dim, N) complex; u, delta, z, D, delta_bias real.  Returns
+    (out real (batch, dim, L), last_state complex (batch, dim, N)) with
+    y_t = Re(sum_n C_t[n] h_t[n]) + D u_t gated by SiLU(z)."""
+    lib = _load()
+    u, delta, D, z, delta_bias = (_f64(t) for t in (u, delta, D, z, delta_bias))
+    A, B, C, h0 = (_c128(t) for t in (A, B, C, h0))
+    batch, dim, L = u.shape
+    N = A.shape[1] // 2
+    out = np.zeros((batch, dim, L), np.float64)
+    last = np.zeros((batch, dim, N), np.complex128)
+    lastv = last.view(np.float64)
+    args = [_ptr(t) for t in (u, delta, A, B, C, D, z, delta_bias, h0)]
+
+    def work(rng):
+        lib.oracle_scan_fwd_complex(*args, int(bool(delta_softplus)), int(disc), batch, dim, N,
+                                    L, rng[0], rng[1], _ptr(out), _ptr(lastv))
+
+    ranges = _split(batch * dim, threads or default_threads())
+    if len(ranges) == 1:
+        work(ranges[0])
+    else:
+        with ThreadPoolExecutor(len(ranges)) as ex:
+            list(ex.map(work, ranges))
+    return out, last
 
 
 def version() -> int:

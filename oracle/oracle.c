@@ -37,6 +37,7 @@
  * Built without fast-math and without FP contraction: every operation is
  * the plain IEEE double operation written here.
  */
+#include <complex.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -339,4 +340,57 @@ void oracle_conv1d_silu_bwd(const double* x, const double* w, const double* cb,
   }
 }
 
-int oracle_version(void) { return 3; }
+/*
+ * Complex-valued variant: diagonal A, B, C and the state h complex (the
+ * S4D-Lin parameterization A_n = -1/2 + i*pi*n of [SUM-3.4] "Real vs.
+ * Complex", used by the paper for audio [ESSAY] Part III).  The pages fix no
+ * output convention for a complex state; the reading taken here is
+ *   y_t = Re( sum_n C[b,n,t] * h_t[n] ) + D[d] * u_t,  out = y * SiLU(z)
+ * with Abar = exp(dt*A) and Bbar = (Abar - 1)/A * B (ZOH; limit dt*B at A = 0)
+ * or dt*B (Euler), all complex.  Complex arrays are interleaved (re, im)
+ * pairs: A (dim, dstate), B and C (batch, dstate, seqlen), h0 and last_state
+ * (batch, dim, dstate).  u, delta, z, D, bias and out are real.
+ */
+static double complex cload(const double* p, int64_t i) { return p[2 * i] + I * p[2 * i + 1]; }
+
+static double complex cbbar_coef(double dt, double complex a, int disc) {
+  if (disc == ORACLE_EULER) return dt;
+  if (a == 0.0) return dt;
+  return (cexp(dt * a) - 1.0) / a;
+}
+
+void oracle_scan_fwd_complex(const double* u, const double* delta, const double* A,
+                             const double* B, const double* C, const double* D, const double* z,
+                             const double* bias, const double* h0, int softplus_on, int disc,
+                             int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                             int64_t c_begin, int64_t c_end, double* out, double* last_state) {
+  (void)batch;
+  double complex* h = (double complex*)malloc(sizeof(double complex) * (size_t)dstate);
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    int64_t b = c / dim, d = c % dim;
+    for (int64_t n = 0; n < dstate; ++n) h[n] = h0 ? cload(h0, c * dstate + n) : 0.0;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      double dt = step_size(delta[c * seqlen + t], bias, d, softplus_on);
+      double ut = u[c * seqlen + t];
+      double y = 0.0;
+      for (int64_t n = 0; n < dstate; ++n) {
+        double complex a = cload(A, d * dstate + n);
+        double complex abar = cexp(dt * a);
+        double complex bbar = cbbar_coef(dt, a, disc) * cload(B, (b * dstate + n) * seqlen + t);
+        h[n] = abar * h[n] + bbar * ut;
+        y += creal(cload(C, (b * dstate + n) * seqlen + t) * h[n]);
+      }
+      if (D) y += D[d] * ut;
+      if (z) y = y * (z[c * seqlen + t] * sigmoid(z[c * seqlen + t]));
+      out[c * seqlen + t] = y;
+    }
+    if (last_state)
+      for (int64_t n = 0; n < dstate; ++n) {
+        last_state[2 * (c * dstate + n)] = creal(h[n]);
+        last_state[2 * (c * dstate + n) + 1] = cimag(h[n]);
+      }
+  }
+  free(h);
+}
+
+int oracle_version(void) { return 4; }

@@ -1,0 +1,78 @@
+"""Pins of the float64 oracle's complex-valued forward (diagonal complex A,
+B, C and state; the S4D-Lin parameterization A_n = -1/2 + i*pi*n that the
+paper-graph-ui summary, section 3.4 "Real vs. Complex", and the
+trishampatil essay, Part III, describe for audio), with the reading
+y = Re(sum_n C h) + D u.
+
+Pinned against: the real oracle when every imaginary part is zero; an
+independent numpy brute-force convolution with the complex kernel
+Re(C Abar^k Bbar) when delta, B, C are constant along t; and the
+conjugate-pair identity (a pair (a, conj a) gives twice the real part of one).
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _inputs(seed, batch=2, dim=3, N=4, L=40):
+    g = np.random.default_rng(seed)
+    A = -0.5 * np.ones((dim, N)) + 1j * np.pi * np.arange(N)[None, :] * (1 + 0.1 * g.random((dim, 1)))
+    cplx = lambda *s: g.standard_normal(s) + 1j * g.standard_normal(s)
+    return dict(u=g.standard_normal((batch, dim, L)), delta=g.standard_normal((batch, dim, L)),
+                A=A, B=cplx(batch, N, L), C=cplx(batch, N, L), D=g.standard_normal(dim),
+                z=g.standard_normal((batch, dim, L)), delta_bias=g.standard_normal(dim) - 1.0,
+                h0=cplx(batch, dim, N))
+
+
+@pytest.mark.parametrize("disc", [oracle.ZOH, oracle.EULER])
+def test_real_parts_only_equal_the_real_oracle(disc):
+    p = _inputs(1)
+    p["A"] = -np.exp(np.random.default_rng(2).standard_normal(p["A"].shape)) + 0j
+    for k in ("B", "C", "h0"):
+        p[k] = p[k].real + 0j
+    out, last = oracle.scan_fwd_complex(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"],
+                                        p["z"], p["delta_bias"], p["h0"], disc=disc)
+    ro, rl = oracle.scan_fwd(p["u"], p["delta"], p["A"].real, p["B"].real, p["C"].real, p["D"],
+                             p["z"], p["delta_bias"], p["h0"].real, disc=disc)
+    np.testing.assert_allclose(out, ro, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(last.real, rl, rtol=1e-13, atol=1e-13)
+    assert np.all(last.imag == 0.0)
+
+
+@pytest.mark.parametrize("disc", [oracle.ZOH, oracle.EULER])
+@pytest.mark.parametrize("softplus", [True, False])
+def test_constant_parameters_equal_complex_kernel_convolution(disc, softplus):
+    g = np.random.default_rng(3)
+    batch, dim, N, L = 1, 2, 3, 30
+    p = _inputs(4, batch, dim, N, L)
+    dt_raw = g.random((batch, dim, 1)) + 0.1 if not softplus else g.standard_normal((batch, dim, 1))
+    delta = np.repeat(dt_raw, L, axis=2)
+    Bc = np.repeat(p["B"][:, :, :1], L, axis=2)
+    Cc = np.repeat(p["C"][:, :, :1], L, axis=2)
+    out, _ = oracle.scan_fwd_complex(p["u"], delta, p["A"], Bc, Cc, p["D"], None, None, None,
+                                     delta_softplus=softplus, disc=disc)
+    for d in range(dim):
+        dt = np.log1p(np.exp(dt_raw[0, d, 0])) if softplus else dt_raw[0, d, 0]
+        a = p["A"][d]
+        abar = np.exp(dt * a)
+        bbar = ((abar - 1) / a if disc == oracle.ZOH else dt) * Bc[0, :, 0]
+        K = np.array([np.real(np.sum(Cc[0, :, 0] * abar ** k * bbar)) for k in range(L)])
+        x = p["u"][0, d]
+        y = np.array([np.sum(K[:t + 1][::-1] * x[:t + 1]) for t in range(L)]) + p["D"][d] * x
+        np.testing.assert_allclose(out[0, d], y, rtol=1e-11, atol=1e-11)
+
+
+def test_conjugate_pair_gives_twice_the_real_part():
+    p = _inputs(5, N=1)
+    pair = {k: p[k] for k in ("u", "delta", "delta_bias")}
+    pair["A"] = np.concatenate([p["A"], np.conj(p["A"])], axis=1)
+    pair["B"] = np.concatenate([p["B"], np.conj(p["B"])], axis=1)
+    pair["C"] = np.concatenate([p["C"], np.conj(p["C"])], axis=1)
+    pair["h0"] = np.concatenate([p["h0"], np.conj(p["h0"])], axis=2)
+    one, l1 = oracle.scan_fwd_complex(p["u"], p["delta"], p["A"], p["B"], p["C"], None, None,
+                                      p["delta_bias"], p["h0"])
+    two, l2 = oracle.scan_fwd_complex(pair["u"], pair["delta"], pair["A"], pair["B"], pair["C"],
+                                      None, None, pair["delta_bias"], pair["h0"])
+    np.testing.assert_allclose(two, 2 * one, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l2[..., 1], np.conj(l1[..., 0]), rtol=1e-12, atol=1e-12)
