@@ -197,6 +197,28 @@ mamba_status mamba_scan_bwd_varlen(const void* u, const void* delta, const float
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * Complex-valued forward: diagonal complex A, complex B, C and state (the
+ * S4D-Lin parameterization A_n = -1/2 + i*pi*n that paper-graph-ui summary,
+ * section 3.4 "Real vs. Complex", and trishampatil essay, Part III, describe
+ * for audio).  Abar = exp(delta A); Bbar = (Abar - 1)/A B (ZOH, delta B at
+ * A = 0) or delta B (Euler); h_t = Abar h_{t-1} + Bbar u_t;
+ * y_t = Re(sum_n C_t[n] h_t[n]) + D u_t; out = y * SiLU(z).  The pages fix no
+ * output convention for a complex state: the real part is this library's
+ * reading (a caller that pairs each state with its conjugate may double it).
+ * Complex arrays are interleaved (re, im) float32 pairs: A (dim, dstate),
+ * B and C (batch, dstate, seqlen), h0 and last_state (batch, dim, dstate),
+ * both nullable.  u, delta, z, out follow mamba_scan_fwd (float32 or
+ * bfloat16); D, delta_bias float32.  dstate <= 16 (MAMBA_ERR_UNSUPPORTED
+ * otherwise).  No workspace; errors as for mamba_scan_fwd.
+ */
+mamba_status mamba_scan_fwd_complex(const void* u, const void* delta, const float* A,
+                                    const float* B, const float* C, const float* D,
+                                    const void* z, const float* delta_bias, const float* h0,
+                                    int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                                    int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                    void* out, float* last_state, void* stream);
+
+/*
  * Short causal depthwise convolution + SiLU, the stage that feeds the SSM
  * in the Mamba block (chapterpal.com page, Knowl 3 "Mamba Block
  * Architecture": a width-4 temporal convolution, then SiLU; trishampatil

@@ -243,6 +243,38 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
     return out
 
 
+def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
+                     delta_softplus=True, disc="zoh", out=None):
+    """Complex-valued forward: A (dim, N), B, C (batch, N, L), h0 (batch, dim,
+    N) complex64; u, delta, z real.  Returns (out, last_state complex64) with
+    y = Re(sum_n C h) + D u gated by SiLU(z)."""
+    L_ = lib()
+    if not u.is_cuda:
+        raise ValueError("u must be a GPU tensor (no CPU path exists)")
+    dev = u.device
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    sdt = u.dtype
+    _req(u, "u", sdt, (batch, dim, L), dev)
+    _req(delta, "delta", sdt, (batch, dim, L), dev)
+    _req(A, "A", torch.complex64, (dim, N), dev)
+    _req(B, "B", torch.complex64, (batch, N, L), dev)
+    _req(C, "C", torch.complex64, (batch, N, L), dev)
+    _req(D, "D", torch.float32, (dim,), dev)
+    _req(z, "z", sdt, (batch, dim, L), dev)
+    _req(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _req(h0, "h0", torch.complex64, (batch, dim, N), dev)
+    if out is None:
+        out = torch.empty((batch, dim, L), dtype=sdt, device=dev)
+    last = torch.empty((batch, dim, N), dtype=torch.complex64, device=dev)
+    st = L_.mamba_scan_fwd_complex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                   _ptr(z), _ptr(delta_bias), _ptr(h0), int(bool(delta_softplus)),
+                                   _disc_code(disc), _dtype_code(u), batch, dim, N, L, _ptr(out),
+                                   _ptr(last), _stream(dev))
+    _lib.check(st, "mamba_scan_fwd_complex")
+    return out, last
+
+
 def conv1d_silu_fwd(x, w, b=None, *, reset=None, out=None):
     """Short causal depthwise convolution (w: (dim, W), W <= 4) followed by
     SiLU.  x (batch, dim, L) float32 or bfloat16; returns u like x."""

@@ -26,7 +26,7 @@ EXPORTS = (
     "mamba_scan_fwd_varlen", "mamba_scan_bwd_varlen", "mamba_conv1d_silu_fwd",
     "mamba_conv1d_silu_bwd",
     "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size_ex", "mamba_scan_bwd_workspace_size_ex",
-    "mamba_scan_bwd_ex", "mamba_scan_checkpoint_size",
+    "mamba_scan_bwd_ex", "mamba_scan_checkpoint_size", "mamba_scan_fwd_complex",
 )
 
 
@@ -88,6 +88,8 @@ def load(path: str = LIB_PATH):
     lib.mamba_conv1d_silu_fwd.argtypes = [_vp] * 4 + [_i64, _int] + [_i64] * 3 + [_vp, _vp]
     lib.mamba_conv1d_silu_bwd.restype = _int
     lib.mamba_conv1d_silu_bwd.argtypes = [_vp] * 5 + [_i64, _int] + [_i64] * 3 + [_vp] * 4
+    lib.mamba_scan_fwd_complex.restype = _int
+    lib.mamba_scan_fwd_complex.argtypes = [_vp] * 9 + [_int, _int, _int] + [_i64] * 4 + [_vp] * 3
     lib.mamba_state_update.restype = _int
     lib.mamba_state_update.argtypes = [_vp] * 9 + [_int, _int, _int] + [_i64] * 3 + [_vp, _vp]
     _lib = lib

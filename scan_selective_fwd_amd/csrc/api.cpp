@@ -389,6 +389,35 @@ mamba_status mamba_state_update(float* state, const void* u, const void* delta, 
                                                  static_cast<hipStream_t>(stream)));
 }
 
+// ---- complex-valued forward ----
+mamba_status mamba_scan_fwd_complex(const void* u, const void* delta, const float* A,
+                                    const float* B, const float* C, const float* D,
+                                    const void* z, const float* delta_bias, const float* h0,
+                                    int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                                    int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                    void* out, float* last_state, void* stream) {
+  mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
+  if (st != MAMBA_OK) return st;
+  if (dstate > 16) return MAMBA_ERR_UNSUPPORTED;
+  if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL_PTR;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, out, last_state};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MAMBA_ERR_ALIGNMENT;
+  mscan::CplxParams p;
+  memset(&p, 0, sizeof(p));
+  p.u = u; p.delta = delta; p.A = reinterpret_cast<const float2*>(A);
+  p.B = reinterpret_cast<const float2*>(B); p.C = reinterpret_cast<const float2*>(C);
+  p.D = D; p.z = z; p.bias = delta_bias; p.h0 = reinterpret_cast<const float2*>(h0);
+  p.out = out; p.last_state = reinterpret_cast<float2*>(last_state);
+  p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
+  p.groups = mscan::channel_groups(dim, 16);
+  p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
+  if (batch * p.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
+  const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  return hip_status(mscan::dispatch_scan_fwd_complex(p, dt == MAMBA_F32 ? 0 : 1, (int)disc, vec,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 // ---- short causal convolution + SiLU ----
 mamba_status mamba_conv1d_silu_fwd(const void* x, const float* w, const float* b,
                                    const uint8_t* reset, int64_t width, mamba_dtype dt,

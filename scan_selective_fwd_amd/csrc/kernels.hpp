@@ -99,6 +99,29 @@ struct StepParams {
   int softplus;
 };
 
+// Complex-valued forward (scan_fwd_complex.hip); complex arrays are
+// interleaved (re, im) pairs.
+struct CplxParams {
+  const void* u;
+  const void* delta;
+  const float2* A;         // (dim, N)
+  const float2* B;         // (batch, N, L)
+  const float2* C;         // (batch, N, L)
+  const float* D;          // nullable
+  const void* z;           // nullable
+  const float* bias;       // nullable
+  const float2* h0;        // nullable (batch, dim, N)
+  void* out;
+  float2* last_state;      // nullable (batch, dim, N)
+  int64_t batch, dim, L;
+  int64_t nchannels;
+  int64_t groups;          // channel groups of 16 per batch row
+  int N;                   // <= 16
+  int softplus;
+};
+hipError_t dispatch_scan_fwd_complex(const CplxParams& p, int dtype, int disc, bool vec,
+                                     hipStream_t s);
+
 // Short causal convolution + SiLU (conv1d_silu.hip).
 struct ConvParams {
   const void* x;           // (batch, dim, L), sequence dtype

@@ -1,0 +1,79 @@
+"""GPU parity of the complex-valued forward (diagonal complex A, B, C and
+state; y = Re(sum_n C h) + D u, gated) against the float64 oracle on the
+same seeded inputs: float32 and bfloat16 sequences, ZOH and Euler, several
+state sizes, ragged lengths, an initial state, optional inputs absent and
+the softplus off."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scan_selective_fwd_amd as ms
+import workloads as W
+from parity_utils import RTOL, announce, assert_match, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(x, dtype):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None):
+    opts = opts or {}
+    announce(f"complex fwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} h0={h0} "
+             f"softplus={softplus} opts={opts}")
+    inp = W.make_complex_inputs(wid, batch, dim, N, L, dtype=dtype, **opts)
+    if not softplus:   # a positive raw step without the softplus
+        raw = np.abs(W.as_f64(inp["delta"], dtype)) * 0.05 + 0.01
+        inp["delta"] = W.bf16_round_bits(raw) if dtype == "bf16" else raw.astype(np.float32)
+        if "delta_bias" in inp:
+            inp["delta_bias"] = (np.abs(inp["delta_bias"]) * 0.01).astype(np.float32)
+    h0v = None
+    if h0:
+        g = np.random.default_rng([wid, 13])
+        h0v = (g.standard_normal((batch, dim, N)) + 1j * g.standard_normal((batch, dim, N))
+               ).astype(np.complex64)
+    t = {k: _dev(v, dtype) for k, v in inp.items()}
+    out, last = ms.scan_fwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t.get("D"),
+                                    t.get("z"), t.get("delta_bias"),
+                                    None if h0v is None else torch.from_numpy(h0v).cuda(),
+                                    delta_softplus=softplus, disc=disc)
+    torch.cuda.synchronize()
+    f = {k: (W.as_f64(v, dtype) if v.dtype == np.uint16 else v) for k, v in inp.items()}
+    ref, ref_last = oracle.scan_fwd_complex(
+        f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"), f.get("z"), f.get("delta_bias"),
+        h0v, delta_softplus=softplus, disc=oracle.ZOH if disc == "zoh" else oracle.EULER)
+    assert_match(to_f64(out), ref, RTOL[dtype], "out")
+    got_last = last.cpu().numpy().astype(np.complex128)
+    assert_match(np.stack([got_last.real, got_last.imag], -1),
+                 np.stack([ref_last.real, ref_last.imag], -1), RTOL[dtype], "last_state")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_complex_fwd_dtypes_discs(dtype, disc):
+    # 700 steps: five 128-step chunks and a ragged tail; 37 channels: a
+    # partial block
+    _case(70, 2, 37, 16, 700, dtype, disc, h0=True)
+
+
+@pytest.mark.parametrize("N", [1, 5, 16])
+@pytest.mark.parametrize("L", [1, 129, 1000])
+def test_complex_fwd_sizes(N, L):
+    _case(71, 1, 9, N, L, "f32", "zoh")
+
+
+def test_complex_fwd_optional_inputs_and_softplus_off():
+    _case(72, 2, 20, 8, 300, "f32", "zoh", softplus=False,
+          opts=dict(with_D=False, with_z=False, with_bias=False))
+    _case(73, 2, 20, 8, 300, "f32", "euler", softplus=False, h0=True)
+
+
+def test_complex_fwd_rejects_large_state():
+    inp = W.make_complex_inputs(74, 1, 4, 17, 64)
+    t = {k: _dev(v, "f32") for k, v in inp.items()}
+    with pytest.raises(ms.MambaScanError):
+        ms.scan_fwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"])
