@@ -69,6 +69,8 @@ def _load():
         lib.oracle_conv1d_silu_bwd.restype = None
         lib.oracle_scan_fwd_complex.argtypes = [_dp] * 9 + [_int, _int] + [_i64] * 6 + [_dp, _dp]
         lib.oracle_scan_fwd_complex.restype = None
+        lib.oracle_scan_bwd_complex.argtypes = [_dp] * 10 + [_int, _int] + [_i64] * 6 + [_dp] * 9
+        lib.oracle_scan_bwd_complex.restype = None
         lib.oracle_version.restype = _int
         _lib = lib
         return lib
@@ -296,6 +298,41 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None
         with ThreadPoolExecutor(len(ranges)) as ex:
             list(ex.map(work, ranges))
     return out, last
+
+
+def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
+                     delta_softplus=True, disc=ZOH):
+    """Gradients of sum(dout * out) for scan_fwd_complex, in float64 (one
+    thread).  dA, dB, dC, dh0 are complex (the gradient of a complex w is
+    dL/dRe(w) + i dL/dIm(w)); the others real.  Returns a dict like scan_bwd."""
+    lib = _load()
+    u, delta, D, z, delta_bias, dout = (_f64(t) for t in (u, delta, D, z, delta_bias, dout))
+    A, B, C, h0 = (_c128(t) for t in (A, B, C, h0))
+    batch, dim, L = u.shape
+    N = A.shape[1] // 2
+    du, ddelta = np.zeros_like(u), np.zeros_like(u)
+    dz = np.zeros_like(u) if z is not None else None
+    dA = np.zeros((dim, N), np.complex128)
+    dB = np.zeros((batch, N, L), np.complex128)
+    dC = np.zeros((batch, N, L), np.complex128)
+    dD = np.zeros(dim) if D is not None else None
+    ddb = np.zeros(dim) if delta_bias is not None else None
+    dh0 = np.zeros((batch, dim, N), np.complex128) if h0 is not None else None
+    v = lambda a: None if a is None else a.view(np.float64)
+    lib.oracle_scan_bwd_complex(*[_ptr(t) for t in (u, delta, A, B, C, D, z, delta_bias, h0, dout)],
+                                int(bool(delta_softplus)), int(disc), batch, dim, N, L, 0,
+                                batch * dim, _ptr(du), _ptr(ddelta), _ptr(v(dA)), _ptr(v(dB)),
+                                _ptr(v(dC)), _ptr(dD), _ptr(dz), _ptr(ddb), _ptr(v(dh0)))
+    res = dict(du=du, ddelta=ddelta, dA=dA, dB=dB, dC=dC)
+    if D is not None:
+        res["dD"] = dD
+    if z is not None:
+        res["dz"] = dz
+    if delta_bias is not None:
+        res["ddelta_bias"] = ddb
+    if h0 is not None:
+        res["dh0"] = dh0
+    return res
 
 
 def version() -> int:

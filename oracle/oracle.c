@@ -393,4 +393,101 @@ void oracle_scan_fwd_complex(const double* u, const double* delta, const double*
   free(h);
 }
 
-int oracle_version(void) { return 4; }
+/*
+ * Backward of the complex forward above for L = sum(dout * out), by the
+ * chain rule with the gradient of a complex variable w written
+ * g_w = dL/dRe(w) + i dL/dIm(w):
+ *   y = Re(C h)          -> g_h += conj(C) gy,  g_C = gy conj(h)
+ *   h_t = Abar h_{t-1} + beta -> g_{h_{t-1}} += conj(Abar) g_h,
+ *                               g_Abar = g_h conj(h_{t-1}),  g_beta = g_h
+ *   Abar = exp(dt A)     -> d/ddt: A Abar;   d/dA: dt Abar
+ *   beta = E B u, E = (Abar - 1)/A (ZOH) or dt (Euler)
+ *                        -> dE/ddt = Abar (ZOH) or 1;  dE/dA = (dt Abar - E)/A (ZOH,
+ *                           limit dt^2/2 at A = 0) or 0
+ * A real variable x gets Re(conj(g_w) dw/dx); a complex one conj(dw/dx) g_w
+ * (the maps are holomorphic in A).  dA, dB, dC, dh0 are complex and
+ * accumulated with +=, like dD, ddelta_bias; du, ddelta, dz are written.
+ */
+void oracle_scan_bwd_complex(const double* u, const double* delta, const double* A,
+                             const double* B, const double* C, const double* D, const double* z,
+                             const double* bias, const double* h0, const double* dout,
+                             int softplus_on, int disc, int64_t batch, int64_t dim, int64_t dstate,
+                             int64_t seqlen, int64_t c_begin, int64_t c_end, double* du,
+                             double* ddelta, double* dA, double* dB, double* dC, double* dD,
+                             double* dz, double* ddelta_bias, double* dh0) {
+  (void)batch;
+  double complex* hs = (double complex*)malloc(sizeof(double complex) * (size_t)((seqlen + 1) * dstate));
+  double complex* gh = (double complex*)malloc(sizeof(double complex) * (size_t)dstate);
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    int64_t b = c / dim, d = c % dim;
+    for (int64_t n = 0; n < dstate; ++n) hs[n] = h0 ? cload(h0, c * dstate + n) : 0.0;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      double dt = step_size(delta[c * seqlen + t], bias, d, softplus_on);
+      for (int64_t n = 0; n < dstate; ++n) {
+        double complex a = cload(A, d * dstate + n);
+        double complex bbar = cbbar_coef(dt, a, disc) * cload(B, (b * dstate + n) * seqlen + t);
+        hs[(t + 1) * dstate + n] = cexp(dt * a) * hs[t * dstate + n] + bbar * u[c * seqlen + t];
+      }
+    }
+    for (int64_t n = 0; n < dstate; ++n) gh[n] = 0.0;
+    for (int64_t t = seqlen - 1; t >= 0; --t) {
+      double r = delta[c * seqlen + t] + (bias ? bias[d] : 0.0);
+      double dt = softplus_on ? softplus(r) : r;
+      double ut = u[c * seqlen + t];
+      double y = 0.0;
+      for (int64_t n = 0; n < dstate; ++n)
+        y += creal(cload(C, (b * dstate + n) * seqlen + t) * hs[(t + 1) * dstate + n]);
+      if (D) y += D[d] * ut;
+      double gy = dout[c * seqlen + t];
+      if (z) {
+        double zt = z[c * seqlen + t], sg = sigmoid(zt);
+        gy = dout[c * seqlen + t] * (zt * sg);
+        dz[c * seqlen + t] = dout[c * seqlen + t] * y * sg * (1.0 + zt * (1.0 - sg));
+      }
+      double du_t = D ? gy * D[d] : 0.0;
+      if (D) dD[d] += gy * ut;
+      double gdt = 0.0;
+      for (int64_t n = 0; n < dstate; ++n) {
+        int64_t k = (b * dstate + n) * seqlen + t;
+        double complex a = cload(A, d * dstate + n);
+        double complex abar = cexp(dt * a);
+        double complex Bv = cload(B, k), Cv = cload(C, k);
+        double complex E = cbbar_coef(dt, a, disc);
+        double complex hprev = hs[t * dstate + n], hcur = hs[(t + 1) * dstate + n];
+        gh[n] += conj(Cv) * gy;                       /* g_h_t */
+        double complex gC = gy * conj(hcur);
+        dC[2 * k] += creal(gC);
+        dC[2 * k + 1] += cimag(gC);
+        double complex gAbar = gh[n] * conj(hprev);
+        double complex gbeta = gh[n];
+        double complex dE_ddt = (disc == ORACLE_EULER) ? 1.0 : abar;
+        double complex dE_dA;
+        if (disc == ORACLE_EULER) dE_dA = 0.0;
+        else if (a == 0.0) dE_dA = dt * dt / 2.0;
+        else dE_dA = (dt * abar - E) / a;
+        gdt += creal(conj(gAbar) * a * abar) + creal(conj(gbeta) * dE_ddt * Bv * ut);
+        du_t += creal(conj(gbeta) * E * Bv);
+        double complex gB = conj(E * ut) * gbeta;
+        dB[2 * k] += creal(gB);
+        dB[2 * k + 1] += cimag(gB);
+        double complex gA = conj(dt * abar) * gAbar + conj(dE_dA * Bv * ut) * gbeta;
+        dA[2 * (d * dstate + n)] += creal(gA);
+        dA[2 * (d * dstate + n) + 1] += cimag(gA);
+        gh[n] = conj(abar) * gh[n];                   /* carry to t-1 */
+      }
+      du[c * seqlen + t] = du_t;
+      double gr = softplus_on ? gdt * sigmoid(r) : gdt;
+      ddelta[c * seqlen + t] = gr;
+      if (ddelta_bias) ddelta_bias[d] += gr;
+    }
+    if (dh0)
+      for (int64_t n = 0; n < dstate; ++n) {
+        dh0[2 * (c * dstate + n)] += creal(gh[n]);
+        dh0[2 * (c * dstate + n) + 1] += cimag(gh[n]);
+      }
+  }
+  free(hs);
+  free(gh);
+}
+
+int oracle_version(void) { return 5; }

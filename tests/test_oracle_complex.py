@@ -8,6 +8,8 @@ Pinned against: the real oracle when every imaginary part is zero; an
 independent numpy brute-force convolution with the complex kernel
 Re(C Abar^k Bbar) when delta, B, C are constant along t; and the
 conjugate-pair identity (a pair (a, conj a) gives twice the real part of one).
+The complex backward is pinned to central differences of the forward, in
+the real and the imaginary direction of every complex input.
 """
 import numpy as np
 import pytest
@@ -76,3 +78,61 @@ def test_conjugate_pair_gives_twice_the_real_part():
                                       None, None, pair["delta_bias"], pair["h0"])
     np.testing.assert_allclose(two, 2 * one, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(l2[..., 1], np.conj(l1[..., 0]), rtol=1e-12, atol=1e-12)
+
+
+def _loss(p, dout, disc, softplus):
+    out, _ = oracle.scan_fwd_complex(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                                     p["delta_bias"], p["h0"], delta_softplus=softplus,
+                                     disc=disc, threads=1)
+    return float(np.sum(out * dout))
+
+
+def _fd(p, name, dout, disc, softplus, eps=1e-6):
+    x = p[name]
+    is_c = np.iscomplexobj(x)
+    g = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        parts = [1.0, 1j] if is_c else [1.0]
+        for unit in parts:
+            old = x[idx]
+            h = eps * max(1.0, abs(old))
+            x[idx] = old + unit * h
+            lp = _loss(p, dout, disc, softplus)
+            x[idx] = old - unit * h
+            lm = _loss(p, dout, disc, softplus)
+            x[idx] = old
+            g[idx] += unit * (lp - lm) / (2 * h)
+    return g
+
+
+GRADS = dict(u="du", delta="ddelta", A="dA", B="dB", C="dC", D="dD", z="dz",
+             delta_bias="ddelta_bias", h0="dh0")
+
+
+@pytest.mark.parametrize("disc,softplus", [(oracle.ZOH, True), (oracle.EULER, True),
+                                           (oracle.ZOH, False)])
+def test_complex_backward_matches_central_differences(disc, softplus):
+    p = _inputs(6, batch=2, dim=2, N=3, L=9)
+    if not softplus:
+        p["delta"] = np.abs(p["delta"]) + 0.05
+        p["delta_bias"] = np.abs(p["delta_bias"]) * 0.1
+    dout = np.random.default_rng(7).standard_normal(p["u"].shape)
+    g = oracle.scan_bwd_complex(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                                p["delta_bias"], dout, p["h0"], delta_softplus=softplus,
+                                disc=disc)
+    for name, gname in GRADS.items():
+        ref = _fd(p, name, dout, disc, softplus)
+        scale = max(1.0, np.abs(ref).max())
+        np.testing.assert_allclose(g[gname], ref, rtol=1e-6, atol=1e-6 * scale, err_msg=name)
+
+
+def test_complex_backward_zero_A_limit():
+    p = _inputs(8, batch=1, dim=2, N=2, L=6)
+    p["A"][0, 0] = 0.0
+    dout = np.random.default_rng(9).standard_normal(p["u"].shape)
+    g = oracle.scan_bwd_complex(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                                p["delta_bias"], dout, p["h0"])
+    # (Abar - 1)/A near A = 0 has no complex expm1 in the forward: a wider
+    # difference step keeps the rounding of the differences small
+    ref = _fd(p, "A", dout, oracle.ZOH, True, eps=1e-4)
+    np.testing.assert_allclose(g["dA"], ref, rtol=1e-5, atol=1e-6 * max(1, np.abs(ref).max()))
