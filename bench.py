@@ -77,6 +77,9 @@ def algorithmic_bytes(w, call: str) -> float:
         return 2 * state + 4 * w.batch * w.dim * es + 2 * w.batch * w.dstate * es + params
     if call == "cfwd":     # complex forward: u, delta, z read, out written; complex B, C, A, state
         return 4 * ct * es + 2 * w.batch * w.dstate * w.seqlen * 8 + 2 * params + 2 * state
+    if call == "cbwd":     # complex backward: as bwd with complex B, C, dB, dC
+        return (4 * ct * es + 3 * ct * 4 + 4 * w.batch * w.dstate * w.seqlen * 8 + 2 * params
+                + 2 * state)
     if call == "conv_fwd":  # read x, write u; taps and bias
         return 2 * ct * es + 5 * w.dim * 4
     if call == "conv_bwd":  # read x and du (f32), write dx (f32); dw, db
@@ -236,7 +239,7 @@ def main():
         calls = args.calls.split(",")
     if args.copy_calibration:
         copy_calibration(torch)
-    g = gpu_inputs(w, torch, "bwd" in calls)
+    g = gpu_inputs(w, torch, "bwd" in calls or "cbwd" in calls)
     ws = None
     if "bwd" in calls:
         ws = torch.empty(ms.bwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen,
@@ -257,7 +260,7 @@ def main():
     t_out = torch.empty_like(g["u"])
     step_args = {k: g[k][..., 0].contiguous() for k in ("u", "delta", "B", "C", "z")}
     cplx = None
-    if "cfwd" in calls:
+    if "cfwd" in calls or "cbwd" in calls:
         ci = W.make_complex_inputs(w.wid, w.batch, w.dim, w.dstate, w.seqlen, dtype=w.dtype,
                                    bias=w.bias, per_row=w.per_row)
         cplx = {k: torch.from_numpy(ci[k]).cuda() for k in ("A", "B", "C")}
@@ -282,6 +285,9 @@ def main():
         elif c == "cfwd":       # complex A, B, C with the workload's real sequences
             ms.scan_fwd_complex(g["u"], g["delta"], cplx["A"], cplx["B"], cplx["C"], g["D"],
                                 g["z"], g["delta_bias"], disc=args.disc, out=t_out)
+        elif c == "cbwd":
+            ms.scan_bwd_complex(g["u"], g["delta"], cplx["A"], cplx["B"], cplx["C"], g["D"],
+                                g["z"], g["delta_bias"], g["dout"], disc=args.disc)
         elif c == "conv_fwd":   # x = the workload's u sequence
             ms.conv1d_silu_fwd(g["u"], conv_w, conv_b, reset=rst, out=t_out)
         elif c == "conv_bwd":

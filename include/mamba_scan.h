@@ -219,6 +219,31 @@ mamba_status mamba_scan_fwd_complex(const void* u, const void* delta, const floa
                                     void* out, float* last_state, void* stream);
 
 /*
+ * Backward of mamba_scan_fwd_complex for the loss sum(dout * out): the
+ * states are recomputed chunkwise (one state per 128-step chunk is
+ * recomputed into the workspace first).  The gradient of a complex input w
+ * is dL/dRe(w) + i dL/dIm(w): dA (dim, dstate), dB, dC (batch, dstate,
+ * seqlen) and dh0 (batch, dim, dstate; NULL unless h0 is given) are complex
+ * (interleaved pairs); du, ddelta, dz (batch, dim, seqlen) and dD,
+ * ddelta_bias (dim) are real float32.  Null-pairing rules, dtypes and errors
+ * follow mamba_scan_bwd; the workspace is
+ * mamba_scan_bwd_complex_workspace_size bytes.  Reductions use float32
+ * atomics (deterministic up to rounding order).
+ */
+size_t mamba_scan_bwd_complex_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                             int64_t seqlen);
+
+mamba_status mamba_scan_bwd_complex(const void* u, const void* delta, const float* A,
+                                    const float* B, const float* C, const float* D,
+                                    const void* z, const float* delta_bias, const float* h0,
+                                    const void* dout, int delta_softplus, mamba_disc disc,
+                                    mamba_dtype dt, int64_t batch, int64_t dim, int64_t dstate,
+                                    int64_t seqlen, float* du, float* ddelta, float* dA,
+                                    float* dB, float* dC, float* dD, float* dz,
+                                    float* ddelta_bias, float* dh0, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * Short causal depthwise convolution + SiLU, the stage that feeds the SSM
  * in the Mamba block (chapterpal.com page, Knowl 3 "Mamba Block
  * Architecture": a width-4 temporal convolution, then SiLU; trishampatil

@@ -275,6 +275,53 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None
     return out, last
 
 
+def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
+                     delta_softplus=True, disc="zoh"):
+    """Backward of scan_fwd_complex.  Returns a dict: du, ddelta (and dD, dz,
+    ddelta_bias when given) float32; dA, dB, dC (and dh0) complex64, the
+    gradient of a complex input w being dL/dRe(w) + i dL/dIm(w)."""
+    L_ = lib()
+    dev = u.device
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    sdt = u.dtype
+    for t, name, shp, ty in ((u, "u", (batch, dim, L), sdt), (delta, "delta", (batch, dim, L), sdt),
+                             (A, "A", (dim, N), torch.complex64),
+                             (B, "B", (batch, N, L), torch.complex64),
+                             (C, "C", (batch, N, L), torch.complex64),
+                             (D, "D", (dim,), torch.float32), (z, "z", (batch, dim, L), sdt),
+                             (delta_bias, "delta_bias", (dim,), torch.float32),
+                             (h0, "h0", (batch, dim, N), torch.complex64),
+                             (dout, "dout", (batch, dim, L), sdt)):
+        _req(t, name, ty, shp, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    c64 = dict(dtype=torch.complex64, device=dev)
+    g = dict(du=torch.empty((batch, dim, L), **f32), ddelta=torch.empty((batch, dim, L), **f32),
+             dA=torch.empty((dim, N), **c64), dB=torch.empty((batch, N, L), **c64),
+             dC=torch.empty((batch, N, L), **c64))
+    if D is not None:
+        g["dD"] = torch.empty((dim,), **f32)
+    if z is not None:
+        g["dz"] = torch.empty((batch, dim, L), **f32)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty((dim,), **f32)
+    if h0 is not None:
+        g["dh0"] = torch.empty((batch, dim, N), **c64)
+    nbytes = int(L_.mamba_scan_bwd_complex_workspace_size(batch, dim, N, L))
+    if nbytes >= 2 ** 63:
+        raise MambaScanError(6, "mamba_scan_bwd_complex_workspace_size")
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = L_.mamba_scan_bwd_complex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                   _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(dout),
+                                   int(bool(delta_softplus)), _disc_code(disc), _dtype_code(u),
+                                   batch, dim, N, L, _ptr(g["du"]), _ptr(g["ddelta"]),
+                                   _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
+                                   _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
+                                   _ptr(g.get("dh0")), ws.data_ptr(), ws.numel(), _stream(dev))
+    _lib.check(st, "mamba_scan_bwd_complex")
+    return g
+
+
 def conv1d_silu_fwd(x, w, b=None, *, reset=None, out=None):
     """Short causal depthwise convolution (w: (dim, W), W <= 4) followed by
     SiLU.  x (batch, dim, L) float32 or bfloat16; returns u like x."""

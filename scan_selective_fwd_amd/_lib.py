@@ -27,6 +27,7 @@ EXPORTS = (
     "mamba_conv1d_silu_bwd",
     "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size_ex", "mamba_scan_bwd_workspace_size_ex",
     "mamba_scan_bwd_ex", "mamba_scan_checkpoint_size", "mamba_scan_fwd_complex",
+    "mamba_scan_bwd_complex", "mamba_scan_bwd_complex_workspace_size",
 )
 
 
@@ -90,6 +91,10 @@ def load(path: str = LIB_PATH):
     lib.mamba_conv1d_silu_bwd.argtypes = [_vp] * 5 + [_i64, _int] + [_i64] * 3 + [_vp] * 4
     lib.mamba_scan_fwd_complex.restype = _int
     lib.mamba_scan_fwd_complex.argtypes = [_vp] * 9 + [_int, _int, _int] + [_i64] * 4 + [_vp] * 3
+    lib.mamba_scan_bwd_complex.restype = _int
+    lib.mamba_scan_bwd_complex.argtypes = bwd_args
+    lib.mamba_scan_bwd_complex_workspace_size.restype = _sz
+    lib.mamba_scan_bwd_complex_workspace_size.argtypes = [_i64] * 4
     lib.mamba_state_update.restype = _int
     lib.mamba_state_update.argtypes = [_vp] * 9 + [_int, _int, _int] + [_i64] * 3 + [_vp, _vp]
     _lib = lib

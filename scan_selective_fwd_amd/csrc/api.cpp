@@ -418,6 +418,69 @@ mamba_status mamba_scan_fwd_complex(const void* u, const void* delta, const floa
                                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t mamba_scan_bwd_complex_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                             int64_t seqlen) {
+  if (check_sizes(MAMBA_F32, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK ||
+      dstate > 16)
+    return SIZE_MAX;
+  const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
+  return round_up((size_t)(batch * dim) * (size_t)w.nchunks * (size_t)dstate * 8);
+}
+
+mamba_status mamba_scan_bwd_complex(const void* u, const void* delta, const float* A,
+                                    const float* B, const float* C, const float* D,
+                                    const void* z, const float* delta_bias, const float* h0,
+                                    const void* dout, int delta_softplus, mamba_disc disc,
+                                    mamba_dtype dt, int64_t batch, int64_t dim, int64_t dstate,
+                                    int64_t seqlen, float* du, float* ddelta, float* dA,
+                                    float* dB, float* dC, float* dD, float* dz,
+                                    float* ddelta_bias, float* dh0, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
+  if (st != MAMBA_OK) return st;
+  if (dstate > 16) return MAMBA_ERR_UNSUPPORTED;
+  if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
+    return MAMBA_ERR_NULL_PTR;
+  if ((D == nullptr) != (dD == nullptr) || (z == nullptr) != (dz == nullptr) ||
+      (delta_bias == nullptr) != (ddelta_bias == nullptr) || (h0 == nullptr && dh0 != nullptr))
+    return MAMBA_ERR_INVALID;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, dout, du, ddelta, dA, dB, dC,
+                        dD, dz, ddelta_bias, dh0, workspace};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MAMBA_ERR_ALIGNMENT;
+  const size_t need = mamba_scan_bwd_complex_workspace_size(batch, dim, dstate, seqlen);
+  if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
+  const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
+  if (batch * w.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
+  const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  const int dti = dt == MAMBA_F32 ? 0 : 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* states = static_cast<float2*>(workspace);
+
+  mscan::CplxParams fp;
+  memset(&fp, 0, sizeof(fp));
+  fp.u = u; fp.delta = delta; fp.A = reinterpret_cast<const float2*>(A);
+  fp.B = reinterpret_cast<const float2*>(B); fp.C = reinterpret_cast<const float2*>(C);
+  fp.D = D; fp.z = z; fp.bias = delta_bias; fp.h0 = reinterpret_cast<const float2*>(h0);
+  fp.chunk_states = states;
+  fp.batch = batch; fp.dim = dim; fp.L = seqlen; fp.nchannels = batch * dim;
+  fp.groups = w.groups; fp.N = (int)dstate; fp.softplus = delta_softplus ? 1 : 0;
+  if (mscan::dispatch_chunk_states_complex(fp, dti, (int)disc, vec, s) != hipSuccess)
+    return MAMBA_ERR_HIP;
+
+  mscan::CplxBwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.u = u; p.delta = delta; p.A = fp.A; p.B = fp.B; p.C = fp.C; p.D = D; p.z = z;
+  p.bias = delta_bias; p.h0 = fp.h0; p.dout = dout; p.du = du; p.ddelta = ddelta;
+  p.dA = reinterpret_cast<float2*>(dA); p.dB = reinterpret_cast<float2*>(dB);
+  p.dC = reinterpret_cast<float2*>(dC); p.dD = dD; p.dz = dz; p.dbias = ddelta_bias;
+  p.dh0 = reinterpret_cast<float2*>(dh0); p.chunk_states = states;
+  p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
+  p.nchunks = w.nchunks; p.groups = w.groups; p.N = (int)dstate;
+  p.softplus = delta_softplus ? 1 : 0;
+  return hip_status(mscan::dispatch_scan_bwd_complex(p, dti, (int)disc, vec, s));
+}
+
 // ---- short causal convolution + SiLU ----
 mamba_status mamba_conv1d_silu_fwd(const void* x, const float* w, const float* b,
                                    const uint8_t* reset, int64_t width, mamba_dtype dt,

@@ -116,10 +116,45 @@ struct CplxParams {
   int64_t batch, dim, L;
   int64_t nchannels;
   int64_t groups;          // channel groups of 16 per batch row
+  float2* chunk_states;    // recompute pass: (nchannels, nchunks, N) state entering each chunk
   int N;                   // <= 16
   int softplus;
 };
 hipError_t dispatch_scan_fwd_complex(const CplxParams& p, int dtype, int disc, bool vec,
+                                     hipStream_t s);
+hipError_t dispatch_chunk_states_complex(const CplxParams& p, int dtype, int disc, bool vec,
+                                         hipStream_t s);
+
+// Complex-valued backward (scan_bwd_complex.hip).
+struct CplxBwdParams {
+  const void* u;
+  const void* delta;
+  const float2* A;
+  const float2* B;
+  const float2* C;
+  const float* D;          // nullable
+  const void* z;           // nullable
+  const float* bias;       // nullable
+  const float2* h0;        // nullable
+  const void* dout;
+  float* du;
+  float* ddelta;
+  float2* dA;
+  float2* dB;
+  float2* dC;
+  float* dD;               // nullable
+  float* dz;               // nullable
+  float* dbias;            // nullable
+  float2* dh0;             // nullable
+  const float2* chunk_states;  // (nchannels, nchunks, N) state entering each 128-step chunk
+  int64_t batch, dim, L;
+  int64_t nchannels;
+  int64_t nchunks;
+  int64_t groups;
+  int N;                   // <= 16
+  int softplus;
+};
+hipError_t dispatch_scan_bwd_complex(const CplxBwdParams& p, int dtype, int disc, bool vec,
                                      hipStream_t s);
 
 // Short causal convolution + SiLU (conv1d_silu.hip).

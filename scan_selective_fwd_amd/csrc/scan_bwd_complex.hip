@@ -1,0 +1,354 @@
+// Complex-valued selective scan, backward (for scan_fwd_complex.hip): the
+// states are recomputed chunkwise from the state entering each 128-step
+// chunk (paper-graph-ui summary, section 3.4, and trishampatil essay, Part
+// III §4: the expanded states are recomputed, not stored), the adjoint runs
+// in reverse time as a complex affine scan, and every gradient is formed.
+//
+// With the gradient of a complex w written g_w = dL/dRe(w) + i dL/dIm(w) and
+// gy_t = dout_t * SiLU(z_t), the chain rule of the forward gives
+//   G_t = conj(C_t) gy_t + conj(Abar_{t+1}) G_{t+1}           (adjoint of h_t)
+//   ddelta_t += Re(conj(G) Abar (A h_{t-1} + B u))            (ZOH; Euler: A Abar h + B u)
+//   dA  += conj((delta Abar (A h_{t-1} + B u) - Bbar u) / A) G (ZOH; limits at A = 0)
+//   du_t += Re(conj(G) E B),  dB_t += u conj(E) G,  dC_t += gy conj(h_t)
+// where E = Bbar / B.  Structure as in the real backward: 16 channels of one
+// batch row per block, 16 lanes per channel along time, 8 steps per lane;
+// per chunk (last to first) and state index: replay (prefix scan), adjoint
+// (suffix scan, the later chunk's adjoint entering lane 15), gradients.  dB
+// and dC are summed over the wave's 4 channels with permlane swaps, over the
+// block's waves through per-wave LDS slices, and into global memory with one
+// float atomic per (n, t, re/im) per block.
+#include "complex_common.hpp"
+#include "kernels.hpp"
+#include "scan_fwd_impl.hpp"
+
+namespace mscan {
+
+namespace {
+
+constexpr int R = 16;
+constexpr int K = 8;
+constexpr int CPB = (kBlock / 64) * (64 / R);
+constexpr int TCH = R * K;
+constexpr int NT = 16;
+constexpr int G = 2;                 // state indices per dB/dC flush
+constexpr int NW = kBlock / 64;
+
+template <typename T, bool ZOH, bool VEC>
+__global__ __launch_bounds__(kBlock) void scan_bwd_complex_kernel(const CplxBwdParams p) {
+  __shared__ float4 prm[CPB][NT];            // {A, 1/A} (1/A = 0 where A ~ 0)
+  __shared__ float2 gcs[CPB][NT];            // adjoint entering from the later chunk
+  __shared__ float2 dAs[CPB][NT];            // dA of each channel, this batch row
+  __shared__ float red[2][NW][4][G][TCH];    // dB.re, dB.im, dC.re, dC.im partials per wave
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j = lane % R;
+  const int row = lane / R;
+  const int cl = wave * (64 / R) + row;
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = blk / p.groups;
+  const int64_t grp = blk - b * p.groups;
+  const int64_t d_raw = grp * CPB + cl;
+  const bool active = d_raw < p.dim;
+  const int64_t d = active ? d_raw : p.dim - 1;
+  const int64_t c = b * p.dim + d;
+  const int N = p.N;
+  const int64_t L = p.L;
+  const int64_t nchunks = p.nchunks;
+
+  for (int i = tid; i < CPB * NT; i += kBlock) {
+    const int ci = i / NT, n = i - ci * NT;
+    const int64_t dd = grp * CPB + ci;
+    const bool real = dd < p.dim && n < N;
+    const float2 a = real ? p.A[dd * N + n] : make_float2(-1.0f, 0.0f);
+    const float m2 = a.x * a.x + a.y * a.y;
+    const bool tiny = __builtin_fabsf(a.x) < 1e-30f && __builtin_fabsf(a.y) < 1e-30f;
+    const float2 ia = tiny ? make_float2(0.0f, 0.0f) : make_float2(a.x / m2, -a.y / m2);
+    prm[ci][n] = make_float4(a.x, a.y, ia.x, ia.y);
+    gcs[ci][n] = make_float2(0.0f, 0.0f);    // no gradient flows into the final state
+    dAs[ci][n] = make_float2(0.0f, 0.0f);
+  }
+  __syncthreads();
+
+  const T* __restrict__ u_row = static_cast<const T*>(p.u) + c * L;
+  const T* __restrict__ dl_row = static_cast<const T*>(p.delta) + c * L;
+  const T* __restrict__ z_row = p.z ? static_cast<const T*>(p.z) + c * L : nullptr;
+  const T* __restrict__ do_row = static_cast<const T*>(p.dout) + c * L;
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const float Dd = p.D ? p.D[d] : 0.0f;
+  float dD_acc = 0.0f, db_acc = 0.0f;
+
+  for (int64_t ch = nchunks - 1; ch >= 0; --ch) {
+    const int64_t t0 = ch * TCH;
+    const int64_t tl = t0 + (int64_t)j * K;
+    const bool full = VEC && t0 + TCH <= L;
+    const int64_t rem = L - tl;
+    const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
+    float uv[K], dt[K], gy[K], yv[K], du[K], gdt[K];
+    {
+      float raw[K], dov[K];
+      load_items<T, K>(u_row, tl, L, full, uv);
+      load_items<T, K>(dl_row, tl, L, full, raw);
+      load_items<T, K>(do_row, tl, L, full, dov);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float r = raw[k] + bias;
+        const float s = p.softplus ? softplus(r) : r;
+        dt[k] = (k < nvalid) ? s : 0.0f;
+        gy[k] = dov[k];
+      }
+      if (z_row) {
+        float zv[K];
+        load_items<T, K>(z_row, tl, L, full, zv);
+#pragma unroll
+        for (int k = 0; k < K; ++k) gy[k] *= silu(zv[k]);
+      }
+    }
+    float dsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      uv[k] = active ? uv[k] : 0.0f;
+      gy[k] = active ? gy[k] : 0.0f;
+      dsum += dt[k];
+      yv[k] = Dd * uv[k];
+      du[k] = Dd * gy[k];
+      gdt[k] = 0.0f;
+      dD_acc = __builtin_fmaf(gy[k], uv[k], dD_acc);
+    }
+
+    for (int n = 0; n < N; ++n) {
+      const float4 pr = prm[cl][n];
+      const float2 a = make_float2(pr.x, pr.y), ia = make_float2(pr.z, pr.w);
+      const bool tiny = ZOH && ia.x == 0.0f && ia.y == 0.0f;
+      const float2 h_in = p.chunk_states[(c * nchunks + ch) * N + n];
+      const float2 gc = gcs[cl][n];
+      const float2* __restrict__ Brow = p.B + (b * N + n) * L;
+      const float2* __restrict__ Crow = p.C + (b * N + n) * L;
+      float2 Bv[K], Cv[K], ab[K], beta[K], hv[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const bool in = k < nvalid;
+        Bv[k] = in ? Brow[tl + k] : make_float2(0.0f, 0.0f);
+        Cv[k] = in ? Crow[tl + k] : make_float2(0.0f, 0.0f);
+      }
+
+      // ---- forward replay ----
+      float2 agg = make_float2(0.0f, 0.0f);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float mag = fast_exp2(dt[k] * a.x * kLog2e);
+        const float ang = dt[k] * a.y;
+        ab[k] = make_float2(mag * __cosf(ang), mag * __sinf(ang));
+        const float2 e = (ZOH && !tiny) ? cmul(make_float2(ab[k].x - 1.0f, ab[k].y), ia)
+                                        : make_float2(dt[k], 0.0f);
+        beta[k] = cmul(e, cscale(Bv[k], uv[k]));
+        agg = cfma(ab[k], agg, beta[k]);
+      }
+      float sa, ca;
+      sincosf(a.y * dsum, &sa, &ca);
+      const float lm = fast_exp2(a.x * dsum * kLog2e);
+      const float2 Alane = make_float2(lm * ca, lm * sa);
+      float2 Ag = Alane;
+      if (j == 0) agg = cfma(Ag, h_in, agg);
+      cplx_scan_step<kRowShr1>(Ag, agg);
+      cplx_scan_step<kRowShr2>(Ag, agg);
+      cplx_scan_step<kRowShr4>(Ag, agg);
+      cplx_scan_step<kRowShr8>(Ag, agg);
+      const float2 hstart =
+          make_float2(dpp_mov<kRowShr1>(h_in.x, agg.x), dpp_mov<kRowShr1>(h_in.y, agg.y));
+      {
+        float2 h = hstart;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          h = cfma(ab[k], h, beta[k]);
+          hv[k] = h;
+          yv[k] = __builtin_fmaf(Cv[k].x, h.x, __builtin_fmaf(-Cv[k].y, h.y, yv[k]));
+        }
+      }
+
+      // ---- reverse adjoint: g leaving step t = conj(Abar_t) (conj(C_t) gy_t + g) ----
+      float2 gagg = make_float2(0.0f, 0.0f);
+#pragma unroll
+      for (int k = K - 1; k >= 0; --k)
+        gagg = cmul(cconj(ab[k]), cadd(cscale(cconj(Cv[k]), gy[k]), gagg));
+      float2 As = cconj(Alane);
+      if (j == R - 1) gagg = cfma(As, gc, gagg);      // the later chunk enters lane 15
+      cplx_scan_step<0x101 /*row_shl:1*/>(As, gagg);
+      cplx_scan_step<0x102 /*row_shl:2*/>(As, gagg);
+      cplx_scan_step<0x104 /*row_shl:4*/>(As, gagg);
+      cplx_scan_step<0x108 /*row_shl:8*/>(As, gagg);
+      // adjoint arriving at each lane from the right (lane 15: the later chunk's)
+      float2 g = make_float2(dpp_mov<0x101>(gc.x, gagg.x), dpp_mov<0x101>(gc.y, gagg.y));
+      if (j == 0) gcs[cl][n] = gagg;                   // leaves the chunk at lane 0
+
+      // ---- gradient terms ----
+      float2 dAc = make_float2(0.0f, 0.0f);   // ZOH: times conj(1/A) below
+      float2 dAl = make_float2(0.0f, 0.0f);   // Euler and the A = 0 limit
+      float pv[4], sv[4][4], Tq[4][2];
+#pragma unroll
+      for (int k = K - 1; k >= 0; --k) {
+        const float2 Gk = cadd(cscale(cconj(Cv[k]), gy[k]), g);
+        const float2 hprev = (k == 0) ? hstart : hv[k - 1];
+        const float2 Bu = cscale(Bv[k], uv[k]);
+        float2 e;
+        if (ZOH && !tiny) {
+          e = cmul(make_float2(ab[k].x - 1.0f, ab[k].y), ia);
+          const float2 W = cmul(ab[k], cfma(a, hprev, Bu));       // Abar (A h_{t-1} + B u)
+          gdt[k] += cdot(Gk, W);
+          const float2 q = make_float2(__builtin_fmaf(dt[k], W.x, -beta[k].x),
+                                       __builtin_fmaf(dt[k], W.y, -beta[k].y));
+          dAc = cfma(cconj(q), Gk, dAc);
+        } else {
+          e = make_float2(dt[k], 0.0f);
+          const float2 Ah = cmul(ab[k], hprev);
+          const float2 dEdt = ZOH ? ab[k] : make_float2(1.0f, 0.0f);
+          gdt[k] += cdot(Gk, cmul(a, Ah)) + cdot(Gk, cmul(dEdt, Bu));
+          dAl = cfma(cconj(cscale(Ah, dt[k])), Gk, dAl);
+          if (ZOH) dAl = cfma(cconj(cscale(Bu, 0.5f * dt[k] * dt[k])), Gk, dAl);
+        }
+        du[k] += cdot(Gk, cmul(e, Bv[k]));
+        const float2 vB = cscale(cmul(cconj(e), Gk), uv[k]);
+        const float2 vC = cscale(cconj(hv[k]), gy[k]);
+        const float v[4] = {vB.x, vB.y, vC.x, vC.y};
+        // sum over the wave's 4 channels, two steps at a time
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          if (k & 1) {
+            pv[qq] = v[qq];
+          } else {
+            sv[qq][k / 2] = rs_pair16(v[qq], pv[qq]);
+            if (k == 4) Tq[qq][1] = rs_pair32(sv[qq][2], sv[qq][3]);
+            else if (k == 0) Tq[qq][0] = rs_pair32(sv[qq][0], sv[qq][1]);
+          }
+        }
+        g = cmul(cconj(ab[k]), Gk);
+      }
+      const int buf = (n / G) & 1;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {   // lane (row r, j) owns step j*K + 4m + r
+        const int pos = (4 * m + row) * 16 + j;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) red[buf][wave][qq][n % G][pos] = Tq[qq][m];
+      }
+      const float2 dAn = cadd(cmul(dAc, cconj(ia)), dAl);
+      const float sx = row_sum_to_last(dAn.x);
+      const float sy = row_sum_to_last(dAn.y);
+      if (j == R - 1) dAs[cl][n] = cadd(dAs[cl][n], make_float2(sx, sy));
+
+      if (n % G == G - 1 || n == N - 1) {
+        // sum the waves' partials of this group of states into dB, dC
+        // (block-uniform: N is the same for every thread)
+        __syncthreads();
+        const int n0 = n - (n % G);
+        for (int s = 0; s < 4 * G * TCH / kBlock; ++s) {
+          const int i = s * kBlock + tid;
+          const int qq = i / (G * TCH);
+          const int nn = (i / TCH) % G;
+          const int tt = i % TCH;
+          const int pos = (tt % K) * 16 + tt / K;
+          float v = 0.0f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) v += red[buf][w][qq][nn][pos];
+          if (n0 + nn < N && t0 + tt < L) {
+            float* dst = reinterpret_cast<float*>(qq < 2 ? p.dB : p.dC);
+            unsafeAtomicAdd(dst + 2 * ((b * N + n0 + nn) * L + t0 + tt) + (qq & 1), v);
+          }
+        }
+      }
+    }
+
+    // ---- per-step outputs ----
+    {
+      float raw[K], ddl[K];
+      load_items<T, K>(dl_row, tl, L, full, raw);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float sg = p.softplus ? sigmoid(raw[k] + bias) : 1.0f;
+        ddl[k] = (k < nvalid) ? gdt[k] * sg : 0.0f;
+        db_acc += ddl[k];
+      }
+      if (active) {
+        store_items<float, K>(p.du + c * L, tl, L, full, du);
+        store_items<float, K>(p.ddelta + c * L, tl, L, full, ddl);
+      }
+    }
+    if (z_row) {
+      float zv[K], dov[K], dzv[K];
+      load_items<T, K>(z_row, tl, L, full, zv);
+      load_items<T, K>(do_row, tl, L, full, dov);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float sg = sigmoid(zv[k]);
+        dzv[k] = dov[k] * yv[k] * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
+      }
+      if (active) store_items<float, K>(p.dz + c * L, tl, L, full, dzv);
+    }
+    __syncthreads();   // keeps the next chunk's slice stores behind this chunk's flushes
+  }
+
+  for (int i = tid; i < CPB * NT; i += kBlock) {
+    const int ci = i / NT, n = i - ci * NT;
+    const int64_t dd = grp * CPB + ci;
+    if (dd < p.dim && n < N) {
+      if (p.dh0) p.dh0[(b * p.dim + dd) * N + n] = gcs[ci][n];
+      float* dA = reinterpret_cast<float*>(p.dA + dd * N + n);
+      unsafeAtomicAdd(dA, dAs[ci][n].x);
+      unsafeAtomicAdd(dA + 1, dAs[ci][n].y);
+    }
+  }
+  const float sD = row_sum_to_last(dD_acc);
+  const float sb = row_sum_to_last(db_acc);
+  if (active && j == R - 1) {
+    if (p.dD) unsafeAtomicAdd(p.dD + d, sD);
+    if (p.dbias) unsafeAtomicAdd(p.dbias + d, sb);
+  }
+}
+
+__global__ __launch_bounds__(256) void cplx_bwd_zero_kernel(const CplxBwdParams p) {
+  const int64_t nbc = 2 * p.batch * p.N * p.L;   // floats of dB (and of dC)
+  const int64_t na = 2 * p.dim * p.N;
+  const int64_t total = 2 * nbc + na + 2 * p.dim;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    if (i < nbc) reinterpret_cast<float*>(p.dB)[i] = 0.0f;
+    else if (i < 2 * nbc) reinterpret_cast<float*>(p.dC)[i - nbc] = 0.0f;
+    else if (i < 2 * nbc + na) reinterpret_cast<float*>(p.dA)[i - 2 * nbc] = 0.0f;
+    else {
+      const int64_t k = i - 2 * nbc - na;
+      float* dst = k < p.dim ? p.dD : p.dbias;
+      if (dst) dst[k < p.dim ? k : k - p.dim] = 0.0f;
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_bwd_complex(const CplxBwdParams& p, int disc, bool vec, hipStream_t s) {
+  {
+    const int64_t total = 4 * p.batch * p.N * p.L + 2 * p.dim * p.N + 2 * p.dim;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(cplx_bwd_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(p.batch * p.groups)), block(kBlock);
+  if (disc == 0) {
+    if (vec) hipLaunchKernelGGL((scan_bwd_complex_kernel<T, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_bwd_complex_kernel<T, true, false>), grid, block, 0, s, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((scan_bwd_complex_kernel<T, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_bwd_complex_kernel<T, false, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t dispatch_scan_bwd_complex(const CplxBwdParams& p, int dtype, int disc, bool vec,
+                                     hipStream_t s) {
+  return dtype == 0 ? launch_bwd_complex<float>(p, disc, vec, s)
+                    : launch_bwd_complex<bf16_t>(p, disc, vec, s);
+}
+
+}  // namespace mscan

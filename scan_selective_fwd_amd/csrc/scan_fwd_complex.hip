@@ -16,28 +16,12 @@
 // interleaved (re, im) float pairs.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "complex_common.hpp"
 #include "scan_fwd_impl.hpp"
 
 namespace mscan {
 
 namespace {
-
-__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
-  return make_float2(__builtin_fmaf(a.x, b.x, -a.y * b.y), __builtin_fmaf(a.x, b.y, a.y * b.x));
-}
-// a * b + c
-__device__ __forceinline__ float2 cfma(float2 a, float2 b, float2 c) {
-  return make_float2(__builtin_fmaf(a.x, b.x, __builtin_fmaf(-a.y, b.y, c.x)),
-                     __builtin_fmaf(a.x, b.y, __builtin_fmaf(a.y, b.x, c.y)));
-}
-
-template <int CTRL>
-__device__ __forceinline__ void cplx_scan_step(float2& A, float2& Bv) {
-  const float2 Ap = make_float2(dpp_mov<CTRL>(1.0f, A.x), dpp_mov<CTRL>(0.0f, A.y));
-  const float2 Bp = make_float2(dpp_mov<CTRL>(0.0f, Bv.x), dpp_mov<CTRL>(0.0f, Bv.y));
-  Bv = cfma(A, Bp, Bv);
-  A = cmul(A, Ap);
-}
 
 constexpr int R = 16;
 constexpr int K = 8;
@@ -45,7 +29,9 @@ constexpr int CPB = (kBlock / 64) * (64 / R);
 constexpr int TCH = R * K;
 constexpr int NT = 16;
 
-template <typename T, bool ZOH, bool VEC>
+// STATES: the backward's recompute pass: only the state entering every
+// chunk is written (to p.chunk_states); C, y and out are skipped.
+template <typename T, bool ZOH, bool VEC, bool STATES>
 __global__ __launch_bounds__(kBlock) void scan_fwd_complex_kernel(const CplxParams p) {
   __shared__ float4 prm[CPB][NT];   // {A.re, A.im, (1/A).re, (1/A).im}; 1/A = 0 where A ~ 0
   __shared__ float2 carry[CPB][NT];
@@ -70,7 +56,7 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_complex_kernel(const CplxPara
     const bool real = dd < p.dim && n < N;
     const float2 a = real ? p.A[dd * N + n] : make_float2(-1.0f, 0.0f);
     const float m2 = a.x * a.x + a.y * a.y;
-    const bool tiny = m2 < 1e-60f;
+    const bool tiny = __builtin_fabsf(a.x) < 1e-30f && __builtin_fabsf(a.y) < 1e-30f;
     const float2 ia = tiny ? make_float2(0.0f, 0.0f) : make_float2(a.x / m2, -a.y / m2);
     prm[ci][n] = make_float4(a.x, a.y, ia.x, ia.y);
     const int64_t cc = b * p.dim + dd;
@@ -90,6 +76,9 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_complex_kernel(const CplxPara
     const bool full = VEC && ch * TCH + TCH <= L;
     const int64_t rem = L - tl;
     const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
+    if (STATES && active && j == 0) {
+      for (int n = 0; n < N; ++n) p.chunk_states[(c * nchunks + ch) * N + n] = carry[cl][n];
+    }
     float uv[K], dt[K], y[K];
     load_items<T, K>(u_row, tl, L, full, uv);
     load_items<T, K>(dl_row, tl, L, full, dt);
@@ -135,41 +124,45 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_complex_kernel(const CplxPara
       cplx_scan_step<kRowShr2>(Ag, agg);
       cplx_scan_step<kRowShr4>(Ag, agg);
       cplx_scan_step<kRowShr8>(Ag, agg);
-      // state before this lane's steps: the previous lane's end (lane 0: the carry)
-      float2 h = make_float2(dpp_mov<kRowShr1>(cin.x, agg.x), dpp_mov<kRowShr1>(cin.y, agg.y));
+      if constexpr (!STATES) {
+        // state before this lane's steps: the previous lane's end (lane 0: the carry)
+        float2 h = make_float2(dpp_mov<kRowShr1>(cin.x, agg.x), dpp_mov<kRowShr1>(cin.y, agg.y));
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const float2 Cv = k < nvalid ? Crow[tl + k] : make_float2(0.0f, 0.0f);
-        h = cfma(ab[k], h, beta[k]);
-        y[k] = __builtin_fmaf(Cv.x, h.x, __builtin_fmaf(-Cv.y, h.y, y[k]));
+        for (int k = 0; k < K; ++k) {
+          const float2 Cv = k < nvalid ? Crow[tl + k] : make_float2(0.0f, 0.0f);
+          h = cfma(ab[k], h, beta[k]);
+          y[k] = __builtin_fmaf(Cv.x, h.x, __builtin_fmaf(-Cv.y, h.y, y[k]));
+        }
       }
       // all lanes have read carry[cl][n] above; lane 15 holds the chunk's end
       if (j == R - 1) carry[cl][n] = agg;
     }
 
-    if (z_row) {
-      float zv[K];
-      load_items<T, K>(z_row, tl, L, full, zv);
+    if constexpr (!STATES) {
+      if (z_row) {
+        float zv[K];
+        load_items<T, K>(z_row, tl, L, full, zv);
 #pragma unroll
-      for (int k = 0; k < K; ++k) y[k] *= silu(zv[k]);
+        for (int k = 0; k < K; ++k) y[k] *= silu(zv[k]);
+      }
+      if (active) store_items<T, K>(static_cast<T*>(p.out) + c * L, tl, L, full, y);
     }
-    if (active) store_items<T, K>(static_cast<T*>(p.out) + c * L, tl, L, full, y);
   }
 
-  if (p.last_state && active && j == 0) {
+  if (!STATES && p.last_state && active && j == 0) {
     for (int n = 0; n < N; ++n) p.last_state[c * N + n] = carry[cl][n];
   }
 }
 
-template <typename T>
+template <typename T, bool STATES>
 hipError_t launch_complex(const CplxParams& p, int disc, bool vec, hipStream_t s) {
   const dim3 grid((unsigned)(p.batch * p.groups)), block(kBlock);
   if (disc == 0) {
-    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, false>), grid, block, 0, s, p);
+    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, true, STATES>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, false, STATES>), grid, block, 0, s, p);
   } else {
-    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, false>), grid, block, 0, s, p);
+    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, true, STATES>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, false, STATES>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
@@ -178,8 +171,14 @@ hipError_t launch_complex(const CplxParams& p, int disc, bool vec, hipStream_t s
 
 hipError_t dispatch_scan_fwd_complex(const CplxParams& p, int dtype, int disc, bool vec,
                                      hipStream_t s) {
-  return dtype == 0 ? launch_complex<float>(p, disc, vec, s)
-                    : launch_complex<bf16_t>(p, disc, vec, s);
+  return dtype == 0 ? launch_complex<float, false>(p, disc, vec, s)
+                    : launch_complex<bf16_t, false>(p, disc, vec, s);
+}
+
+hipError_t dispatch_chunk_states_complex(const CplxParams& p, int dtype, int disc, bool vec,
+                                         hipStream_t s) {
+  return dtype == 0 ? launch_complex<float, true>(p, disc, vec, s)
+                    : launch_complex<bf16_t, true>(p, disc, vec, s);
 }
 
 }  // namespace mscan

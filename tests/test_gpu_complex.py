@@ -21,7 +21,8 @@ def _dev(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def _case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None):
+def _case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None,
+          zero_A=False):
     opts = opts or {}
     announce(f"complex fwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} h0={h0} "
              f"softplus={softplus} opts={opts}")
@@ -31,6 +32,8 @@ def _case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None
         inp["delta"] = W.bf16_round_bits(raw) if dtype == "bf16" else raw.astype(np.float32)
         if "delta_bias" in inp:
             inp["delta_bias"] = (np.abs(inp["delta_bias"]) * 0.01).astype(np.float32)
+    if zero_A:
+        inp["A"][::3, 0] = 0.0          # the ZOH limit delta*B for these channels
     h0v = None
     if h0:
         g = np.random.default_rng([wid, 13])
@@ -72,8 +75,73 @@ def test_complex_fwd_optional_inputs_and_softplus_off():
     _case(73, 2, 20, 8, 300, "f32", "euler", softplus=False, h0=True)
 
 
+def test_complex_fwd_zero_A_limit():
+    _case(79, 1, 12, 4, 260, "f32", "zoh", h0=True, zero_A=True)
+
+
 def test_complex_fwd_rejects_large_state():
     inp = W.make_complex_inputs(74, 1, 4, 17, 64)
     t = {k: _dev(v, "f32") for k, v in inp.items()}
     with pytest.raises(ms.MambaScanError):
         ms.scan_fwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"])
+
+
+def _as_pairs(x):
+    x = np.asarray(x).astype(np.complex128)
+    return np.stack([x.real, x.imag], -1)
+
+
+def _bwd_case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None,
+              zero_A=False):
+    opts = opts or {}
+    announce(f"complex bwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} h0={h0} "
+             f"softplus={softplus} opts={opts} zero_A={zero_A}")
+    inp = W.make_complex_inputs(wid, batch, dim, N, L, dtype=dtype, with_dout=True, **opts)
+    if not softplus:
+        raw = np.abs(W.as_f64(inp["delta"], dtype)) * 0.05 + 0.01
+        inp["delta"] = W.bf16_round_bits(raw) if dtype == "bf16" else raw.astype(np.float32)
+        if "delta_bias" in inp:
+            inp["delta_bias"] = (np.abs(inp["delta_bias"]) * 0.01).astype(np.float32)
+    if zero_A:
+        inp["A"][::3, 0] = 0.0
+    h0v = None
+    if h0:
+        g = np.random.default_rng([wid, 13])
+        h0v = (g.standard_normal((batch, dim, N)) + 1j * g.standard_normal((batch, dim, N))
+               ).astype(np.complex64)
+    t = {k: _dev(v, dtype) for k, v in inp.items()}
+    res = ms.scan_bwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t.get("D"), t.get("z"),
+                              t.get("delta_bias"), t["dout"],
+                              None if h0v is None else torch.from_numpy(h0v).cuda(),
+                              delta_softplus=softplus, disc=disc)
+    torch.cuda.synchronize()
+    f = {k: (W.as_f64(v, dtype) if v.dtype == np.uint16 else v) for k, v in inp.items()}
+    ref = oracle.scan_bwd_complex(f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"),
+                                  f.get("z"), f.get("delta_bias"), f["dout"], h0v,
+                                  delta_softplus=softplus,
+                                  disc=oracle.ZOH if disc == "zoh" else oracle.EULER)
+    assert set(res) == set(ref), (set(res), set(ref))
+    for k in ref:
+        got = res[k].cpu().numpy()
+        if np.iscomplexobj(ref[k]):
+            assert_match(_as_pairs(got), _as_pairs(ref[k]), RTOL[dtype], k)
+        else:
+            assert_match(got.astype(np.float64), ref[k], RTOL[dtype], k)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_complex_bwd_dtypes_discs(dtype, disc):
+    _bwd_case(75, 2, 19, 16, 400, dtype, disc, h0=True)
+
+
+@pytest.mark.parametrize("N", [1, 5])
+@pytest.mark.parametrize("L", [1, 129])
+def test_complex_bwd_sizes(N, L):
+    _bwd_case(76, 2, 7, N, L, "f32", "zoh")
+
+
+def test_complex_bwd_optional_inputs_softplus_off_zero_A():
+    _bwd_case(77, 2, 9, 6, 300, "f32", "zoh", softplus=False,
+              opts=dict(with_D=False, with_z=False, with_bias=False))
+    _bwd_case(78, 1, 12, 4, 260, "f32", "zoh", h0=True, zero_A=True)
