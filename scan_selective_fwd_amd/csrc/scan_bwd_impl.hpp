@@ -112,9 +112,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   // slower than stores on this chip.)  Step tt of the chunk sits at
   // position (tt % 8) * 16 + tt / 8, which makes each wave's 64 stores hit
   // 64 consecutive words.
-  constexpr int G = 4;
+  constexpr int G = 2;
   constexpr int NW = kBlock / 64;
   __shared__ float red[2][NW][2][G][TCH];
+  // per-step factors of the epilogue, made when the inputs are first read
+  // (softplus'(r) for ddelta and dout*SiLU'(z) for dz), so that the inputs
+  // are not read from memory a second time; [k][tid] keeps accesses
+  // conflict-free
+  __shared__ float stash[2][kItemsBwd][kBlock];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -211,12 +216,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         const float s = p.softplus ? softplus(r) : r;
         dt[k] = (k < nvalid) ? s : 0.0f;
         gy[k] = dov[k];
+        stash[0][k][tid] = p.softplus ? sigmoid(r) : 1.0f;   // softplus'
       }
       if (z_row) {
         float zv[K];
         load_items<T, K>(z_row, tl, L, full, zv);
 #pragma unroll
-        for (int k = 0; k < K; ++k) gy[k] *= silu(zv[k]);
+        for (int k = 0; k < K; ++k) {
+          const float sg = sigmoid(zv[k]);
+          gy[k] *= zv[k] * sg;                                        // dout * SiLU(z)
+          stash[1][k][tid] = dov[k] * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);   // dz / y
+        }
       }
     }
     float dsum = 0.0f;
@@ -412,12 +422,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
     // ---- per-step outputs ----
     {
-      float raw[K], ddl[K];
-      load_items<T, K>(dl_row, tl, L, full, raw);
+      float ddl[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const float sg = p.softplus ? sigmoid(raw[k] + bias) : 1.0f;   // softplus'
-        ddl[k] = (k < nvalid) ? gdt[k] * sg : 0.0f;
+        ddl[k] = (k < nvalid) ? gdt[k] * stash[0][k][tid] : 0.0f;
         db_acc += ddl[k];
       }
       if (active) {
@@ -426,14 +434,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       }
     }
     if (z_row) {
-      float zv[K], dov[K], dzv[K];
-      load_items<T, K>(z_row, tl, L, full, zv);
-      load_items<T, K>(do_row, tl, L, full, dov);
+      float dzv[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const float sg = sigmoid(zv[k]);
-        dzv[k] = dov[k] * yv[k] * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
-      }
+      for (int k = 0; k < K; ++k) dzv[k] = yv[k] * stash[1][k][tid];
       if (active) store_items<float, K>(p.dz + c * L, tl, L, full, dzv);
     }
     // every wave is past the last group barrier, so no wave still reads the
