@@ -56,7 +56,7 @@ KERNEL_SOURCES = {
     "scan_fwd_kernel": ["scan_fwd_impl.hpp", "tile_stage.hpp", "device_common.hpp",
                         "kernels.hpp", "scan_fwd_f32.hip", "scan_fwd_bf16.hip"],
     "scan_bwd_kernel": ["scan_bwd_impl.hpp", "tile_stage.hpp", "device_common.hpp",
-                        "kernels.hpp", "scan_bwd_f32.hip", "scan_bwd_bf16.hip"],
+                        "kernels.hpp", "scan_bwd_f32_n16.hip", "scan_bwd_bf16_n16.hip"],
 }
 COPY_BYTES = 1 << 30   # calibration copy: reads and writes 1 GiB
 

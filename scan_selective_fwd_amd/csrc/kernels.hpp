@@ -231,23 +231,37 @@ inline hipError_t dispatch_chunk_states(const FwdParams& p, int dtype, int disc,
 }
 // The backward always spreads a channel over 16 lanes (kBwdLanes).
 constexpr int kBwdLanes = 16;
-// ev_begin / ev_end (nullable) are recorded on the stream right before and
-// after the main backward kernel, for timing it alone.
-hipError_t dispatch_scan_bwd_f32(const BwdParams& p, int disc, bool vec, hipStream_t s,
-                                 hipEvent_t ev_begin, hipEvent_t ev_end);
-hipError_t dispatch_scan_bwd_bf16(const BwdParams& p, int disc, bool vec, hipStream_t s,
-                                  hipEvent_t ev_begin, hipEvent_t ev_end);
-hipError_t dispatch_scan_bwd_reset_f32(const BwdParams& p, int disc, bool vec, hipStream_t s,
-                                       hipEvent_t ev_begin, hipEvent_t ev_end);
-hipError_t dispatch_scan_bwd_reset_bf16(const BwdParams& p, int disc, bool vec, hipStream_t s,
-                                        hipEvent_t ev_begin, hipEvent_t ev_end);
+// Backward launchers, one per (dtype, reset flags, state-size variant):
+// NT = 16 for N <= 16, NT = 64 for N <= 64.  ev_begin / ev_end (nullable) are
+// recorded on the stream right before and after the main backward kernel,
+// for timing it alone.
+#define MSCAN_BWD_DECL(NAME)                                                             \
+  hipError_t NAME(const BwdParams& p, int disc, bool vec, hipStream_t s, hipEvent_t ev_begin, \
+                  hipEvent_t ev_end);
+MSCAN_BWD_DECL(dispatch_scan_bwd_f32_n16)
+MSCAN_BWD_DECL(dispatch_scan_bwd_f32_n64)
+MSCAN_BWD_DECL(dispatch_scan_bwd_bf16_n16)
+MSCAN_BWD_DECL(dispatch_scan_bwd_bf16_n64)
+MSCAN_BWD_DECL(dispatch_scan_bwd_reset_f32_n16)
+MSCAN_BWD_DECL(dispatch_scan_bwd_reset_f32_n64)
+MSCAN_BWD_DECL(dispatch_scan_bwd_reset_bf16_n16)
+MSCAN_BWD_DECL(dispatch_scan_bwd_reset_bf16_n64)
+#undef MSCAN_BWD_DECL
 inline hipError_t dispatch_scan_bwd(const BwdParams& p, int dtype, int disc, bool vec,
                                     hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  if (p.reset)
-    return dtype == 0 ? dispatch_scan_bwd_reset_f32(p, disc, vec, s, ev_begin, ev_end)
-                      : dispatch_scan_bwd_reset_bf16(p, disc, vec, s, ev_begin, ev_end);
-  return dtype == 0 ? dispatch_scan_bwd_f32(p, disc, vec, s, ev_begin, ev_end)
-                    : dispatch_scan_bwd_bf16(p, disc, vec, s, ev_begin, ev_end);
+  const bool small = p.N <= 16;
+  if (p.reset) {
+    if (dtype == 0)
+      return small ? dispatch_scan_bwd_reset_f32_n16(p, disc, vec, s, ev_begin, ev_end)
+                   : dispatch_scan_bwd_reset_f32_n64(p, disc, vec, s, ev_begin, ev_end);
+    return small ? dispatch_scan_bwd_reset_bf16_n16(p, disc, vec, s, ev_begin, ev_end)
+                 : dispatch_scan_bwd_reset_bf16_n64(p, disc, vec, s, ev_begin, ev_end);
+  }
+  if (dtype == 0)
+    return small ? dispatch_scan_bwd_f32_n16(p, disc, vec, s, ev_begin, ev_end)
+                 : dispatch_scan_bwd_f32_n64(p, disc, vec, s, ev_begin, ev_end);
+  return small ? dispatch_scan_bwd_bf16_n16(p, disc, vec, s, ev_begin, ev_end)
+               : dispatch_scan_bwd_bf16_n64(p, disc, vec, s, ev_begin, ev_end);
 }
 hipError_t dispatch_state_update(const StepParams& p, int dtype, int disc, hipStream_t stream);
 

@@ -247,15 +247,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
     const float* tB = reinterpret_cast<const float*>(tile_mem);
     float4 pr_next = prm[cl][0];
-    static_for<0, NT>([&](auto nc) {
-      constexpr int n = decltype(nc)::value;
-      constexpr int q = n / 16, nl = n % 16;
+    // state indices in groups of 16 (the 16 lanes of a channel hold one
+    // group's per-state registers); N <= 16 is a single group
+    for (int q = 0; q < NQ; ++q) {
+     float hq = hreg[q], gq = gcreg[q], dq = dAreg[q];
+     static_for<0, 16>([&](auto nc) {
+      constexpr int nl = decltype(nc)::value;
+      const int n = q * 16 + nl;
       const float4 pr = pr_next;
-      if constexpr (n + 1 < NT) pr_next = prm[cl][n + 1];
+      if (n + 1 < NT) pr_next = prm[cl][n + 1];
       if (n < N) {
         const float a2 = pr.x, ia = pr.y, An = pr.z;
-        const float h_in = row_lane_to_first<nl>(hreg[q]);   // state n, in lane 0
-        const float gc = row_lane_to_last<nl>(gcreg[q]);     // carry n, in lane 15
+        const float h_in = row_lane_to_first<nl>(hq);   // state n, in lane 0
+        const float gc = row_lane_to_last<nl>(gq);      // carry n, in lane 15
         float Bv[K], Cv[K];
         if constexpr (TILE) {
           tile_read<K>(tB + n * TCH, j, Bv);
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         affine_suffix_scan_row_fused(As, gagg);
         float g = row_shift_left(gagg, gc);                 // adjoint entering each lane from the right
         const float gc_new = row_first_to_lane<nl>(gagg);   // leaving lane 0, now in lane n
-        gcreg[q] = (j == nl) ? gc_new : gcreg[q];
+        gq = (j == nl) ? gc_new : gq;
 
         // ---- gradient terms, with dB/dC summed over the wave's 4 channels
         //      as soon as each pair of steps is done ----
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           }
           g = RST ? P * keep[k] : P;
         }
-        constexpr int buf = (n / G) & 1;
+        const int buf = (n / G) & 1;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {   // lane (row r, j) owns step j*K + 4m + r
           const int pos = (4 * m + row) * 16 + j;
@@ -384,13 +388,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         if constexpr (ZOH && !TINY) dAp = (dAp - dA2) * ia;
         else if constexpr (ZOH) dAp = __builtin_fmaf(-dA2, ia, dAp);
         const float dAn = row_last_to_lane<nl>(row_sum_to_last(dAp));
-        dAreg[q] += (j == nl) ? dAn : 0.0f;
+        dq += (j == nl) ? dAn : 0.0f;
       }
-      if constexpr (n % G == G - 1) {
+      if constexpr (nl % G == G - 1) {
         // end of a group of G states: sum the waves' partials and add them
         // to dB, dC (block-uniform condition: N is the same for all threads)
-        constexpr int n0 = n - (G - 1);
-        constexpr int buf = (n / G) & 1;
+        const int n0 = n - (G - 1);
+        const int buf = (n / G) & 1;
         if (n0 < N) {
           __syncthreads();
 #pragma unroll 1
@@ -411,7 +415,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         }
       }
       mem_fence_compiler();
-    });
+     });
+     gcreg[q] = gq;
+     dAreg[q] = dq;
+    }
 
     // the earlier chunk's B/C rows and states: issued here (not at the chunk
     // start) so their registers are not live across the state-index loop
@@ -501,9 +508,12 @@ static hipError_t launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t ev_be
   return hipGetLastError();
 }
 
-template <typename T, bool RST = false>
-static hipError_t dispatch_bwd_t(const BwdParams& p, int disc, bool vec, hipStream_t s,
-                                 hipEvent_t ev_begin, hipEvent_t ev_end) {
+// The backward for one state-size variant (NT = 16: N <= 16; NT = 64: N <= 64):
+// the zero fill, then the kernel for the discretization and load width.
+// Each variant is compiled in a translation unit of its own.
+template <typename T, int NT, bool RST>
+static hipError_t dispatch_bwd_nt(const BwdParams& p, int disc, bool vec, hipStream_t s,
+                                  hipEvent_t ev_begin, hipEvent_t ev_end) {
   {
     const int64_t total = 2 * p.batch * p.N * p.L + p.dim * p.N + 2 * p.dim;
     int64_t blocks = (total + 255) / 256;
@@ -512,18 +522,12 @@ static hipError_t dispatch_bwd_t(const BwdParams& p, int disc, bool vec, hipStre
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const bool zoh = disc == 0;
   const hipEvent_t b = ev_begin, e = ev_end;
-  if (p.N <= 16) {
-    if (zoh) return vec ? launch_bwd<T, 16, true, true, RST>(p, s, b, e)
-                        : launch_bwd<T, 16, true, false, RST>(p, s, b, e);
-    return vec ? launch_bwd<T, 16, false, true, RST>(p, s, b, e)
-               : launch_bwd<T, 16, false, false, RST>(p, s, b, e);
-  }
-  if (zoh) return vec ? launch_bwd<T, 64, true, true, RST>(p, s, b, e)
-                      : launch_bwd<T, 64, true, false, RST>(p, s, b, e);
-  return vec ? launch_bwd<T, 64, false, true, RST>(p, s, b, e)
-             : launch_bwd<T, 64, false, false, RST>(p, s, b, e);
+  if (disc == 0)
+    return vec ? launch_bwd<T, NT, true, true, RST>(p, s, b, e)
+               : launch_bwd<T, NT, true, false, RST>(p, s, b, e);
+  return vec ? launch_bwd<T, NT, false, true, RST>(p, s, b, e)
+             : launch_bwd<T, NT, false, false, RST>(p, s, b, e);
 }
 
 }  // namespace mscan
