@@ -16,11 +16,14 @@ timed alone with HIP events that the library records around it on the
 stream it runs on; its `traffic` comes from the committed counter summary of
 that kernel when the kernel's sources are unchanged since it was taken.
 `cpu_baseline` is the float64 CPU oracle on a bounded sample of the same
-workload.
+workload.  `per_call.<call>.cold` times each scan kernel again with the
+caches flushed before every launch (a 1 GiB buffer is written first, more
+than the L2s and the 256 MB last-level cache hold): median, p10 and p90 of
+--cold-iters launches.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4|5]
                        [--disc zoh|euler] [--calls fwd,bwd,step] [--no-cpu-baseline]
-                       [--copy-calibration]
+                       [--copy-calibration] [--cold-iters N]
        python bench.py --summarize-counters counter_collection.csv [...]
 """
 from __future__ import annotations
@@ -59,6 +62,7 @@ KERNEL_SOURCES = {
                         "kernels.hpp", "scan_bwd_f32_n16.hip", "scan_bwd_bf16_n16.hip"],
 }
 COPY_BYTES = 1 << 30   # calibration copy: reads and writes 1 GiB
+FLUSH_BYTES = 1 << 30  # written before each cold launch: evicts L2 and the last-level cache
 
 
 def algorithmic_bytes(w, call: str) -> float:
@@ -218,6 +222,9 @@ def main():
                     help="run a 1 GiB device copy first (for counter calibration)")
     ap.add_argument("--calls", default=None,
                     help="comma list of calls to time instead of the full step (fwd,bwd,step)")
+    ap.add_argument("--cold-iters", type=int, default=50,
+                    help="launches of each scan kernel timed with the caches flushed before "
+                         "each (0: skip)")
     ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="CSV")
     args = ap.parse_args()
     if args.summarize_counters:
@@ -328,6 +335,26 @@ def main():
     call_ms = {c: float(np.mean([a.elapsed_time(b) for a, b in ev[c]])) for c in calls}
     kern_ms = {c: float(np.mean([a.elapsed_time(b) for a, b in kev[c]])) for c in kev}
 
+    # cold-cache protocol: each scan kernel alone, a 1 GiB write before every
+    # launch; the other calls' outputs stay as the timed steps left them
+    cold = {}
+    if args.cold_iters > 0 and kev:
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        for c in kev:
+            pairs = [(new_event(), new_event()) for _ in range(args.cold_iters)]
+            torch.cuda.synchronize()
+            for i in range(args.cold_iters):
+                flush.fill_(float(i))
+                run_call(c, pairs[i])
+            torch.cuda.synchronize()
+            t = np.array([a.elapsed_time(b) for a, b in pairs])
+            med = float(np.median(t))
+            cold[c] = {"iters": args.cold_iters, "median_ms": round(med, 5),
+                       "p10_ms": round(float(np.percentile(t, 10)), 5),
+                       "p90_ms": round(float(np.percentile(t, 90)), 5),
+                       "GB/s_median": round(algorithmic_bytes(w, c) / (med * 1e-3) / 1e9, 1)}
+        del flush
+
     step_bytes = sum(algorithmic_bytes(w, c) for c in calls)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     ct = w.batch * w.dim * w.seqlen
@@ -339,6 +366,8 @@ def main():
     for c in kern_ms:
         per_call[c]["kernel"] = kernel_names[c]
         per_call[c]["kernel_ms"] = round(kern_ms[c], 5)
+        if c in cold:
+            per_call[c]["cold"] = cold[c]
     res = {
         "metric": "selective-scan fwd/bwd achieved HBM GB/s (% peak); channel-tokens/s, "
                   "D=1536 L=2048",

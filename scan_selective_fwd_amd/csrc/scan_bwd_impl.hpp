@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
         // ---- forward replay of this chunk for state index n ----
         float a[K], beta[K], hv[K];
-        float agg = 0.0f;
+        float agg;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           a[k] = fast_exp2(dt[k] * a2);
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           } else {
             beta[k] = dt[k] * Bv[k] * uv[k];
           }
-          agg = __builtin_fmaf(RST ? a[k] * keep[k] : a[k], agg, beta[k]);
+          agg = k == 0 ? beta[0] : __builtin_fmaf(RST ? a[k] * keep[k] : a[k], agg, beta[k]);
         }
         const float Alane = RST ? fast_exp2(a2 * dsum) * lane_keep : fast_exp2(a2 * dsum);
         float Ag = Alane;

@@ -97,7 +97,12 @@ __device__ __forceinline__ void store_items(T* __restrict__ row, int64_t t, int6
 // RST: packed sequences.  Where p.reset flags a step the state entering it is
 // zero: the step's decay factor in the recurrence (not in Bbar) becomes 0,
 // and so does the decay of any lane summary that contains the step.
-template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE, bool RST = false>
+//
+// EXACT: N == NT, known at compile time.  The unrolled loop over state
+// indices then has no per-index branch, and the operands of index n + 1
+// need no copies at the join of one (a fifth fewer VALU instructions).
+template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE, bool RST = false,
+          bool EXACT = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_fwd_kernel(
     const FwdParams p) {
   constexpr bool STATES = MODE != kModeOut;
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const bool active = d_raw < p.dim;
   const int64_t d = active ? d_raw : p.dim - 1;
   const int64_t c = b * p.dim + d;
-  const int N = p.N;
+  const int N = EXACT ? NT : p.N;
   const int64_t L = p.L;
 
   const T* __restrict__ u_row = static_cast<const T*>(p.u) + c * L;
@@ -203,7 +208,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   // barrier for the LDS fills; also: does any channel of the block have A ~ 0?
   const bool any_tiny = __syncthreads_or(my_tiny);
 
-  {
+  // TP: some channel of the block has A ~ 0 (ZOH; block-uniform): the chunk
+  // loop is compiled twice, and only the copy such blocks run tests for the
+  // limit of the ZOH coefficient.
+  auto run_chunks = [&](auto tp_c) {
+    constexpr bool TP = decltype(tp_c)::value;
     for (int64_t ch = ch_begin; ch < ch_end; ++ch) {
       const int buf = (int)((ch - ch_begin) & 1);
       const int64_t t0 = ch * TCH;
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           }
           float a[K], beta[K];
           float agg = 0.0f;
-          if (!ZOH || !any_tiny || __builtin_amdgcn_ballot_w64(ia == 0.0f) == 0) {
+          if constexpr (!TP) {
 #pragma unroll
             for (int k = 0; k < K; ++k) {
               a[k] = fast_exp2(dt[k] * a2);
@@ -288,7 +297,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
                 beta[k] = Bv[k] * uv[k];
               }
               if constexpr (RST) a[k] *= keep[k];
-              agg = __builtin_fmaf(a[k], agg, beta[k]);
+              agg = k == 0 ? beta[0] : __builtin_fmaf(a[k], agg, beta[k]);
             }
           } else {
             // a channel of this wave has A ~ 0 (stored as 1/A = 0):
@@ -299,7 +308,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
               const float coef = ia == 0.0f ? dt[k] : (a[k] - 1.0f) * ia;
               beta[k] = coef * Bv[k] * uv[k];
               if constexpr (RST) a[k] *= keep[k];
-              agg = __builtin_fmaf(a[k], agg, beta[k]);
+              agg = k == 0 ? beta[0] : __builtin_fmaf(a[k], agg, beta[k]);
             }
           }
           float Ag = fast_exp2(a2 * dsum);
@@ -334,7 +343,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         __syncthreads();
       }
     }
-  }
+  };
+  if (ZOH && any_tiny) run_chunks(std::true_type{});
+  else run_chunks(std::false_type{});
 
   if (MODE == kModeOut && active && j == 0 && p.last_state && seg == p.nseg - 1) {
 #pragma unroll
@@ -354,17 +365,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   }
 }
 
-template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE, bool RST = false>
+template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE, bool RST = false,
+          bool EXACT = false>
 static hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
   const int64_t nblocks = p.batch * p.groups * p.nseg;
-  hipLaunchKernelGGL((scan_fwd_kernel<T, R, K, NT, ZOH, VEC, MODE, RST>),
+  hipLaunchKernelGGL((scan_fwd_kernel<T, R, K, NT, ZOH, VEC, MODE, RST, EXACT>),
                      dim3((unsigned)nblocks), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
-// N <= 16 takes the NT = 16 kernel, 16 < N <= 64 the NT = 64 kernel.
+// N <= 16 takes the NT = 16 kernel, 16 < N <= 64 the NT = 64 kernel; with
+// 16 lanes per channel, N == 16 (the usual state size) has a variant of its own.
 template <typename T, int R, int K, bool ZOH, int MODE, bool RST = false>
 static hipError_t fwd_nv(const FwdParams& p, bool vec, hipStream_t s) {
+  if constexpr (R == 16) {
+    if (p.N == 16)
+      return vec ? launch_fwd<T, R, K, 16, ZOH, true, MODE, RST, true>(p, s)
+                 : launch_fwd<T, R, K, 16, ZOH, false, MODE, RST, true>(p, s);
+  }
   if (p.N <= 16)
     return vec ? launch_fwd<T, R, K, 16, ZOH, true, MODE, RST>(p, s)
                : launch_fwd<T, R, K, 16, ZOH, false, MODE, RST>(p, s);
