@@ -187,11 +187,54 @@ def cpu_baseline(w, calls, disc, budget_s=10.0):
     ws = copy.copy(w)
     ws.batch, ws.seqlen = nb, L
     nbytes = passes * sum(algorithmic_bytes(ws, c) for c in calls)
+    # one core: the same calls on the first 64 channels of the first batch row
+    sub = {k: (v[:1, :64] if k in ("u", "delta", "z", "dout") else
+               v[:1] if k in ("B", "C") else v[:64] if k in ("A", "D", "delta_bias") else v)
+           for k, v in f.items()}
+    t1 = time.perf_counter()
+    if "fwd" in calls:
+        oracle.scan_fwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"],
+                        sub["delta_bias"], disc=dcode, threads=1)
+    if "bwd" in calls:
+        oracle.scan_bwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"],
+                        sub["delta_bias"], sub["dout"], disc=dcode, threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{passes} pass(es) over {nb} batch rows x {w.dim} channels x {L} steps "
                       f"({'+'.join(calls)}, float64), {dt:.2f} s wall",
-            "channel_tokens_per_s": round(passes * nb * w.dim * L / dt, 1)}
+            "channel_tokens_per_s": round(passes * nb * w.dim * L / dt, 1),
+            "cpu_model": _cpu_model(),
+            "single_core_channel_tokens_per_s": round(64 * L / dt1, 1)}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_bandwidth(torch, nbytes=COPY_BYTES, iters=10):
+    """Achieved rate of a plain device-to-device copy (bytes read + written
+    per second): the streaming ceiling the scan kernels are compared with."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
 
 
 def copy_calibration(torch):
@@ -335,6 +378,8 @@ def main():
     call_ms = {c: float(np.mean([a.elapsed_time(b) for a, b in ev[c]])) for c in calls}
     kern_ms = {c: float(np.mean([a.elapsed_time(b) for a, b in kev[c]])) for c in kev}
 
+    copy_gbs = copy_bandwidth(torch)
+
     # cold-cache protocol: each scan kernel alone, a 1 GiB write before every
     # launch; the other calls' outputs stay as the timed steps left them
     cold = {}
@@ -390,6 +435,8 @@ def main():
                    "disc": args.disc, "delta_softplus": True, "D": True, "z": True,
                    "delta_bias": w.bias},
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "stream_copy_GBs": round(copy_gbs, 1),
+        "pct_of_stream_copy": round(100.0 * value / copy_gbs, 2),
         "channel_tokens_per_s": round(ct / (ms_per_step * 1e-3), 1),
         "per_call": per_call,
     }

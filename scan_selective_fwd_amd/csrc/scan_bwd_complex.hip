@@ -16,10 +16,14 @@
 // (suffix scan, the later chunk's adjoint entering lane 15), gradients.  dB
 // and dC are summed over the wave's 4 channels with permlane swaps, over the
 // block's waves through per-wave LDS slices, and into global memory with one
-// float atomic per (n, t, re/im) per block.
+// float atomic per (n, t, re/im) per block.  B and C of a chunk are staged
+// once per block into an LDS tile (tile_stage.hpp; a complex row of TCH steps
+// is a float row of 2*TCH); the earlier chunk's loads are issued after the
+// state loop and written to the tile at the chunk's end.
 #include "complex_common.hpp"
 #include "kernels.hpp"
 #include "scan_fwd_impl.hpp"
+#include "tile_stage.hpp"
 
 namespace mscan {
 
@@ -34,11 +38,14 @@ constexpr int G = 2;                 // state indices per dB/dC flush
 constexpr int NW = kBlock / 64;
 
 template <typename T, bool ZOH, bool VEC>
-__global__ __launch_bounds__(kBlock) void scan_bwd_complex_kernel(const CplxBwdParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void scan_bwd_complex_kernel(
+    const CplxBwdParams p) {
   __shared__ float4 prm[CPB][NT];            // {A, 1/A} (1/A = 0 where A ~ 0)
   __shared__ float2 gcs[CPB][NT];            // adjoint entering from the later chunk
   __shared__ float2 dAs[CPB][NT];            // dA of each channel, this batch row
   __shared__ float red[2][NW][4][G][TCH];    // dB.re, dB.im, dC.re, dC.im partials per wave
+  constexpr int RW = 2 * TCH;                // floats per tile row
+  __shared__ float4 tile_mem[2 * NT * RW / 4];   // B rows, then C rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -78,6 +85,13 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_complex_kernel(const CplxBwdP
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
   float dD_acc = 0.0f, db_acc = 0.0f;
+  const float* __restrict__ Bf = reinterpret_cast<const float*>(p.B) + b * N * 2 * L;
+  const float* __restrict__ Cf = reinterpret_cast<const float*>(p.C) + b * N * 2 * L;
+  float* tile = reinterpret_cast<float*>(tile_mem);
+  TileStager<float, RW, 2 * K, NT, 2 * NT, kBlock> stage;
+  stage.load(Bf, Cf, N, 2 * L, 2 * (nchunks - 1) * TCH, VEC && nchunks * TCH <= L, tid);
+  stage.store(tile, N, tid);
+  __syncthreads();
 
   for (int64_t ch = nchunks - 1; ch >= 0; --ch) {
     const int64_t t0 = ch * TCH;
@@ -117,20 +131,23 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_complex_kernel(const CplxBwdP
       dD_acc = __builtin_fmaf(gy[k], uv[k], dD_acc);
     }
 
+#pragma unroll 1
     for (int n = 0; n < N; ++n) {
       const float4 pr = prm[cl][n];
       const float2 a = make_float2(pr.x, pr.y), ia = make_float2(pr.z, pr.w);
       const bool tiny = ZOH && ia.x == 0.0f && ia.y == 0.0f;
       const float2 h_in = p.chunk_states[(c * nchunks + ch) * N + n];
       const float2 gc = gcs[cl][n];
-      const float2* __restrict__ Brow = p.B + (b * N + n) * L;
-      const float2* __restrict__ Crow = p.C + (b * N + n) * L;
       float2 Bv[K], Cv[K], ab[K], beta[K], hv[K];
+      {
+        float bf[2 * K], cf[2 * K];   // steps past L were staged as 0
+        tile_read<2 * K>(tile + n * RW, j, bf);
+        tile_read<2 * K>(tile + (NT + n) * RW, j, cf);
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const bool in = k < nvalid;
-        Bv[k] = in ? Brow[tl + k] : make_float2(0.0f, 0.0f);
-        Cv[k] = in ? Crow[tl + k] : make_float2(0.0f, 0.0f);
+        for (int k = 0; k < K; ++k) {
+          Bv[k] = make_float2(bf[2 * k], bf[2 * k + 1]);
+          Cv[k] = make_float2(cf[2 * k], cf[2 * k + 1]);
+        }
       }
 
       // ---- forward replay ----
@@ -145,10 +162,9 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_complex_kernel(const CplxBwdP
         beta[k] = cmul(e, cscale(Bv[k], uv[k]));
         agg = cfma(ab[k], agg, beta[k]);
       }
-      float sa, ca;
-      sincosf(a.y * dsum, &sa, &ca);
+      const float lang = a.y * dsum;
       const float lm = fast_exp2(a.x * dsum * kLog2e);
-      const float2 Alane = make_float2(lm * ca, lm * sa);
+      const float2 Alane = make_float2(lm * __cosf(lang), lm * __sinf(lang));
       float2 Ag = Alane;
       if (j == 0) agg = cfma(Ag, h_in, agg);
       cplx_scan_step<kRowShr1>(Ag, agg);
@@ -258,6 +274,9 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_complex_kernel(const CplxBwdP
       }
     }
 
+    // the earlier chunk's B/C rows (every earlier chunk is whole)
+    if (ch > 0) stage.load(Bf, Cf, N, 2 * L, 2 * (ch - 1) * TCH, VEC, tid);
+
     // ---- per-step outputs ----
     {
       float raw[K], ddl[K];
@@ -284,7 +303,13 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_complex_kernel(const CplxBwdP
       }
       if (active) store_items<float, K>(p.dz + c * L, tl, L, full, dzv);
     }
-    __syncthreads();   // keeps the next chunk's slice stores behind this chunk's flushes
+    // keeps the next chunk's slice stores behind this chunk's flushes, and
+    // every wave's tile reads behind the refill
+    __syncthreads();
+    if (ch > 0) {
+      stage.store(tile, N, tid);
+      __syncthreads();
+    }
   }
 
   for (int i = tid; i < CPB * NT; i += kBlock) {

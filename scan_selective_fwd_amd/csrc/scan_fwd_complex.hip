@@ -18,6 +18,7 @@
 #include "kernels.hpp"
 #include "complex_common.hpp"
 #include "scan_fwd_impl.hpp"
+#include "tile_stage.hpp"
 
 namespace mscan {
 
@@ -31,8 +32,17 @@ constexpr int NT = 16;
 
 // STATES: the backward's recompute pass: only the state entering every
 // chunk is written (to p.chunk_states); C, y and out are skipped.
+//
+// B and C (complex, shared by the block's 16 channels) are staged per chunk
+// into one LDS tile by the whole block with 16-byte loads (tile_stage.hpp:
+// a complex row of TCH steps is a float row of 2*TCH); the next chunk's
+// loads are in flight in registers while the current chunk computes.
 template <typename T, bool ZOH, bool VEC, bool STATES>
-__global__ __launch_bounds__(kBlock) void scan_fwd_complex_kernel(const CplxParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_fwd_complex_kernel(
+    const CplxParams p) {
+  constexpr int ROWS = STATES ? NT : 2 * NT;   // B rows, then C rows
+  constexpr int RW = 2 * TCH;                  // floats per tile row
+  __shared__ float4 tile_mem[ROWS * RW / 4];
   __shared__ float4 prm[CPB][NT];   // {A.re, A.im, (1/A).re, (1/A).im}; 1/A = 0 where A ~ 0
   __shared__ float2 carry[CPB][NT];
 
@@ -62,18 +72,27 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_complex_kernel(const CplxPara
     const int64_t cc = b * p.dim + dd;
     carry[ci][n] = (real && p.h0) ? p.h0[cc * N + n] : make_float2(0.0f, 0.0f);
   }
-  __syncthreads();
 
   const T* __restrict__ u_row = static_cast<const T*>(p.u) + c * L;
   const T* __restrict__ dl_row = static_cast<const T*>(p.delta) + c * L;
   const T* __restrict__ z_row = p.z ? static_cast<const T*>(p.z) + c * L : nullptr;
+  const float* __restrict__ Bf = reinterpret_cast<const float*>(p.B) + b * N * 2 * L;
+  const float* __restrict__ Cf = reinterpret_cast<const float*>(p.C) + b * N * 2 * L;
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
   const int64_t nchunks = (L + TCH - 1) / TCH;
+  float* tile = reinterpret_cast<float*>(tile_mem);
+
+  TileStager<float, RW, 2 * K, NT, ROWS, kBlock> stage;
+  stage.load(Bf, Cf, N, 2 * L, 0, VEC && TCH <= L, tid);
+  stage.store(tile, N, tid);
+  __syncthreads();
 
   for (int64_t ch = 0; ch < nchunks; ++ch) {
     const int64_t tl = ch * TCH + (int64_t)j * K;
     const bool full = VEC && ch * TCH + TCH <= L;
+    const bool more = ch + 1 < nchunks;
+    if (more) stage.load(Bf, Cf, N, 2 * L, 2 * (ch + 1) * TCH, VEC && (ch + 2) * TCH <= L, tid);
     const int64_t rem = L - tl;
     const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
     if (STATES && active && j == 0) {
@@ -96,28 +115,25 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_complex_kernel(const CplxPara
       const float4 pr = prm[cl][n];
       const float2 a = make_float2(pr.x, pr.y), ia = make_float2(pr.z, pr.w);
       const bool tiny = ZOH && ia.x == 0.0f && ia.y == 0.0f;
-      const float2* __restrict__ Brow = p.B + (b * N + n) * L;
-      const float2* __restrict__ Crow = p.C + (b * N + n) * L;
+      float bf[2 * K];
+      tile_read<2 * K>(tile + n * RW, j, bf);   // steps past L were staged as 0
       float2 ab[K], beta[K];
       float2 agg = make_float2(0.0f, 0.0f);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const bool in = k < nvalid;
-        const float2 Bv = in ? Brow[tl + k] : make_float2(0.0f, 0.0f);
         const float mag = fast_exp2(dt[k] * a.x * kLog2e);
         const float ang = dt[k] * a.y;
         ab[k] = make_float2(mag * __cosf(ang), mag * __sinf(ang));
         float2 e;
         if (ZOH && !tiny) e = cmul(make_float2(ab[k].x - 1.0f, ab[k].y), ia);
         else e = make_float2(dt[k], 0.0f);
-        beta[k] = cmul(e, make_float2(Bv.x * uv[k], Bv.y * uv[k]));
-        agg = cfma(ab[k], agg, beta[k]);
+        beta[k] = cmul(e, make_float2(bf[2 * k] * uv[k], bf[2 * k + 1] * uv[k]));
+        agg = k == 0 ? beta[0] : cfma(ab[k], agg, beta[k]);
       }
-      // the lane's decay: exp(A * sum of its steps), with an accurate angle
-      float sa, ca;
-      sincosf(a.y * dsum, &sa, &ca);
+      // the lane's decay: exp(A * sum of its steps)
+      const float lang = a.y * dsum;
       const float lm = fast_exp2(a.x * dsum * kLog2e);
-      float2 Ag = make_float2(lm * ca, lm * sa);
+      float2 Ag = make_float2(lm * __cosf(lang), lm * __sinf(lang));
       const float2 cin = carry[cl][n];
       if (j == 0) agg = cfma(Ag, cin, agg);    // the carried state enters lane 0
       cplx_scan_step<kRowShr1>(Ag, agg);
@@ -125,13 +141,14 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_complex_kernel(const CplxPara
       cplx_scan_step<kRowShr4>(Ag, agg);
       cplx_scan_step<kRowShr8>(Ag, agg);
       if constexpr (!STATES) {
+        float cf[2 * K];
+        tile_read<2 * K>(tile + (NT + n) * RW, j, cf);
         // state before this lane's steps: the previous lane's end (lane 0: the carry)
         float2 h = make_float2(dpp_mov<kRowShr1>(cin.x, agg.x), dpp_mov<kRowShr1>(cin.y, agg.y));
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          const float2 Cv = k < nvalid ? Crow[tl + k] : make_float2(0.0f, 0.0f);
           h = cfma(ab[k], h, beta[k]);
-          y[k] = __builtin_fmaf(Cv.x, h.x, __builtin_fmaf(-Cv.y, h.y, y[k]));
+          y[k] = __builtin_fmaf(cf[2 * k], h.x, __builtin_fmaf(-cf[2 * k + 1], h.y, y[k]));
         }
       }
       // all lanes have read carry[cl][n] above; lane 15 holds the chunk's end
@@ -146,6 +163,12 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_complex_kernel(const CplxPara
         for (int k = 0; k < K; ++k) y[k] *= silu(zv[k]);
       }
       if (active) store_items<T, K>(static_cast<T*>(p.out) + c * L, tl, L, full, y);
+    }
+    // every wave is done with this chunk's tile: write the next one
+    __syncthreads();
+    if (more) {
+      stage.store(tile, N, tid);
+      __syncthreads();
     }
   }
 
