@@ -314,6 +314,10 @@ def main():
         ci = W.make_complex_inputs(w.wid, w.batch, w.dim, w.dstate, w.seqlen, dtype=w.dtype,
                                    bias=w.bias, per_row=w.per_row)
         cplx = {k: torch.from_numpy(ci[k]).cuda() for k in ("A", "B", "C")}
+        if "cfwd" in calls and "cbwd" in calls and not args.no_checkpoints:
+            cplx["ckpt"] = torch.empty(ms.complex_checkpoint_shape(w.batch, w.dim, w.dstate,
+                                                                   w.seqlen),
+                                       dtype=torch.complex64, device="cuda")
     conv_w = conv_b = conv_du = None
     if any(c.startswith("conv") for c in calls):
         cg = np.random.default_rng([w.wid, 10])
@@ -334,10 +338,12 @@ def main():
                         reset=rst, checkpoints=ckpt)
         elif c == "cfwd":       # complex A, B, C with the workload's real sequences
             ms.scan_fwd_complex(g["u"], g["delta"], cplx["A"], cplx["B"], cplx["C"], g["D"],
-                                g["z"], g["delta_bias"], disc=args.disc, out=t_out)
+                                g["z"], g["delta_bias"], disc=args.disc, out=t_out,
+                                checkpoints=cplx.get("ckpt"))
         elif c == "cbwd":
             ms.scan_bwd_complex(g["u"], g["delta"], cplx["A"], cplx["B"], cplx["C"], g["D"],
-                                g["z"], g["delta_bias"], g["dout"], disc=args.disc)
+                                g["z"], g["delta_bias"], g["dout"], disc=args.disc,
+                                checkpoints=cplx.get("ckpt"))
         elif c == "conv_fwd":   # x = the workload's u sequence
             ms.conv1d_silu_fwd(g["u"], conv_w, conv_b, reset=rst, out=t_out)
         elif c == "conv_bwd":

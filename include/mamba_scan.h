@@ -340,6 +340,43 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
  * sizes). */
 size_t mamba_scan_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
 
+/*
+ * The complex-valued forward and backward with chunk checkpoints, as the
+ * real _ex calls have them (same argument meaning as mamba_scan_fwd_complex
+ * and mamba_scan_bwd_complex, plus the buffer):
+ *  - checkpoints (forward: float* output, backward: const float* input;
+ *    NULL = none, and the calls then behave exactly as the plain ones): the
+ *    complex state entering every 128-step chunk, (batch, dim,
+ *    ceil(seqlen/128), dstate) interleaved (re, im) float32 pairs,
+ *    mamba_scan_complex_checkpoint_size bytes, 16-byte aligned.  A backward
+ *    given the buffer skips its state-recompute pass and needs no workspace
+ *    (workspace may be NULL, workspace_bytes 0).  The backward still replays
+ *    every state inside each chunk from its checkpoint (paper-graph-ui
+ *    summary, section 3.4, and trishampatil essay, Part III §4: only the
+ *    chunk-boundary states are kept).  Checkpoints must come from a forward
+ *    over the same inputs.
+ */
+size_t mamba_scan_complex_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate,
+                                          int64_t seqlen);
+
+mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const float* A,
+                                       const float* B, const float* C, const float* D,
+                                       const void* z, const float* delta_bias, const float* h0,
+                                       int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                                       int64_t batch, int64_t dim, int64_t dstate,
+                                       int64_t seqlen, void* out, float* last_state,
+                                       float* checkpoints, void* stream);
+
+mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const float* A,
+                                       const float* B, const float* C, const float* D,
+                                       const void* z, const float* delta_bias, const float* h0,
+                                       const void* dout, int delta_softplus, mamba_disc disc,
+                                       mamba_dtype dt, int64_t batch, int64_t dim,
+                                       int64_t dstate, int64_t seqlen, float* du, float* ddelta,
+                                       float* dA, float* dB, float* dC, float* dD, float* dz,
+                                       float* ddelta_bias, float* dh0, const float* checkpoints,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

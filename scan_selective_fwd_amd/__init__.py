@@ -243,11 +243,19 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
     return out
 
 
+def complex_checkpoint_shape(batch, dim, N, L):
+    """Shape of the complex forward's checkpoint buffer (complex64): the state
+    entering every 128-step chunk."""
+    return (batch, dim, (L + 127) // 128, N)
+
+
 def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
-                     delta_softplus=True, disc="zoh", out=None):
+                     delta_softplus=True, disc="zoh", out=None, checkpoints=None):
     """Complex-valued forward: A (dim, N), B, C (batch, N, L), h0 (batch, dim,
     N) complex64; u, delta, z real.  Returns (out, last_state complex64) with
-    y = Re(sum_n C h) + D u gated by SiLU(z)."""
+    y = Re(sum_n C h) + D u gated by SiLU(z).  `checkpoints`: optional
+    complex64 tensor of complex_checkpoint_shape, filled with the state
+    entering every chunk (for scan_bwd_complex)."""
     L_ = lib()
     if not u.is_cuda:
         raise ValueError("u must be a GPU tensor (no CPU path exists)")
@@ -264,22 +272,27 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None
     _req(z, "z", sdt, (batch, dim, L), dev)
     _req(delta_bias, "delta_bias", torch.float32, (dim,), dev)
     _req(h0, "h0", torch.complex64, (batch, dim, N), dev)
+    _req(checkpoints, "checkpoints", torch.complex64, complex_checkpoint_shape(batch, dim, N, L),
+         dev)
     if out is None:
         out = torch.empty((batch, dim, L), dtype=sdt, device=dev)
     last = torch.empty((batch, dim, N), dtype=torch.complex64, device=dev)
-    st = L_.mamba_scan_fwd_complex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                   _ptr(z), _ptr(delta_bias), _ptr(h0), int(bool(delta_softplus)),
-                                   _disc_code(disc), _dtype_code(u), batch, dim, N, L, _ptr(out),
-                                   _ptr(last), _stream(dev))
-    _lib.check(st, "mamba_scan_fwd_complex")
+    st = L_.mamba_scan_fwd_complex_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(z), _ptr(delta_bias), _ptr(h0),
+                                      int(bool(delta_softplus)), _disc_code(disc),
+                                      _dtype_code(u), batch, dim, N, L, _ptr(out), _ptr(last),
+                                      _ptr(checkpoints), _stream(dev))
+    _lib.check(st, "mamba_scan_fwd_complex_ex")
     return out, last
 
 
 def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
-                     delta_softplus=True, disc="zoh"):
+                     delta_softplus=True, disc="zoh", checkpoints=None):
     """Backward of scan_fwd_complex.  Returns a dict: du, ddelta (and dD, dz,
     ddelta_bias when given) float32; dA, dB, dC (and dh0) complex64, the
-    gradient of a complex input w being dL/dRe(w) + i dL/dIm(w)."""
+    gradient of a complex input w being dL/dRe(w) + i dL/dIm(w).
+    `checkpoints`: the buffer a scan_fwd_complex over the same inputs filled;
+    the chunk states are then not recomputed."""
     L_ = lib()
     dev = u.device
     batch, dim, L = u.shape
@@ -294,6 +307,8 @@ def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
                              (h0, "h0", (batch, dim, N), torch.complex64),
                              (dout, "dout", (batch, dim, L), sdt)):
         _req(t, name, ty, shp, dev)
+    _req(checkpoints, "checkpoints", torch.complex64, complex_checkpoint_shape(batch, dim, N, L),
+         dev)
     f32 = dict(dtype=torch.float32, device=dev)
     c64 = dict(dtype=torch.complex64, device=dev)
     g = dict(du=torch.empty((batch, dim, L), **f32), ddelta=torch.empty((batch, dim, L), **f32),
@@ -307,18 +322,22 @@ def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
         g["ddelta_bias"] = torch.empty((dim,), **f32)
     if h0 is not None:
         g["dh0"] = torch.empty((batch, dim, N), **c64)
-    nbytes = int(L_.mamba_scan_bwd_complex_workspace_size(batch, dim, N, L))
-    if nbytes >= 2 ** 63:
-        raise MambaScanError(6, "mamba_scan_bwd_complex_workspace_size")
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    st = L_.mamba_scan_bwd_complex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                   _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(dout),
-                                   int(bool(delta_softplus)), _disc_code(disc), _dtype_code(u),
-                                   batch, dim, N, L, _ptr(g["du"]), _ptr(g["ddelta"]),
-                                   _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
-                                   _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
-                                   _ptr(g.get("dh0")), ws.data_ptr(), ws.numel(), _stream(dev))
-    _lib.check(st, "mamba_scan_bwd_complex")
+    ws_ptr, ws_bytes = None, 0
+    if checkpoints is None:
+        nbytes = int(L_.mamba_scan_bwd_complex_workspace_size(batch, dim, N, L))
+        if nbytes >= 2 ** 63:
+            raise MambaScanError(6, "mamba_scan_bwd_complex_workspace_size")
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
+    st = L_.mamba_scan_bwd_complex_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(dout),
+                                      int(bool(delta_softplus)), _disc_code(disc),
+                                      _dtype_code(u), batch, dim, N, L, _ptr(g["du"]),
+                                      _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                                      _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
+                                      _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")),
+                                      _ptr(checkpoints), ws_ptr, ws_bytes, _stream(dev))
+    _lib.check(st, "mamba_scan_bwd_complex_ex")
     return g
 
 

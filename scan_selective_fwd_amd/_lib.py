@@ -28,6 +28,8 @@ EXPORTS = (
     "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size_ex", "mamba_scan_bwd_workspace_size_ex",
     "mamba_scan_bwd_ex", "mamba_scan_checkpoint_size", "mamba_scan_fwd_complex",
     "mamba_scan_bwd_complex", "mamba_scan_bwd_complex_workspace_size",
+    "mamba_scan_complex_checkpoint_size", "mamba_scan_fwd_complex_ex",
+    "mamba_scan_bwd_complex_ex",
 )
 
 
@@ -95,6 +97,14 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_bwd_complex.argtypes = bwd_args
     lib.mamba_scan_bwd_complex_workspace_size.restype = _sz
     lib.mamba_scan_bwd_complex_workspace_size.argtypes = [_i64] * 4
+    lib.mamba_scan_complex_checkpoint_size.restype = _sz
+    lib.mamba_scan_complex_checkpoint_size.argtypes = [_i64] * 4
+    lib.mamba_scan_fwd_complex_ex.restype = _int
+    lib.mamba_scan_fwd_complex_ex.argtypes = ([_vp] * 9 + [_int, _int, _int] + [_i64] * 4
+                                              + [_vp] * 4)
+    lib.mamba_scan_bwd_complex_ex.restype = _int
+    lib.mamba_scan_bwd_complex_ex.argtypes = ([_vp] * 10 + [_int, _int, _int] + [_i64] * 4
+                                              + [_vp] * 11 + [_sz, _vp])
     lib.mamba_state_update.restype = _int
     lib.mamba_state_update.argtypes = [_vp] * 9 + [_int, _int, _int] + [_i64] * 3 + [_vp, _vp]
     _lib = lib

@@ -390,17 +390,38 @@ mamba_status mamba_state_update(float* state, const void* u, const void* delta, 
 }
 
 // ---- complex-valued forward ----
+size_t mamba_scan_complex_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate,
+                                          int64_t seqlen) {
+  if (check_sizes(MAMBA_F32, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK ||
+      dstate > 16)
+    return SIZE_MAX;
+  const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
+  return (size_t)(batch * dim) * (size_t)w.nchunks * (size_t)dstate * 8;
+}
+
 mamba_status mamba_scan_fwd_complex(const void* u, const void* delta, const float* A,
                                     const float* B, const float* C, const float* D,
                                     const void* z, const float* delta_bias, const float* h0,
                                     int delta_softplus, mamba_disc disc, mamba_dtype dt,
                                     int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                     void* out, float* last_state, void* stream) {
+  return mamba_scan_fwd_complex_ex(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, disc,
+                                   dt, batch, dim, dstate, seqlen, out, last_state, nullptr,
+                                   stream);
+}
+
+mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const float* A,
+                                       const float* B, const float* C, const float* D,
+                                       const void* z, const float* delta_bias, const float* h0,
+                                       int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                                       int64_t batch, int64_t dim, int64_t dstate,
+                                       int64_t seqlen, void* out, float* last_state,
+                                       float* checkpoints, void* stream) {
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
   if (st != MAMBA_OK) return st;
   if (dstate > 16) return MAMBA_ERR_UNSUPPORTED;
   if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL_PTR;
-  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, out, last_state};
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, out, last_state, checkpoints};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MAMBA_ERR_ALIGNMENT;
   mscan::CplxParams p;
@@ -409,6 +430,7 @@ mamba_status mamba_scan_fwd_complex(const void* u, const void* delta, const floa
   p.B = reinterpret_cast<const float2*>(B); p.C = reinterpret_cast<const float2*>(C);
   p.D = D; p.z = z; p.bias = delta_bias; p.h0 = reinterpret_cast<const float2*>(h0);
   p.out = out; p.last_state = reinterpret_cast<float2*>(last_state);
+  p.chunk_states = reinterpret_cast<float2*>(checkpoints);
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.groups = mscan::channel_groups(dim, 16);
   p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
@@ -436,6 +458,21 @@ mamba_status mamba_scan_bwd_complex(const void* u, const void* delta, const floa
                                     float* dB, float* dC, float* dD, float* dz,
                                     float* ddelta_bias, float* dh0, void* workspace,
                                     size_t workspace_bytes, void* stream) {
+  return mamba_scan_bwd_complex_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout,
+                                   delta_softplus, disc, dt, batch, dim, dstate, seqlen, du,
+                                   ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, nullptr,
+                                   workspace, workspace_bytes, stream);
+}
+
+mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const float* A,
+                                       const float* B, const float* C, const float* D,
+                                       const void* z, const float* delta_bias, const float* h0,
+                                       const void* dout, int delta_softplus, mamba_disc disc,
+                                       mamba_dtype dt, int64_t batch, int64_t dim,
+                                       int64_t dstate, int64_t seqlen, float* du, float* ddelta,
+                                       float* dA, float* dB, float* dC, float* dD, float* dz,
+                                       float* ddelta_bias, float* dh0, const float* checkpoints,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
   if (st != MAMBA_OK) return st;
   if (dstate > 16) return MAMBA_ERR_UNSUPPORTED;
@@ -445,17 +482,20 @@ mamba_status mamba_scan_bwd_complex(const void* u, const void* delta, const floa
       (delta_bias == nullptr) != (ddelta_bias == nullptr) || (h0 == nullptr && dh0 != nullptr))
     return MAMBA_ERR_INVALID;
   const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, dout, du, ddelta, dA, dB, dC,
-                        dD, dz, ddelta_bias, dh0, workspace};
+                        dD, dz, ddelta_bias, dh0, workspace, checkpoints};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MAMBA_ERR_ALIGNMENT;
-  const size_t need = mamba_scan_bwd_complex_workspace_size(batch, dim, dstate, seqlen);
-  if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
+  if (!checkpoints) {   // the chunk states are recomputed into the workspace
+    const size_t need = mamba_scan_bwd_complex_workspace_size(batch, dim, dstate, seqlen);
+    if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
+  }
   const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
   if (batch * w.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
   const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
   const int dti = dt == MAMBA_F32 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float2* states = static_cast<float2*>(workspace);
+  float2* states = checkpoints ? reinterpret_cast<float2*>(const_cast<float*>(checkpoints))
+                               : static_cast<float2*>(workspace);
 
   mscan::CplxParams fp;
   memset(&fp, 0, sizeof(fp));
@@ -465,7 +505,7 @@ mamba_status mamba_scan_bwd_complex(const void* u, const void* delta, const floa
   fp.chunk_states = states;
   fp.batch = batch; fp.dim = dim; fp.L = seqlen; fp.nchannels = batch * dim;
   fp.groups = w.groups; fp.N = (int)dstate; fp.softplus = delta_softplus ? 1 : 0;
-  if (mscan::dispatch_chunk_states_complex(fp, dti, (int)disc, vec, s) != hipSuccess)
+  if (!checkpoints && mscan::dispatch_chunk_states_complex(fp, dti, (int)disc, vec, s) != hipSuccess)
     return MAMBA_ERR_HIP;
 
   mscan::CplxBwdParams p;

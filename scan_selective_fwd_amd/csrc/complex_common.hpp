@@ -1,5 +1,5 @@
 // Complex float32 arithmetic on (re, im) float2 pairs and the complex affine
-// scan step shared by the complex-valued forward and backward kernels.
+// scans shared by the complex-valued forward and backward kernels.
 #pragma once
 
 #include "device_common.hpp"
@@ -22,16 +22,57 @@ __device__ __forceinline__ float cdot(float2 a, float2 b) {
   return __builtin_fmaf(a.x, b.x, a.y * b.y);
 }
 
-// One step of a scan of complex affine pairs (A, B) over lanes: combine with
-// the pair the DPP pattern CTRL brings from another lane (row_shr: the
-// earlier lane, prefix; row_shl: the later lane, suffix).  A lane without a
-// source lane keeps its pair (the identity (1, 0) enters).
-template <int CTRL>
-__device__ __forceinline__ void cplx_scan_step(float2& A, float2& Bv) {
-  const float2 Ap = make_float2(dpp_mov<CTRL>(1.0f, A.x), dpp_mov<CTRL>(0.0f, A.y));
-  const float2 Bp = make_float2(dpp_mov<CTRL>(0.0f, Bv.x), dpp_mov<CTRL>(0.0f, Bv.y));
-  Bv = cfma(A, Bp, Bv);
-  A = cmul(A, Ap);
+// Scans of complex affine pairs (A, B) over the 16 lanes of a row, combining
+// each lane with the pair of the lane the DPP pattern names (row_shr: the
+// earlier lane, prefix; row_shl: the later lane, suffix), in four steps
+// (shift 1, 2, 4, 8) of DPP-modified VOP2 instructions.  Per step, with (a, b) this lane's pair and
+// (a', b') the source lane's:  b <- a b' + b  and  a <- a a'.  A lane whose
+// source lies outside its row is not written by the DPP instructions: t0 then
+// keeps 0 and the new a starts from the lane's own a, so the lane keeps its
+// pair (the identity enters).  12 instructions per step (moving each operand
+// with the update_dpp builtin takes 16); two wait states precede each step's
+// first DPP read.
+#define MSCAN_CPLX_DPP_STEP(CTRL)                                               \
+  "s_nop 1\n\t"                                                                 \
+  "v_mov_b32 %2, 0\n\t"                                                         \
+  "v_mov_b32_dpp %2, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %1, %0, %6 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+  "v_fmac_f32 %1, %2, %5\n\t"                                                   \
+  "v_fmac_f32_dpp %0, %0, %5 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+  "v_fma_f32 %0, -%2, %6, %0\n\t"                                               \
+  "v_mov_b32 %3, %5\n\t"                                                        \
+  "v_mul_f32_dpp %3, %5, %5 " CTRL " row_mask:0xf bank_mask:0xf\n\t"            \
+  "v_fmac_f32_dpp %3, %6, -%6 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+  "v_mov_b32 %4, %6\n\t"                                                        \
+  "v_mul_f32_dpp %4, %5, %6 " CTRL " row_mask:0xf bank_mask:0xf\n\t"            \
+  "v_fmac_f32_dpp %4, %6, %5 " CTRL " row_mask:0xf bank_mask:0xf\n\t"
+
+#define MSCAN_CPLX_DPP_STEP_CALL(CTRL)                                               \
+  do {                                                                                \
+    float t0, nx, ny;                                                                 \
+    asm volatile(MSCAN_CPLX_DPP_STEP(CTRL)                                            \
+                 : "+v"(B.x), "+v"(B.y), "=&v"(t0), "=&v"(nx), "=&v"(ny)             \
+                 : "v"(A.x), "v"(A.y));                                               \
+    A = make_float2(nx, ny);                                                          \
+  } while (0)
+
+// Inclusive prefix scan over each 16-lane row (row_shr: the earlier lane).
+__device__ __forceinline__ void cplx_scan_prefix_row(float2& A, float2& B) {
+  MSCAN_CPLX_DPP_STEP_CALL("row_shr:1");
+  MSCAN_CPLX_DPP_STEP_CALL("row_shr:2");
+  MSCAN_CPLX_DPP_STEP_CALL("row_shr:4");
+  MSCAN_CPLX_DPP_STEP_CALL("row_shr:8");
 }
+
+// Inclusive suffix scan over each 16-lane row (row_shl: the later lane).
+__device__ __forceinline__ void cplx_scan_suffix_row(float2& A, float2& B) {
+  MSCAN_CPLX_DPP_STEP_CALL("row_shl:1");
+  MSCAN_CPLX_DPP_STEP_CALL("row_shl:2");
+  MSCAN_CPLX_DPP_STEP_CALL("row_shl:4");
+  MSCAN_CPLX_DPP_STEP_CALL("row_shl:8");
+}
+
+#undef MSCAN_CPLX_DPP_STEP_CALL
+#undef MSCAN_CPLX_DPP_STEP
 
 }  // namespace mscan

@@ -116,7 +116,8 @@ struct CplxParams {
   int64_t batch, dim, L;
   int64_t nchannels;
   int64_t groups;          // channel groups of 16 per batch row
-  float2* chunk_states;    // recompute pass: (nchannels, nchunks, N) state entering each chunk
+  float2* chunk_states;    // (nchannels, nchunks, N) state entering each chunk: the recompute
+                           // pass, or checkpoints of the output pass (nullable there)
   int N;                   // <= 16
   int softplus;
 };

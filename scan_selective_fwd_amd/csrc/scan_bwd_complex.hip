@@ -167,10 +167,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       const float2 Alane = make_float2(lm * __cosf(lang), lm * __sinf(lang));
       float2 Ag = Alane;
       if (j == 0) agg = cfma(Ag, h_in, agg);
-      cplx_scan_step<kRowShr1>(Ag, agg);
-      cplx_scan_step<kRowShr2>(Ag, agg);
-      cplx_scan_step<kRowShr4>(Ag, agg);
-      cplx_scan_step<kRowShr8>(Ag, agg);
+      cplx_scan_prefix_row(Ag, agg);
       const float2 hstart =
           make_float2(dpp_mov<kRowShr1>(h_in.x, agg.x), dpp_mov<kRowShr1>(h_in.y, agg.y));
       {
@@ -190,10 +187,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         gagg = cmul(cconj(ab[k]), cadd(cscale(cconj(Cv[k]), gy[k]), gagg));
       float2 As = cconj(Alane);
       if (j == R - 1) gagg = cfma(As, gc, gagg);      // the later chunk enters lane 15
-      cplx_scan_step<0x101 /*row_shl:1*/>(As, gagg);
-      cplx_scan_step<0x102 /*row_shl:2*/>(As, gagg);
-      cplx_scan_step<0x104 /*row_shl:4*/>(As, gagg);
-      cplx_scan_step<0x108 /*row_shl:8*/>(As, gagg);
+      cplx_scan_suffix_row(As, gagg);
       // adjoint arriving at each lane from the right (lane 15: the later chunk's)
       float2 g = make_float2(dpp_mov<0x101>(gc.x, gagg.x), dpp_mov<0x101>(gc.y, gagg.y));
       if (j == 0) gcs[cl][n] = gagg;                   // leaves the chunk at lane 0
@@ -223,8 +217,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
           dAl = cfma(cconj(cscale(Ah, dt[k])), Gk, dAl);
           if (ZOH) dAl = cfma(cconj(cscale(Bu, 0.5f * dt[k] * dt[k])), Gk, dAl);
         }
-        du[k] += cdot(Gk, cmul(e, Bv[k]));
-        const float2 vB = cscale(cmul(cconj(e), Gk), uv[k]);
+        // Re(conj(G) E B) = Re(conj(s) B) with s = conj(E) G, which dB also uses
+        const float2 sG = cmul(cconj(e), Gk);
+        du[k] += cdot(sG, Bv[k]);
+        const float2 vB = cscale(sG, uv[k]);
         const float2 vC = cscale(cconj(hv[k]), gy[k]);
         const float v[4] = {vB.x, vB.y, vC.x, vC.y};
         // sum over the wave's 4 channels, two steps at a time

@@ -31,7 +31,9 @@ constexpr int TCH = R * K;
 constexpr int NT = 16;
 
 // STATES: the backward's recompute pass: only the state entering every
-// chunk is written (to p.chunk_states); C, y and out are skipped.
+// chunk is written (to p.chunk_states); C, y and out are skipped.  Without
+// STATES the outputs are computed, and the chunk states are also written
+// when p.chunk_states is set (checkpoints for a later backward).
 //
 // B and C (complex, shared by the block's 16 channels) are staged per chunk
 // into one LDS tile by the whole block with 16-byte loads (tile_stage.hpp:
@@ -95,7 +97,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     if (more) stage.load(Bf, Cf, N, 2 * L, 2 * (ch + 1) * TCH, VEC && (ch + 2) * TCH <= L, tid);
     const int64_t rem = L - tl;
     const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
-    if (STATES && active && j == 0) {
+    // the state entering the chunk: the backward's recompute pass, or the
+    // checkpoints a forward may save for a later backward
+    if ((STATES || p.chunk_states) && active && j == 0) {
       for (int n = 0; n < N; ++n) p.chunk_states[(c * nchunks + ch) * N + n] = carry[cl][n];
     }
     float uv[K], dt[K], y[K];
@@ -136,10 +140,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       float2 Ag = make_float2(lm * __cosf(lang), lm * __sinf(lang));
       const float2 cin = carry[cl][n];
       if (j == 0) agg = cfma(Ag, cin, agg);    // the carried state enters lane 0
-      cplx_scan_step<kRowShr1>(Ag, agg);
-      cplx_scan_step<kRowShr2>(Ag, agg);
-      cplx_scan_step<kRowShr4>(Ag, agg);
-      cplx_scan_step<kRowShr8>(Ag, agg);
+      cplx_scan_prefix_row(Ag, agg);
       if constexpr (!STATES) {
         float cf[2 * K];
         tile_read<2 * K>(tile + (NT + n) * RW, j, cf);

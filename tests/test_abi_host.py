@@ -122,6 +122,25 @@ def test_checkpoint_size_and_backward_workspace(lib):
     assert bwd_ex(P, full, P + 8) == 4
 
 
+def test_complex_checkpoints_size_and_workspace(lib):
+    # one complex state (2 floats) per channel, 128-step chunk and state index
+    assert lib.mamba_scan_complex_checkpoint_size(2, 64, 16, 2049) == 2 * 64 * 17 * 16 * 8
+    assert lib.mamba_scan_complex_checkpoint_size(2, 64, 17, 2049) == 2 ** 64 - 1   # N <= 16
+    need = lib.mamba_scan_bwd_complex_workspace_size(2, 64, 16, 2048)
+
+    def bwd_ex(ws, wsb, ckpt):
+        return lib.mamba_scan_bwd_complex_ex(P, P, P, P, P, None, None, None, None, P, 1, 0, 0,
+                                             2, 64, 16, 2048, P, P, P, P, P, None, None, None,
+                                             None, ckpt, ws, wsb, None)
+    assert bwd_ex(None, 0, None) == 5                # no checkpoints: the states need room
+    assert bwd_ex(P, need - 1, None) == 5
+    assert bwd_ex(P, need, P + 8) == 4               # misaligned checkpoints
+    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 2, 64,
+                                         16, 2048, P, None, P + 4, None) == 4
+    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 2, 64,
+                                         17, 2048, P, None, P, None) == 6
+
+
 def test_varlen_requires_flags(lib):
     assert lib.mamba_scan_fwd_varlen(P, P, P, P, P, None, None, None, None, None, 1, 0, 0, 1, 16,
                                      4, 128, P, None, None, 0, None) == 1

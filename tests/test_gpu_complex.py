@@ -145,3 +145,44 @@ def test_complex_bwd_optional_inputs_softplus_off_zero_A():
     _bwd_case(77, 2, 9, 6, 300, "f32", "zoh", softplus=False,
               opts=dict(with_D=False, with_z=False, with_bias=False))
     _bwd_case(78, 1, 12, 4, 260, "f32", "zoh", h0=True, zero_A=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_complex_checkpoints_forward_states_and_backward(dtype):
+    """The forward's checkpoints equal the oracle's state after each 128-step
+    prefix, and the backward that uses them matches the oracle's gradients."""
+    wid, batch, dim, N, L = 80, 2, 19, 16, 400
+    announce(f"complex checkpoints wid={wid} shape=({batch},{dim},{N},{L}) {dtype}")
+    inp = W.make_complex_inputs(wid, batch, dim, N, L, dtype=dtype, with_dout=True)
+    g = np.random.default_rng([wid, 13])
+    h0v = (g.standard_normal((batch, dim, N)) + 1j * g.standard_normal((batch, dim, N))
+           ).astype(np.complex64)
+    t = {k: _dev(v, dtype) for k, v in inp.items()}
+    h0t = torch.from_numpy(h0v).cuda()
+    ckpt = torch.empty(ms.complex_checkpoint_shape(batch, dim, N, L), dtype=torch.complex64,
+                       device="cuda")
+    ms.scan_fwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t.get("D"), t.get("z"),
+                        t.get("delta_bias"), h0t, checkpoints=ckpt)
+    res = ms.scan_bwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t.get("D"), t.get("z"),
+                              t.get("delta_bias"), t["dout"], h0t, checkpoints=ckpt)
+    torch.cuda.synchronize()
+    f = {k: (W.as_f64(v, dtype) if v.dtype == np.uint16 else v) for k, v in inp.items()}
+    got = ckpt.cpu().numpy()
+    for k in range(got.shape[2]):
+        if k == 0:
+            ref_k = h0v.astype(np.complex128)
+        else:
+            T = 128 * k
+            _, ref_k = oracle.scan_fwd_complex(
+                f["u"][..., :T], f["delta"][..., :T], f["A"], f["B"][..., :T], f["C"][..., :T],
+                f.get("D"), None, f.get("delta_bias"), h0v)
+        assert_match(_as_pairs(got[:, :, k]), _as_pairs(ref_k), RTOL[dtype], f"checkpoint {k}")
+    ref = oracle.scan_bwd_complex(f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"),
+                                  f.get("z"), f.get("delta_bias"), f["dout"], h0v)
+    assert set(res) == set(ref), (set(res), set(ref))
+    for k in ref:
+        r = res[k].cpu().numpy()
+        if np.iscomplexobj(ref[k]):
+            assert_match(_as_pairs(r), _as_pairs(ref[k]), RTOL[dtype], k)
+        else:
+            assert_match(r.astype(np.float64), ref[k], RTOL[dtype], k)
