@@ -22,6 +22,22 @@ __device__ __forceinline__ float cdot(float2 a, float2 b) {
   return __builtin_fmaf(a.x, b.x, a.y * b.y);
 }
 
+// exp(dt * a) for a = ar + i ai given as ar2 = ar * log2(e) and air =
+// ai / (2 pi): the hardware exponential and sine / cosine (which take
+// revolutions), without the scaling multiplies of the generic forms.
+__device__ __forceinline__ float2 cexp_scaled(float dt, float ar2, float air) {
+  const float mag = fast_exp2(dt * ar2);
+  const float rev = dt * air;
+  return make_float2(mag * __builtin_amdgcn_cosf(rev), mag * __builtin_amdgcn_sinf(rev));
+}
+
+// (ab - 1) q, with q = (1/A) B u computed once per step: the ZOH term
+// Bbar u = (Abar - 1)/A B u.
+__device__ __forceinline__ float2 cmul_minus_one(float2 ab, float2 q) {
+  return make_float2(__builtin_fmaf(ab.x, q.x, __builtin_fmaf(-ab.y, q.y, -q.x)),
+                     __builtin_fmaf(ab.x, q.y, __builtin_fmaf(ab.y, q.x, -q.y)));
+}
+
 // Scans of complex affine pairs (A, B) over the 16 lanes of a row, combining
 // each lane with the pair of the lane the DPP pattern names (row_shr: the
 // earlier lane, prefix; row_shl: the later lane, suffix), in four steps

@@ -19,6 +19,7 @@ namespace mscan {
 typedef uint16_t bf16_t;  // bfloat16 stored as its 16-bit pattern
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInv2Pi = 0.15915494309189535f;   // 1 / (2 pi)
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------

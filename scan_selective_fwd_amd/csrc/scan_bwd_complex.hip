@@ -41,6 +41,7 @@ template <typename T, bool ZOH, bool VEC>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void scan_bwd_complex_kernel(
     const CplxBwdParams p) {
   __shared__ float4 prm[CPB][NT];            // {A, 1/A} (1/A = 0 where A ~ 0)
+  __shared__ float2 prs[CPB][NT];            // {A.re log2(e), A.im / (2 pi)}
   __shared__ float2 gcs[CPB][NT];            // adjoint entering from the later chunk
   __shared__ float2 dAs[CPB][NT];            // dA of each channel, this batch row
   __shared__ float red[2][NW][4][G][TCH];    // dB.re, dB.im, dC.re, dC.im partials per wave
@@ -73,6 +74,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const bool tiny = __builtin_fabsf(a.x) < 1e-30f && __builtin_fabsf(a.y) < 1e-30f;
     const float2 ia = tiny ? make_float2(0.0f, 0.0f) : make_float2(a.x / m2, -a.y / m2);
     prm[ci][n] = make_float4(a.x, a.y, ia.x, ia.y);
+    prs[ci][n] = make_float2(a.x * kLog2e, a.y * kInv2Pi);
     gcs[ci][n] = make_float2(0.0f, 0.0f);    // no gradient flows into the final state
     dAs[ci][n] = make_float2(0.0f, 0.0f);
   }
@@ -135,6 +137,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int n = 0; n < N; ++n) {
       const float4 pr = prm[cl][n];
       const float2 a = make_float2(pr.x, pr.y), ia = make_float2(pr.z, pr.w);
+      const float2 ps = prs[cl][n];
       const bool tiny = ZOH && ia.x == 0.0f && ia.y == 0.0f;
       const float2 h_in = p.chunk_states[(c * nchunks + ch) * N + n];
       const float2 gc = gcs[cl][n];
@@ -151,20 +154,27 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
 
       // ---- forward replay ----
-      float2 agg = make_float2(0.0f, 0.0f);
+      if (!ZOH || __builtin_amdgcn_ballot_w64(tiny) == 0) {
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const float mag = fast_exp2(dt[k] * a.x * kLog2e);
-        const float ang = dt[k] * a.y;
-        ab[k] = make_float2(mag * __cosf(ang), mag * __sinf(ang));
-        const float2 e = (ZOH && !tiny) ? cmul(make_float2(ab[k].x - 1.0f, ab[k].y), ia)
-                                        : make_float2(dt[k], 0.0f);
-        beta[k] = cmul(e, cscale(Bv[k], uv[k]));
-        agg = cfma(ab[k], agg, beta[k]);
+        for (int k = 0; k < K; ++k) {
+          ab[k] = cexp_scaled(dt[k], ps.x, ps.y);
+          const float2 Bu = cscale(Bv[k], uv[k]);
+          if constexpr (ZOH) beta[k] = cmul_minus_one(ab[k], cmul(ia, Bu));
+          else beta[k] = cscale(Bu, dt[k]);
+        }
+      } else {
+        // a channel of this wave has A ~ 0 (1/A stored as 0): delta B u there
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          ab[k] = cexp_scaled(dt[k], ps.x, ps.y);
+          const float2 Bu = cscale(Bv[k], uv[k]);
+          beta[k] = tiny ? cscale(Bu, dt[k]) : cmul_minus_one(ab[k], cmul(ia, Bu));
+        }
       }
-      const float lang = a.y * dsum;
-      const float lm = fast_exp2(a.x * dsum * kLog2e);
-      const float2 Alane = make_float2(lm * __cosf(lang), lm * __sinf(lang));
+      float2 agg = beta[0];
+#pragma unroll
+      for (int k = 1; k < K; ++k) agg = cfma(ab[k], agg, beta[k]);
+      const float2 Alane = cexp_scaled(dsum, ps.x, ps.y);
       float2 Ag = Alane;
       if (j == 0) agg = cfma(Ag, h_in, agg);
       cplx_scan_prefix_row(Ag, agg);

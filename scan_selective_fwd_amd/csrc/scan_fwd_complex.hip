@@ -45,7 +45,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   constexpr int ROWS = STATES ? NT : 2 * NT;   // B rows, then C rows
   constexpr int RW = 2 * TCH;                  // floats per tile row
   __shared__ float4 tile_mem[ROWS * RW / 4];
-  __shared__ float4 prm[CPB][NT];   // {A.re, A.im, (1/A).re, (1/A).im}; 1/A = 0 where A ~ 0
+  // {A.re log2(e), A.im / (2 pi), (1/A).re, (1/A).im}; 1/A = 0 where A ~ 0
+  __shared__ float4 prm[CPB][NT];
   __shared__ float2 carry[CPB][NT];
 
   const int tid = threadIdx.x;
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const float m2 = a.x * a.x + a.y * a.y;
     const bool tiny = __builtin_fabsf(a.x) < 1e-30f && __builtin_fabsf(a.y) < 1e-30f;
     const float2 ia = tiny ? make_float2(0.0f, 0.0f) : make_float2(a.x / m2, -a.y / m2);
-    prm[ci][n] = make_float4(a.x, a.y, ia.x, ia.y);
+    prm[ci][n] = make_float4(a.x * kLog2e, a.y * kInv2Pi, ia.x, ia.y);
     const int64_t cc = b * p.dim + dd;
     carry[ci][n] = (real && p.h0) ? p.h0[cc * N + n] : make_float2(0.0f, 0.0f);
   }
@@ -117,27 +118,34 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
     for (int n = 0; n < N; ++n) {
       const float4 pr = prm[cl][n];
-      const float2 a = make_float2(pr.x, pr.y), ia = make_float2(pr.z, pr.w);
+      const float ar2 = pr.x, air = pr.y;
+      const float2 ia = make_float2(pr.z, pr.w);
       const bool tiny = ZOH && ia.x == 0.0f && ia.y == 0.0f;
       float bf[2 * K];
       tile_read<2 * K>(tile + n * RW, j, bf);   // steps past L were staged as 0
       float2 ab[K], beta[K];
-      float2 agg = make_float2(0.0f, 0.0f);
+      if (!ZOH || __builtin_amdgcn_ballot_w64(tiny) == 0) {
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const float mag = fast_exp2(dt[k] * a.x * kLog2e);
-        const float ang = dt[k] * a.y;
-        ab[k] = make_float2(mag * __cosf(ang), mag * __sinf(ang));
-        float2 e;
-        if (ZOH && !tiny) e = cmul(make_float2(ab[k].x - 1.0f, ab[k].y), ia);
-        else e = make_float2(dt[k], 0.0f);
-        beta[k] = cmul(e, make_float2(bf[2 * k] * uv[k], bf[2 * k + 1] * uv[k]));
-        agg = k == 0 ? beta[0] : cfma(ab[k], agg, beta[k]);
+        for (int k = 0; k < K; ++k) {
+          ab[k] = cexp_scaled(dt[k], ar2, air);
+          const float2 Bu = make_float2(bf[2 * k] * uv[k], bf[2 * k + 1] * uv[k]);
+          if constexpr (ZOH) beta[k] = cmul_minus_one(ab[k], cmul(ia, Bu));
+          else beta[k] = cscale(Bu, dt[k]);
+        }
+      } else {
+        // a channel of this wave has A ~ 0 (1/A stored as 0): delta B u there
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          ab[k] = cexp_scaled(dt[k], ar2, air);
+          const float2 Bu = make_float2(bf[2 * k] * uv[k], bf[2 * k + 1] * uv[k]);
+          beta[k] = tiny ? cscale(Bu, dt[k]) : cmul_minus_one(ab[k], cmul(ia, Bu));
+        }
       }
+      float2 agg = beta[0];
+#pragma unroll
+      for (int k = 1; k < K; ++k) agg = cfma(ab[k], agg, beta[k]);
       // the lane's decay: exp(A * sum of its steps)
-      const float lang = a.y * dsum;
-      const float lm = fast_exp2(a.x * dsum * kLog2e);
-      float2 Ag = make_float2(lm * __cosf(lang), lm * __sinf(lang));
+      float2 Ag = cexp_scaled(dsum, ar2, air);
       const float2 cin = carry[cl][n];
       if (j == 0) agg = cfma(Ag, cin, agg);    // the carried state enters lane 0
       cplx_scan_prefix_row(Ag, agg);
