@@ -208,28 +208,31 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       float pv[4], sv[4][4], Tq[4][2];
 #pragma unroll
       for (int k = K - 1; k >= 0; --k) {
-        const float2 Gk = cadd(cscale(cconj(Cv[k]), gy[k]), g);
+        const float2 Gk = make_float2(__builtin_fmaf(Cv[k].x, gy[k], g.x),
+                                      __builtin_fmaf(-Cv[k].y, gy[k], g.y));
+        const float2 gn = cmul(cconj(ab[k]), Gk);   // the adjoint passed to step t - 1
         const float2 hprev = (k == 0) ? hstart : hv[k - 1];
         const float2 Bu = cscale(Bv[k], uv[k]);
-        float2 e;
+        // s = conj(E) G with E = Bbar / B; du and dB both use it
+        float2 sG;
         if (ZOH && !tiny) {
-          e = cmul(make_float2(ab[k].x - 1.0f, ab[k].y), ia);
           const float2 W = cmul(ab[k], cfma(a, hprev, Bu));       // Abar (A h_{t-1} + B u)
-          gdt[k] += cdot(Gk, W);
+          gdt[k] = __builtin_fmaf(Gk.x, W.x, __builtin_fmaf(Gk.y, W.y, gdt[k]));
           const float2 q = make_float2(__builtin_fmaf(dt[k], W.x, -beta[k].x),
                                        __builtin_fmaf(dt[k], W.y, -beta[k].y));
           dAc = cfma(cconj(q), Gk, dAc);
+          // conj(E) G = conj(1/A) (conj(Abar) G - G)
+          sG = cmul(cconj(ia), make_float2(gn.x - Gk.x, gn.y - Gk.y));
         } else {
-          e = make_float2(dt[k], 0.0f);
           const float2 Ah = cmul(ab[k], hprev);
           const float2 dEdt = ZOH ? ab[k] : make_float2(1.0f, 0.0f);
           gdt[k] += cdot(Gk, cmul(a, Ah)) + cdot(Gk, cmul(dEdt, Bu));
           dAl = cfma(cconj(cscale(Ah, dt[k])), Gk, dAl);
           if (ZOH) dAl = cfma(cconj(cscale(Bu, 0.5f * dt[k] * dt[k])), Gk, dAl);
+          sG = cscale(Gk, dt[k]);                    // E = delta
         }
-        // Re(conj(G) E B) = Re(conj(s) B) with s = conj(E) G, which dB also uses
-        const float2 sG = cmul(cconj(e), Gk);
-        du[k] += cdot(sG, Bv[k]);
+        // Re(conj(G) E B) = Re(conj(s) B)
+        du[k] = __builtin_fmaf(sG.x, Bv[k].x, __builtin_fmaf(sG.y, Bv[k].y, du[k]));
         const float2 vB = cscale(sG, uv[k]);
         const float2 vC = cscale(cconj(hv[k]), gy[k]);
         const float v[4] = {vB.x, vB.y, vC.x, vC.y};
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             else if (k == 0) Tq[qq][0] = rs_pair32(sv[qq][0], sv[qq][1]);
           }
         }
-        g = cmul(cconj(ab[k]), Gk);
+        g = gn;
       }
       const int buf = (n / G) & 1;
 #pragma unroll
