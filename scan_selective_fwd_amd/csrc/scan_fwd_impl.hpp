@@ -61,6 +61,20 @@ template <int K>
 __device__ __forceinline__ bool load_keep(const uint8_t* __restrict__ row, int64_t tl, int64_t L,
                                           float (&keep)[K]) {
   bool any = false;
+  if (K % 8 == 0 && tl + K <= L && (reinterpret_cast<uintptr_t>(row + tl) & 7) == 0) {
+    // the lane's flags with 8-byte loads
+#pragma unroll
+    for (int i = 0; i < K / 8; ++i) {
+      const uint2 v = *reinterpret_cast<const uint2*>(row + tl + 8 * i);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool r = (((k < 4 ? v.x : v.y) >> (8 * (k & 3))) & 0xFFu) != 0u;
+        keep[8 * i + k] = r ? 0.0f : 1.0f;
+        any |= r;
+      }
+    }
+    return any;
+  }
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int64_t t = tl + k;
