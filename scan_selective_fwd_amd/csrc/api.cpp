@@ -20,6 +20,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int elem_size(mamba_dtype dt) { return dt == MAMBA_F32 ? 4 : 2; }
 
+// Whether rows of `seqlen` elements of `esize` bytes start 16-byte aligned
+// (the vector-load kernels need it), without forming seqlen * esize.
+bool rows_aligned16(int64_t seqlen, int esize) { return seqlen % (16 / esize) == 0; }
+
 size_t round_up(size_t x) { return (x + kAlignWs - 1) / kAlignWs * kAlignWs; }
 
 // Lanes per channel: enough waves to cover the 1024 SIMDs of the chip a few
@@ -46,7 +50,7 @@ mamba_status check_sizes(mamba_dtype dt, int disc, int64_t batch, int64_t dim, i
   if (batch > lim / dim) return MAMBA_ERR_UNSUPPORTED;
   const int64_t nch = batch * dim;
   if (nch > lim / seqlen || nch > lim / kMaxState) return MAMBA_ERR_UNSUPPORTED;
-  if (batch > lim / (dstate * seqlen)) return MAMBA_ERR_UNSUPPORTED;
+  if (seqlen > lim / dstate || batch > lim / (dstate * seqlen)) return MAMBA_ERR_UNSUPPORTED;
   // grid sizes must fit the 32-bit grid dimension
   if (nch / 4 + 1 > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
   return MAMBA_OK;
@@ -224,8 +228,8 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
   p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
   p.nseg = 1;
   p.seg_chunks = 0;
-  if (batch * p.groups * w.nseg > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
-  const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  if (batch * p.groups > (int64_t)0x7FFFFFFF / w.nseg) return MAMBA_ERR_UNSUPPORTED;
+  const bool vec = rows_aligned16(seqlen, elem_size(dt));
   const int dti = dt == MAMBA_F32 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (segmented) {
@@ -303,7 +307,7 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
 
   float* states = checkpoints ? const_cast<float*>(checkpoints) : static_cast<float*>(workspace);
   const size_t off_flags = checkpoints ? 0 : w.off_flags;
-  const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  const bool vec = rows_aligned16(seqlen, elem_size(dt));
   const int dti = dt == MAMBA_F32 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -435,7 +439,7 @@ mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const f
   p.groups = mscan::channel_groups(dim, 16);
   p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
   if (batch * p.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
-  const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  const bool vec = rows_aligned16(seqlen, elem_size(dt));
   return hip_status(mscan::dispatch_scan_fwd_complex(p, dt == MAMBA_F32 ? 0 : 1, (int)disc, vec,
                                                      static_cast<hipStream_t>(stream)));
 }
@@ -491,7 +495,7 @@ mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const f
   }
   const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
   if (batch * w.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
-  const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  const bool vec = rows_aligned16(seqlen, elem_size(dt));
   const int dti = dt == MAMBA_F32 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float2* states = checkpoints ? reinterpret_cast<float2*>(const_cast<float*>(checkpoints))
@@ -539,7 +543,7 @@ mamba_status mamba_conv1d_silu_fwd(const void* x, const float* w, const float* b
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.tiles = mscan::conv_tiles(seqlen); p.W = (int)width;
   if (p.nchannels * p.tiles > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
-  const bool vec = (seqlen * elem_size(dt)) % 16 == 0;
+  const bool vec = rows_aligned16(seqlen, elem_size(dt));
   return hip_status(mscan::dispatch_conv_fwd(p, dt == MAMBA_F32 ? 0 : 1, vec,
                                              static_cast<hipStream_t>(stream)));
 }
@@ -563,7 +567,7 @@ mamba_status mamba_conv1d_silu_bwd(const void* x, const float* w, const float* b
   p.tiles = mscan::conv_tiles(seqlen); p.W = (int)width;
   if (p.nchannels * p.tiles > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
   // vector loads need 16-byte rows for both x and the float32 du / dx
-  const bool vec = (seqlen * elem_size(dt)) % 16 == 0 && (seqlen * 4) % 16 == 0;
+  const bool vec = rows_aligned16(seqlen, elem_size(dt)) && rows_aligned16(seqlen, 4);
   return hip_status(mscan::dispatch_conv_bwd(p, dt == MAMBA_F32 ? 0 : 1, vec,
                                              static_cast<hipStream_t>(stream)));
 }

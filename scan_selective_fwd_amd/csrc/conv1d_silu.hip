@@ -24,8 +24,8 @@ namespace mscan {
 
 namespace {
 
-constexpr int kRun = 8;                    // steps per thread
-constexpr int kTile = kRun * 256;          // steps per block
+constexpr int kRun = kConvRun;             // steps per thread
+constexpr int kTile = kConvTile;           // steps per block
 constexpr int kTaps = 4;                   // taps held per thread (W <= 4)
 
 // Taps right-aligned to x_{t-3..t}: tap j multiplies x_{t-3+j}.
@@ -234,8 +234,6 @@ hipError_t conv_bwd_t(const ConvParams& p, bool vec, hipStream_t s) {
 }
 
 }  // namespace
-
-int64_t conv_tiles(int64_t L) { return (L + kTile - 1) / kTile; }
 
 hipError_t dispatch_conv_fwd(const ConvParams& p, int dtype, bool vec, hipStream_t s) {
   return dtype == 0 ? conv_fwd_t<float>(p, vec, s) : conv_fwd_t<bf16_t>(p, vec, s);

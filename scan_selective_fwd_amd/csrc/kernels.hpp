@@ -174,7 +174,11 @@ struct ConvParams {
   int64_t tiles;           // blocks per channel (conv_tiles(L))
   int W;                   // taps, 1..4
 };
-int64_t conv_tiles(int64_t L);
+// The convolution kernels give each thread kConvRun consecutive steps and
+// each 256-thread block kConvTile steps of one channel.
+constexpr int kConvRun = 8;
+constexpr int kConvTile = kConvRun * 256;
+inline int64_t conv_tiles(int64_t L) { return (L + kConvTile - 1) / kConvTile; }
 hipError_t dispatch_conv_fwd(const ConvParams& p, int dtype, bool vec, hipStream_t s);
 hipError_t dispatch_conv_bwd(const ConvParams& p, int dtype, bool vec, hipStream_t s);
 

@@ -399,3 +399,31 @@ def test_autograd_function_matches_bwd():
                  delta_bias="ddelta_bias")
     for k, gk in names.items():
         assert_match(to_f64(leaves[k].grad), ref[gk], 1e-4, gk)
+
+
+@pytest.mark.parametrize("split", [128, 333])
+def test_fwd_split_sequence_resumes_exactly(split):
+    """Splitting the sequence and carrying the final state as the initial
+    state of the rest gives the outputs of one pass (the chunk-boundary carry
+    is exact), and both match the oracle."""
+    wid, batch, dim, N, L = 81, 2, 20, 16, 900
+    announce(f"split-L wid={wid} shape=({batch},{dim},{N},{L}) split={split}")
+    inp, f = _make(wid, batch, dim, N, L, "f32")
+    t = to_device(inp, "f32")
+    full, last = ms.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                             t["delta_bias"], return_last_state=True)
+    part = lambda k, a, b: t[k][..., a:b].contiguous()
+    o1, l1 = ms.scan_fwd(part("u", 0, split), part("delta", 0, split), t["A"],
+                         part("B", 0, split), part("C", 0, split), t["D"], part("z", 0, split),
+                         t["delta_bias"], return_last_state=True)
+    o2, l2 = ms.scan_fwd(part("u", split, L), part("delta", split, L), t["A"],
+                         part("B", split, L), part("C", split, L), t["D"], part("z", split, L),
+                         t["delta_bias"], l1, return_last_state=True)
+    torch.cuda.synchronize()
+    ref, ref_last = _oracle_fwd(f, "zoh")
+    joined = torch.cat([o1, o2], dim=-1)
+    assert_match(to_f64(joined), ref, RTOL["f32"], "split out")
+    assert_match(to_f64(l2), ref_last, RTOL["f32"], "split last_state")
+    assert_match(to_f64(full), ref, RTOL["f32"], "full out")
+    # the two GPU runs agree more closely with each other than with the oracle
+    assert_match(to_f64(joined), to_f64(full), 1e-5, "split vs full")
