@@ -1,0 +1,85 @@
+"""HIP graph capture of the training step.  The library enqueues only kernels
+on the caller's stream (no memset, no allocation of its own when the caller
+passes the workspaces, no synchronization), so a forward that saves
+checkpoints, the backward from them and a decode step can be captured once
+with torch.cuda.graph and replayed.  Each replay follows eager work that
+overwrites the outputs and a synchronization, and is checked against the
+eager run (the forward bit for bit; the backward, whose reductions use float
+atomics, to rounding) and against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scan_selective_fwd_amd as ms
+import workloads as W
+from parity_utils import RTOL, announce, assert_match, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def test_captured_step_replays_match_eager_and_oracle():
+    wid, batch, dim, N, L = 82, 2, 20, 16, 700
+    announce(f"graph capture wid={wid} shape=({batch},{dim},{N},{L}) f32 zoh")
+    inp = W.make_inputs(wid, batch, dim, N, L, dtype="f32", bias="uniform", with_dout=True)
+    f = W.inputs_f64(inp, "f32")
+    t = to_device(inp, "f32")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = torch.empty((batch, dim, L), **f32)
+    state = torch.empty((batch, dim, N), **f32)      # final state, then one decode step
+    ckpt = torch.empty(ms.checkpoint_shape(batch, dim, N, L), **f32)
+    step_out = torch.empty((batch, dim), **f32)
+    nf = ms.fwd_workspace_bytes(batch, dim, N, L, torch.float32)
+    fws = torch.empty(nf, dtype=torch.uint8, device="cuda") if nf else None
+    bws = torch.empty(ms.bwd_workspace_bytes(batch, dim, N, L, torch.float32), dtype=torch.uint8,
+                      device="cuda")
+    step = {k: t[k][..., 0].contiguous() for k in ("u", "delta", "B", "C", "z")}
+
+    def run():
+        ms.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                    out=out, last_state=state, return_last_state=True, workspace=fws,
+                    checkpoints=ckpt)
+        grads = ms.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                            t["delta_bias"], t["dout"], workspace=bws, checkpoints=ckpt)
+        ms.state_update(state, step["u"], step["delta"], t["A"], step["B"], step["C"], t["D"],
+                        step["z"], t["delta_bias"], out=step_out)
+        return grads
+
+    eager_g = run()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in eager_g.items()}
+    eager_out, eager_state, eager_step = out.clone(), state.clone(), step_out.clone()
+
+    side = torch.cuda.Stream()            # warm-up on a side stream before capture
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graph_g = run()
+    torch.cuda.synchronize()
+
+    for r in range(3):
+        # eager work between replays: every output overwritten
+        for buf in (out, state, step_out, ckpt, *graph_g.values()):
+            buf.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), f"replay {r}: forward output differs"
+        assert torch.equal(state, eager_state), f"replay {r}: decode state differs"
+        assert torch.equal(step_out, eager_step), f"replay {r}: decode output differs"
+        assert set(graph_g) == set(eager)
+        for k in eager:
+            assert_match(to_f64(graph_g[k]), to_f64(eager[k]), 1e-5, f"replay {r} {k}")
+
+    ref_out, _ = oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                                 f["delta_bias"])
+    assert_match(to_f64(out), ref_out, RTOL["f32"], "graph out vs oracle")
+    ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                          f["delta_bias"], f["dout"])
+    for k in ref:
+        assert_match(to_f64(graph_g[k]), ref[k], RTOL["f32"], f"graph {k} vs oracle")
