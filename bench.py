@@ -19,7 +19,9 @@ that kernel when the kernel's sources are unchanged since it was taken.
 workload.  `per_call.<call>.cold` times each scan kernel again with the
 caches flushed before every launch (a 1 GiB buffer is written first, more
 than the L2s and the 256 MB last-level cache hold): median, p10 and p90 of
---cold-iters launches.
+--cold-iters launches.  `ms_per_step_graph` is the same step captured once
+into a HIP graph and replayed (context: the launch gaps between the calls
+removed; `value` stays the plain calls).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4|5]
                        [--disc zoh|euler] [--calls fwd,bwd,step] [--no-cpu-baseline]
@@ -268,6 +270,8 @@ def main():
     ap.add_argument("--cold-iters", type=int, default=50,
                     help="launches of each scan kernel timed with the caches flushed before "
                          "each (0: skip)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step replayed from a captured HIP graph")
     ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="CSV")
     args = ap.parse_args()
     if args.summarize_counters:
@@ -386,6 +390,33 @@ def main():
 
     copy_gbs = copy_bandwidth(torch)
 
+    # the same step captured once into a HIP graph and replayed K times (the
+    # launch gaps of K separate library calls removed); context beside `value`
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for c in calls:
+                run_call(c)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in calls:
+                run_call(c)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = new_event(), new_event()
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        del graph
+
     # cold-cache protocol: each scan kernel alone, a 1 GiB write before every
     # launch; the other calls' outputs stay as the timed steps left them
     cold = {}
@@ -428,6 +459,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
