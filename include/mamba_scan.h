@@ -219,6 +219,24 @@ mamba_status mamba_scan_fwd_complex(const void* u, const void* delta, const floa
                                     void* out, float* last_state, void* stream);
 
 /*
+ * One recurrent (decode) step of the complex-valued model, in place on the
+ * complex state (batch, dim, dstate) interleaved (re, im) float32 pairs: the
+ * body of mamba_scan_fwd_complex's step loop on a stored state (autoregressive
+ * generation; paper-graph-ui summary, section 3.4, recurrent mode).  u,
+ * delta, z, out are (batch, dim) float32 or bfloat16; A complex (dim,
+ * dstate); B, C complex (batch, dstate); D, delta_bias float32 (dim),
+ * nullable; dstate <= 16.  Continuing a forward's last_state with this call
+ * gives the outputs of a forward over the longer sequence.  Errors as for
+ * mamba_state_update.
+ */
+mamba_status mamba_state_update_complex(float* state, const void* u, const void* delta,
+                                        const float* A, const float* B, const float* C,
+                                        const float* D, const void* z, const float* delta_bias,
+                                        int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                                        int64_t batch, int64_t dim, int64_t dstate, void* out,
+                                        void* stream);
+
+/*
  * Backward of mamba_scan_fwd_complex for the loss sum(dout * out): the
  * states are recomputed chunkwise (one state per 128-step chunk is
  * recomputed into the workspace first).  The gradient of a complex input w

@@ -243,6 +243,35 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
     return out
 
 
+def state_update_complex(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
+                         delta_softplus=True, disc="zoh", out=None):
+    """One recurrent step of the complex-valued model; `state` (batch, dim, N)
+    complex64 is updated in place.  Per-step tensors: u, delta, z (batch,
+    dim) real; B, C (batch, N) complex64; A (dim, N) complex64.  Returns out."""
+    L_ = lib()
+    dev = state.device
+    batch, dim, N = state.shape
+    sdt = u.dtype
+    _req(state, "state", torch.complex64, (batch, dim, N), dev)
+    _req(u, "u", sdt, (batch, dim), dev)
+    _req(delta, "delta", sdt, (batch, dim), dev)
+    _req(A, "A", torch.complex64, (dim, N), dev)
+    _req(B, "B", torch.complex64, (batch, N), dev)
+    _req(C, "C", torch.complex64, (batch, N), dev)
+    _req(D, "D", torch.float32, (dim,), dev)
+    _req(z, "z", sdt, (batch, dim), dev)
+    _req(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    if out is None:
+        out = torch.empty((batch, dim), dtype=sdt, device=dev)
+    _req(out, "out", sdt, (batch, dim), dev)
+    st = L_.mamba_state_update_complex(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                       _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                       int(bool(delta_softplus)), _disc_code(disc),
+                                       _dtype_code(u), batch, dim, N, _ptr(out), _stream(dev))
+    _lib.check(st, "mamba_state_update_complex")
+    return out
+
+
 def complex_checkpoint_shape(batch, dim, N, L):
     """Shape of the complex forward's checkpoint buffer (complex64): the state
     entering every 128-step chunk."""

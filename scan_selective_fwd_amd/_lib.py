@@ -29,7 +29,7 @@ EXPORTS = (
     "mamba_scan_bwd_ex", "mamba_scan_checkpoint_size", "mamba_scan_fwd_complex",
     "mamba_scan_bwd_complex", "mamba_scan_bwd_complex_workspace_size",
     "mamba_scan_complex_checkpoint_size", "mamba_scan_fwd_complex_ex",
-    "mamba_scan_bwd_complex_ex",
+    "mamba_scan_bwd_complex_ex", "mamba_state_update_complex",
 )
 
 
@@ -105,6 +105,9 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_bwd_complex_ex.restype = _int
     lib.mamba_scan_bwd_complex_ex.argtypes = ([_vp] * 10 + [_int, _int, _int] + [_i64] * 4
                                               + [_vp] * 11 + [_sz, _vp])
+    lib.mamba_state_update_complex.restype = _int
+    lib.mamba_state_update_complex.argtypes = ([_vp] * 9 + [_int, _int, _int] + [_i64] * 3
+                                               + [_vp, _vp])
     lib.mamba_state_update.restype = _int
     lib.mamba_state_update.argtypes = [_vp] * 9 + [_int, _int, _int] + [_i64] * 3 + [_vp, _vp]
     _lib = lib

@@ -393,6 +393,31 @@ mamba_status mamba_state_update(float* state, const void* u, const void* delta, 
                                                  static_cast<hipStream_t>(stream)));
 }
 
+// ---- complex-valued decode step ----
+mamba_status mamba_state_update_complex(float* state, const void* u, const void* delta,
+                                        const float* A, const float* B, const float* C,
+                                        const float* D, const void* z, const float* delta_bias,
+                                        int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                                        int64_t batch, int64_t dim, int64_t dstate, void* out,
+                                        void* stream) {
+  mamba_status st = check_sizes(dt, disc, batch, dim, dstate, 1);
+  if (st != MAMBA_OK) return st;
+  if (dstate > 16) return MAMBA_ERR_UNSUPPORTED;
+  if (!state || !u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL_PTR;
+  const void* ptrs[] = {state, u, delta, A, B, C, D, z, delta_bias, out};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MAMBA_ERR_ALIGNMENT;
+  mscan::CplxStepParams p;
+  memset(&p, 0, sizeof(p));
+  p.state = reinterpret_cast<float2*>(state); p.u = u; p.delta = delta;
+  p.A = reinterpret_cast<const float2*>(A); p.B = reinterpret_cast<const float2*>(B);
+  p.C = reinterpret_cast<const float2*>(C); p.D = D; p.z = z; p.bias = delta_bias; p.out = out;
+  p.batch = batch; p.dim = dim; p.nchannels = batch * dim;
+  p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
+  return hip_status(mscan::dispatch_state_update_complex(p, dt == MAMBA_F32 ? 0 : 1, (int)disc,
+                                                         static_cast<hipStream_t>(stream)));
+}
+
 // ---- complex-valued forward ----
 size_t mamba_scan_complex_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate,
                                           int64_t seqlen) {

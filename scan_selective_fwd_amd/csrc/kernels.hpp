@@ -126,6 +126,27 @@ hipError_t dispatch_scan_fwd_complex(const CplxParams& p, int dtype, int disc, b
 hipError_t dispatch_chunk_states_complex(const CplxParams& p, int dtype, int disc, bool vec,
                                          hipStream_t s);
 
+// Complex-valued decode step (state_update_complex.hip): one recurrence step
+// on a complex state, in place.  B, C are (batch, N) complex, A (dim, N).
+struct CplxStepParams {
+  float2* state;           // (batch, dim, N)
+  const void* u;
+  const void* delta;
+  const float2* A;
+  const float2* B;
+  const float2* C;
+  const float* D;          // nullable
+  const void* z;           // nullable
+  const float* bias;       // nullable
+  void* out;
+  int64_t batch, dim;
+  int64_t nchannels;
+  int N;                   // <= 16
+  int softplus;
+};
+hipError_t dispatch_state_update_complex(const CplxStepParams& p, int dtype, int disc,
+                                         hipStream_t s);
+
 // Complex-valued backward (scan_bwd_complex.hip).
 struct CplxBwdParams {
   const void* u;

@@ -67,6 +67,8 @@ void sweep(int64_t b, int64_t d, int64_t n, int64_t l) {
     (void)bwd(b, d, n, l, dt, P, BIG, F, 16, P);
     (void)mamba_state_update(P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d, n, P,
                              nullptr);
+    (void)mamba_state_update_complex(P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d, n,
+                                     P, nullptr);
     (void)mamba_scan_fwd_complex_ex(P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d, n, l,
                                     P, P, P, nullptr);
     (void)mamba_scan_bwd_complex_ex(P, P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d, n,

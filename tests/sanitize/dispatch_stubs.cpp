@@ -78,5 +78,8 @@ STUB_BWD(dispatch_scan_bwd_reset_bf16_n16)
 STUB_BWD(dispatch_scan_bwd_reset_bf16_n64)
 #undef STUB_BWD
 hipError_t dispatch_state_update(const StepParams&, int, int, hipStream_t) { return reached(); }
+hipError_t dispatch_state_update_complex(const CplxStepParams&, int, int, hipStream_t) {
+  return reached();
+}
 
 }  // namespace mscan

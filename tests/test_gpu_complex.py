@@ -186,3 +186,42 @@ def test_complex_checkpoints_forward_states_and_backward(dtype):
             assert_match(_as_pairs(r), _as_pairs(ref[k]), RTOL[dtype], k)
         else:
             assert_match(r.astype(np.float64), ref[k], RTOL[dtype], k)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_complex_state_update_continues_forward(dtype, disc):
+    """A forward over L steps, then k decode steps from its final state,
+    gives the outputs and final state of the oracle's forward over L + k
+    steps (one decode step is the forward's step on a stored state)."""
+    wid, batch, dim, N, L, k = 83, 2, 21, 16, 300, 3
+    announce(f"complex state update wid={wid} shape=({batch},{dim},{N},{L}+{k}) {dtype} {disc}")
+    inp = W.make_complex_inputs(wid, batch, dim, N, L + k, dtype=dtype)
+    inp["A"][::4, 0] = 0.0                      # the ZOH limit delta B for these channels
+    t = {kk: _dev(v, dtype) for kk, v in inp.items()}
+    head = lambda name: t[name][..., :L].contiguous()
+    _, state = ms.scan_fwd_complex(head("u"), head("delta"), t["A"], head("B"), head("C"),
+                                   t.get("D"), head("z"), t.get("delta_bias"), disc=disc)
+    outs = []
+    for s in range(L, L + k):
+        col = lambda name: t[name][..., s].contiguous()
+        outs.append(ms.state_update_complex(state, col("u"), col("delta"), t["A"], col("B"),
+                                            col("C"), t.get("D"), col("z"), t.get("delta_bias"),
+                                            disc=disc))
+    torch.cuda.synchronize()
+    f = {kk: (W.as_f64(v, dtype) if v.dtype == np.uint16 else v) for kk, v in inp.items()}
+    ref, ref_last = oracle.scan_fwd_complex(
+        f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"), f.get("z"), f.get("delta_bias"),
+        None, disc=oracle.ZOH if disc == "zoh" else oracle.EULER)
+    got = np.stack([to_f64(o) for o in outs], -1)
+    assert_match(got, ref[..., L:], RTOL[dtype], "decode outputs")
+    assert_match(_as_pairs(state.cpu().numpy()), _as_pairs(ref_last), RTOL[dtype], "state")
+
+
+def test_complex_state_update_rejects_large_state():
+    st = torch.zeros((1, 4, 17), dtype=torch.complex64, device="cuda")
+    v = torch.zeros((1, 4), device="cuda")
+    A = torch.zeros((4, 17), dtype=torch.complex64, device="cuda")
+    BC = torch.zeros((1, 17), dtype=torch.complex64, device="cuda")
+    with pytest.raises(ms.MambaScanError):
+        ms.state_update_complex(st, v, v, A, BC, BC)
