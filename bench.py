@@ -44,11 +44,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
-# float32 vector peak without packed math: 256 CUs x 64 lanes x 2 flops (FMA)
-# x 2.4 GHz.  The chip's published 157.3 TFLOP/s counts packed FP32, which
-# these kernels do not use.
-PEAK_F32_TFLOPS = 78.6
-PEAK_F32_PACKED_TFLOPS = 157.3
+# float32 vector peak: the chip's published 157.3 TFLOP/s (256 CUs, 2.4 GHz).
+# Plain (non-packed) FMAs reach 119 TFLOP/s on the box (`bench.py --probe`:
+# one wave64 FMA per SIMD every ~2.2 cycles), so the published figure is the
+# honest ceiling for these kernels too, although they use no packed FP32.
+PEAK_F32_TFLOPS = 157.3
 # Algorithmic float32 work per (t, n) (an exp counts as one flop):
 #   forward : dA 1, exp 1, ZOH Bbar*u 4, h update 2, y accumulate 2       = 10
 #   backward: forward replay incl. y 10, adjoint 3, ddelta 6, dA 5, du 5,
@@ -239,6 +239,50 @@ def copy_bandwidth(torch, nbytes=COPY_BYTES, iters=10):
     return gbs
 
 
+PROBE_KINDS = {0: ("v_fma_f32", 2), 1: ("v_exp_f32", 1), 2: ("v_mul_f32", 1), 3: ("v_rcp_f32", 1),
+               4: ("v_fma_f32 1 chain", 2), 5: ("v_fma_f32 2 chains", 2)}
+
+
+def probe_rates(torch, blocks=8192, iters=2048):
+    """Issue rates of single VALU instruction kinds on this GPU (8 independent
+    chains per thread, a grid of many waves), from the probe library built
+    next to the scan library.  Returns {name: {"G_per_s": lane-instructions per
+    second, "vs_fma": rate / FMA rate}} plus the FMA rate in TFLOP/s."""
+    import ctypes
+    path = os.path.join(ROOT, "scan_selective_fwd_amd", "libmscan_probe.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build the library first")
+    lib = ctypes.CDLL(path)
+    lib.mscan_probe_valu.restype = ctypes.c_int
+    lib.mscan_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for kind, (name, flops) in PROBE_KINDS.items():
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)   # creates the events; the probe records them again
+            e1.record(stream)
+            st = lib.mscan_probe_valu(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                      ctypes.c_void_p(stream.cuda_stream),
+                                      ctypes.c_void_p(e0.cuda_event), ctypes.c_void_p(e1.cuda_event))
+            if st != 0:
+                raise RuntimeError(f"mscan_probe_valu({kind}) failed: {st}")
+            torch.cuda.synchronize()
+            ms_ = e0.elapsed_time(e1)
+            best = ms_ if best is None else min(best, ms_)
+        n = blocks * 256 * iters * 8
+        res[name] = {"G_per_s": round(n / (best * 1e-3) / 1e9, 1), "ms": round(best, 4),
+                     "instructions": n}
+    fma = res["v_fma_f32"]["G_per_s"]
+    for v in res.values():
+        v["vs_fma"] = round(v["G_per_s"] / fma, 3)
+    res["fma_TFLOP_s"] = round(2 * fma / 1e3, 2)
+    return res
+
+
 def copy_calibration(torch):
     """A plain device copy of known size, so that counter runs over this
     process can scale FETCH_SIZE / WRITE_SIZE to bytes."""
@@ -270,6 +314,9 @@ def main():
     ap.add_argument("--cold-iters", type=int, default=50,
                     help="launches of each scan kernel timed with the caches flushed before "
                          "each (0: skip)")
+    ap.add_argument("--probe", action="store_true",
+                    help="print the measured VALU issue rates (FMA, exp, mul, rcp) and the "
+                         "streaming-copy rate as one JSON line instead of the benchmark")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the step replayed from a captured HIP graph")
     ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="CSV")
@@ -286,6 +333,15 @@ def main():
     import torch
     import scan_selective_fwd_amd as ms
     import workloads as W
+
+    if args.probe:
+        # 8192 blocks: many waves per SIMD; 768 blocks: 3 waves per SIMD (the
+        # scan kernels' occupancy)
+        print(json.dumps({"probe": "valu issue rates and streaming copy, one GPU",
+                          "valu_8192_blocks": probe_rates(torch, blocks=8192),
+                          "valu_768_blocks": probe_rates(torch, blocks=768, iters=8192),
+                          "stream_copy_GBs": round(copy_bandwidth(torch), 1)}), flush=True)
+        return
 
     w = W.WORKLOADS[args.workload]
     calls = {2: ["fwd", "bwd", "step"], 3: ["fwd"], 4: ["fwd"], 5: ["bwd"]}[w.wid]
@@ -479,9 +535,9 @@ def main():
         "per_call": per_call,
     }
     if kern_ms:
-        # The scan kernels are bound by float32 vector arithmetic (their VALU
-        # issue rate is the limit; HBM runs far below its peak), so the roofline
-        # is the ALU one; the HBM view of the same launch is reported beside it.
+        # The scan kernels are bound by float32 vector arithmetic, not by HBM
+        # (which runs far below its peak): the roofline is the ALU one, and the
+        # HBM view of the same launch is reported beside it.
         dom = max(kern_ms, key=lambda c: kern_ms[c])
         kname = kernel_names[dom]
         dom_bytes = algorithmic_bytes(w, dom)
@@ -496,7 +552,6 @@ def main():
                            "kernel": kname, "call": f"mamba_scan_{dom}",
                            "algorithmic_flops_per_launch": int(dom_flops),
                            "flops_per_state_step": FLOPS_PER_TN[dom],
-                           "peak_with_packed_fp32": PEAK_F32_PACKED_TFLOPS,
                            "hbm": {"achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS,
                                    "frac": round(gbs / PEAK_HBM_GBS, 4),
                                    "algorithmic_bytes_per_launch": int(dom_bytes)},
