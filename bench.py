@@ -283,6 +283,62 @@ def probe_rates(torch, blocks=8192, iters=2048):
     return res
 
 
+# The pages' scan benchmark shape (batch 1, D 1024, N 16, bf16; sequence
+# lengths 2^9 .. 2^19) and the times they read for the fused scan on an A100
+# (paper-graph-ui summary, "Speed and Memory Benchmarks", Figure 8 left;
+# context only: other hardware, and the page does not say whether forward or
+# forward + backward).
+SWEEP_PAGES_MS = {32768: 2.0, 131072: 10.0}
+
+
+def sweep(torch, ms_lib, W, steps=10):
+    """Forward (and backward up to 2^14 steps) time over the sequence
+    lengths of the pages' scan benchmark, inputs drawn like workload 1."""
+    rows = []
+    for e in range(9, 20):
+        L = 1 << e
+        inp = W.make_inputs(9, 1, 1024, 16, L, dtype="bf16", bias="const", with_dout=e <= 14)
+        g = {}
+        for k, v in inp.items():
+            if k in ("u", "delta", "B", "C", "z", "dout"):
+                g[k] = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(
+                    torch.bfloat16).cuda()
+            else:
+                g[k] = torch.from_numpy(np.ascontiguousarray(v)).cuda()
+        nfws = ms_lib.fwd_workspace_bytes(1, 1024, 16, L, torch.bfloat16)
+        fws = torch.empty(nfws, dtype=torch.uint8, device="cuda") if nfws else None
+        out = torch.empty_like(g["u"])
+
+        def fwd():
+            ms_lib.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                            g["delta_bias"], out=out, workspace=fws)
+
+        def bwd():
+            ms_lib.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                            g["delta_bias"], g["dout"])
+
+        row = {"L": L}
+        for name, fn in (("fwd", fwd), ("bwd", bwd)):
+            if name == "bwd" and "dout" not in g:
+                continue
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / steps
+            row[f"{name}_ms"] = round(t, 4)
+            row[f"{name}_channel_tokens_per_s"] = round(1024 * L / (t * 1e-3), 1)
+        if L in SWEEP_PAGES_MS:
+            row["pages_a100_ms"] = SWEEP_PAGES_MS[L]
+        rows.append(row)
+        del g, out, fws
+    return rows
+
+
 def copy_calibration(torch):
     """A plain device copy of known size, so that counter runs over this
     process can scale FETCH_SIZE / WRITE_SIZE to bytes."""
@@ -314,6 +370,9 @@ def main():
     ap.add_argument("--cold-iters", type=int, default=50,
                     help="launches of each scan kernel timed with the caches flushed before "
                          "each (0: skip)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the forward (and short backward) over sequence lengths 2^9..2^19 "
+                         "at the pages' scan benchmark shape; one JSON line")
     ap.add_argument("--probe", action="store_true",
                     help="print the measured VALU issue rates (FMA, exp, mul, rcp) and the "
                          "streaming-copy rate as one JSON line instead of the benchmark")
@@ -334,6 +393,11 @@ def main():
     import scan_selective_fwd_amd as ms
     import workloads as W
 
+    if args.sweep:
+        print(json.dumps({"sweep": "the pages' scan benchmark shape: batch 1, D 1024, N 16, "
+                                   "bf16 inputs, ZOH, softplus, D and z",
+                          "rows": sweep(torch, ms, W)}), flush=True)
+        return
     if args.probe:
         # 8192 blocks: many waves per SIMD; 768 blocks: 3 waves per SIMD (the
         # scan kernels' occupancy)

@@ -70,7 +70,9 @@ int64_t auto_segments(int64_t batch, int64_t dim, int64_t seqlen) {
   int64_t nseg = (3072 + blocks - 1) / blocks;
   const int64_t cap = nchunks / 16;   // segments of at least 16 chunks
   if (nseg > cap) nseg = cap;
-  return nseg < 1 ? 1 : nseg;
+  // fewer than 4 segments gain less parallelism than the summary pass (about
+  // 0.7 of an output pass) and the two extra launches cost
+  return nseg < 4 ? 1 : nseg;
 }
 
 // Forward workspace (segmented only): the segment end states and the
