@@ -292,12 +292,13 @@ SWEEP_PAGES_MS = {32768: 2.0, 131072: 10.0}
 
 
 def sweep(torch, ms_lib, W, steps=10):
-    """Forward (and backward up to 2^14 steps) time over the sequence
-    lengths of the pages' scan benchmark, inputs drawn like workload 1."""
+    """Forward and backward time over the sequence lengths of the pages'
+    scan benchmark, inputs drawn like workload 1; each call with its default
+    (automatic) sequence segmentation."""
     rows = []
     for e in range(9, 20):
         L = 1 << e
-        inp = W.make_inputs(9, 1, 1024, 16, L, dtype="bf16", bias="const", with_dout=e <= 14)
+        inp = W.make_inputs(9, 1, 1024, 16, L, dtype="bf16", bias="const", with_dout=True)
         g = {}
         for k, v in inp.items():
             if k in ("u", "delta", "B", "C", "z", "dout"):
@@ -313,14 +314,15 @@ def sweep(torch, ms_lib, W, steps=10):
             ms_lib.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
                             g["delta_bias"], out=out, workspace=fws)
 
+        nbws = ms_lib.bwd_workspace_bytes(1, 1024, 16, L, torch.bfloat16)
+        bws = torch.empty(nbws, dtype=torch.uint8, device="cuda")
+
         def bwd():
             ms_lib.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
-                            g["delta_bias"], g["dout"])
+                            g["delta_bias"], g["dout"], workspace=bws)
 
         row = {"L": L}
         for name, fn in (("fwd", fwd), ("bwd", bwd)):
-            if name == "bwd" and "dout" not in g:
-                continue
             fn()
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -335,7 +337,7 @@ def sweep(torch, ms_lib, W, steps=10):
         if L in SWEEP_PAGES_MS:
             row["pages_a100_ms"] = SWEEP_PAGES_MS[L]
         rows.append(row)
-        del g, out, fws
+        del g, out, fws, bws
     return rows
 
 
@@ -371,7 +373,7 @@ def main():
                     help="launches of each scan kernel timed with the caches flushed before "
                          "each (0: skip)")
     ap.add_argument("--sweep", action="store_true",
-                    help="time the forward (and short backward) over sequence lengths 2^9..2^19 "
+                    help="time the forward and backward over sequence lengths 2^9..2^19 "
                          "at the pages' scan benchmark shape; one JSON line")
     ap.add_argument("--probe", action="store_true",
                     help="print the measured VALU issue rates (FMA, exp, mul, rcp) and the "

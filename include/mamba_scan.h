@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 1
+#define MAMBA_SCAN_ABI_VERSION 2
 
 typedef enum {
   MAMBA_OK = 0,
@@ -102,9 +102,10 @@ const char* mamba_status_string(mamba_status status);
 
 /* Bytes of device workspace mamba_scan_fwd needs for these sizes (may be 0;
  * then workspace may be NULL).  Returns SIZE_MAX for unsupported sizes.
- * It is non-zero when the sequence is long and the channels alone would give
- * too few workgroups to fill the GPU: the forward then splits the sequence
- * into segments that run in parallel, joined by an exact carry of the state
+ * It is non-zero when the sequence spans at least 8 chunks of 128 steps and
+ * the channels alone give at most 256 workgroups of 16 channels (batch *
+ * ceil(dim/16) <= 256), too few to fill the GPU: the forward then splits the
+ * sequence into segments that run in parallel, joined by an exact carry of the state
  * (the associative scan composition of trishampatil essay, Part III §2, with
  * the chunking of its Part III §4).  The workspace holds, per channel and
  * segment, the segment's end state, its entering state (float32, dstate
@@ -113,7 +114,17 @@ const char* mamba_status_string(mamba_status status);
 size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                      mamba_dtype dt);
 
-/* Bytes of device workspace mamba_scan_bwd needs (SIZE_MAX if unsupported). */
+/* Bytes of device workspace mamba_scan_bwd needs (SIZE_MAX if unsupported).
+ * It holds the state entering every 128-step chunk (batch, dim,
+ * ceil(seqlen/128), dstate) float32 and one int per workgroup.  When the
+ * channels alone give at most 512 workgroups of 16 channels (batch *
+ * ceil(dim/16) <= 512) the backward splits the sequence into segments run in
+ * parallel (the reverse adjoint scan composes over segments like the state,
+ * trishampatil essay, Part III §2), and the workspace adds per channel and
+ * segment the state-pass buffers of the forward's segmentation and the
+ * adjoint's (its value at the segment start from a zero end, the value
+ * entering it, the delta sum).  mamba_scan_bwd given only the unsegmented
+ * size runs in one pass over the sequence (slower for such shapes). */
 size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                      mamba_dtype dt);
 
@@ -300,12 +311,15 @@ mamba_status mamba_conv1d_silu_bwd(const void* x, const float* w, const float* b
  *    use; the backward accepts 0 and 16 only).  The result does not depend on
  *    the choice beyond float32 rounding order; tests and launch-shape sweeps
  *    use it.  mamba_scan_bwd_ex needs the workspace reported by
- *    mamba_scan_bwd_workspace_size_ex for the same lanes value.
- *  - segments (forward only): 0 = automatic (as mamba_scan_fwd), 1 = one pass
- *    over the sequence, k >= 2 = split the sequence into k segments (at most
- *    one per 128-step chunk).  Segmented runs need the workspace reported by
- *    mamba_scan_fwd_workspace_size_ex for the same lanes and segments values
- *    (MAMBA_ERR_WORKSPACE otherwise) and 16 lanes per channel.
+ *    mamba_scan_bwd_workspace_size_ex for the same lanes and segments values.
+ *  - segments: 0 = automatic (as mamba_scan_fwd / mamba_scan_bwd), 1 = one
+ *    pass over the sequence, k >= 2 = split the sequence into k segments of
+ *    whole 128-step chunks (fewer when there are fewer chunks, or when k does
+ *    not divide them evenly).  Segmented runs need the workspace reported by
+ *    mamba_scan_fwd_workspace_size_ex / mamba_scan_bwd_workspace_size_ex for
+ *    the same lanes and segments values (MAMBA_ERR_WORKSPACE otherwise) and
+ *    16 lanes per channel; a segments value below 0 is
+ *    MAMBA_ERR_UNSUPPORTED.
  *  - checkpoints (forward: float* output, backward: const float* input;
  *    NULL = none): the state entering every 128-step chunk, (batch, dim,
  *    ceil(seqlen/128), dstate) float32, mamba_scan_checkpoint_size bytes.
@@ -341,7 +355,8 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
                                void* timing_end);
 
 size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
-                                        int64_t seqlen, mamba_dtype dt, int lanes_per_channel);
+                                        int64_t seqlen, mamba_dtype dt, int lanes_per_channel,
+                                        int segments);
 
 mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
                                const void* C, const float* D, const void* z,
@@ -351,7 +366,7 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
                                int64_t seqlen, float* du, float* ddelta, float* dA, float* dB,
                                float* dC, float* dD, float* dz, float* ddelta_bias, float* dh0,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel, const float* checkpoints,
+                               int lanes_per_channel, int segments, const float* checkpoints,
                                void* timing_begin, void* timing_end);
 
 /* Bytes of the checkpoint buffer of the _ex calls (SIZE_MAX for unsupported

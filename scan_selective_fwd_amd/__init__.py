@@ -159,9 +159,9 @@ def fwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0, segments
     return int(n)
 
 
-def bwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0) -> int:
+def bwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0, segments=0) -> int:
     code = F32 if dtype == torch.float32 else BF16
-    n = lib().mamba_scan_bwd_workspace_size_ex(batch, dim, N, L, code, int(lanes))
+    n = lib().mamba_scan_bwd_workspace_size_ex(batch, dim, N, L, code, int(lanes), int(segments))
     if n >= 2 ** 63:
         raise MambaScanError(6, "mamba_scan_bwd_workspace_size")
     return int(n)
@@ -169,11 +169,12 @@ def bwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0) -> int:
 
 def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softplus=True,
              disc="zoh", lanes=0, workspace=None, want_dh0=True, timing=None, reset=None,
-             checkpoints=None):
+             checkpoints=None, segments=0):
     """Backward with state recomputation.  Returns a dict of float32 gradients:
     du, ddelta, dA, dB, dC and, when the input is given, dD, dz, ddelta_bias, dh0.
     `timing`: optional (begin, end) torch.cuda.Event pair recorded around the
-    reverse-scan kernel on the current stream."""
+    reverse-scan kernel on the current stream.  `segments`: 0 = automatic, 1 =
+    one pass, k = k sequence segments run in parallel."""
     L_ = lib()
     dev = u.device
     batch, dim, L = u.shape
@@ -202,7 +203,7 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
         g["ddelta_bias"] = torch.empty((dim,), **f32)
     if h0 is not None and want_dh0:
         g["dh0"] = torch.empty((batch, dim, N), **f32)
-    nbytes = bwd_workspace_bytes(batch, dim, N, L, sdt, lanes)
+    nbytes = bwd_workspace_bytes(batch, dim, N, L, sdt, lanes, segments)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     st = L_.mamba_scan_bwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -212,7 +213,8 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
                               _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
                               _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
                               _ptr(g.get("dh0")), workspace.data_ptr(), workspace.numel(),
-                              _stream(dev), int(lanes), _ptr(checkpoints), *_events(timing))
+                              _stream(dev), int(lanes), int(segments), _ptr(checkpoints),
+                              *_events(timing))
     _lib.check(st, "mamba_scan_bwd")
     return g
 

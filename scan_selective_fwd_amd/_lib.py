@@ -18,6 +18,8 @@ STATUS = {
 }
 F32, BF16 = 0, 1
 ZOH, EULER = 0, 1
+# MAMBA_SCAN_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 2
 
 # Every symbol the header declares.
 EXPORTS = (
@@ -59,6 +61,11 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     lib.mamba_abi_version.restype = _int
     lib.mamba_abi_version.argtypes = []
+    found = lib.mamba_abi_version()
+    if found != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {found}, these bindings need {ABI_VERSION}: "
+                          f"rebuild it")
+    lib.mamba_abi_version.argtypes = []
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [_int]
     for name in ("mamba_scan_fwd_workspace_size", "mamba_scan_bwd_workspace_size"):
@@ -68,7 +75,7 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_fwd_workspace_size_ex.restype = _sz
     lib.mamba_scan_fwd_workspace_size_ex.argtypes = [_i64, _i64, _i64, _i64, _int, _int, _int]
     lib.mamba_scan_bwd_workspace_size_ex.restype = _sz
-    lib.mamba_scan_bwd_workspace_size_ex.argtypes = [_i64, _i64, _i64, _i64, _int, _int]
+    lib.mamba_scan_bwd_workspace_size_ex.argtypes = [_i64, _i64, _i64, _i64, _int, _int, _int]
     fwd_args = [_vp] * 9 + [_int, _int, _int] + [_i64] * 4 + [_vp, _vp, _vp, _sz, _vp]
     lib.mamba_scan_fwd.restype = _int
     lib.mamba_scan_fwd.argtypes = fwd_args
@@ -84,7 +91,7 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_bwd_varlen.restype = _int
     lib.mamba_scan_bwd_varlen.argtypes = bwd_rst
     lib.mamba_scan_bwd_ex.restype = _int
-    lib.mamba_scan_bwd_ex.argtypes = bwd_rst + [_int, _vp, _vp, _vp]
+    lib.mamba_scan_bwd_ex.argtypes = bwd_rst + [_int, _int, _vp, _vp, _vp]
     lib.mamba_scan_checkpoint_size.restype = _sz
     lib.mamba_scan_checkpoint_size.argtypes = [_i64] * 4
     lib.mamba_conv1d_silu_fwd.restype = _int

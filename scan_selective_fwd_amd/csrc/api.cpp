@@ -56,23 +56,49 @@ mamba_status check_sizes(mamba_dtype dt, int disc, int64_t batch, int64_t dim, i
   return MAMBA_OK;
 }
 
-// Forward segmentation.  When a sequence is long and its channels alone give
-// too few blocks to fill the chip, the sequence is split into segments run in
-// parallel: a summary launch (each segment's end state from zero and its
-// delta sum), a carry launch (the state entering each segment) and the
-// output launch.  Segments are whole chunks of 16 lanes x kItems steps.
+// Sequence segmentation.  When a sequence is long and its channels alone give
+// too few workgroups to fill the chip, the sequence is split into segments run
+// in parallel.  Forward: a summary launch (each segment's end state from zero
+// and its delta sum), a carry launch (the state entering each segment) and the
+// output launch.  Backward: the same for the chunk-start states, then the
+// adjoint's summary and reverse carry, then the backward kernel per segment.
+// Segments are whole chunks of 16 lanes x kItems steps.
 constexpr int64_t kFwdChunk = 16 * kItems;
 
+// Segment count for `blocks` workgroups (16 channels each) over `nchunks`
+// chunks: none above `max_blocks`; else the power of two that gives about
+// 2048 workgroups (a power of two splits power-of-two chunk counts evenly:
+// uneven splits measured slower), at most one segment per chunk, and none
+// when that leaves fewer than `min_seg`.
+int64_t split_segments(int64_t blocks, int64_t nchunks, int64_t max_blocks, int64_t min_seg) {
+  if (blocks > max_blocks) return 1;
+  const int64_t want = (2048 + blocks - 1) / blocks;
+  int64_t nseg = 1;
+  while (nseg < want) nseg *= 2;
+  if (nseg > nchunks) nseg = nchunks;
+  return nseg < min_seg ? 1 : nseg;
+}
+
+// Timings on MI355X (batch 1, N = 16, bf16, ZOH) behind the two choices.
+// Forward: with 64 workgroups, 4096 steps take 0.104 ms in one pass and 0.065
+// ms in 16 segments, 131072 steps 5.0 ms and 1.39 ms in 64; with 256
+// workgroups 16384 steps take 1.19 ms and 0.70 ms in 32; with 512 workgroups
+// every split is slower (4096 steps: 0.27 ms, 0.35 ms in 8), the summary pass
+// re-reading about half of what the output pass reads; 2 segments never gain,
+// and sequences of 4 chunks lose in 4 (0.019 ms, 0.025 ms) and break even in 8.
 int64_t auto_segments(int64_t batch, int64_t dim, int64_t seqlen) {
   const int64_t blocks = batch * mscan::channel_groups(dim, 16);
-  if (blocks >= 1024) return 1;
-  const int64_t nchunks = (seqlen + kFwdChunk - 1) / kFwdChunk;
-  int64_t nseg = (3072 + blocks - 1) / blocks;
-  const int64_t cap = nchunks / 16;   // segments of at least 16 chunks
-  if (nseg > cap) nseg = cap;
-  // fewer than 4 segments gain less parallelism than the summary pass (about
-  // 0.7 of an output pass) and the two extra launches cost
-  return nseg < 4 ? 1 : nseg;
+  return split_segments(blocks, (seqlen + kFwdChunk - 1) / kFwdChunk, 256, 8);
+}
+
+// Backward: heavier per chunk, so its extra passes cost relatively less.  With
+// 64 workgroups 32768 steps take 5.8 ms in one pass and 1.14 ms in 32
+// segments (2 segments: 4.1 ms); with 384 workgroups 4096 steps take 1.07 ms
+// and 0.83 ms in 8; with 512, 1.18 ms and 1.09 ms; with 640 (and more) a split
+// is slower (2048 steps: 0.66 ms, 0.70 ms in 4 or 8).
+int64_t bwd_auto_segments(int64_t batch, int64_t dim, int64_t seqlen) {
+  const int64_t blocks = batch * mscan::channel_groups(dim, mscan::kBwdLanes);
+  return split_segments(blocks, (seqlen + kFwdChunk - 1) / kFwdChunk, 512, 2);
 }
 
 // Forward workspace (segmented only): the segment end states and the
@@ -102,20 +128,66 @@ FwdLayout fwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
 }
 
 // Backward workspace: the chunk-start states (nchannels, nchunks, dstate)
-// float32, then one int flag per block.
+// float32, then one int flag per block, then (segmented runs only) the
+// forward's segment buffers (end states from zero, entering states,
+// (nchannels, nseg, dstate) each; delta sums and reset-free factors,
+// (nchannels, nseg) each) and the same four for the adjoint (summaries from
+// a zero end, entering adjoints, delta sums, factors).  Segments are whole
+// 128-step chunks, as in the forward, with a choice of their own
+// (bwd_auto_segments).
 struct BwdLayout {
-  int64_t nchunks, groups;
-  size_t off_flags, total;
+  int64_t nchunks, groups, nseg, seg_chunks;
+  size_t off_flags, off_seg, total;
 };
 
-BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                     int64_t segments = 1) {
   BwdLayout w;
   const int64_t tch = (int64_t)mscan::kBwdLanes * kItemsBwd;
+  static_assert(mscan::kBwdLanes * kItemsBwd == kFwdChunk, "forward and backward chunks agree");
   w.nchunks = (seqlen + tch - 1) / tch;
   w.groups = mscan::channel_groups(dim, mscan::kBwdLanes);
+  w.nseg = 1;
+  w.seg_chunks = 0;
+  const int64_t want = segments < w.nchunks ? segments : w.nchunks;
+  if (want > 1) {
+    const int64_t sc = (w.nchunks + want - 1) / want;
+    const int64_t ns = (w.nchunks + sc - 1) / sc;
+    if (ns > 1) {
+      w.nseg = ns;
+      w.seg_chunks = sc;
+    }
+  }
   w.off_flags = round_up((size_t)(batch * dim) * (size_t)w.nchunks * (size_t)dstate * 4);
-  w.total = w.off_flags + round_up((size_t)(batch * w.groups) * 4);
+  w.off_seg = w.off_flags + round_up((size_t)(batch * w.groups) * (size_t)w.nseg * 4);
+  w.total = w.off_seg;
+  if (w.nseg > 1) {
+    const size_t nst = round_up((size_t)(batch * dim) * (size_t)w.nseg * (size_t)dstate * 4);
+    const size_t nsc = round_up((size_t)(batch * dim) * (size_t)w.nseg * 4);
+    w.total += 4 * nst + 4 * nsc;
+  }
   return w;
+}
+
+// The segment buffers of a segmented backward, from `q` (offset w.off_seg of
+// the layout).
+struct BwdSegBuffers {
+  float *h_end, *h_in, *dsum, *keep, *g_loc, *g_in, *g_dsum, *g_keep;
+};
+
+BwdSegBuffers bwd_seg_buffers(const BwdLayout& w, int64_t nchannels, int64_t dstate, char* q) {
+  const size_t nst = round_up((size_t)nchannels * (size_t)w.nseg * (size_t)dstate * 4);
+  const size_t nsc = round_up((size_t)nchannels * (size_t)w.nseg * 4);
+  BwdSegBuffers s;
+  s.h_end = reinterpret_cast<float*>(q);
+  s.h_in = reinterpret_cast<float*>(q + nst);
+  s.g_loc = reinterpret_cast<float*>(q + 2 * nst);
+  s.g_in = reinterpret_cast<float*>(q + 3 * nst);
+  s.dsum = reinterpret_cast<float*>(q + 4 * nst);
+  s.keep = reinterpret_cast<float*>(q + 4 * nst + nsc);
+  s.g_dsum = reinterpret_cast<float*>(q + 4 * nst + 2 * nsc);
+  s.g_keep = reinterpret_cast<float*>(q + 4 * nst + 3 * nsc);
+  return s;
 }
 
 inline mamba_status hip_status(hipError_t e) { return e == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP; }
@@ -160,13 +232,16 @@ size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
   return mamba_scan_fwd_workspace_size_ex(batch, dim, dstate, seqlen, dt, 0, 0);
 }
 
-// Workspace of mamba_scan_bwd_ex for a lanes-per-channel choice.  The
-// backward always spreads a channel over 16 lanes: 0 and 16 are accepted.
+// Workspace of mamba_scan_bwd_ex for a lanes-per-channel and segments
+// choice.  The backward always spreads a channel over 16 lanes: 0 and 16 are
+// accepted.
 size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                                        mamba_dtype dt, int lanes_per_channel) {
+                                        mamba_dtype dt, int lanes_per_channel, int segments) {
   if (check_sizes(dt, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK) return SIZE_MAX;
   if (lanes_per_channel != 0 && lanes_per_channel != mscan::kBwdLanes) return SIZE_MAX;
-  return bwd_layout(batch, dim, dstate, seqlen).total;
+  if (segments < 0) return SIZE_MAX;
+  const int64_t want = segments != 0 ? segments : bwd_auto_segments(batch, dim, seqlen);
+  return bwd_layout(batch, dim, dstate, seqlen, want).total;
 }
 
 size_t mamba_scan_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
@@ -178,7 +253,7 @@ size_t mamba_scan_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate, in
 
 size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                      mamba_dtype dt) {
-  return mamba_scan_bwd_workspace_size_ex(batch, dim, dstate, seqlen, dt, 0);
+  return mamba_scan_bwd_workspace_size_ex(batch, dim, dstate, seqlen, dt, 0, 0);
 }
 
 // Same as mamba_scan_fwd with an explicit lanes-per-channel choice (16, 32 or
@@ -286,7 +361,7 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
                                int64_t seqlen, float* du, float* ddelta, float* dA, float* dB,
                                float* dC, float* dD, float* dz, float* ddelta_bias, float* dh0,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               int lanes_per_channel, const float* checkpoints,
+                               int lanes_per_channel, int segments, const float* checkpoints,
                                void* timing_begin, void* timing_end) {
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
   if (st != MAMBA_OK) return st;
@@ -301,14 +376,26 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
     if (p && !aligned16(p)) return MAMBA_ERR_ALIGNMENT;
   if (lanes_per_channel != 0 && lanes_per_channel != mscan::kBwdLanes) return MAMBA_ERR_UNSUPPORTED;
   const int lanes = mscan::kBwdLanes;
-  const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
-  // with checkpoints from the forward only the flags live in the workspace
-  const size_t need = checkpoints ? w.total - w.off_flags : w.total;
+  if (segments < 0) return MAMBA_ERR_UNSUPPORTED;
+  const int64_t want = segments != 0 ? segments : bwd_auto_segments(batch, dim, seqlen);
+  BwdLayout w = bwd_layout(batch, dim, dstate, seqlen, want);
+  // with checkpoints from the forward only the part past the states is used
+  size_t need = checkpoints ? w.total - w.off_flags : w.total;
+  if (w.nseg > 1 && (!workspace || workspace_bytes < need)) {
+    if (segments != 0) return MAMBA_ERR_WORKSPACE;
+    w = bwd_layout(batch, dim, dstate, seqlen);   // automatic choice without the room: one pass
+    need = checkpoints ? w.total - w.off_flags : w.total;
+  }
   if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
-  if (batch * w.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
+  if (batch * w.groups > (int64_t)0x7FFFFFFF / w.nseg) return MAMBA_ERR_UNSUPPORTED;
 
   float* states = checkpoints ? const_cast<float*>(checkpoints) : static_cast<float*>(workspace);
-  const size_t off_flags = checkpoints ? 0 : w.off_flags;
+  // with checkpoints the workspace starts at the flags
+  char* flags = static_cast<char*>(workspace) + (checkpoints ? 0 : w.off_flags);
+  const bool segmented = w.nseg > 1;
+  BwdSegBuffers sb;
+  memset(&sb, 0, sizeof(sb));
+  if (segmented) sb = bwd_seg_buffers(w, batch * dim, dstate, flags + (w.off_seg - w.off_flags));
   const bool vec = rows_aligned16(seqlen, elem_size(dt));
   const int dti = dt == MAMBA_F32 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -325,6 +412,19 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   fp.seg_chunks = 0;
   fp.N = (int)dstate; fp.softplus = delta_softplus ? 1 : 0;
   if (!checkpoints) {
+    if (segmented) {
+      // the states at every chunk start, segment by segment: summaries,
+      // carry, then each segment from its entering state
+      fp.nseg = w.nseg;
+      fp.seg_chunks = w.seg_chunks;
+      fp.seg_state = sb.h_end;
+      fp.seg_h0 = sb.h_in;
+      fp.seg_dsum = sb.dsum;
+      fp.seg_keep = sb.keep;
+      if (mscan::dispatch_seg_summary(fp, dti, (int)disc, vec, s) != hipSuccess)
+        return MAMBA_ERR_HIP;
+      if (mscan::dispatch_seg_carry(fp, s) != hipSuccess) return MAMBA_ERR_HIP;
+    }
     const hipError_t e = mscan::dispatch_chunk_states(fp, dti, (int)disc, lanes, vec, s);
     if (e != hipSuccess) return MAMBA_ERR_HIP;
   }
@@ -336,10 +436,20 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0;
   p.chunk_states = states;
   p.reset = reset;
-  p.deferred = reinterpret_cast<int*>(static_cast<char*>(workspace) + off_flags);
+  p.deferred = reinterpret_cast<int*>(flags);
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.nchunks = w.nchunks; p.groups = w.groups; p.N = (int)dstate;
   p.softplus = delta_softplus ? 1 : 0;
+  p.nseg = w.nseg;
+  p.seg_chunks = w.seg_chunks;
+  if (segmented) {
+    p.seg_gloc = sb.g_loc;
+    p.seg_gdsum = sb.g_dsum;
+    p.seg_gkeep = sb.g_keep;
+    p.seg_gin = sb.g_in;
+    if (mscan::dispatch_bwd_seg_summary(p, dti, vec, s) != hipSuccess) return MAMBA_ERR_HIP;
+    if (mscan::dispatch_bwd_seg_carry(p, s) != hipSuccess) return MAMBA_ERR_HIP;
+  }
   return hip_status(mscan::dispatch_scan_bwd(p, dti, (int)disc, vec, s,
                                              static_cast<hipEvent_t>(timing_begin),
                                              static_cast<hipEvent_t>(timing_end)));
@@ -356,7 +466,7 @@ mamba_status mamba_scan_bwd(const void* u, const void* delta, const float* A, co
   return mamba_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout, nullptr,
                            delta_softplus, disc, dt, batch, dim, dstate, seqlen, du, ddelta, dA,
                            dB, dC, dD, dz, ddelta_bias, dh0, workspace, workspace_bytes, stream, 0,
-                           nullptr, nullptr, nullptr);
+                           0, nullptr, nullptr, nullptr);
 }
 
 mamba_status mamba_scan_bwd_varlen(const void* u, const void* delta, const float* A,
@@ -371,7 +481,7 @@ mamba_status mamba_scan_bwd_varlen(const void* u, const void* delta, const float
   if (!reset) return MAMBA_ERR_NULL_PTR;
   return mamba_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout, reset, delta_softplus,
                            disc, dt, batch, dim, dstate, seqlen, du, ddelta, dA, dB, dC, dD, dz,
-                           ddelta_bias, dh0, workspace, workspace_bytes, stream, 0, nullptr,
+                           ddelta_bias, dh0, workspace, workspace_bytes, stream, 0, 0, nullptr,
                            nullptr, nullptr);
 }
 

@@ -78,6 +78,17 @@ struct BwdParams {
   int64_t nchannels;
   int64_t nchunks;         // chunks of 16*kItemsBwd steps
   int64_t groups;          // channel groups per batch row (ceil(dim / channels per block))
+  // Sequence segments, as in FwdParams: each block walks seg_chunks chunks of
+  // one channel group (seg_chunks = 0, nseg = 1: the whole sequence).
+  int64_t seg_chunks;
+  int64_t nseg;
+  // adjoint g entering each segment from the later ones, (nchannels, nseg, N)
+  // (nullable: zero); written by the carry kernel from the summaries
+  float* seg_gin;
+  float* seg_gloc;         // summary: (nchannels, nseg, N) adjoint at the segment start, zero g
+                           // entering its end
+  float* seg_gdsum;        // summary: (nchannels, nseg) sum of delta over the segment
+  float* seg_gkeep;        // summary: (nchannels, nseg) 0 if the segment has a reset, else 1
   int N;
   int softplus;
 };
@@ -289,6 +300,11 @@ inline hipError_t dispatch_scan_bwd(const BwdParams& p, int dtype, int disc, boo
   return small ? dispatch_scan_bwd_bf16_n16(p, disc, vec, s, ev_begin, ev_end)
                : dispatch_scan_bwd_bf16_n64(p, disc, vec, s, ev_begin, ev_end);
 }
+// Segmented backward, adjoint side (scan_bwd_seg.hip): each segment's adjoint
+// at its start from a zero adjoint at its end, then the carry over segments
+// in reverse order into p.seg_gin.
+hipError_t dispatch_bwd_seg_summary(const BwdParams& p, int dtype, bool vec, hipStream_t s);
+hipError_t dispatch_bwd_seg_carry(const BwdParams& p, hipStream_t s);
 hipError_t dispatch_state_update(const StepParams& p, int dtype, int disc, hipStream_t stream);
 
 }  // namespace mscan

@@ -32,6 +32,13 @@
 // one float atomic per (n, t) per block.  dA, dD, ddelta_bias are summed over the
 // channel's lanes and atomically over batch rows.  Atomics make the result
 // deterministic only up to float32 rounding order.
+//
+// Long sequences with few channels are split into segments of whole chunks,
+// one block per (batch row, segment, channel group).  The adjoint entering a
+// segment from the right is then the composition of the later segments' affine
+// maps (each an adjoint from a zero end plus a decay exp(A sum(delta))),
+// carried by scan_bwd_seg.hip before this kernel; the chunk-start states come
+// from a segmented forward pass.  Only segment 0 writes dh0.
 #pragma once
 
 #include <type_traits>
@@ -127,9 +134,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const int j = lane % R;
   const int row = lane / R;
   const int cl = wave * CPW + row;
+  // block order (b, segment, group) with the group fastest, as in the forward
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t b = blk / p.groups;
-  const int64_t grp = blk - b * p.groups;
+  const int64_t per_b = p.groups * p.nseg;
+  const int64_t b = blk / per_b;
+  const int64_t seg = (blk - b * per_b) / p.groups;
+  const int64_t grp = blk - b * per_b - seg * p.groups;
   const int64_t d_raw = grp * CPB + cl;
   const bool active = d_raw < p.dim;
   const int64_t d = active ? d_raw : p.dim - 1;
@@ -137,6 +147,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const int N = p.N;
   const int64_t L = p.L;
   const int64_t nchunks = p.nchunks;
+  const int64_t ch_begin = p.seg_chunks > 0 ? seg * p.seg_chunks : 0;
+  const int64_t ch_end =
+      p.seg_chunks > 0 ? (ch_begin + p.seg_chunks < nchunks ? ch_begin + p.seg_chunks : nchunks)
+                       : nchunks;
 
   const T* __restrict__ u_row = static_cast<const T*>(p.u) + c * L;
   const T* __restrict__ dl_row = static_cast<const T*>(p.delta) + c * L;
@@ -171,13 +185,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
   TileStager<T, TCH, K, NT, TILE ? 2 * NT : 1, kBlock> stage;
   float hreg[NQ], gcreg[NQ], dAreg[NQ];
+  // the adjoint entering the block's last chunk from the right: zero at the
+  // end of the sequence (no gradient flows into the final state), else the
+  // carry over the later segments
+  const float* gin = p.seg_gin ? p.seg_gin + (c * p.nseg + seg) * N : nullptr;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    gcreg[q] = 0.0f;     // no gradient flows into the final state
+    const int n = 16 * q + j;
+    gcreg[q] = (gin && active && n < N) ? gin[n] : 0.0f;
     dAreg[q] = 0.0f;
   }
   {
-    const int64_t last = nchunks - 1;
+    const int64_t last = ch_end - 1;
     const bool full_last = VEC && last * TCH + TCH <= L;
     if constexpr (TILE) {
       stage.load(B_b, C_b, N, L, last * TCH, full_last, tid);
@@ -198,7 +217,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
   float dD_acc = 0.0f, db_acc = 0.0f;
 
-  for (int64_t ch = nchunks - 1; ch >= 0; --ch) {
+  for (int64_t ch = ch_end - 1; ch >= ch_begin; --ch) {
     const int64_t t0 = ch * TCH;
     const int64_t tl = t0 + (int64_t)j * K;
     const bool full = VEC && t0 + TCH <= L;
@@ -422,7 +441,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
     // the earlier chunk's B/C rows and states: issued here (not at the chunk
     // start) so their registers are not live across the state-index loop
-    if (ch > 0) {
+    if (ch > ch_begin) {
       if constexpr (TILE) stage.load(B_b, C_b, N, L, t0 - TCH, VEC, tid);   // earlier chunks are full
       load_states(ch - 1, hreg);
     }
@@ -449,7 +468,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     // every wave is past the last group barrier, so no wave still reads the
     // tile: refill it with the earlier chunk.  The barrier also keeps the
     // next chunk's slice stores behind this chunk's last flush.
-    if (ch > 0) {
+    if (ch > ch_begin) {
       if constexpr (TILE) stage.store(reinterpret_cast<float*>(tile_mem), N, tid);
       __syncthreads();
     }
@@ -460,7 +479,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   for (int q = 0; q < NQ; ++q) {
     const int n = 16 * q + j;
     if (active && n < N) {
-      if (p.dh0) p.dh0[c * N + n] = gcreg[q];
+      if (p.dh0 && seg == 0) p.dh0[c * N + n] = gcreg[q];
       unsafeAtomicAdd(p.dA + d * N + n, dAreg[q]);
     }
   }
@@ -494,7 +513,7 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(const BwdParams p)
 template <typename T, int NT, bool ZOH, bool VEC, bool RST>
 static hipError_t launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin,
                              hipEvent_t ev_end) {
-  const int64_t nblocks = p.batch * p.groups;
+  const int64_t nblocks = p.batch * p.groups * p.nseg;
   hipError_t e;
   if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
   hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, false, RST>), dim3((unsigned)nblocks),

@@ -106,7 +106,8 @@ __device__ __forceinline__ void store_items(T* __restrict__ row, int64_t t, int6
 //
 // A block serves one channel group of one batch row, for the whole sequence
 // or (p.seg_chunks > 0) for one segment of it; the segment's entering state
-// then comes from p.seg_h0, which the carry kernel filled from the summaries.
+// then comes from p.seg_h0, which the carry kernel filled from the summaries
+// (the output and the chunk-state modes).
 //
 // RST: packed sequences.  Where p.reset flags a step the state entering it is
 // zero: the step's decay factor in the recurrence (not in Bbar) becomes 0,
@@ -181,10 +182,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       p.seg_chunks > 0 ? (ch_begin + p.seg_chunks < nchunks ? ch_begin + p.seg_chunks : nchunks)
                        : nchunks;
   const float* h_enter = nullptr;
-  if constexpr (MODE == kModeOut)
+  if constexpr (MODE != kModeSegSummary)
     h_enter = p.seg_h0 ? p.seg_h0 + (c * p.nseg + seg) * N : (p.h0 ? p.h0 + c * N : nullptr);
-  else if constexpr (MODE == kModeChunkStates)
-    h_enter = p.h0 ? p.h0 + c * N : nullptr;
   float cr[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) cr[n] = (n < N && h_enter) ? h_enter[n] : 0.0f;

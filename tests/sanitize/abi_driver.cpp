@@ -41,9 +41,10 @@ mamba_status fwd(int64_t b, int64_t d, int64_t n, int64_t l, mamba_dtype dt = MA
 
 mamba_status bwd(int64_t b, int64_t d, int64_t n, int64_t l, mamba_dtype dt = MAMBA_F32,
                  void* ws = P, size_t wsb = BIG, const uint8_t* rst = nullptr, int lanes = 0,
-                 const float* ck = nullptr) {
+                 const float* ck = nullptr, int segs = 0) {
   return mamba_scan_bwd_ex(P, P, P, P, P, P, P, P, P, P, rst, 1, MAMBA_DISC_ZOH, dt, b, d, n, l, P,
-                           P, P, P, P, P, P, P, P, ws, wsb, nullptr, lanes, ck, nullptr, nullptr);
+                           P, P, P, P, P, P, P, P, ws, wsb, nullptr, lanes, segs, ck, nullptr,
+                           nullptr);
 }
 
 // Every query and call over one size tuple; the statuses only have to be
@@ -57,9 +58,11 @@ void sweep(int64_t b, int64_t d, int64_t n, int64_t l) {
         const int s = fwd(b, d, n, l, dt, MAMBA_DISC_ZOH, P, BIG, nullptr, lanes, segs);
         if (s < 0 || s > 8) ++g_fail;
       }
-      (void)mamba_scan_bwd_workspace_size_ex(b, d, n, l, dt, lanes);
-      const int s = bwd(b, d, n, l, dt, P, BIG, nullptr, lanes);
-      if (s < 0 || s > 8) ++g_fail;
+      for (int segs : {0, 1, 2, 1000}) {
+        (void)mamba_scan_bwd_workspace_size_ex(b, d, n, l, dt, lanes, segs);
+        const int s = bwd(b, d, n, l, dt, P, BIG, nullptr, lanes, nullptr, segs);
+        if (s < 0 || s > 8) ++g_fail;
+      }
     }
     (void)mamba_scan_fwd_workspace_size(b, d, n, l, dt);
     (void)mamba_scan_bwd_workspace_size(b, d, n, l, dt);
@@ -85,7 +88,7 @@ void sweep(int64_t b, int64_t d, int64_t n, int64_t l) {
 }  // namespace
 
 int main() {
-  EXPECT(mamba_abi_version(), 1);
+  EXPECT(mamba_abi_version(), 2);
   for (int s = -1; s <= 10; ++s)
     if (mamba_status_string((mamba_status)s) == nullptr) ++g_fail;
 
@@ -108,12 +111,27 @@ int main() {
          MAMBA_ERR_NULL_PTR);
   const size_t bws = mamba_scan_bwd_workspace_size(2, 64, 16, 2048, MAMBA_F32);
   EXPECT(bwd(2, 64, 16, 2048, MAMBA_F32, P, bws), MAMBA_OK);
-  EXPECT(bwd(2, 64, 16, 2048, MAMBA_F32, P, bws - 1), MAMBA_ERR_WORKSPACE);
+  const size_t bws1 = mamba_scan_bwd_workspace_size_ex(2, 64, 16, 2048, MAMBA_F32, 0, 1);
+  EXPECT(bwd(2, 64, 16, 2048, MAMBA_F32, P, bws - 1), MAMBA_OK);   // automatic: one pass
+  EXPECT(bwd(2, 64, 16, 2048, MAMBA_F32, P, bws1 - 1, nullptr, 0, nullptr, 1),
+         MAMBA_ERR_WORKSPACE);
   EXPECT(bwd(2, 64, 16, 2048, MAMBA_F32, nullptr, 0), MAMBA_ERR_WORKSPACE);
   EXPECT(bwd(2, 64, 16, 2048, MAMBA_F32, Q, bws), MAMBA_ERR_ALIGNMENT);
   EXPECT(mamba_scan_bwd(P, P, P, P, P, P, P, P, nullptr, P, 1, MAMBA_DISC_ZOH, MAMBA_F32, 2, 64,
                         16, 2048, P, P, P, P, P, nullptr, P, P, nullptr, P, bws, nullptr),
          MAMBA_ERR_INVALID);                                       // D given without dD
+  {
+    // segmented backward: its own workspace; the automatic choice falls back
+    // to one pass when given only the unsegmented size
+    const size_t seg = mamba_scan_bwd_workspace_size(1, 16, 16, 65536, MAMBA_F32);
+    const size_t one = mamba_scan_bwd_workspace_size_ex(1, 16, 16, 65536, MAMBA_F32, 0, 1);
+    if (!(seg > one)) ++g_fail;
+    EXPECT(bwd(1, 16, 16, 65536, MAMBA_F32, P, one), MAMBA_OK);
+    EXPECT(bwd(1, 16, 16, 65536, MAMBA_F32, P, seg), MAMBA_OK);
+    EXPECT(bwd(1, 16, 16, 65536, MAMBA_F32, P, one, nullptr, 0, nullptr, 8), MAMBA_ERR_WORKSPACE);
+    EXPECT(bwd(1, 16, 16, 65536, MAMBA_F32, P, seg, nullptr, 0, nullptr, -1),
+           MAMBA_ERR_UNSUPPORTED);
+  }
   EXPECT(mamba_scan_complex_checkpoint_size(2, 64, 17, 2049), SIZE_MAX);
   EXPECT(mamba_scan_bwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, P, 1,
                                    MAMBA_DISC_ZOH, MAMBA_F32, 2, 64, 16, 2048, P, P, P, P, P,

@@ -77,6 +77,10 @@ STUB_BWD(dispatch_scan_bwd_reset_f32_n64)
 STUB_BWD(dispatch_scan_bwd_reset_bf16_n16)
 STUB_BWD(dispatch_scan_bwd_reset_bf16_n64)
 #undef STUB_BWD
+hipError_t dispatch_bwd_seg_summary(const BwdParams&, int, bool, hipStream_t) {
+  return reached();
+}
+hipError_t dispatch_bwd_seg_carry(const BwdParams&, hipStream_t) { return reached(); }
 hipError_t dispatch_state_update(const StepParams&, int, int, hipStream_t) { return reached(); }
 hipError_t dispatch_state_update_complex(const CplxStepParams&, int, int, hipStream_t) {
   return reached();

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mamba_abi_version() == 1
+    assert lib.mamba_abi_version() == 2
     for code in range(0, 9):
         s = lib.mamba_status_string(code)
         assert s and isinstance(s, bytes)
@@ -61,13 +61,67 @@ def test_workspace_queries(lib):
     assert lib.mamba_scan_bwd_workspace_size(2, 5120, 65, 2048, 1) == 2 ** 64 - 1
     assert lib.mamba_scan_bwd_workspace_size(0, 5120, 16, 2048, 1) == 2 ** 64 - 1
     # the backward spreads a channel over 16 lanes: 0 (default) and 16 only
-    n16 = lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 16)
-    assert n16 > 0 and n16 == lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 0)
-    # the workspace holds the state at each 128-step chunk start, (2*64) * 4 * 16
-    # floats, then one flag per block of 16 channels (8 blocks), 256-byte rounded
+    n16 = lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 16, 1)
+    assert n16 > 0 and n16 == lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 0, 1)
+    # one pass: the workspace holds the state at each 128-step chunk start,
+    # (2*64) * 4 * 16 floats, then one flag per block of 16 channels (8
+    # blocks), 256-byte rounded
     assert n16 == 2 * 64 * 4 * 16 * 4 + 256
+    # (the automatic choice splits these 8 blocks' 4 chunks into 4 segments)
+    assert (lib.mamba_scan_bwd_workspace_size(2, 64, 16, 512, 0)
+            == lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, 0, 4) > n16)
     for lanes in (8, 32, 64):
-        assert lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, lanes) == 2 ** 64 - 1
+        assert lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 512, 0, lanes, 1) == 2 ** 64 - 1
+
+
+def test_backward_segment_workspace(lib):
+    # 1536 channels are 96 blocks: 2048 / 96 rounded up to a power of two, 32
+    # segments of 256 chunks.  The chunk-start states, one flag per (block,
+    # segment), then per channel and segment four state-sized buffers (forward
+    # end and entering states, adjoint summary and entering adjoint) and four
+    # scalars
+    states = 1536 * 8192 * 16 * 4
+    n = lib.mamba_scan_bwd_workspace_size(1, 1536, 16, 1 << 20, 1)
+    assert n == states + 96 * 32 * 4 + 4 * (1536 * 32 * 16 * 4) + 4 * (1536 * 32 * 4)
+    assert n == lib.mamba_scan_bwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 0, 32)
+    # short sequences split down to one chunk per segment: 8 chunks, 8 segments
+    assert (lib.mamba_scan_bwd_workspace_size(1, 1024, 16, 1024, 1)
+            == lib.mamba_scan_bwd_workspace_size_ex(1, 1024, 16, 1024, 1, 0, 8)
+            > lib.mamba_scan_bwd_workspace_size_ex(1, 1024, 16, 1024, 1, 0, 1))
+    # 512 blocks still split (4 segments), 640 do not
+    assert (lib.mamba_scan_bwd_workspace_size(1, 8192, 16, 4096, 1)
+            == lib.mamba_scan_bwd_workspace_size_ex(1, 8192, 16, 4096, 1, 0, 4))
+    assert (lib.mamba_scan_bwd_workspace_size(2, 5120, 16, 2048, 1)
+            == lib.mamba_scan_bwd_workspace_size_ex(2, 5120, 16, 2048, 1, 0, 1))
+    assert lib.mamba_scan_bwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 0, 0) == n
+    # one pass: states and one flag per block (96 ints, 256-byte rounded)
+    assert lib.mamba_scan_bwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 0, 1) == states + 512
+    # more segments than chunks are capped; negative counts are rejected
+    assert (lib.mamba_scan_bwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, 100)
+            == lib.mamba_scan_bwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, 8))
+    assert lib.mamba_scan_bwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, -1) == 2 ** 64 - 1
+    # shapes that fill the chip are not split
+    assert (lib.mamba_scan_bwd_workspace_size_ex(8, 1536, 16, 2048, 1, 0, 0)
+            == lib.mamba_scan_bwd_workspace_size_ex(8, 1536, 16, 2048, 1, 0, 1))
+
+
+def bwd_ex(lib, segments, ws=None, wsb=0, ckpt=None):
+    return lib.mamba_scan_bwd_ex(P, P, P, P, P, None, None, None, None, P, None, 1, 0, 0, 1, 16,
+                                 4, 1024, P, P, P, P, P, None, None, None, None, ws, wsb, None, 0,
+                                 segments, ckpt, None, None)
+
+
+def test_backward_segment_arguments(lib):
+    need = lib.mamba_scan_bwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, 3)
+    one = lib.mamba_scan_bwd_workspace_size_ex(1, 16, 4, 1024, 0, 0, 1)
+    assert need > one > 0
+    assert bwd_ex(lib, 3) == 5                          # explicit segments, no workspace
+    assert bwd_ex(lib, 3, ws=P, wsb=need - 1) == 5
+    assert bwd_ex(lib, 3, ws=P + 8, wsb=need) == 4      # misaligned workspace
+    assert bwd_ex(lib, -1, ws=P, wsb=need) == 6
+    # with checkpoints the states are not in the workspace, the rest is
+    ckpt = lib.mamba_scan_checkpoint_size(1, 16, 4, 1024)
+    assert bwd_ex(lib, 3, ws=P, wsb=need - ckpt - 1, ckpt=P) == 5
 
 
 def test_forward_segment_workspace(lib):
@@ -78,6 +132,14 @@ def test_forward_segment_workspace(lib):
     assert n == 2 * (1536 * 32 * 16 * 4) + 2 * (1536 * 32 * 4)
     assert lib.mamba_scan_fwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 0, 0) == n
     assert lib.mamba_scan_fwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 16, 0) == n
+    # 256 blocks split (2048 / 256: 8 segments), 512 do not; at least 8
+    # segments of one chunk or more
+    assert (lib.mamba_scan_fwd_workspace_size(1, 4096, 16, 4096, 1)
+            == lib.mamba_scan_fwd_workspace_size_ex(1, 4096, 16, 4096, 1, 0, 8) > 0)
+    assert lib.mamba_scan_fwd_workspace_size(1, 8192, 16, 4096, 1) == 0
+    assert (lib.mamba_scan_fwd_workspace_size(1, 1024, 16, 1024, 1)
+            == lib.mamba_scan_fwd_workspace_size_ex(1, 1024, 16, 1024, 1, 0, 8) > 0)
+    assert lib.mamba_scan_fwd_workspace_size(1, 1024, 16, 896, 1) == 0      # 7 chunks
     # one pass: no workspace; explicit wider lanes run in one pass as well
     assert lib.mamba_scan_fwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 0, 1) == 0
     assert lib.mamba_scan_fwd_workspace_size_ex(1, 1536, 16, 1 << 20, 1, 64, 0) == 0
@@ -110,13 +172,13 @@ def test_checkpoint_size_and_backward_workspace(lib):
     # one state of 16 floats per channel and 128-step chunk (ragged: 17 chunks)
     assert lib.mamba_scan_checkpoint_size(2, 64, 16, 2049) == 2 * 64 * 17 * 16 * 4
     assert lib.mamba_scan_checkpoint_size(0, 64, 16, 2049) == 2 ** 64 - 1
-    full = lib.mamba_scan_bwd_workspace_size(2, 64, 16, 2048, 0)
+    full = lib.mamba_scan_bwd_workspace_size_ex(2, 64, 16, 2048, 0, 0, 1)   # one pass
     flags = full - 2 * 64 * 16 * 16 * 4          # with checkpoints: the block flags only
 
     def bwd_ex(ws, wsb, ckpt):
         return lib.mamba_scan_bwd_ex(P, P, P, P, P, None, None, None, None, P, None, 1, 0, 0, 2,
                                      64, 16, 2048, P, P, P, P, P, None, None, None, None, ws, wsb,
-                                     None, 0, ckpt, None, None)
+                                     None, 0, 1, ckpt, None, None)
     assert bwd_ex(P, flags - 1, P) == 5
     assert bwd_ex(P, flags, None) == 5               # without them the states need room
     assert bwd_ex(P, full, P + 8) == 4

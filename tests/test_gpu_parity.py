@@ -259,10 +259,10 @@ def test_state_update_without_optionals():
 # backward
 # --------------------------------------------------------------------------
 def run_bwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=False,
-                 opts=None, zero_A=False, A_mode="s4d_real", rtol=None, reset=None):
+                 opts=None, zero_A=False, A_mode="s4d_real", rtol=None, reset=None, segments=0):
     opts = opts or {}
     announce(f"bwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} lanes={lanes} "
-             f"h0={h0} opts={opts} zero_A={zero_A} "
+             f"h0={h0} opts={opts} zero_A={zero_A} segments={segments} "
              f"resets={None if reset is None else int(reset.sum())}")
     inp, f = _make(wid, batch, dim, N, L, dtype, with_dout=True, A_mode=A_mode, **opts)
     if not softplus:
@@ -276,7 +276,7 @@ def run_bwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=
     h0t = torch.from_numpy(h0v).cuda() if h0v is not None else None
     res = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g.get("D"), g.get("z"),
                       g.get("delta_bias"), g["dout"], h0t, delta_softplus=softplus, disc=disc,
-                      lanes=lanes,
+                      lanes=lanes, segments=segments,
                       reset=None if reset is None else torch.from_numpy(reset).cuda())
     torch.cuda.synchronize()
     ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"), f.get("z"),
@@ -323,11 +323,13 @@ def test_bwd_varlen_state_sizes_and_zero_A():
                  reset=W.make_resets(46, 2, 500, 10, 100))
 
 
-def _ckpt_case(wid, batch, dim, N, L, dtype, disc, h0=False, segments=0, reset=None):
+def _ckpt_case(wid, batch, dim, N, L, dtype, disc, h0=False, segments=0, reset=None,
+               bwd_segments=0):
     # the forward saves the state entering every 128-step chunk; the backward
     # given them must match the oracle (and the run that recomputes them)
     announce(f"checkpoints wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} h0={h0} "
-             f"segments={segments} resets={None if reset is None else int(reset.sum())}")
+             f"segments={segments} bwd_segments={bwd_segments} "
+             f"resets={None if reset is None else int(reset.sum())}")
     inp, f = _make(wid, batch, dim, N, L, dtype, with_dout=True)
     h0v = np.random.default_rng(wid).standard_normal((batch, dim, N)).astype(np.float32) \
         if h0 else None
@@ -338,9 +340,11 @@ def _ckpt_case(wid, batch, dim, N, L, dtype, disc, h0=False, segments=0, reset=N
     ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["delta_bias"], h0t,
                 disc=disc, segments=segments, reset=rt, checkpoints=ck)
     res = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
-                      g["delta_bias"], g["dout"], h0t, disc=disc, reset=rt, checkpoints=ck)
+                      g["delta_bias"], g["dout"], h0t, disc=disc, reset=rt, checkpoints=ck,
+                      segments=bwd_segments)
     res2 = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
-                       g["delta_bias"], g["dout"], h0t, disc=disc, reset=rt)
+                       g["delta_bias"], g["dout"], h0t, disc=disc, reset=rt,
+                       segments=bwd_segments)
     torch.cuda.synchronize()
     assert not torch.isnan(ck).any()
     ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
@@ -363,6 +367,51 @@ def test_bwd_from_forward_checkpoints_segmented_varlen_sizes():
     _ckpt_case(48, 2, 9, 5, 1000, "f32", "zoh",
                reset=W.make_resets(48, 2, 1000, 20, 300, force=(0, 128)))
     _ckpt_case(49, 2, 9, 33, 513, "bf16", "euler", h0=True)
+
+
+@pytest.mark.parametrize("segments", [2, 3, 10])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_bwd_segmented(segments, dtype, disc):
+    # the backward split into segments: states from a segmented forward pass,
+    # the adjoint entering each segment from the reverse carry.  1189 steps
+    # are 9 full chunks and a ragged one (3 segments: 4 + 4 + 2 chunks, 10:
+    # one chunk each); dh0 comes from the first segment only.
+    run_bwd_case(51, 1, 20, 16, 1189, dtype, disc, h0=True, segments=segments)
+
+
+def test_bwd_segmented_state_sizes_optionals_zero_A():
+    run_bwd_case(52, 2, 9, 5, 1300, "f32", "zoh", segments=4, h0=True)
+    run_bwd_case(52, 2, 9, 33, 1300, "f32", "zoh", segments=4, A_mode="random_neg")
+    run_bwd_case(53, 1, 12, 16, 1024, "f32", "zoh", segments=8, zero_A=True, h0=True)
+    run_bwd_case(53, 1, 12, 16, 1024, "f32", "euler", segments=5, softplus=False,
+                 opts=dict(with_D=False, with_z=False, with_bias=False))
+
+
+def test_bwd_segmented_varlen():
+    # resets on segment and chunk boundaries, in a segment's first and last
+    # step, and a segment free of resets between two that have them
+    L = 2048
+    rs = W.make_resets(54, 2, L, 1, 700, force=(0, 1, 255, 256, 511, 1024, 1025, L - 1))
+    rs[1, 512:1024] = 0
+    run_bwd_case(54, 2, 9, 16, L, "f32", "zoh", h0=True, reset=rs, segments=8)
+    run_bwd_case(55, 2, 9, 5, L, "bf16", "euler", reset=rs, segments=3)
+
+
+def test_bwd_automatic_segmentation():
+    # 16 channels over 8192 steps: one channel group, 64 chunks, so the
+    # automatic choice splits the sequence (64 segments of one chunk); it must
+    # agree with the oracle and with the one-pass backward
+    res = run_bwd_case(56, 1, 16, 16, 8192, "bf16", "zoh", h0=True)
+    one = run_bwd_case(56, 1, 16, 16, 8192, "bf16", "zoh", h0=True, segments=1)
+    for k in res:
+        assert_match(to_f64(res[k]), to_f64(one[k]), RTOL["f32"], k + " auto vs one pass")
+
+
+def test_bwd_segmented_from_checkpoints():
+    _ckpt_case(57, 1, 16, 16, 2048, "f32", "zoh", h0=True, segments=4, bwd_segments=4)
+    _ckpt_case(57, 2, 9, 5, 1000, "bf16", "euler", bwd_segments=3,
+               reset=W.make_resets(57, 2, 1000, 20, 300, force=(0, 384)))
 
 
 def test_bwd_rejects_other_lane_counts():
