@@ -334,9 +334,11 @@ mamba_status mamba_conv1d_silu_bwd(const void* x, const float* w, const float* b
  *    same inputs.
  *  - timing_begin, timing_end: hipEvent_t handles (NULL = none).  When given,
  *    they are recorded on `stream` immediately before and after the main
- *    scan kernel of the call (the forward's output kernel, after a segmented
- *    run's summary and carry kernels; the backward's reverse-scan kernel,
- *    after its state-recompute and zeroing kernels have been enqueued), so a
+ *    scan kernel of the call (the forward's output kernel; in a segmented
+ *    run its first launch, which runs every segment from a zero state, before
+ *    the carry and the launch that corrects each segment's first chunks; the
+ *    backward's reverse-scan kernel, after its state-recompute, adjoint-carry
+ *    and zeroing kernels have been enqueued), so a
  *    caller can time that kernel alone with hipEventElapsedTime.  The caller
  *    owns the events; failure to record one returns MAMBA_ERR_HIP.
  */

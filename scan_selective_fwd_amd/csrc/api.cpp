@@ -101,6 +101,16 @@ int64_t bwd_auto_segments(int64_t batch, int64_t dim, int64_t seqlen) {
   return split_segments(blocks, (seqlen + kFwdChunk - 1) / kFwdChunk, 512, 2);
 }
 
+// Segments of at least this many chunks take the zero-start pass, the carry
+// and the correcting pass over each segment's first chunks; shorter ones the
+// summary pass, the carry and the pass from each segment's entering state.
+// The correcting pass costs the chunks the entering state takes to decay
+// below float32 resolution (a few chunks at the usual delta and A), so it
+// only gains over the summary pass (about 0.65 of an output pass) on long
+// segments: at batch 1, D 1024, 32 segments of 128 chunks take 3.7 ms instead
+// of 5.8 ms, 16 segments of one chunk 0.056 ms instead of 0.043 ms.
+constexpr int64_t kLongSegmentChunks = 16;
+
 // Forward workspace (segmented only): the segment end states and the
 // entering states (nchannels, nseg, dstate) float32, then the delta sums and
 // the reset-free factors (nchannels, nseg) float32.
@@ -309,7 +319,12 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
   const bool vec = rows_aligned16(seqlen, elem_size(dt));
   const int dti = dt == MAMBA_F32 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool long_seg = segmented && w.seg_chunks >= kLongSegmentChunks;
   if (segmented) {
+    // long segments: every segment from zero (with its summary), the carry,
+    // then each segment's first chunks again from its entering state; short
+    // ones: the summaries, the carry, then every segment from its entering
+    // state
     char* ws = static_cast<char*>(workspace);
     p.nseg = w.nseg;
     p.seg_chunks = w.seg_chunks;
@@ -317,8 +332,13 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
     p.seg_h0 = reinterpret_cast<float*>(ws + w.off_h0);
     p.seg_dsum = reinterpret_cast<float*>(ws + w.off_dsum);
     p.seg_keep = reinterpret_cast<float*>(ws + w.off_keep);
-    if (mscan::dispatch_seg_summary(p, dti, (int)disc, vec, s) != hipSuccess) return MAMBA_ERR_HIP;
-    if (mscan::dispatch_seg_carry(p, s) != hipSuccess) return MAMBA_ERR_HIP;
+    if (long_seg) {
+      p.seg_pass = mscan::kSegLocal;
+    } else {
+      if (mscan::dispatch_seg_summary(p, dti, (int)disc, vec, s) != hipSuccess)
+        return MAMBA_ERR_HIP;
+      if (mscan::dispatch_seg_carry(p, s) != hipSuccess) return MAMBA_ERR_HIP;
+    }
   }
   if (timing_begin && hipEventRecord(static_cast<hipEvent_t>(timing_begin), s) != hipSuccess)
     return MAMBA_ERR_HIP;
@@ -326,6 +346,11 @@ mamba_status mamba_scan_fwd_ex(const void* u, const void* delta, const float* A,
     return MAMBA_ERR_HIP;
   if (timing_end && hipEventRecord(static_cast<hipEvent_t>(timing_end), s) != hipSuccess)
     return MAMBA_ERR_HIP;
+  if (segmented && long_seg) {
+    if (mscan::dispatch_seg_carry(p, s) != hipSuccess) return MAMBA_ERR_HIP;
+    if (mscan::dispatch_scan_fwd_fix(p, dti, (int)disc, vec, s) != hipSuccess)
+      return MAMBA_ERR_HIP;
+  }
   return MAMBA_OK;
 }
 
@@ -412,21 +437,31 @@ mamba_status mamba_scan_bwd_ex(const void* u, const void* delta, const float* A,
   fp.seg_chunks = 0;
   fp.N = (int)dstate; fp.softplus = delta_softplus ? 1 : 0;
   if (!checkpoints) {
+    // the states at every chunk start, segment by segment, in the forward's
+    // two schemes
+    const bool long_seg = segmented && w.seg_chunks >= kLongSegmentChunks;
     if (segmented) {
-      // the states at every chunk start, segment by segment: summaries,
-      // carry, then each segment from its entering state
       fp.nseg = w.nseg;
       fp.seg_chunks = w.seg_chunks;
       fp.seg_state = sb.h_end;
       fp.seg_h0 = sb.h_in;
       fp.seg_dsum = sb.dsum;
       fp.seg_keep = sb.keep;
-      if (mscan::dispatch_seg_summary(fp, dti, (int)disc, vec, s) != hipSuccess)
-        return MAMBA_ERR_HIP;
-      if (mscan::dispatch_seg_carry(fp, s) != hipSuccess) return MAMBA_ERR_HIP;
+      if (long_seg) {
+        fp.seg_pass = mscan::kSegLocal;
+      } else {
+        if (mscan::dispatch_seg_summary(fp, dti, (int)disc, vec, s) != hipSuccess)
+          return MAMBA_ERR_HIP;
+        if (mscan::dispatch_seg_carry(fp, s) != hipSuccess) return MAMBA_ERR_HIP;
+      }
     }
-    const hipError_t e = mscan::dispatch_chunk_states(fp, dti, (int)disc, lanes, vec, s);
-    if (e != hipSuccess) return MAMBA_ERR_HIP;
+    if (mscan::dispatch_chunk_states(fp, dti, (int)disc, lanes, vec, s) != hipSuccess)
+      return MAMBA_ERR_HIP;
+    if (long_seg) {
+      if (mscan::dispatch_seg_carry(fp, s) != hipSuccess) return MAMBA_ERR_HIP;
+      if (mscan::dispatch_chunk_states_fix(fp, dti, (int)disc, vec, s) != hipSuccess)
+        return MAMBA_ERR_HIP;
+    }
   }
 
   mscan::BwdParams p;

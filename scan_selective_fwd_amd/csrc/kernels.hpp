@@ -35,11 +35,12 @@ struct FwdParams {
   // whole sequence.
   int64_t seg_chunks;
   int64_t nseg;
-  float* seg_h0;           // (nchannels, nseg, N): state entering each segment
-  float* seg_state;        // summary mode: (nchannels, nseg, N) end state from a zero start
-  float* seg_dsum;         // summary mode: (nchannels, nseg) sum of delta over the segment
-  float* seg_keep;         // summary mode: (nchannels, nseg) 0 if the segment has a reset, else 1
+  float* seg_h0;           // (nchannels, nseg, N): state entering each segment (carry kernel)
+  float* seg_state;        // local pass: (nchannels, nseg, N) end state from a zero start
+  float* seg_dsum;         // local pass: (nchannels, nseg) sum of delta over the segment
+  float* seg_keep;         // local pass: (nchannels, nseg) 0 if the segment has a reset, else 1
   const uint8_t* reset;    // nullable (batch, L): zero the state before each flagged step
+  int seg_pass;            // SegPass
   int N;
   int softplus;
 };
@@ -49,6 +50,13 @@ enum FwdMode : int {
   kModeOut = 0,           // outputs (and the last state)
   kModeChunkStates = 1,   // only the state at every chunk start (backward recompute)
   kModeSegSummary = 2,    // only each segment's end state from zero and its delta sum
+};
+
+// Which pass of a (possibly segmented) run a forward-kernel launch is.
+enum SegPass : int {
+  kSegWhole = 0,          // from h0, or from p.seg_h0 per segment when that is set
+  kSegLocal = 1,          // every segment from a zero state; writes the segment summaries
+  kSegFix = 2,            // each segment's first chunks again from its entering state
 };
 
 struct BwdParams {
@@ -232,15 +240,16 @@ hipError_t dispatch_chunk_states_bf16(const FwdParams& p, int disc, int lanes, b
 // Packed sequences with reset flags (p.reset != NULL): 16 lanes per channel.
 hipError_t dispatch_scan_fwd_reset_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
 hipError_t dispatch_scan_fwd_reset_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
-hipError_t dispatch_seg_summary_reset_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
-hipError_t dispatch_seg_summary_reset_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
 hipError_t dispatch_chunk_states_reset_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
 hipError_t dispatch_chunk_states_reset_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
-// Segmented forward, first two launches: per-segment summaries (16 lanes per
-// channel) and the sequential carry over segments.
+// Segmented runs (16 lanes per channel): the summary pass (short segments),
+// the carry over segments (also the last state), and the correcting launch of
+// the output or chunk-state kernel (long segments), from each segment's
+// entering state over the chunks it still changes.
 hipError_t dispatch_seg_summary_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
 hipError_t dispatch_seg_summary_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
-hipError_t dispatch_seg_carry(const FwdParams& p, hipStream_t s);
+hipError_t dispatch_seg_summary_reset_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_seg_summary_reset_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
 inline hipError_t dispatch_seg_summary(const FwdParams& p, int dtype, int disc, bool vec,
                                        hipStream_t s) {
   if (p.reset)
@@ -248,6 +257,33 @@ inline hipError_t dispatch_seg_summary(const FwdParams& p, int dtype, int disc, 
                       : dispatch_seg_summary_reset_bf16(p, disc, vec, s);
   return dtype == 0 ? dispatch_seg_summary_f32(p, disc, vec, s)
                     : dispatch_seg_summary_bf16(p, disc, vec, s);
+}
+hipError_t dispatch_seg_carry(const FwdParams& p, hipStream_t s);
+hipError_t dispatch_scan_fwd_fix_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_scan_fwd_fix_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_scan_fwd_fix_reset_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_scan_fwd_fix_reset_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_chunk_states_fix_f32(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_chunk_states_fix_bf16(const FwdParams& p, int disc, bool vec, hipStream_t s);
+hipError_t dispatch_chunk_states_fix_reset_f32(const FwdParams& p, int disc, bool vec,
+                                               hipStream_t s);
+hipError_t dispatch_chunk_states_fix_reset_bf16(const FwdParams& p, int disc, bool vec,
+                                                hipStream_t s);
+inline hipError_t dispatch_scan_fwd_fix(const FwdParams& p, int dtype, int disc, bool vec,
+                                        hipStream_t s) {
+  if (p.reset)
+    return dtype == 0 ? dispatch_scan_fwd_fix_reset_f32(p, disc, vec, s)
+                      : dispatch_scan_fwd_fix_reset_bf16(p, disc, vec, s);
+  return dtype == 0 ? dispatch_scan_fwd_fix_f32(p, disc, vec, s)
+                    : dispatch_scan_fwd_fix_bf16(p, disc, vec, s);
+}
+inline hipError_t dispatch_chunk_states_fix(const FwdParams& p, int dtype, int disc, bool vec,
+                                            hipStream_t s) {
+  if (p.reset)
+    return dtype == 0 ? dispatch_chunk_states_fix_reset_f32(p, disc, vec, s)
+                      : dispatch_chunk_states_fix_reset_bf16(p, disc, vec, s);
+  return dtype == 0 ? dispatch_chunk_states_fix_f32(p, disc, vec, s)
+                    : dispatch_chunk_states_fix_bf16(p, disc, vec, s);
 }
 inline hipError_t dispatch_scan_fwd(const FwdParams& p, int dtype, int disc, int lanes, bool vec,
                                     hipStream_t s) {

@@ -100,14 +100,27 @@ __device__ __forceinline__ void store_items(T* __restrict__ row, int64_t t, int6
 // MODE (FwdMode): kModeOut computes the outputs (and, when p.chunk_states is
 // set, also saves the state at the start of every chunk as checkpoints for
 // the backward).  kModeChunkStates is the backward's recompute pass: it only
-// writes the state at the start of every chunk (to p.chunk_states).  kModeSegSummary runs one segment of a long
-// sequence from a zero state and writes its end state and delta sum.  The
-// two state-only modes skip C, z, y and out.
+// writes the state at the start of every chunk (to p.chunk_states).
+// kModeSegSummary runs each segment of a long sequence from a zero state and
+// writes its end state and delta sum.  The two state-only modes skip C, z, y
+// and out.
 //
 // A block serves one channel group of one batch row, for the whole sequence
-// or (p.seg_chunks > 0) for one segment of it; the segment's entering state
-// then comes from p.seg_h0, which the carry kernel filled from the summaries
-// (the output and the chunk-state modes).
+// or (p.seg_chunks > 0) for one segment of it.  A segmented run takes three
+// launches, in one of two schemes (the carry kernel in the middle composes
+// the segments' end states from zero into the state entering each segment,
+// p.seg_h0):
+//  * short segments: the summary mode, the carry, then SEG = kSegWhole runs
+//    every segment from p.seg_h0;
+//  * long segments: SEG = kSegLocal runs every segment from a zero state and
+//    also writes the summaries, the carry, then SEG = kSegFix runs each
+//    segment again from its entering state over its first chunks only.  The
+//    true state is the zero-start state plus exp(A * sum(delta)) times the
+//    entering state; kSegFix stops once that second term is below 2^-160 for
+//    every (channel, n) of the block, or a reset flag has cut it, and from
+//    there on the first launch's outputs and checkpoints stand.  This saves
+//    the summary pass (about 0.65 of an output pass) at the price of the
+//    chunks the entering state takes to decay.
 //
 // RST: packed sequences.  Where p.reset flags a step the state entering it is
 // zero: the step's decay factor in the recurrence (not in Bbar) becomes 0,
@@ -117,10 +130,12 @@ __device__ __forceinline__ void store_items(T* __restrict__ row, int64_t t, int6
 // indices then has no per-index branch, and the operands of index n + 1
 // need no copies at the join of one (a fifth fewer VALU instructions).
 template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE, bool RST = false,
-          bool EXACT = false>
+          bool EXACT = false, int SEG = kSegWhole>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_fwd_kernel(
     const FwdParams p) {
   constexpr bool STATES = MODE != kModeOut;
+  constexpr bool FIX = SEG == kSegFix;
+  constexpr bool LOCAL = SEG == kSegLocal;   // every segment from zero, summaries written
   constexpr int CPW = 64 / R;   // channels per wave
   constexpr int CPB = (kBlock / 64) * CPW;
   constexpr int TCH = R * K;    // steps per chunk
@@ -182,7 +197,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       p.seg_chunks > 0 ? (ch_begin + p.seg_chunks < nchunks ? ch_begin + p.seg_chunks : nchunks)
                        : nchunks;
   const float* h_enter = nullptr;
-  if constexpr (MODE != kModeSegSummary)
+  if constexpr (FIX) h_enter = p.seg_h0 + (c * p.nseg + seg) * N;
+  else if constexpr (!LOCAL && MODE != kModeSegSummary)
     h_enter = p.seg_h0 ? p.seg_h0 + (c * p.nseg + seg) * N : (p.h0 ? p.h0 + c * N : nullptr);
   float cr[NT];
 #pragma unroll
@@ -227,6 +243,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   auto run_chunks = [&](auto tp_c) {
     constexpr bool TP = decltype(tp_c)::value;
     for (int64_t ch = ch_begin; ch < ch_end; ++ch) {
+      if constexpr (FIX) {
+        // what is left of the entering state: |h_enter[n]| exp(A_n sum(delta)),
+        // in log2 so that a large entering state is not lost to underflow
+        const float S = group_sum<R>(dtot);
+        const bool cut = RST && group_sum<R>(seg_reset ? 1.0f : 0.0f) > 0.0f;
+        bool alive = false;
+        if (active && !cut)
+          for (int n = 0; n < N; ++n)
+            alive |= __builtin_fmaf(a2s[cl][n], S,
+                                    __builtin_amdgcn_logf(__builtin_fabsf(h_enter[n]))) > -160.0f;
+        if (!__syncthreads_or(alive)) break;   // block-uniform
+      }
       const int buf = (int)((ch - ch_begin) & 1);
       const int64_t t0 = ch * TCH;
       const int64_t tl = t0 + (int64_t)j * K;   // this lane's first step
@@ -360,12 +388,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   if (ZOH && any_tiny) run_chunks(std::true_type{});
   else run_chunks(std::false_type{});
 
-  if (MODE == kModeOut && active && j == 0 && p.last_state && seg == p.nseg - 1) {
+  // one pass: the last state (segmented runs: the carry kernel writes it)
+  if (MODE == kModeOut && SEG == kSegWhole && p.nseg == 1 && active && j == 0 && p.last_state) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
       if (n < N) p.last_state[c * N + n] = cr[n];
   }
-  if constexpr (MODE == kModeSegSummary) {
+  if constexpr (LOCAL || MODE == kModeSegSummary) {
     const float dseg = group_sum<R>(dtot);
     const float nreset = group_sum<R>(seg_reset ? 1.0f : 0.0f);
     if (active && j == 0) {
@@ -379,35 +408,54 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 }
 
 template <typename T, int R, int K, int NT, bool ZOH, bool VEC, int MODE, bool RST = false,
-          bool EXACT = false>
+          bool EXACT = false, int SEG = kSegWhole>
 static hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
   const int64_t nblocks = p.batch * p.groups * p.nseg;
-  hipLaunchKernelGGL((scan_fwd_kernel<T, R, K, NT, ZOH, VEC, MODE, RST, EXACT>),
+  hipLaunchKernelGGL((scan_fwd_kernel<T, R, K, NT, ZOH, VEC, MODE, RST, EXACT, SEG>),
                      dim3((unsigned)nblocks), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
 // N <= 16 takes the NT = 16 kernel, 16 < N <= 64 the NT = 64 kernel; with
 // 16 lanes per channel, N == 16 (the usual state size) has a variant of its own.
-template <typename T, int R, int K, bool ZOH, int MODE, bool RST = false>
+template <typename T, int R, int K, bool ZOH, int MODE, bool RST = false, int SEG = kSegWhole>
 static hipError_t fwd_nv(const FwdParams& p, bool vec, hipStream_t s) {
   if constexpr (R == 16) {
     if (p.N == 16)
-      return vec ? launch_fwd<T, R, K, 16, ZOH, true, MODE, RST, true>(p, s)
-                 : launch_fwd<T, R, K, 16, ZOH, false, MODE, RST, true>(p, s);
+      return vec ? launch_fwd<T, R, K, 16, ZOH, true, MODE, RST, true, SEG>(p, s)
+                 : launch_fwd<T, R, K, 16, ZOH, false, MODE, RST, true, SEG>(p, s);
   }
   if (p.N <= 16)
-    return vec ? launch_fwd<T, R, K, 16, ZOH, true, MODE, RST>(p, s)
-               : launch_fwd<T, R, K, 16, ZOH, false, MODE, RST>(p, s);
-  return vec ? launch_fwd<T, R, K, 64, ZOH, true, MODE, RST>(p, s)
-             : launch_fwd<T, R, K, 64, ZOH, false, MODE, RST>(p, s);
+    return vec ? launch_fwd<T, R, K, 16, ZOH, true, MODE, RST, false, SEG>(p, s)
+               : launch_fwd<T, R, K, 16, ZOH, false, MODE, RST, false, SEG>(p, s);
+  return vec ? launch_fwd<T, R, K, 64, ZOH, true, MODE, RST, false, SEG>(p, s)
+             : launch_fwd<T, R, K, 64, ZOH, false, MODE, RST, false, SEG>(p, s);
+}
+
+// 16 lanes per channel, the segment pass from p.seg_pass (first launch) or
+// kSegFix (second launch of a segmented run).
+template <typename T, int K, bool ZOH, int MODE, bool RST, bool FIX>
+static hipError_t fwd_seg16(const FwdParams& p, bool vec, hipStream_t s) {
+  if constexpr (FIX) {
+    return fwd_nv<T, 16, K, ZOH, MODE, RST, kSegFix>(p, vec, s);
+  } else {
+    if (p.seg_pass == kSegLocal) return fwd_nv<T, 16, K, ZOH, MODE, RST, kSegLocal>(p, vec, s);
+    return fwd_nv<T, 16, K, ZOH, MODE, RST, kSegWhole>(p, vec, s);
+  }
 }
 
 // Reset flags: 16 lanes per channel only.
-template <typename T, int K, int MODE>
+template <typename T, int K, int MODE, bool FIX = false>
 static hipError_t dispatch_fwd_reset_t(const FwdParams& p, int disc, bool vec, hipStream_t s) {
-  return disc == 0 ? fwd_nv<T, 16, K, true, MODE, true>(p, vec, s)
-                   : fwd_nv<T, 16, K, false, MODE, true>(p, vec, s);
+  return disc == 0 ? fwd_seg16<T, K, true, MODE, true, FIX>(p, vec, s)
+                   : fwd_seg16<T, K, false, MODE, true, FIX>(p, vec, s);
+}
+
+// The second launch of a segmented run (no reset flags).
+template <typename T, int K, int MODE>
+static hipError_t dispatch_fwd_fix_t(const FwdParams& p, int disc, bool vec, hipStream_t s) {
+  return disc == 0 ? fwd_seg16<T, K, true, MODE, false, true>(p, vec, s)
+                   : fwd_seg16<T, K, false, MODE, false, true>(p, vec, s);
 }
 
 template <typename T, int K, int MODE>
@@ -416,7 +464,8 @@ static hipError_t dispatch_fwd_t(const FwdParams& p, int disc, int lanes, bool v
   const bool zoh = disc == 0;
   switch (lanes) {
     case 16:
-      return zoh ? fwd_nv<T, 16, K, true, MODE>(p, vec, s) : fwd_nv<T, 16, K, false, MODE>(p, vec, s);
+      return zoh ? fwd_seg16<T, K, true, MODE, false, false>(p, vec, s)
+                 : fwd_seg16<T, K, false, MODE, false, false>(p, vec, s);
     case 32:
       return zoh ? fwd_nv<T, 32, K, true, MODE>(p, vec, s) : fwd_nv<T, 32, K, false, MODE>(p, vec, s);
     default:

@@ -1,5 +1,6 @@
 // Forward-scan kernels with reset flags (packed sequences) for bf16 sequences
-// (see scan_fwd_impl.hpp): the output pass and the segment summary pass.
+// (see scan_fwd_impl.hpp): the output pass, the summary pass and the
+// correcting launch of a segmented run.
 #include "scan_fwd_impl.hpp"
 
 namespace mscan {
@@ -8,9 +9,15 @@ hipError_t dispatch_scan_fwd_reset_bf16(const FwdParams& p, int disc, bool vec, 
   return dispatch_fwd_reset_t<bf16_t, kItems, kModeOut>(p, disc, vec, stream);
 }
 
+hipError_t dispatch_scan_fwd_fix_reset_bf16(const FwdParams& p, int disc, bool vec,
+                                          hipStream_t stream) {
+  return dispatch_fwd_reset_t<bf16_t, kItems, kModeOut, true>(p, disc, vec, stream);
+}
+
 hipError_t dispatch_seg_summary_reset_bf16(const FwdParams& p, int disc, bool vec,
                                           hipStream_t stream) {
-  return dispatch_fwd_reset_t<bf16_t, kItems, kModeSegSummary>(p, disc, vec, stream);
+  return disc == 0 ? fwd_nv<bf16_t, 16, kItems, true, kModeSegSummary, true>(p, vec, stream)
+                   : fwd_nv<bf16_t, 16, kItems, false, kModeSegSummary, true>(p, vec, stream);
 }
 
 }  // namespace mscan

@@ -9,4 +9,9 @@ hipError_t dispatch_chunk_states_bf16(const FwdParams& p, int disc, int lanes, b
   return dispatch_fwd_t<bf16_t, kItemsBwd, kModeChunkStates>(p, disc, lanes, vec, stream);
 }
 
+hipError_t dispatch_chunk_states_fix_bf16(const FwdParams& p, int disc, bool vec,
+                                      hipStream_t stream) {
+  return dispatch_fwd_fix_t<bf16_t, kItemsBwd, kModeChunkStates>(p, disc, vec, stream);
+}
+
 }  // namespace mscan

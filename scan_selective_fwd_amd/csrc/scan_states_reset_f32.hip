@@ -9,4 +9,9 @@ hipError_t dispatch_chunk_states_reset_f32(const FwdParams& p, int disc, bool ve
   return dispatch_fwd_reset_t<float, kItemsBwd, kModeChunkStates>(p, disc, vec, stream);
 }
 
+hipError_t dispatch_chunk_states_fix_reset_f32(const FwdParams& p, int disc, bool vec,
+                                            hipStream_t stream) {
+  return dispatch_fwd_reset_t<float, kItemsBwd, kModeChunkStates, true>(p, disc, vec, stream);
+}
+
 }  // namespace mscan

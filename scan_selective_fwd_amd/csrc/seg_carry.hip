@@ -1,16 +1,17 @@
 // Carry between the segments of a segmented forward scan.
 //
 // Long sequences with few channels are split into segments that run in
-// parallel.  A first launch of the forward kernel (summary mode) gives each
-// segment's end state from a zero start and its delta sum.  This kernel
-// walks the segments of each (channel, state) in order: the state entering
-// segment s+1 is the one entering s, decayed by exp(A * sum of delta over s),
-// plus s's end state from zero.  That is the associative combination of the
-// (Abar, Bbar u) pairs the pages' parallel scan is built on (trishampatil
-// essay, Part III §2), applied to whole segments; the chunking follows the
-// same essay's Part III §4.  The forward kernel then runs every segment from
-// its entering state.  A segment that contains a reset flag passes nothing on
-// (its keep factor is 0).
+// parallel.  A first launch of the forward kernel runs every segment from a
+// zero state and gives each segment's end state and its delta sum.  This
+// kernel walks the segments of each (channel, state) in order: the state
+// entering segment s+1 is the one entering s, decayed by exp(A * sum of delta
+// over s), plus s's end state from zero.  That is the associative combination
+// of the (Abar, Bbar u) pairs the pages' parallel scan is built on
+// (trishampatil essay, Part III §2), applied to whole segments; the chunking
+// follows the same essay's Part III §4.  The state after the last segment is
+// the sequence's last state.  A second launch of the forward kernel then
+// corrects each segment's first chunks from its entering state.  A segment
+// that contains a reset flag passes nothing on (its keep factor is 0).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -32,6 +33,7 @@ static __global__ __launch_bounds__(256) void seg_carry_kernel(const FwdParams p
     const float decay = exp2f(a2 * p.seg_dsum[k]) * p.seg_keep[k];
     H = __builtin_fmaf(decay, H, p.seg_state[k * p.N + n]);
   }
+  if (p.last_state) p.last_state[c * p.N + n] = H;
 }
 
 hipError_t dispatch_seg_carry(const FwdParams& p, hipStream_t s) {

@@ -45,10 +45,10 @@ hipError_t dispatch_scan_fwd_reset_f32(const FwdParams&, int, bool, hipStream_t)
 hipError_t dispatch_scan_fwd_reset_bf16(const FwdParams&, int, bool, hipStream_t) {
   return reached();
 }
-hipError_t dispatch_seg_summary_reset_f32(const FwdParams&, int, bool, hipStream_t) {
+hipError_t dispatch_scan_fwd_fix_reset_f32(const FwdParams&, int, bool, hipStream_t) {
   return reached();
 }
-hipError_t dispatch_seg_summary_reset_bf16(const FwdParams&, int, bool, hipStream_t) {
+hipError_t dispatch_scan_fwd_fix_reset_bf16(const FwdParams&, int, bool, hipStream_t) {
   return reached();
 }
 hipError_t dispatch_chunk_states_reset_f32(const FwdParams&, int, bool, hipStream_t) {
@@ -57,13 +57,33 @@ hipError_t dispatch_chunk_states_reset_f32(const FwdParams&, int, bool, hipStrea
 hipError_t dispatch_chunk_states_reset_bf16(const FwdParams&, int, bool, hipStream_t) {
   return reached();
 }
-hipError_t dispatch_seg_summary_f32(const FwdParams&, int, bool, hipStream_t) {
+hipError_t dispatch_scan_fwd_fix_f32(const FwdParams&, int, bool, hipStream_t) {
   return reached();
 }
-hipError_t dispatch_seg_summary_bf16(const FwdParams&, int, bool, hipStream_t) {
+hipError_t dispatch_scan_fwd_fix_bf16(const FwdParams&, int, bool, hipStream_t) {
   return reached();
 }
 hipError_t dispatch_seg_carry(const FwdParams&, hipStream_t) { return reached(); }
+hipError_t dispatch_seg_summary_f32(const FwdParams&, int, bool, hipStream_t) { return reached(); }
+hipError_t dispatch_seg_summary_bf16(const FwdParams&, int, bool, hipStream_t) { return reached(); }
+hipError_t dispatch_seg_summary_reset_f32(const FwdParams&, int, bool, hipStream_t) {
+  return reached();
+}
+hipError_t dispatch_seg_summary_reset_bf16(const FwdParams&, int, bool, hipStream_t) {
+  return reached();
+}
+hipError_t dispatch_chunk_states_fix_f32(const FwdParams&, int, bool, hipStream_t) {
+  return reached();
+}
+hipError_t dispatch_chunk_states_fix_bf16(const FwdParams&, int, bool, hipStream_t) {
+  return reached();
+}
+hipError_t dispatch_chunk_states_fix_reset_f32(const FwdParams&, int, bool, hipStream_t) {
+  return reached();
+}
+hipError_t dispatch_chunk_states_fix_reset_bf16(const FwdParams&, int, bool, hipStream_t) {
+  return reached();
+}
 #define STUB_BWD(NAME)                                                                   \
   hipError_t NAME(const BwdParams&, int, bool, hipStream_t, hipEvent_t, hipEvent_t) { \
     return reached();                                                                    \

@@ -38,11 +38,12 @@ def _positive_steps(inp, dtype):
 
 
 def run_fwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=False, opts=None,
-                 zero_A=False, A_mode="s4d_real", rtol=None, segments=0, reset=None):
+                 zero_A=False, A_mode="s4d_real", rtol=None, segments=0, reset=None,
+                 h0_scale=1.0):
     opts = opts or {}
     announce(f"fwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} lanes={lanes} "
-             f"softplus={softplus} h0={h0} opts={opts} zero_A={zero_A} segments={segments} "
-             f"resets={None if reset is None else int(reset.sum())}")
+             f"softplus={softplus} h0={h0}x{h0_scale} opts={opts} zero_A={zero_A} "
+             f"segments={segments} resets={None if reset is None else int(reset.sum())}")
     inp, f = _make(wid, batch, dim, N, L, dtype, A_mode=A_mode, **opts)
     if not softplus:
         inp, f = _positive_steps(inp, dtype)
@@ -51,7 +52,8 @@ def run_fwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=
         f["A"] = inp["A"].astype(np.float64)
     h0v = None
     if h0:
-        h0v = np.random.default_rng(wid).standard_normal((batch, dim, N)).astype(np.float32)
+        h0v = (np.random.default_rng(wid).standard_normal((batch, dim, N))
+               * h0_scale).astype(np.float32)
     g = to_device(inp, dtype)
     h0t = torch.from_numpy(h0v).cuda() if h0v is not None else None
     out, last = ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g.get("D"), g.get("z"),
@@ -130,6 +132,37 @@ def test_fwd_segmented_state_sizes_initial_state_zero_A():
     run_fwd_case(20, 2, 9, 33, 1300, "f32", "zoh", segments=4, A_mode="random_neg")
     run_fwd_case(21, 1, 12, 16, 1024, "f32", "zoh", segments=8, zero_A=True, h0=True)
     run_fwd_case(21, 1, 12, 16, 1024, "f32", "euler", segments=5, softplus=False, h0=True)
+
+
+# Long segments (at least 16 chunks) run from a zero state first; after the
+# carry a second launch redoes each segment's first chunks from its entering
+# state, until what is left of that state is below float32 resolution.
+# 4173 steps are 33 chunks (ragged): 2 segments of 17 and 16 chunks.
+LONG_L = 4173
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_fwd_long_segments(dtype, disc):
+    run_fwd_case(58, 1, 20, 16, LONG_L, dtype, disc, segments=2, h0=True)
+
+
+def test_fwd_long_segments_edge_cases():
+    run_fwd_case(59, 2, 9, 5, LONG_L, "f32", "zoh", segments=2, h0=True)
+    run_fwd_case(59, 2, 9, 33, LONG_L, "f32", "zoh", segments=2, A_mode="random_neg")
+    # A = 0 channels never forget the entering state: the second launch
+    # redoes the whole segment
+    run_fwd_case(60, 1, 12, 16, LONG_L, "f32", "zoh", segments=2, zero_A=True, h0=True)
+    # a huge initial state takes longer to fall below resolution
+    run_fwd_case(61, 1, 12, 16, LONG_L, "f32", "zoh", segments=2, h0=True, h0_scale=1e20)
+    # small steps decay slowly
+    run_fwd_case(62, 1, 12, 16, LONG_L, "f32", "euler", segments=2, softplus=False, h0=True)
+    # resets, one in the second segment's first chunk
+    rs = W.make_resets(63, 2, LONG_L, 100, 1500, force=(0, 17 * 128 + 5))
+    rs[1, :] = 0
+    rs[1, 3000] = 1
+    run_fwd_case(63, 2, 9, 16, LONG_L, "f32", "zoh", segments=2, h0=True, reset=rs)
+    run_fwd_case(63, 2, 9, 16, LONG_L, "bf16", "euler", segments=2, reset=rs)
 
 
 def test_fwd_automatic_segmentation():
@@ -408,10 +441,21 @@ def test_bwd_automatic_segmentation():
         assert_match(to_f64(res[k]), to_f64(one[k]), RTOL["f32"], k + " auto vs one pass")
 
 
+def test_bwd_long_segments():
+    # the state pass in the long-segment scheme (zero start, carry, correction)
+    run_bwd_case(64, 1, 20, 16, LONG_L, "f32", "zoh", h0=True, segments=2)
+    run_bwd_case(64, 1, 20, 16, LONG_L, "bf16", "euler", h0=True, segments=2)
+    run_bwd_case(65, 1, 12, 16, LONG_L, "f32", "zoh", zero_A=True, h0=True, segments=2)
+    rs = W.make_resets(66, 2, LONG_L, 100, 1500, force=(0, 17 * 128 + 5))
+    run_bwd_case(66, 2, 9, 5, LONG_L, "f32", "zoh", h0=True, reset=rs, segments=2)
+
+
 def test_bwd_segmented_from_checkpoints():
     _ckpt_case(57, 1, 16, 16, 2048, "f32", "zoh", h0=True, segments=4, bwd_segments=4)
     _ckpt_case(57, 2, 9, 5, 1000, "bf16", "euler", bwd_segments=3,
                reset=W.make_resets(57, 2, 1000, 20, 300, force=(0, 384)))
+    # checkpoints from a forward in the long-segment scheme
+    _ckpt_case(67, 1, 16, 16, LONG_L, "f32", "zoh", h0=True, segments=2, bwd_segments=2)
 
 
 def test_bwd_rejects_other_lane_counts():
