@@ -5,7 +5,10 @@ checkpoints, the backward from them and a decode step can be captured once
 with torch.cuda.graph and replayed.  Each replay follows eager work that
 overwrites the outputs and a synchronization, and is checked against the
 eager run (the forward bit for bit; the backward, whose reductions use float
-atomics, to rounding) and against the float64 oracle."""
+atomics, to rounding) and against the float64 oracle.  The step is captured in
+one pass and in both segmented schemes (short segments with a summary pass,
+long ones with the zero-start pass and its correction), the backward from the
+forward's checkpoints and recomputing its states."""
 import numpy as np
 import pytest
 import torch
@@ -18,29 +21,40 @@ from parity_utils import RTOL, announce, assert_match, to_device, to_f64
 pytestmark = pytest.mark.gpu
 
 
-def test_captured_step_replays_match_eager_and_oracle():
-    wid, batch, dim, N, L = 82, 2, 20, 16, 700
-    announce(f"graph capture wid={wid} shape=({batch},{dim},{N},{L}) f32 zoh")
+# (wid, batch, dim, N, L, segments, checkpoints): one pass; short segments (a
+# summary pass); long segments (zero-start pass and correction), with the
+# backward from the forward's checkpoints and recomputing its states
+CASES = [(82, 2, 20, 16, 700, 0, True),
+         (83, 1, 20, 16, 1189, 4, False),
+         (84, 1, 20, 16, 4173, 2, True),
+         (85, 1, 20, 16, 4173, 2, False)]
+
+
+@pytest.mark.parametrize("wid,batch,dim,N,L,segments,use_ckpt", CASES)
+def test_captured_step_replays_match_eager_and_oracle(wid, batch, dim, N, L, segments, use_ckpt):
+    announce(f"graph capture wid={wid} shape=({batch},{dim},{N},{L}) f32 zoh "
+             f"segments={segments} checkpoints={use_ckpt}")
     inp = W.make_inputs(wid, batch, dim, N, L, dtype="f32", bias="uniform", with_dout=True)
     f = W.inputs_f64(inp, "f32")
     t = to_device(inp, "f32")
     f32 = dict(dtype=torch.float32, device="cuda")
     out = torch.empty((batch, dim, L), **f32)
     state = torch.empty((batch, dim, N), **f32)      # final state, then one decode step
-    ckpt = torch.empty(ms.checkpoint_shape(batch, dim, N, L), **f32)
+    ckpt = torch.empty(ms.checkpoint_shape(batch, dim, N, L), **f32) if use_ckpt else None
     step_out = torch.empty((batch, dim), **f32)
-    nf = ms.fwd_workspace_bytes(batch, dim, N, L, torch.float32)
+    nf = ms.fwd_workspace_bytes(batch, dim, N, L, torch.float32, segments=segments)
     fws = torch.empty(nf, dtype=torch.uint8, device="cuda") if nf else None
-    bws = torch.empty(ms.bwd_workspace_bytes(batch, dim, N, L, torch.float32), dtype=torch.uint8,
-                      device="cuda")
+    bws = torch.empty(ms.bwd_workspace_bytes(batch, dim, N, L, torch.float32, segments=segments),
+                      dtype=torch.uint8, device="cuda")
     step = {k: t[k][..., 0].contiguous() for k in ("u", "delta", "B", "C", "z")}
 
     def run():
         ms.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
                     out=out, last_state=state, return_last_state=True, workspace=fws,
-                    checkpoints=ckpt)
+                    checkpoints=ckpt, segments=segments)
         grads = ms.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
-                            t["delta_bias"], t["dout"], workspace=bws, checkpoints=ckpt)
+                            t["delta_bias"], t["dout"], workspace=bws, checkpoints=ckpt,
+                            segments=segments)
         ms.state_update(state, step["u"], step["delta"], t["A"], step["B"], step["C"], t["D"],
                         step["z"], t["delta_bias"], out=step_out)
         return grads
@@ -64,8 +78,10 @@ def test_captured_step_replays_match_eager_and_oracle():
 
     for r in range(3):
         # eager work between replays: every output overwritten
-        for buf in (out, state, step_out, ckpt, *graph_g.values()):
+        for buf in (out, state, step_out, *graph_g.values()):
             buf.fill_(float("nan"))
+        if ckpt is not None:
+            ckpt.fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -76,9 +92,15 @@ def test_captured_step_replays_match_eager_and_oracle():
         for k in eager:
             assert_match(to_f64(graph_g[k]), to_f64(eager[k]), 1e-5, f"replay {r} {k}")
 
-    ref_out, _ = oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
-                                 f["delta_bias"])
+    ref_out, ref_last = oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"],
+                                        f["z"], f["delta_bias"])
     assert_match(to_f64(out), ref_out, RTOL["f32"], "graph out vs oracle")
+    # the decode step continued from the forward's last state
+    ref_step, ref_state = oracle.state_update(ref_last, f["u"][..., 0], f["delta"][..., 0],
+                                              f["A"], f["B"][..., 0], f["C"][..., 0], f["D"],
+                                              f["z"][..., 0], f["delta_bias"])
+    assert_match(to_f64(state), ref_state, RTOL["f32"], "graph decode state vs oracle")
+    assert_match(to_f64(step_out), ref_step, RTOL["f32"], "graph decode out vs oracle")
     ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
                           f["delta_bias"], f["dout"])
     for k in ref:
