@@ -5,6 +5,9 @@ Workloads 2, 3 and 5 are compared element by element with the float64 oracle
 over every channel (the oracle is threaded over channels).  Workload 4
 (L = 1,048,576) is compared on sampled channels, which the oracle
 regenerates row by row from the same seeds, including their final states.
+The backward over a long sequence with workload 4's channels (segmented) is
+compared on sampled channels too, with dout zero elsewhere so that the
+gradients summed over channels (dB, dC) come from the sampled ones alone.
 """
 import numpy as np
 import pytest
@@ -100,3 +103,39 @@ def test_workload5_bwd_full():
     for k in ref:
         errs[k] = assert_match(got[k], ref[k], RTOL["bf16"], k)
     print(f"workload 5 rel errors {errs}", flush=True)
+
+
+def test_long_sequence_bwd_segmented_sampled_channels():
+    # batch 1, D 1536, 131072 steps: 1024 chunks over 96 channel groups, so
+    # the automatic choice runs 32 segments of 32 chunks (the zero-start state
+    # pass with its correction, then the reverse adjoint carry)
+    wid, batch, dim, N, L = 68, 1, 1536, 16, 1 << 17
+    announce(f"long-sequence bwd bf16 ({batch},{dim},{N},{L}) sampled channels")
+    assert ms.bwd_workspace_bytes(batch, dim, N, L, torch.bfloat16) > \
+        ms.bwd_workspace_bytes(batch, dim, N, L, torch.bfloat16, segments=1)
+    inp = W.make_inputs(wid, batch, dim, N, L, dtype="bf16", bias="const", per_row=True,
+                        with_dout=True)
+    chans = [0, 1, 700, 1535]
+    others = np.ones(dim, bool)
+    others[chans] = False
+    inp["dout"][:, others] = 0          # bf16 +0.0
+    g = to_device(inp, "bf16")
+    res = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                      g["delta_bias"], g["dout"])
+    torch.cuda.synchronize()
+    for k in ("du", "ddelta", "dz"):
+        assert not res[k][:, torch.from_numpy(others).cuda()].any(), k + ": unsampled channel"
+    got = {k: to_f64(v[:, chans]) for k, v in res.items() if k in ("du", "ddelta", "dz")}
+    got.update({k: to_f64(res[k][chans]) for k in ("dA", "dD", "ddelta_bias")})
+    got.update({k: to_f64(res[k]) for k in ("dB", "dC")})
+    del g, res
+    sub = {k: (v[:, chans] if k in ("u", "delta", "z", "dout") else
+               v[chans] if k in ("A", "D", "delta_bias") else v) for k, v in inp.items()}
+    del inp
+    f = W.inputs_f64(sub, "bf16")
+    ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                          f["delta_bias"], f["dout"])
+    errs = {}
+    for k in got:
+        errs[k] = assert_match(got[k], ref[k], RTOL["bf16"], k)
+    print(f"long-sequence bwd rel errors {errs}", flush=True)
