@@ -220,14 +220,24 @@ mamba_status mamba_scan_bwd_varlen(const void* u, const void* delta, const float
  * B and C (batch, dstate, seqlen), h0 and last_state (batch, dim, dstate),
  * both nullable.  u, delta, z, out follow mamba_scan_fwd (float32 or
  * bfloat16); D, delta_bias float32.  dstate <= 16 (MAMBA_ERR_UNSUPPORTED
- * otherwise).  No workspace; errors as for mamba_scan_fwd.
+ * otherwise).  Errors as for mamba_scan_fwd.  The workspace, of
+ * mamba_scan_fwd_complex_workspace_size bytes (0 when not needed; then it
+ * may be NULL), plays the part it does for mamba_scan_fwd: for long
+ * sequences over few channels the sequence is split into segments run in
+ * parallel, joined by an exact carry of the complex state (per channel,
+ * segment and state: the end state from zero, the entering state and the
+ * segment's product of Abar).  Given less, the call runs in one pass.
  */
+size_t mamba_scan_fwd_complex_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                             int64_t seqlen);
+
 mamba_status mamba_scan_fwd_complex(const void* u, const void* delta, const float* A,
                                     const float* B, const float* C, const float* D,
                                     const void* z, const float* delta_bias, const float* h0,
                                     int delta_softplus, mamba_disc disc, mamba_dtype dt,
                                     int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                                    void* out, float* last_state, void* stream);
+                                    void* out, float* last_state, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent (decode) step of the complex-valued model, in place on the
@@ -256,8 +266,13 @@ mamba_status mamba_state_update_complex(float* state, const void* u, const void*
  * (interleaved pairs); du, ddelta, dz (batch, dim, seqlen) and dD,
  * ddelta_bias (dim) are real float32.  Null-pairing rules, dtypes and errors
  * follow mamba_scan_bwd; the workspace is
- * mamba_scan_bwd_complex_workspace_size bytes.  Reductions use float32
- * atomics (deterministic up to rounding order).
+ * mamba_scan_bwd_complex_workspace_size bytes: the chunk states, plus,
+ * where the sequence is split into segments (the shapes mamba_scan_bwd
+ * splits), the state pass's segment buffers and the adjoint's (its value at
+ * each segment's start from a zero end, the value entering the segment, and
+ * the segment's product of conj(Abar)).  Given only the unsegmented size it
+ * runs in one pass.  Reductions use float32 atomics (deterministic up to
+ * rounding order).
  */
 size_t mamba_scan_bwd_complex_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
                                              int64_t seqlen);
@@ -384,15 +399,26 @@ size_t mamba_scan_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate, in
  *    complex state entering every 128-step chunk, (batch, dim,
  *    ceil(seqlen/128), dstate) interleaved (re, im) float32 pairs,
  *    mamba_scan_complex_checkpoint_size bytes, 16-byte aligned.  A backward
- *    given the buffer skips its state-recompute pass and needs no workspace
- *    (workspace may be NULL, workspace_bytes 0).  The backward still replays
+ *    given the buffer skips its state-recompute pass and needs only the
+ *    workspace's segment buffers (none in one pass: workspace may then be
+ *    NULL, workspace_bytes 0).  The backward still replays
  *    every state inside each chunk from its checkpoint (paper-graph-ui
  *    summary, section 3.4, and trishampatil essay, Part III §4: only the
  *    chunk-boundary states are kept).  Checkpoints must come from a forward
  *    over the same inputs.
+ *  - segments: as for the real _ex calls (0 = automatic, 1 = one pass, k =
+ *    k segments of whole chunks); explicit segments need the workspace the
+ *    _ex size queries report for the same count (MAMBA_ERR_WORKSPACE
+ *    otherwise).
  */
 size_t mamba_scan_complex_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate,
                                           int64_t seqlen);
+
+size_t mamba_scan_fwd_complex_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
+                                                int64_t seqlen, int segments);
+
+size_t mamba_scan_bwd_complex_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
+                                                int64_t seqlen, int segments);
 
 mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const float* A,
                                        const float* B, const float* C, const float* D,
@@ -400,7 +426,8 @@ mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const f
                                        int delta_softplus, mamba_disc disc, mamba_dtype dt,
                                        int64_t batch, int64_t dim, int64_t dstate,
                                        int64_t seqlen, void* out, float* last_state,
-                                       float* checkpoints, void* stream);
+                                       float* checkpoints, void* workspace,
+                                       size_t workspace_bytes, void* stream, int segments);
 
 mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const float* A,
                                        const float* B, const float* C, const float* D,
@@ -410,7 +437,8 @@ mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const f
                                        int64_t dstate, int64_t seqlen, float* du, float* ddelta,
                                        float* dA, float* dB, float* dC, float* dD, float* dz,
                                        float* ddelta_bias, float* dh0, const float* checkpoints,
-                                       void* workspace, size_t workspace_bytes, void* stream);
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       int segments);
 
 #ifdef __cplusplus
 }

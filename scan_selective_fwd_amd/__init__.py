@@ -280,13 +280,29 @@ def complex_checkpoint_shape(batch, dim, N, L):
     return (batch, dim, (L + 127) // 128, N)
 
 
+def fwd_complex_workspace_bytes(batch, dim, N, L, segments=0) -> int:
+    n = lib().mamba_scan_fwd_complex_workspace_size_ex(batch, dim, N, L, int(segments))
+    if n >= 2 ** 63:
+        raise MambaScanError(6, "mamba_scan_fwd_complex_workspace_size")
+    return int(n)
+
+
+def bwd_complex_workspace_bytes(batch, dim, N, L, segments=0) -> int:
+    n = lib().mamba_scan_bwd_complex_workspace_size_ex(batch, dim, N, L, int(segments))
+    if n >= 2 ** 63:
+        raise MambaScanError(6, "mamba_scan_bwd_complex_workspace_size")
+    return int(n)
+
+
 def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
-                     delta_softplus=True, disc="zoh", out=None, checkpoints=None):
+                     delta_softplus=True, disc="zoh", out=None, checkpoints=None, segments=0,
+                     workspace=None):
     """Complex-valued forward: A (dim, N), B, C (batch, N, L), h0 (batch, dim,
     N) complex64; u, delta, z real.  Returns (out, last_state complex64) with
     y = Re(sum_n C h) + D u gated by SiLU(z).  `checkpoints`: optional
     complex64 tensor of complex_checkpoint_shape, filled with the state
-    entering every chunk (for scan_bwd_complex)."""
+    entering every chunk (for scan_bwd_complex).  `segments`: 0 = automatic,
+    1 = one pass, k = k sequence segments run in parallel."""
     L_ = lib()
     if not u.is_cuda:
         raise ValueError("u must be a GPU tensor (no CPU path exists)")
@@ -308,22 +324,29 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None
     if out is None:
         out = torch.empty((batch, dim, L), dtype=sdt, device=dev)
     last = torch.empty((batch, dim, N), dtype=torch.complex64, device=dev)
+    nbytes = fwd_complex_workspace_bytes(batch, dim, N, L, segments)
+    if nbytes and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if nbytes else None
     st = L_.mamba_scan_fwd_complex_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                       _ptr(z), _ptr(delta_bias), _ptr(h0),
                                       int(bool(delta_softplus)), _disc_code(disc),
                                       _dtype_code(u), batch, dim, N, L, _ptr(out), _ptr(last),
-                                      _ptr(checkpoints), _stream(dev))
+                                      _ptr(checkpoints), ws_ptr, nbytes, _stream(dev),
+                                      int(segments))
     _lib.check(st, "mamba_scan_fwd_complex_ex")
     return out, last
 
 
 def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
-                     delta_softplus=True, disc="zoh", checkpoints=None):
+                     delta_softplus=True, disc="zoh", checkpoints=None, segments=0,
+                     workspace=None):
     """Backward of scan_fwd_complex.  Returns a dict: du, ddelta (and dD, dz,
     ddelta_bias when given) float32; dA, dB, dC (and dh0) complex64, the
     gradient of a complex input w being dL/dRe(w) + i dL/dIm(w).
     `checkpoints`: the buffer a scan_fwd_complex over the same inputs filled;
-    the chunk states are then not recomputed."""
+    the chunk states are then not recomputed.  `segments` as for
+    scan_fwd_complex."""
     L_ = lib()
     dev = u.device
     batch, dim, L = u.shape
@@ -353,13 +376,17 @@ def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
         g["ddelta_bias"] = torch.empty((dim,), **f32)
     if h0 is not None:
         g["dh0"] = torch.empty((batch, dim, N), **c64)
+    nbytes = bwd_complex_workspace_bytes(batch, dim, N, L, segments)
+    if checkpoints is not None:
+        # the chunk states (the workspace's first part, 256-byte rounded) come
+        # from the checkpoints instead
+        states = 8 * batch * dim * N * ((L + 127) // 128)
+        nbytes -= (states + 255) // 256 * 256
     ws_ptr, ws_bytes = None, 0
-    if checkpoints is None:
-        nbytes = int(L_.mamba_scan_bwd_complex_workspace_size(batch, dim, N, L))
-        if nbytes >= 2 ** 63:
-            raise MambaScanError(6, "mamba_scan_bwd_complex_workspace_size")
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-        ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
+    if nbytes > 0:
+        if workspace is None or workspace.numel() < nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     st = L_.mamba_scan_bwd_complex_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                       _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(dout),
                                       int(bool(delta_softplus)), _disc_code(disc),
@@ -367,7 +394,8 @@ def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
                                       _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
                                       _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
                                       _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")),
-                                      _ptr(checkpoints), ws_ptr, ws_bytes, _stream(dev))
+                                      _ptr(checkpoints), ws_ptr, ws_bytes, _stream(dev),
+                                      int(segments))
     _lib.check(st, "mamba_scan_bwd_complex_ex")
     return g
 

@@ -32,6 +32,8 @@ EXPORTS = (
     "mamba_scan_bwd_complex", "mamba_scan_bwd_complex_workspace_size",
     "mamba_scan_complex_checkpoint_size", "mamba_scan_fwd_complex_ex",
     "mamba_scan_bwd_complex_ex", "mamba_state_update_complex",
+    "mamba_scan_fwd_complex_workspace_size", "mamba_scan_fwd_complex_workspace_size_ex",
+    "mamba_scan_bwd_complex_workspace_size_ex",
 )
 
 
@@ -99,7 +101,14 @@ def load(path: str = LIB_PATH):
     lib.mamba_conv1d_silu_bwd.restype = _int
     lib.mamba_conv1d_silu_bwd.argtypes = [_vp] * 5 + [_i64, _int] + [_i64] * 3 + [_vp] * 4
     lib.mamba_scan_fwd_complex.restype = _int
-    lib.mamba_scan_fwd_complex.argtypes = [_vp] * 9 + [_int, _int, _int] + [_i64] * 4 + [_vp] * 3
+    lib.mamba_scan_fwd_complex.argtypes = ([_vp] * 9 + [_int, _int, _int] + [_i64] * 4
+                                           + [_vp] * 3 + [_sz, _vp])
+    lib.mamba_scan_fwd_complex_workspace_size.restype = _sz
+    lib.mamba_scan_fwd_complex_workspace_size.argtypes = [_i64] * 4
+    lib.mamba_scan_fwd_complex_workspace_size_ex.restype = _sz
+    lib.mamba_scan_fwd_complex_workspace_size_ex.argtypes = [_i64] * 4 + [_int]
+    lib.mamba_scan_bwd_complex_workspace_size_ex.restype = _sz
+    lib.mamba_scan_bwd_complex_workspace_size_ex.argtypes = [_i64] * 4 + [_int]
     lib.mamba_scan_bwd_complex.restype = _int
     lib.mamba_scan_bwd_complex.argtypes = bwd_args
     lib.mamba_scan_bwd_complex_workspace_size.restype = _sz
@@ -108,10 +117,10 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_complex_checkpoint_size.argtypes = [_i64] * 4
     lib.mamba_scan_fwd_complex_ex.restype = _int
     lib.mamba_scan_fwd_complex_ex.argtypes = ([_vp] * 9 + [_int, _int, _int] + [_i64] * 4
-                                              + [_vp] * 4)
+                                              + [_vp] * 4 + [_sz, _vp, _int])
     lib.mamba_scan_bwd_complex_ex.restype = _int
     lib.mamba_scan_bwd_complex_ex.argtypes = ([_vp] * 10 + [_int, _int, _int] + [_i64] * 4
-                                              + [_vp] * 11 + [_sz, _vp])
+                                              + [_vp] * 11 + [_sz, _vp, _int])
     lib.mamba_state_update_complex.restype = _int
     lib.mamba_state_update_complex.argtypes = ([_vp] * 9 + [_int, _int, _int] + [_i64] * 3
                                                + [_vp, _vp])

@@ -201,6 +201,31 @@ BwdSegBuffers bwd_seg_buffers(const BwdLayout& w, int64_t nchannels, int64_t dst
   return s;
 }
 
+// Complex workspaces (complex float32 = 8 bytes).  Forward (segmented only):
+// per channel, segment and state the end state from zero, the entering state
+// and prod(Abar).  Backward: the chunk-start states (unless the forward's
+// checkpoints are given), then, segmented, the same three buffers for the
+// state pass and three for the adjoint (G from a zero end, the entering
+// adjoint, prod(conj Abar)).  Segments as in the real calls.
+struct CplxLayout {
+  int64_t nchunks, groups, nseg, seg_chunks;
+  size_t off_seg, nst, total;
+};
+
+CplxLayout cplx_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                       int64_t segments, bool bwd) {
+  const BwdLayout b = bwd_layout(batch, dim, dstate, seqlen, segments);
+  CplxLayout w;
+  w.nchunks = b.nchunks;
+  w.groups = b.groups;
+  w.nseg = b.nseg;
+  w.seg_chunks = b.seg_chunks;
+  w.off_seg = bwd ? round_up((size_t)(batch * dim) * (size_t)w.nchunks * (size_t)dstate * 8) : 0;
+  w.nst = round_up((size_t)(batch * dim) * (size_t)w.nseg * (size_t)dstate * 8);
+  w.total = w.off_seg + (w.nseg > 1 ? (bwd ? 6 : 3) * w.nst : 0);
+  return w;
+}
+
 inline mamba_status hip_status(hipError_t e) { return e == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP; }
 
 }  // namespace
@@ -576,15 +601,30 @@ size_t mamba_scan_complex_checkpoint_size(int64_t batch, int64_t dim, int64_t ds
   return (size_t)(batch * dim) * (size_t)w.nchunks * (size_t)dstate * 8;
 }
 
+size_t mamba_scan_fwd_complex_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
+                                                int64_t seqlen, int segments) {
+  if (check_sizes(MAMBA_F32, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK ||
+      dstate > 16 || segments < 0)
+    return SIZE_MAX;
+  const int64_t want = segments != 0 ? segments : auto_segments(batch, dim, seqlen);
+  return cplx_layout(batch, dim, dstate, seqlen, want, false).total;
+}
+
+size_t mamba_scan_fwd_complex_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                             int64_t seqlen) {
+  return mamba_scan_fwd_complex_workspace_size_ex(batch, dim, dstate, seqlen, 0);
+}
+
 mamba_status mamba_scan_fwd_complex(const void* u, const void* delta, const float* A,
                                     const float* B, const float* C, const float* D,
                                     const void* z, const float* delta_bias, const float* h0,
                                     int delta_softplus, mamba_disc disc, mamba_dtype dt,
                                     int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                                    void* out, float* last_state, void* stream) {
+                                    void* out, float* last_state, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   return mamba_scan_fwd_complex_ex(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, disc,
                                    dt, batch, dim, dstate, seqlen, out, last_state, nullptr,
-                                   stream);
+                                   workspace, workspace_bytes, stream, 0);
 }
 
 mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const float* A,
@@ -593,14 +633,24 @@ mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const f
                                        int delta_softplus, mamba_disc disc, mamba_dtype dt,
                                        int64_t batch, int64_t dim, int64_t dstate,
                                        int64_t seqlen, void* out, float* last_state,
-                                       float* checkpoints, void* stream) {
+                                       float* checkpoints, void* workspace,
+                                       size_t workspace_bytes, void* stream, int segments) {
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
   if (st != MAMBA_OK) return st;
-  if (dstate > 16) return MAMBA_ERR_UNSUPPORTED;
+  if (dstate > 16 || segments < 0) return MAMBA_ERR_UNSUPPORTED;
   if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL_PTR;
-  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, out, last_state, checkpoints};
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, out, last_state, checkpoints,
+                        workspace};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MAMBA_ERR_ALIGNMENT;
+  const int64_t want = segments != 0 ? segments : auto_segments(batch, dim, seqlen);
+  CplxLayout w = cplx_layout(batch, dim, dstate, seqlen, want, false);
+  bool segmented = w.nseg > 1;
+  if (segmented && (!workspace || workspace_bytes < w.total)) {
+    if (segments != 0) return MAMBA_ERR_WORKSPACE;
+    segmented = false;   // automatic choice without the workspace: one pass
+    w = cplx_layout(batch, dim, dstate, seqlen, 1, false);
+  }
   mscan::CplxParams p;
   memset(&p, 0, sizeof(p));
   p.u = u; p.delta = delta; p.A = reinterpret_cast<const float2*>(A);
@@ -609,21 +659,41 @@ mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const f
   p.out = out; p.last_state = reinterpret_cast<float2*>(last_state);
   p.chunk_states = reinterpret_cast<float2*>(checkpoints);
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
-  p.groups = mscan::channel_groups(dim, 16);
+  p.groups = w.groups;
+  p.nseg = 1;
   p.N = (int)dstate; p.softplus = delta_softplus ? 1 : 0;
-  if (batch * p.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
+  if (batch * p.groups > (int64_t)0x7FFFFFFF / w.nseg) return MAMBA_ERR_UNSUPPORTED;
   const bool vec = rows_aligned16(seqlen, elem_size(dt));
-  return hip_status(mscan::dispatch_scan_fwd_complex(p, dt == MAMBA_F32 ? 0 : 1, (int)disc, vec,
-                                                     static_cast<hipStream_t>(stream)));
+  const int dti = dt == MAMBA_F32 ? 0 : 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (segmented) {
+    // the summaries (each segment from zero), the carry (also the last
+    // state), then every segment from its entering state
+    char* ws = static_cast<char*>(workspace);
+    p.nseg = w.nseg;
+    p.seg_chunks = w.seg_chunks;
+    p.seg_state = reinterpret_cast<float2*>(ws);
+    p.seg_h0 = reinterpret_cast<float2*>(ws + w.nst);
+    p.seg_dec = reinterpret_cast<float2*>(ws + 2 * w.nst);
+    if (mscan::dispatch_seg_summary_complex(p, dti, (int)disc, vec, s) != hipSuccess)
+      return MAMBA_ERR_HIP;
+    if (mscan::dispatch_seg_carry_complex(p, s) != hipSuccess) return MAMBA_ERR_HIP;
+  }
+  return hip_status(mscan::dispatch_scan_fwd_complex(p, dti, (int)disc, vec, s));
+}
+
+size_t mamba_scan_bwd_complex_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate,
+                                                int64_t seqlen, int segments) {
+  if (check_sizes(MAMBA_F32, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK ||
+      dstate > 16 || segments < 0)
+    return SIZE_MAX;
+  const int64_t want = segments != 0 ? segments : bwd_auto_segments(batch, dim, seqlen);
+  return cplx_layout(batch, dim, dstate, seqlen, want, true).total;
 }
 
 size_t mamba_scan_bwd_complex_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
                                              int64_t seqlen) {
-  if (check_sizes(MAMBA_F32, MAMBA_DISC_ZOH, batch, dim, dstate, seqlen) != MAMBA_OK ||
-      dstate > 16)
-    return SIZE_MAX;
-  const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
-  return round_up((size_t)(batch * dim) * (size_t)w.nchunks * (size_t)dstate * 8);
+  return mamba_scan_bwd_complex_workspace_size_ex(batch, dim, dstate, seqlen, 0);
 }
 
 mamba_status mamba_scan_bwd_complex(const void* u, const void* delta, const float* A,
@@ -638,7 +708,7 @@ mamba_status mamba_scan_bwd_complex(const void* u, const void* delta, const floa
   return mamba_scan_bwd_complex_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout,
                                    delta_softplus, disc, dt, batch, dim, dstate, seqlen, du,
                                    ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, nullptr,
-                                   workspace, workspace_bytes, stream);
+                                   workspace, workspace_bytes, stream, 0);
 }
 
 mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const float* A,
@@ -649,10 +719,11 @@ mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const f
                                        int64_t dstate, int64_t seqlen, float* du, float* ddelta,
                                        float* dA, float* dB, float* dC, float* dD, float* dz,
                                        float* ddelta_bias, float* dh0, const float* checkpoints,
-                                       void* workspace, size_t workspace_bytes, void* stream) {
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       int segments) {
   mamba_status st = check_sizes(dt, disc, batch, dim, dstate, seqlen);
   if (st != MAMBA_OK) return st;
-  if (dstate > 16) return MAMBA_ERR_UNSUPPORTED;
+  if (dstate > 16 || segments < 0) return MAMBA_ERR_UNSUPPORTED;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
     return MAMBA_ERR_NULL_PTR;
   if ((D == nullptr) != (dD == nullptr) || (z == nullptr) != (dz == nullptr) ||
@@ -662,17 +733,26 @@ mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const f
                         dD, dz, ddelta_bias, dh0, workspace, checkpoints};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MAMBA_ERR_ALIGNMENT;
-  if (!checkpoints) {   // the chunk states are recomputed into the workspace
-    const size_t need = mamba_scan_bwd_complex_workspace_size(batch, dim, dstate, seqlen);
-    if (!workspace || workspace_bytes < need) return MAMBA_ERR_WORKSPACE;
+  const int64_t want = segments != 0 ? segments : bwd_auto_segments(batch, dim, seqlen);
+  CplxLayout w = cplx_layout(batch, dim, dstate, seqlen, want, true);
+  // with checkpoints the chunk-start states are not in the workspace
+  size_t need = checkpoints ? w.total - w.off_seg : w.total;
+  if (w.nseg > 1 && (!workspace || workspace_bytes < need)) {
+    if (segments != 0) return MAMBA_ERR_WORKSPACE;
+    w = cplx_layout(batch, dim, dstate, seqlen, 1, true);   // automatic: one pass
+    need = checkpoints ? w.total - w.off_seg : w.total;
   }
-  const BwdLayout w = bwd_layout(batch, dim, dstate, seqlen);
-  if (batch * w.groups > (int64_t)0x7FFFFFFF) return MAMBA_ERR_UNSUPPORTED;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MAMBA_ERR_WORKSPACE;
+  if (batch * w.groups > (int64_t)0x7FFFFFFF / w.nseg) return MAMBA_ERR_UNSUPPORTED;
+  const bool segmented = w.nseg > 1;
   const bool vec = rows_aligned16(seqlen, elem_size(dt));
   const int dti = dt == MAMBA_F32 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float2* states = checkpoints ? reinterpret_cast<float2*>(const_cast<float*>(checkpoints))
                                : static_cast<float2*>(workspace);
+  char* segbase = segmented ? static_cast<char*>(workspace) + (checkpoints ? 0 : w.off_seg)
+                            : nullptr;
+  auto seg_buf = [&](int i) { return reinterpret_cast<float2*>(segbase + i * w.nst); };
 
   mscan::CplxParams fp;
   memset(&fp, 0, sizeof(fp));
@@ -682,8 +762,23 @@ mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const f
   fp.chunk_states = states;
   fp.batch = batch; fp.dim = dim; fp.L = seqlen; fp.nchannels = batch * dim;
   fp.groups = w.groups; fp.N = (int)dstate; fp.softplus = delta_softplus ? 1 : 0;
-  if (!checkpoints && mscan::dispatch_chunk_states_complex(fp, dti, (int)disc, vec, s) != hipSuccess)
-    return MAMBA_ERR_HIP;
+  fp.nseg = 1;
+  if (!checkpoints) {
+    if (segmented) {
+      // the states at every chunk start, segment by segment: summaries,
+      // carry, then every segment from its entering state
+      fp.nseg = w.nseg;
+      fp.seg_chunks = w.seg_chunks;
+      fp.seg_state = seg_buf(0);
+      fp.seg_h0 = seg_buf(1);
+      fp.seg_dec = seg_buf(2);
+      if (mscan::dispatch_seg_summary_complex(fp, dti, (int)disc, vec, s) != hipSuccess)
+        return MAMBA_ERR_HIP;
+      if (mscan::dispatch_seg_carry_complex(fp, s) != hipSuccess) return MAMBA_ERR_HIP;
+    }
+    if (mscan::dispatch_chunk_states_complex(fp, dti, (int)disc, vec, s) != hipSuccess)
+      return MAMBA_ERR_HIP;
+  }
 
   mscan::CplxBwdParams p;
   memset(&p, 0, sizeof(p));
@@ -695,6 +790,16 @@ mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const f
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.nchunks = w.nchunks; p.groups = w.groups; p.N = (int)dstate;
   p.softplus = delta_softplus ? 1 : 0;
+  p.nseg = w.nseg;
+  p.seg_chunks = w.seg_chunks;
+  if (segmented) {
+    p.seg_gloc = seg_buf(3);
+    p.seg_gin = seg_buf(4);
+    p.seg_gdec = seg_buf(5);
+    if (mscan::dispatch_bwd_seg_summary_complex(p, dti, vec, s) != hipSuccess)
+      return MAMBA_ERR_HIP;
+    if (mscan::dispatch_bwd_seg_carry_complex(p, s) != hipSuccess) return MAMBA_ERR_HIP;
+  }
   return hip_status(mscan::dispatch_scan_bwd_complex(p, dti, (int)disc, vec, s));
 }
 

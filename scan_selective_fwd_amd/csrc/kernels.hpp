@@ -137,6 +137,15 @@ struct CplxParams {
   int64_t groups;          // channel groups of 16 per batch row
   float2* chunk_states;    // (nchannels, nchunks, N) state entering each chunk: the recompute
                            // pass, or checkpoints of the output pass (nullable there)
+  // Sequence segments, as in FwdParams (seg_chunks = 0, nseg = 1: the whole
+  // sequence).  The summary pass writes each segment's end state from zero
+  // and its decay prod(Abar) per state; the carry turns them into the state
+  // entering each segment, from which the output and state passes start.
+  int64_t seg_chunks;
+  int64_t nseg;
+  float2* seg_h0;          // (nchannels, nseg, N) state entering each segment (nullable)
+  float2* seg_state;       // summary: (nchannels, nseg, N) end state from a zero start
+  float2* seg_dec;         // summary: (nchannels, nseg, N) product of Abar over the segment
   int N;                   // <= 16
   int softplus;
 };
@@ -144,6 +153,10 @@ hipError_t dispatch_scan_fwd_complex(const CplxParams& p, int dtype, int disc, b
                                      hipStream_t s);
 hipError_t dispatch_chunk_states_complex(const CplxParams& p, int dtype, int disc, bool vec,
                                          hipStream_t s);
+hipError_t dispatch_seg_summary_complex(const CplxParams& p, int dtype, int disc, bool vec,
+                                        hipStream_t s);
+// Also writes p.last_state (the state after the last segment) when set.
+hipError_t dispatch_seg_carry_complex(const CplxParams& p, hipStream_t s);
 
 // Complex-valued decode step (state_update_complex.hip): one recurrence step
 // on a complex state, in place.  B, C are (batch, N) complex, A (dim, N).
@@ -192,11 +205,23 @@ struct CplxBwdParams {
   int64_t nchannels;
   int64_t nchunks;
   int64_t groups;
+  // Sequence segments: blocks (batch row, segment, group).  The adjoint
+  // entering each segment from the later ones comes from the adjoint summary
+  // (G at the segment start from a zero end, and prod(Abar) over the
+  // segment) and the reverse carry g <- G + conj(prod Abar) g.
+  int64_t seg_chunks;
+  int64_t nseg;
+  float2* seg_gin;         // (nchannels, nseg, N) adjoint entering each segment (nullable: 0)
+  float2* seg_gloc;        // summary: (nchannels, nseg, N)
+  float2* seg_gdec;        // summary: (nchannels, nseg, N)
   int N;                   // <= 16
   int softplus;
 };
 hipError_t dispatch_scan_bwd_complex(const CplxBwdParams& p, int dtype, int disc, bool vec,
                                      hipStream_t s);
+hipError_t dispatch_bwd_seg_summary_complex(const CplxBwdParams& p, int dtype, bool vec,
+                                            hipStream_t s);
+hipError_t dispatch_bwd_seg_carry_complex(const CplxBwdParams& p, hipStream_t s);
 
 // Short causal convolution + SiLU (conv1d_silu.hip).
 struct ConvParams {

@@ -20,6 +20,14 @@
 // once per block into an LDS tile (tile_stage.hpp; a complex row of TCH steps
 // is a float row of 2*TCH); the earlier chunk's loads are issued after the
 // state loop and written to the tile at the chunk's end.
+//
+// Long sequences with few channels are split into segments of whole chunks,
+// one block per (batch row, segment, channel group), as in the real backward:
+// the adjoint entering a segment from the right comes from the segments after
+// it, each of which maps the adjoint at its end to G + conj(prod Abar) times
+// it, G being its adjoint at its start from a zero end.  The summary and
+// carry kernels at the end of this file compute those; only segment 0 writes
+// dh0.
 #include "complex_common.hpp"
 #include "kernels.hpp"
 #include "scan_fwd_impl.hpp"
@@ -54,9 +62,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int j = lane % R;
   const int row = lane / R;
   const int cl = wave * (64 / R) + row;
+  // block order (b, segment, group) with the group fastest
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t b = blk / p.groups;
-  const int64_t grp = blk - b * p.groups;
+  const int64_t per_b = p.groups * p.nseg;
+  const int64_t b = blk / per_b;
+  const int64_t seg = (blk - b * per_b) / p.groups;
+  const int64_t grp = blk - b * per_b - seg * p.groups;
   const int64_t d_raw = grp * CPB + cl;
   const bool active = d_raw < p.dim;
   const int64_t d = active ? d_raw : p.dim - 1;
@@ -64,6 +75,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int N = p.N;
   const int64_t L = p.L;
   const int64_t nchunks = p.nchunks;
+  const int64_t ch_begin = p.seg_chunks > 0 ? seg * p.seg_chunks : 0;
+  const int64_t ch_end =
+      p.seg_chunks > 0 ? (ch_begin + p.seg_chunks < nchunks ? ch_begin + p.seg_chunks : nchunks)
+                       : nchunks;
 
   for (int i = tid; i < CPB * NT; i += kBlock) {
     const int ci = i / NT, n = i - ci * NT;
@@ -75,7 +90,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const float2 ia = tiny ? make_float2(0.0f, 0.0f) : make_float2(a.x / m2, -a.y / m2);
     prm[ci][n] = make_float4(a.x, a.y, ia.x, ia.y);
     prs[ci][n] = make_float2(a.x * kLog2e, a.y * kInv2Pi);
-    gcs[ci][n] = make_float2(0.0f, 0.0f);    // no gradient flows into the final state
+    // the adjoint entering the block's last chunk: zero at the sequence end
+    // (no gradient flows into the final state), else the later segments'
+    gcs[ci][n] = (real && p.seg_gin) ? p.seg_gin[((b * p.dim + dd) * p.nseg + seg) * N + n]
+                                     : make_float2(0.0f, 0.0f);
     dAs[ci][n] = make_float2(0.0f, 0.0f);
   }
   __syncthreads();
@@ -91,11 +109,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   const float* __restrict__ Cf = reinterpret_cast<const float*>(p.C) + b * N * 2 * L;
   float* tile = reinterpret_cast<float*>(tile_mem);
   TileStager<float, RW, 2 * K, NT, 2 * NT, kBlock> stage;
-  stage.load(Bf, Cf, N, 2 * L, 2 * (nchunks - 1) * TCH, VEC && nchunks * TCH <= L, tid);
+  stage.load(Bf, Cf, N, 2 * L, 2 * (ch_end - 1) * TCH, VEC && ch_end * TCH <= L, tid);
   stage.store(tile, N, tid);
   __syncthreads();
 
-  for (int64_t ch = nchunks - 1; ch >= 0; --ch) {
+  for (int64_t ch = ch_end - 1; ch >= ch_begin; --ch) {
     const int64_t t0 = ch * TCH;
     const int64_t tl = t0 + (int64_t)j * K;
     const bool full = VEC && t0 + TCH <= L;
@@ -284,7 +302,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
 
     // the earlier chunk's B/C rows (every earlier chunk is whole)
-    if (ch > 0) stage.load(Bf, Cf, N, 2 * L, 2 * (ch - 1) * TCH, VEC, tid);
+    if (ch > ch_begin) stage.load(Bf, Cf, N, 2 * L, 2 * (ch - 1) * TCH, VEC, tid);
 
     // ---- per-step outputs ----
     {
@@ -315,7 +333,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // keeps the next chunk's slice stores behind this chunk's flushes, and
     // every wave's tile reads behind the refill
     __syncthreads();
-    if (ch > 0) {
+    if (ch > ch_begin) {
       stage.store(tile, N, tid);
       __syncthreads();
     }
@@ -325,7 +343,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int ci = i / NT, n = i - ci * NT;
     const int64_t dd = grp * CPB + ci;
     if (dd < p.dim && n < N) {
-      if (p.dh0) p.dh0[(b * p.dim + dd) * N + n] = gcs[ci][n];
+      if (p.dh0 && seg == 0) p.dh0[(b * p.dim + dd) * N + n] = gcs[ci][n];
       float* dA = reinterpret_cast<float*>(p.dA + dd * N + n);
       unsafeAtomicAdd(dA, dAs[ci][n].x);
       unsafeAtomicAdd(dA + 1, dAs[ci][n].y);
@@ -356,6 +374,140 @@ __global__ __launch_bounds__(256) void cplx_bwd_zero_kernel(const CplxBwdParams 
   }
 }
 
+// Adjoint summary of a segmented run: per (batch row, segment, group), the
+// segment's chunks from last to first with a zero adjoint entering its end;
+// per state, G (the adjoint at the segment's first step) and prod(conj Abar)
+// over the segment.  Only delta, dout, z and C are read.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kBlock) void bwd_seg_summary_complex_kernel(const CplxBwdParams p) {
+  constexpr int RW = 2 * TCH;
+  __shared__ float4 tile_mem[NT * RW / 4];   // C rows
+  __shared__ float2 prs[CPB][NT];
+  __shared__ float2 gcs[CPB][NT];            // adjoint entering the chunk from the right
+  __shared__ float2 gds[CPB][NT];            // prod(conj Abar) over the chunks done
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int j = lane % R;
+  const int cl = (tid >> 6) * (64 / R) + lane / R;
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t per_b = p.groups * p.nseg;
+  const int64_t b = blk / per_b;
+  const int64_t seg = (blk - b * per_b) / p.groups;
+  const int64_t grp = blk - b * per_b - seg * p.groups;
+  const int64_t d_raw = grp * CPB + cl;
+  const bool active = d_raw < p.dim;
+  const int64_t d = active ? d_raw : p.dim - 1;
+  const int64_t c = b * p.dim + d;
+  const int N = p.N;
+  const int64_t L = p.L;
+  const int64_t nchunks = p.nchunks;
+  const int64_t ch_begin = seg * p.seg_chunks;
+  const int64_t ch_end = ch_begin + p.seg_chunks < nchunks ? ch_begin + p.seg_chunks : nchunks;
+
+  for (int i = tid; i < CPB * NT; i += kBlock) {
+    const int ci = i / NT, n = i - ci * NT;
+    const int64_t dd = grp * CPB + ci;
+    const float2 a = (dd < p.dim && n < N) ? p.A[dd * N + n] : make_float2(-1.0f, 0.0f);
+    prs[ci][n] = make_float2(a.x * kLog2e, a.y * kInv2Pi);
+    gcs[ci][n] = make_float2(0.0f, 0.0f);
+    gds[ci][n] = make_float2(1.0f, 0.0f);
+  }
+
+  const T* __restrict__ dl_row = static_cast<const T*>(p.delta) + c * L;
+  const T* __restrict__ z_row = p.z ? static_cast<const T*>(p.z) + c * L : nullptr;
+  const T* __restrict__ do_row = static_cast<const T*>(p.dout) + c * L;
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const float* __restrict__ Cf = reinterpret_cast<const float*>(p.C) + b * N * 2 * L;
+  float* tile = reinterpret_cast<float*>(tile_mem);
+  TileStager<float, RW, 2 * K, NT, NT, kBlock> stage;
+  stage.load(Cf, Cf, N, 2 * L, 2 * (ch_end - 1) * TCH, VEC && ch_end * TCH <= L, tid);
+  stage.store(tile, N, tid);
+  __syncthreads();
+
+  for (int64_t ch = ch_end - 1; ch >= ch_begin; --ch) {
+    const int64_t tl = ch * TCH + (int64_t)j * K;
+    const bool full = VEC && ch * TCH + TCH <= L;
+    const int64_t rem = L - tl;
+    const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
+    if (ch > ch_begin) stage.load(Cf, Cf, N, 2 * L, 2 * (ch - 1) * TCH, VEC, tid);
+    float dt[K], gy[K];
+    {
+      float raw[K];
+      load_items<T, K>(dl_row, tl, L, full, raw);
+      load_items<T, K>(do_row, tl, L, full, gy);
+      if (z_row) {
+        float zv[K];
+        load_items<T, K>(z_row, tl, L, full, zv);
+#pragma unroll
+        for (int k = 0; k < K; ++k) gy[k] *= silu(zv[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float r = raw[k] + bias;
+        const float sp = p.softplus ? softplus(r) : r;
+        dt[k] = (k < nvalid) ? sp : 0.0f;   // steps past L are the identity map
+        gy[k] = active ? gy[k] : 0.0f;
+      }
+    }
+    float dsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) dsum += dt[k];
+
+    for (int n = 0; n < N; ++n) {
+      const float2 ps = prs[cl][n];
+      float cf[2 * K];
+      tile_read<2 * K>(tile + n * RW, j, cf);
+      // this lane's steps, later first: g <- conj(Abar) (conj(C) gy + g)
+      float2 gagg = make_float2(0.0f, 0.0f);
+#pragma unroll
+      for (int k = K - 1; k >= 0; --k) {
+        const float2 ab = cexp_scaled(dt[k], ps.x, ps.y);
+        gagg = cmul(cconj(ab), make_float2(__builtin_fmaf(cf[2 * k], gy[k], gagg.x),
+                                           __builtin_fmaf(-cf[2 * k + 1], gy[k], gagg.y)));
+      }
+      float2 As = cconj(cexp_scaled(dsum, ps.x, ps.y));
+      const float2 gc = gcs[cl][n];
+      if (j == R - 1) gagg = cfma(As, gc, gagg);       // the later chunk enters lane 15
+      cplx_scan_suffix_row(As, gagg);
+      // lane 0: the adjoint leaving the chunk, and the chunk's prod(conj Abar)
+      if (j == 0) {
+        gcs[cl][n] = gagg;
+        gds[cl][n] = cmul(As, gds[cl][n]);
+      }
+    }
+    __syncthreads();
+    if (ch > ch_begin) {
+      stage.store(tile, N, tid);
+      __syncthreads();
+    }
+  }
+
+  if (active && j == 0) {
+    const int64_t k = (c * p.nseg + seg) * N;
+    for (int n = 0; n < N; ++n) {
+      p.seg_gloc[k + n] = gcs[cl][n];
+      p.seg_gdec[k + n] = gds[cl][n];
+    }
+  }
+}
+
+// One thread per (channel, n): the adjoint entering segment s from the right
+// is segment s + 1's G plus its prod(conj Abar) times the adjoint entering it;
+// zero enters the last segment.
+__global__ __launch_bounds__(256) void bwd_seg_carry_complex_kernel(const CplxBwdParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.nchannels * p.N) return;
+  const int64_t c = i / p.N;
+  const int n = (int)(i - c * p.N);
+  float2 g = make_float2(0.0f, 0.0f);
+  for (int64_t s = p.nseg - 1; s >= 0; --s) {
+    const int64_t k = (c * p.nseg + s) * p.N + n;
+    p.seg_gin[k] = g;
+    g = cfma(p.seg_gdec[k], g, p.seg_gloc[k]);
+  }
+}
+
 template <typename T>
 hipError_t launch_bwd_complex(const CplxBwdParams& p, int disc, bool vec, hipStream_t s) {
   {
@@ -366,7 +518,7 @@ hipError_t launch_bwd_complex(const CplxBwdParams& p, int disc, bool vec, hipStr
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((unsigned)(p.batch * p.groups)), block(kBlock);
+  const dim3 grid((unsigned)(p.batch * p.groups * p.nseg)), block(kBlock);
   if (disc == 0) {
     if (vec) hipLaunchKernelGGL((scan_bwd_complex_kernel<T, true, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((scan_bwd_complex_kernel<T, true, false>), grid, block, 0, s, p);
@@ -383,6 +535,25 @@ hipError_t dispatch_scan_bwd_complex(const CplxBwdParams& p, int dtype, int disc
                                      hipStream_t s) {
   return dtype == 0 ? launch_bwd_complex<float>(p, disc, vec, s)
                     : launch_bwd_complex<bf16_t>(p, disc, vec, s);
+}
+
+hipError_t dispatch_bwd_seg_summary_complex(const CplxBwdParams& p, int dtype, bool vec,
+                                            hipStream_t s) {
+  const dim3 grid((unsigned)(p.batch * p.groups * p.nseg)), block(kBlock);
+  if (dtype == 0) {
+    if (vec) hipLaunchKernelGGL((bwd_seg_summary_complex_kernel<float, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((bwd_seg_summary_complex_kernel<float, false>), grid, block, 0, s, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((bwd_seg_summary_complex_kernel<bf16_t, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((bwd_seg_summary_complex_kernel<bf16_t, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t dispatch_bwd_seg_carry_complex(const CplxBwdParams& p, hipStream_t s) {
+  const int64_t blocks = (p.nchannels * p.N + 255) / 256;
+  hipLaunchKernelGGL(bwd_seg_carry_complex_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace mscan

@@ -30,32 +30,46 @@ constexpr int CPB = (kBlock / 64) * (64 / R);
 constexpr int TCH = R * K;
 constexpr int NT = 16;
 
-// STATES: the backward's recompute pass: only the state entering every
-// chunk is written (to p.chunk_states); C, y and out are skipped.  Without
-// STATES the outputs are computed, and the chunk states are also written
-// when p.chunk_states is set (checkpoints for a later backward).
+// MODE 0: the outputs, and the chunk states too when p.chunk_states is set
+// (checkpoints for a later backward).  MODE 1: the backward's recompute pass,
+// only the state entering every chunk (to p.chunk_states).  MODE 2: the
+// summary pass of a segmented run, each segment's end state from a zero start
+// and its decay prod(Abar) per state (p.seg_state, p.seg_dec).  Modes 1 and 2
+// skip C, y and out.
+//
+// A block serves one channel group of one batch row for the whole sequence
+// or, in a segmented run (p.seg_chunks > 0), for one segment of it; the
+// output and state passes then start each segment from p.seg_h0, which the
+// carry kernel below filled from the summaries (the associative combination
+// of trishampatil essay, Part III §2, on whole segments).
 //
 // B and C (complex, shared by the block's 16 channels) are staged per chunk
 // into one LDS tile by the whole block with 16-byte loads (tile_stage.hpp:
 // a complex row of TCH steps is a float row of 2*TCH); the next chunk's
 // loads are in flight in registers while the current chunk computes.
-template <typename T, bool ZOH, bool VEC, bool STATES>
+template <typename T, bool ZOH, bool VEC, int MODE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_fwd_complex_kernel(
     const CplxParams p) {
+  constexpr bool STATES = MODE != 0;
+  constexpr bool SUMMARY = MODE == 2;
   constexpr int ROWS = STATES ? NT : 2 * NT;   // B rows, then C rows
   constexpr int RW = 2 * TCH;                  // floats per tile row
   __shared__ float4 tile_mem[ROWS * RW / 4];
   // {A.re log2(e), A.im / (2 pi), (1/A).re, (1/A).im}; 1/A = 0 where A ~ 0
   __shared__ float4 prm[CPB][NT];
   __shared__ float2 carry[CPB][NT];
+  __shared__ float2 decs[SUMMARY ? CPB : 1][NT];   // summary: prod(Abar) so far
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int j = lane % R;
   const int cl = (tid >> 6) * (64 / R) + lane / R;
+  // block order (b, segment, group) with the group fastest
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t b = blk / p.groups;
-  const int64_t grp = blk - b * p.groups;
+  const int64_t per_b = p.groups * p.nseg;
+  const int64_t b = blk / per_b;
+  const int64_t seg = (blk - b * per_b) / p.groups;
+  const int64_t grp = blk - b * per_b - seg * p.groups;
   const int64_t d_raw = grp * CPB + cl;
   const bool active = d_raw < p.dim;
   const int64_t d = active ? d_raw : p.dim - 1;
@@ -73,7 +87,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const float2 ia = tiny ? make_float2(0.0f, 0.0f) : make_float2(a.x / m2, -a.y / m2);
     prm[ci][n] = make_float4(a.x * kLog2e, a.y * kInv2Pi, ia.x, ia.y);
     const int64_t cc = b * p.dim + dd;
-    carry[ci][n] = (real && p.h0) ? p.h0[cc * N + n] : make_float2(0.0f, 0.0f);
+    float2 h = make_float2(0.0f, 0.0f);
+    if (real && !SUMMARY) {
+      if (p.seg_h0) h = p.seg_h0[(cc * p.nseg + seg) * N + n];
+      else if (p.h0) h = p.h0[cc * N + n];
+    }
+    carry[ci][n] = h;
+    if constexpr (SUMMARY) decs[ci][n] = make_float2(1.0f, 0.0f);
   }
 
   const T* __restrict__ u_row = static_cast<const T*>(p.u) + c * L;
@@ -84,23 +104,27 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
   const int64_t nchunks = (L + TCH - 1) / TCH;
+  const int64_t ch_begin = p.seg_chunks > 0 ? seg * p.seg_chunks : 0;
+  const int64_t ch_end =
+      p.seg_chunks > 0 ? (ch_begin + p.seg_chunks < nchunks ? ch_begin + p.seg_chunks : nchunks)
+                       : nchunks;
   float* tile = reinterpret_cast<float*>(tile_mem);
 
   TileStager<float, RW, 2 * K, NT, ROWS, kBlock> stage;
-  stage.load(Bf, Cf, N, 2 * L, 0, VEC && TCH <= L, tid);
+  stage.load(Bf, Cf, N, 2 * L, 2 * ch_begin * TCH, VEC && (ch_begin + 1) * TCH <= L, tid);
   stage.store(tile, N, tid);
   __syncthreads();
 
-  for (int64_t ch = 0; ch < nchunks; ++ch) {
+  for (int64_t ch = ch_begin; ch < ch_end; ++ch) {
     const int64_t tl = ch * TCH + (int64_t)j * K;
     const bool full = VEC && ch * TCH + TCH <= L;
-    const bool more = ch + 1 < nchunks;
+    const bool more = ch + 1 < ch_end;
     if (more) stage.load(Bf, Cf, N, 2 * L, 2 * (ch + 1) * TCH, VEC && (ch + 2) * TCH <= L, tid);
     const int64_t rem = L - tl;
     const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
     // the state entering the chunk: the backward's recompute pass, or the
     // checkpoints a forward may save for a later backward
-    if ((STATES || p.chunk_states) && active && j == 0) {
+    if (!SUMMARY && (STATES || p.chunk_states) && active && j == 0) {
       for (int n = 0; n < N; ++n) p.chunk_states[(c * nchunks + ch) * N + n] = carry[cl][n];
     }
     float uv[K], dt[K], y[K];
@@ -161,7 +185,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         }
       }
       // all lanes have read carry[cl][n] above; lane 15 holds the chunk's end
-      if (j == R - 1) carry[cl][n] = agg;
+      // (and, after the scan, the chunk's decay prod(Abar) in Ag)
+      if (j == R - 1) {
+        carry[cl][n] = agg;
+        if constexpr (SUMMARY) decs[cl][n] = cmul(Ag, decs[cl][n]);
+      }
     }
 
     if constexpr (!STATES) {
@@ -181,20 +209,47 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     }
   }
 
-  if (!STATES && p.last_state && active && j == 0) {
+  // one pass: the last state (segmented runs: the carry kernel writes it)
+  if (!STATES && p.nseg == 1 && p.last_state && active && j == 0) {
     for (int n = 0; n < N; ++n) p.last_state[c * N + n] = carry[cl][n];
+  }
+  if constexpr (SUMMARY) {
+    // the loop's last barrier has made every lane 15's writes visible
+    if (active && j == 0) {
+      const int64_t k = (c * p.nseg + seg) * N;
+      for (int n = 0; n < N; ++n) {
+        p.seg_state[k + n] = carry[cl][n];
+        p.seg_dec[k + n] = decs[cl][n];
+      }
+    }
   }
 }
 
-template <typename T, bool STATES>
+// One thread per (channel, n): the state entering segment s + 1 is the one
+// entering s times the segment's decay plus its end state from zero.
+__global__ __launch_bounds__(256) void seg_carry_complex_kernel(const CplxParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.nchannels * p.N) return;
+  const int64_t c = i / p.N;
+  const int n = (int)(i - c * p.N);
+  float2 H = p.h0 ? p.h0[c * p.N + n] : make_float2(0.0f, 0.0f);
+  for (int64_t s = 0; s < p.nseg; ++s) {
+    const int64_t k = (c * p.nseg + s) * p.N + n;
+    p.seg_h0[k] = H;
+    H = cfma(p.seg_dec[k], H, p.seg_state[k]);
+  }
+  if (p.last_state) p.last_state[c * p.N + n] = H;
+}
+
+template <typename T, int MODE>
 hipError_t launch_complex(const CplxParams& p, int disc, bool vec, hipStream_t s) {
-  const dim3 grid((unsigned)(p.batch * p.groups)), block(kBlock);
+  const dim3 grid((unsigned)(p.batch * p.groups * p.nseg)), block(kBlock);
   if (disc == 0) {
-    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, true, STATES>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, false, STATES>), grid, block, 0, s, p);
+    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, true, MODE>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, false, MODE>), grid, block, 0, s, p);
   } else {
-    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, true, STATES>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, false, STATES>), grid, block, 0, s, p);
+    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, true, MODE>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, false, MODE>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
@@ -203,14 +258,26 @@ hipError_t launch_complex(const CplxParams& p, int disc, bool vec, hipStream_t s
 
 hipError_t dispatch_scan_fwd_complex(const CplxParams& p, int dtype, int disc, bool vec,
                                      hipStream_t s) {
-  return dtype == 0 ? launch_complex<float, false>(p, disc, vec, s)
-                    : launch_complex<bf16_t, false>(p, disc, vec, s);
+  return dtype == 0 ? launch_complex<float, 0>(p, disc, vec, s)
+                    : launch_complex<bf16_t, 0>(p, disc, vec, s);
 }
 
 hipError_t dispatch_chunk_states_complex(const CplxParams& p, int dtype, int disc, bool vec,
                                          hipStream_t s) {
-  return dtype == 0 ? launch_complex<float, true>(p, disc, vec, s)
-                    : launch_complex<bf16_t, true>(p, disc, vec, s);
+  return dtype == 0 ? launch_complex<float, 1>(p, disc, vec, s)
+                    : launch_complex<bf16_t, 1>(p, disc, vec, s);
+}
+
+hipError_t dispatch_seg_summary_complex(const CplxParams& p, int dtype, int disc, bool vec,
+                                        hipStream_t s) {
+  return dtype == 0 ? launch_complex<float, 2>(p, disc, vec, s)
+                    : launch_complex<bf16_t, 2>(p, disc, vec, s);
+}
+
+hipError_t dispatch_seg_carry_complex(const CplxParams& p, hipStream_t s) {
+  const int64_t blocks = (p.nchannels * p.N + 255) / 256;
+  hipLaunchKernelGGL(seg_carry_complex_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace mscan

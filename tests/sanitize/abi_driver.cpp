@@ -72,10 +72,15 @@ void sweep(int64_t b, int64_t d, int64_t n, int64_t l) {
                              nullptr);
     (void)mamba_state_update_complex(P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d, n,
                                      P, nullptr);
-    (void)mamba_scan_fwd_complex_ex(P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d, n, l,
-                                    P, P, P, nullptr);
-    (void)mamba_scan_bwd_complex_ex(P, P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d, n,
-                                    l, P, P, P, P, P, P, P, P, P, nullptr, P, BIG, nullptr);
+    for (int segs : {0, 1, 3, 1000}) {
+      (void)mamba_scan_fwd_complex_workspace_size_ex(b, d, n, l, segs);
+      (void)mamba_scan_bwd_complex_workspace_size_ex(b, d, n, l, segs);
+      (void)mamba_scan_fwd_complex_ex(P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d, n,
+                                      l, P, P, P, P, BIG, nullptr, segs);
+      (void)mamba_scan_bwd_complex_ex(P, P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d,
+                                      n, l, P, P, P, P, P, P, P, P, P, nullptr, P, BIG, nullptr,
+                                      segs);
+    }
     for (int64_t w : {1, 4, 5})
       (void)mamba_conv1d_silu_fwd(P, P, P, F, w, dt, b, d, l, P, nullptr);
     (void)mamba_conv1d_silu_bwd(P, P, P, F, P, 4, dt, b, d, l, P, P, P, nullptr);
@@ -83,6 +88,7 @@ void sweep(int64_t b, int64_t d, int64_t n, int64_t l) {
   (void)mamba_scan_checkpoint_size(b, d, n, l);
   (void)mamba_scan_complex_checkpoint_size(b, d, n, l);
   (void)mamba_scan_bwd_complex_workspace_size(b, d, n, l);
+  (void)mamba_scan_fwd_complex_workspace_size(b, d, n, l);
 }
 
 }  // namespace
@@ -135,8 +141,37 @@ int main() {
   EXPECT(mamba_scan_complex_checkpoint_size(2, 64, 17, 2049), SIZE_MAX);
   EXPECT(mamba_scan_bwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, P, 1,
                                    MAMBA_DISC_ZOH, MAMBA_F32, 2, 64, 16, 2048, P, P, P, P, P,
-                                   nullptr, nullptr, nullptr, nullptr, P, nullptr, 0, nullptr),
-         MAMBA_OK);                                                // checkpoints: no workspace
+                                   nullptr, nullptr, nullptr, nullptr, P, nullptr, 0, nullptr,
+                                   0),
+         MAMBA_OK);                             // checkpoints, automatic: no workspace, one pass
+  {
+    // complex segments: explicit counts need their workspace
+    const size_t fw = mamba_scan_fwd_complex_workspace_size_ex(1, 16, 16, 65536, 8);
+    const size_t bw = mamba_scan_bwd_complex_workspace_size_ex(1, 16, 16, 65536, 8);
+    if (!(fw > 0 && bw > fw)) ++g_fail;
+    EXPECT(mamba_scan_fwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, 1,
+                                     MAMBA_DISC_ZOH, MAMBA_F32, 1, 16, 16, 65536, P, nullptr,
+                                     nullptr, P, fw - 1, nullptr, 8),
+           MAMBA_ERR_WORKSPACE);
+    EXPECT(mamba_scan_fwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, 1,
+                                     MAMBA_DISC_ZOH, MAMBA_F32, 1, 16, 16, 65536, P, P, nullptr,
+                                     P, fw, nullptr, 8),
+           MAMBA_OK);
+    EXPECT(mamba_scan_fwd_complex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, 1,
+                                  MAMBA_DISC_ZOH, MAMBA_F32, 1, 16, 16, 65536, P, nullptr,
+                                  nullptr, 0, nullptr),
+           MAMBA_OK);                           // automatic without the workspace: one pass
+    EXPECT(mamba_scan_bwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, P, 1,
+                                     MAMBA_DISC_ZOH, MAMBA_F32, 1, 16, 16, 65536, P, P, P, P, P,
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, P, bw - 1,
+                                     nullptr, 8),
+           MAMBA_ERR_WORKSPACE);
+    EXPECT(mamba_scan_bwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, P, 1,
+                                     MAMBA_DISC_ZOH, MAMBA_F32, 1, 16, 16, 65536, P, P, P, P, P,
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, P, bw, nullptr,
+                                     -1),
+           MAMBA_ERR_UNSUPPORTED);
+  }
   EXPECT(mamba_conv1d_silu_fwd(P, P, nullptr, nullptr, 5, MAMBA_F32, 1, 8, 64, P, nullptr),
          MAMBA_ERR_UNSUPPORTED);
   EXPECT(mamba_state_update(P, P, P, P, P, P, nullptr, nullptr, nullptr, 1, MAMBA_DISC_ZOH,

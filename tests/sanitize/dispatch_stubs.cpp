@@ -22,6 +22,14 @@ hipError_t dispatch_scan_fwd_complex(const CplxParams&, int, int, bool, hipStrea
 hipError_t dispatch_chunk_states_complex(const CplxParams&, int, int, bool, hipStream_t) {
   return reached();
 }
+hipError_t dispatch_seg_summary_complex(const CplxParams&, int, int, bool, hipStream_t) {
+  return reached();
+}
+hipError_t dispatch_seg_carry_complex(const CplxParams&, hipStream_t) { return reached(); }
+hipError_t dispatch_bwd_seg_summary_complex(const CplxBwdParams&, int, bool, hipStream_t) {
+  return reached();
+}
+hipError_t dispatch_bwd_seg_carry_complex(const CplxBwdParams&, hipStream_t) { return reached(); }
 hipError_t dispatch_scan_bwd_complex(const CplxBwdParams&, int, int, bool, hipStream_t) {
   return reached();
 }

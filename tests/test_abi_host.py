@@ -188,19 +188,44 @@ def test_complex_checkpoints_size_and_workspace(lib):
     # one complex state (2 floats) per channel, 128-step chunk and state index
     assert lib.mamba_scan_complex_checkpoint_size(2, 64, 16, 2049) == 2 * 64 * 17 * 16 * 8
     assert lib.mamba_scan_complex_checkpoint_size(2, 64, 17, 2049) == 2 ** 64 - 1   # N <= 16
-    need = lib.mamba_scan_bwd_complex_workspace_size(2, 64, 16, 2048)
+    # one pass: the workspace holds the complex chunk states only
+    need = lib.mamba_scan_bwd_complex_workspace_size_ex(2, 64, 16, 2048, 1)
+    assert need == 2 * 64 * 16 * 16 * 8
 
     def bwd_ex(ws, wsb, ckpt):
         return lib.mamba_scan_bwd_complex_ex(P, P, P, P, P, None, None, None, None, P, 1, 0, 0,
                                              2, 64, 16, 2048, P, P, P, P, P, None, None, None,
-                                             None, ckpt, ws, wsb, None)
+                                             None, ckpt, ws, wsb, None, 1)
     assert bwd_ex(None, 0, None) == 5                # no checkpoints: the states need room
     assert bwd_ex(P, need - 1, None) == 5
     assert bwd_ex(P, need, P + 8) == 4               # misaligned checkpoints
     assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 2, 64,
-                                         16, 2048, P, None, P + 4, None) == 4
+                                         16, 2048, P, None, P + 4, None, 0, None, 1) == 4
     assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 2, 64,
-                                         17, 2048, P, None, P, None) == 6
+                                         17, 2048, P, None, P, None, 0, None, 1) == 6
+
+
+def test_complex_segment_workspace(lib):
+    # 1536 channels over 2^20 steps: 96 blocks, 32 segments of 256 chunks (as
+    # the real calls); per channel, segment and state three complex buffers in
+    # the forward, six in the backward after the chunk states
+    nst = 1536 * 32 * 16 * 8
+    assert lib.mamba_scan_fwd_complex_workspace_size(1, 1536, 16, 1 << 20) == 3 * nst
+    assert lib.mamba_scan_fwd_complex_workspace_size_ex(1, 1536, 16, 1 << 20, 32) == 3 * nst
+    assert lib.mamba_scan_fwd_complex_workspace_size_ex(1, 1536, 16, 1 << 20, 1) == 0
+    states = 1536 * 8192 * 16 * 8
+    assert lib.mamba_scan_bwd_complex_workspace_size(1, 1536, 16, 1 << 20) == states + 6 * nst
+    assert lib.mamba_scan_bwd_complex_workspace_size_ex(1, 1536, 16, 1 << 20, 1) == states
+    # shapes that fill the chip run in one pass; bad counts are rejected
+    assert lib.mamba_scan_fwd_complex_workspace_size(8, 1536, 16, 2048) == 0
+    assert lib.mamba_scan_fwd_complex_workspace_size_ex(1, 16, 16, 1024, -1) == 2 ** 64 - 1
+    assert lib.mamba_scan_bwd_complex_workspace_size_ex(1, 16, 17, 1024, 2) == 2 ** 64 - 1
+    fw = lib.mamba_scan_fwd_complex_workspace_size_ex(1, 16, 16, 1024, 4)
+    assert fw > 0
+    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 1, 16,
+                                         16, 1024, P, None, None, P, fw - 1, None, 4) == 5
+    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 1, 16,
+                                         16, 1024, P, None, None, P, fw, None, -1) == 6
 
 
 def test_varlen_requires_flags(lib):

@@ -1,8 +1,9 @@
-"""GPU parity of the complex-valued forward (diagonal complex A, B, C and
-state; y = Re(sum_n C h) + D u, gated) against the float64 oracle on the
-same seeded inputs: float32 and bfloat16 sequences, ZOH and Euler, several
-state sizes, ragged lengths, an initial state, optional inputs absent and
-the softplus off."""
+"""GPU parity of the complex-valued forward, backward and decode step
+(diagonal complex A, B, C and state; y = Re(sum_n C h) + D u, gated) against
+the float64 oracle on the same seeded inputs: float32 and bfloat16
+sequences, ZOH and Euler, several state sizes, ragged lengths, an initial
+state, optional inputs absent, the softplus off, checkpoints, and sequences
+split into segments."""
 import numpy as np
 import pytest
 import torch
@@ -22,10 +23,10 @@ def _dev(x, dtype):
 
 
 def _case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None,
-          zero_A=False):
+          zero_A=False, segments=0):
     opts = opts or {}
     announce(f"complex fwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} h0={h0} "
-             f"softplus={softplus} opts={opts}")
+             f"softplus={softplus} opts={opts} segments={segments}")
     inp = W.make_complex_inputs(wid, batch, dim, N, L, dtype=dtype, **opts)
     if not softplus:   # a positive raw step without the softplus
         raw = np.abs(W.as_f64(inp["delta"], dtype)) * 0.05 + 0.01
@@ -43,7 +44,7 @@ def _case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None
     out, last = ms.scan_fwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t.get("D"),
                                     t.get("z"), t.get("delta_bias"),
                                     None if h0v is None else torch.from_numpy(h0v).cuda(),
-                                    delta_softplus=softplus, disc=disc)
+                                    delta_softplus=softplus, disc=disc, segments=segments)
     torch.cuda.synchronize()
     f = {k: (W.as_f64(v, dtype) if v.dtype == np.uint16 else v) for k, v in inp.items()}
     ref, ref_last = oracle.scan_fwd_complex(
@@ -92,10 +93,10 @@ def _as_pairs(x):
 
 
 def _bwd_case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None,
-              zero_A=False):
+              zero_A=False, segments=0):
     opts = opts or {}
     announce(f"complex bwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} h0={h0} "
-             f"softplus={softplus} opts={opts} zero_A={zero_A}")
+             f"softplus={softplus} opts={opts} zero_A={zero_A} segments={segments}")
     inp = W.make_complex_inputs(wid, batch, dim, N, L, dtype=dtype, with_dout=True, **opts)
     if not softplus:
         raw = np.abs(W.as_f64(inp["delta"], dtype)) * 0.05 + 0.01
@@ -113,7 +114,7 @@ def _bwd_case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=
     res = ms.scan_bwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t.get("D"), t.get("z"),
                               t.get("delta_bias"), t["dout"],
                               None if h0v is None else torch.from_numpy(h0v).cuda(),
-                              delta_softplus=softplus, disc=disc)
+                              delta_softplus=softplus, disc=disc, segments=segments)
     torch.cuda.synchronize()
     f = {k: (W.as_f64(v, dtype) if v.dtype == np.uint16 else v) for k, v in inp.items()}
     ref = oracle.scan_bwd_complex(f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"),
@@ -132,7 +133,43 @@ def _bwd_case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("disc", ["zoh", "euler"])
 def test_complex_bwd_dtypes_discs(dtype, disc):
+    # few blocks: the automatic choice splits these 4 chunks into 4 segments;
+    # the same case in one pass
     _bwd_case(75, 2, 19, 16, 400, dtype, disc, h0=True)
+    _bwd_case(75, 2, 19, 16, 400, dtype, disc, h0=True, segments=1)
+
+
+# Segmented complex calls: the summary pass writes each segment's end state
+# from zero and its product of Abar, the carry composes them, and every
+# segment runs from its entering state; the backward carries the adjoint
+# from the last segment to the first the same way.  1189 steps are 9 full
+# chunks and a ragged one (3 segments: 4 + 4 + 2 chunks; 10: one each).
+@pytest.mark.parametrize("segments", [2, 3, 10])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_complex_segmented(segments, dtype):
+    _case(84, 1, 20, 16, 1189, dtype, "zoh", h0=True, segments=segments)
+    _bwd_case(84, 1, 20, 16, 1189, dtype, "euler", h0=True, segments=segments)
+
+
+def test_complex_segmented_sizes_zero_A_slow_decay():
+    _case(85, 2, 9, 5, 1300, "f32", "euler", segments=4)
+    _bwd_case(85, 2, 9, 5, 1300, "f32", "zoh", h0=True, segments=4)
+    _case(86, 1, 12, 4, 1024, "f32", "zoh", h0=True, zero_A=True, segments=8)
+    _bwd_case(86, 1, 12, 4, 1024, "f32", "zoh", h0=True, zero_A=True, segments=8)
+    # small steps: the states keep their phase across many segments, so the
+    # carried product of Abar must hold it (A.im up to pi (N - 1))
+    _case(87, 1, 16, 16, 4096, "f32", "zoh", h0=True, softplus=False, segments=32)
+    _bwd_case(87, 1, 16, 16, 4096, "f32", "zoh", h0=True, softplus=False, segments=32)
+
+
+def test_complex_automatic_segmentation_long_sequence():
+    # 16 channels over 8192 steps: one channel group, so the forward splits
+    # into 64 segments and the backward too
+    assert ms.fwd_complex_workspace_bytes(1, 16, 16, 8192) > 0
+    assert ms.bwd_complex_workspace_bytes(1, 16, 16, 8192) > \
+        ms.bwd_complex_workspace_bytes(1, 16, 16, 8192, segments=1)
+    _case(88, 1, 16, 16, 8192, "bf16", "zoh", h0=True)
+    _bwd_case(88, 1, 16, 16, 8192, "bf16", "zoh", h0=True)
 
 
 @pytest.mark.parametrize("N", [1, 5])
@@ -148,11 +185,14 @@ def test_complex_bwd_optional_inputs_softplus_off_zero_A():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_complex_checkpoints_forward_states_and_backward(dtype):
+@pytest.mark.parametrize("segments", [1, 3])
+def test_complex_checkpoints_forward_states_and_backward(dtype, segments):
     """The forward's checkpoints equal the oracle's state after each 128-step
-    prefix, and the backward that uses them matches the oracle's gradients."""
+    prefix, and the backward that uses them matches the oracle's gradients
+    (in one pass and in 3 segments)."""
     wid, batch, dim, N, L = 80, 2, 19, 16, 400
-    announce(f"complex checkpoints wid={wid} shape=({batch},{dim},{N},{L}) {dtype}")
+    announce(f"complex checkpoints wid={wid} shape=({batch},{dim},{N},{L}) {dtype} "
+             f"segments={segments}")
     inp = W.make_complex_inputs(wid, batch, dim, N, L, dtype=dtype, with_dout=True)
     g = np.random.default_rng([wid, 13])
     h0v = (g.standard_normal((batch, dim, N)) + 1j * g.standard_normal((batch, dim, N))
@@ -162,9 +202,10 @@ def test_complex_checkpoints_forward_states_and_backward(dtype):
     ckpt = torch.empty(ms.complex_checkpoint_shape(batch, dim, N, L), dtype=torch.complex64,
                        device="cuda")
     ms.scan_fwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t.get("D"), t.get("z"),
-                        t.get("delta_bias"), h0t, checkpoints=ckpt)
+                        t.get("delta_bias"), h0t, checkpoints=ckpt, segments=segments)
     res = ms.scan_bwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t.get("D"), t.get("z"),
-                              t.get("delta_bias"), t["dout"], h0t, checkpoints=ckpt)
+                              t.get("delta_bias"), t["dout"], h0t, checkpoints=ckpt,
+                              segments=segments)
     torch.cuda.synchronize()
     f = {k: (W.as_f64(v, dtype) if v.dtype == np.uint16 else v) for k, v in inp.items()}
     got = ckpt.cpu().numpy()
