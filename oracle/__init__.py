@@ -67,9 +67,9 @@ def _load():
         lib.oracle_conv1d_silu_fwd.restype = None
         lib.oracle_conv1d_silu_bwd.argtypes = [_dp, _dp, _dp, _u8p, _dp] + [_i64] * 6 + [_dp] * 3
         lib.oracle_conv1d_silu_bwd.restype = None
-        lib.oracle_scan_fwd_complex.argtypes = [_dp] * 9 + [_int, _int] + [_i64] * 6 + [_dp, _dp]
+        lib.oracle_scan_fwd_complex.argtypes = [_dp] * 9 + [_u8p, _int, _int] + [_i64] * 6 + [_dp, _dp]
         lib.oracle_scan_fwd_complex.restype = None
-        lib.oracle_scan_bwd_complex.argtypes = [_dp] * 10 + [_int, _int] + [_i64] * 6 + [_dp] * 9
+        lib.oracle_scan_bwd_complex.argtypes = [_dp] * 10 + [_u8p, _int, _int] + [_i64] * 6 + [_dp] * 9
         lib.oracle_scan_bwd_complex.restype = None
         lib.oracle_version.restype = _int
         _lib = lib
@@ -272,11 +272,12 @@ def _c128(x):
 
 
 def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
-                     delta_softplus=True, disc=ZOH, threads=None):
+                     delta_softplus=True, disc=ZOH, threads=None, reset=None):
     """Complex-valued forward in float64: A (dim, N), B, C (batch, N, L) and
     h0 (batch, dim, N) complex; u, delta, z, D, delta_bias real.  Returns
     (out real (batch, dim, L), last_state complex (batch, dim, N)) with
-    y_t = Re(sum_n C_t[n] h_t[n]) + D u_t gated by SiLU(z)."""
+    y_t = Re(sum_n C_t[n] h_t[n]) + D u_t gated by SiLU(z).  reset (batch,
+    L) flags as in scan_fwd."""
     lib = _load()
     u, delta, D, z, delta_bias = (_f64(t) for t in (u, delta, D, z, delta_bias))
     A, B, C, h0 = (_c128(t) for t in (A, B, C, h0))
@@ -285,7 +286,8 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None
     out = np.zeros((batch, dim, L), np.float64)
     last = np.zeros((batch, dim, N), np.complex128)
     lastv = last.view(np.float64)
-    args = [_ptr(t) for t in (u, delta, A, B, C, D, z, delta_bias, h0)]
+    rs = _reset(reset, batch, L)
+    args = [_ptr(t) for t in (u, delta, A, B, C, D, z, delta_bias, h0)] + [_ptr8(rs)]
 
     def work(rng):
         lib.oracle_scan_fwd_complex(*args, int(bool(delta_softplus)), int(disc), batch, dim, N,
@@ -301,10 +303,11 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None
 
 
 def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
-                     delta_softplus=True, disc=ZOH):
+                     delta_softplus=True, disc=ZOH, reset=None):
     """Gradients of sum(dout * out) for scan_fwd_complex, in float64 (one
     thread).  dA, dB, dC, dh0 are complex (the gradient of a complex w is
-    dL/dRe(w) + i dL/dIm(w)); the others real.  Returns a dict like scan_bwd."""
+    dL/dRe(w) + i dL/dIm(w)); the others real.  Returns a dict like scan_bwd.
+    reset (batch, L) flags as in scan_bwd."""
     lib = _load()
     u, delta, D, z, delta_bias, dout = (_f64(t) for t in (u, delta, D, z, delta_bias, dout))
     A, B, C, h0 = (_c128(t) for t in (A, B, C, h0))
@@ -319,7 +322,9 @@ def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
     ddb = np.zeros(dim) if delta_bias is not None else None
     dh0 = np.zeros((batch, dim, N), np.complex128) if h0 is not None else None
     v = lambda a: None if a is None else a.view(np.float64)
+    rs = _reset(reset, batch, L)
     lib.oracle_scan_bwd_complex(*[_ptr(t) for t in (u, delta, A, B, C, D, z, delta_bias, h0, dout)],
+                                _ptr8(rs),
                                 int(bool(delta_softplus)), int(disc), batch, dim, N, L, 0,
                                 batch * dim, _ptr(du), _ptr(ddelta), _ptr(v(dA)), _ptr(v(dB)),
                                 _ptr(v(dC)), _ptr(dD), _ptr(dz), _ptr(ddb), _ptr(v(dh0)))

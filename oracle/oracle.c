@@ -349,7 +349,9 @@ void oracle_conv1d_silu_bwd(const double* x, const double* w, const double* cb,
  * with Abar = exp(dt*A) and Bbar = (Abar - 1)/A * B (ZOH; limit dt*B at A = 0)
  * or dt*B (Euler), all complex.  Complex arrays are interleaved (re, im)
  * pairs: A (dim, dstate), B and C (batch, dstate, seqlen), h0 and last_state
- * (batch, dim, dstate).  u, delta, z, D, bias and out are real.
+ * (batch, dim, dstate).  u, delta, z, D, bias and out are real.  Reset flags
+ * (nullable) act as in the real forward: the state entering a flagged step is
+ * zero.
  */
 static double complex cload(const double* p, int64_t i) { return p[2 * i] + I * p[2 * i + 1]; }
 
@@ -361,9 +363,10 @@ static double complex cbbar_coef(double dt, double complex a, int disc) {
 
 void oracle_scan_fwd_complex(const double* u, const double* delta, const double* A,
                              const double* B, const double* C, const double* D, const double* z,
-                             const double* bias, const double* h0, int softplus_on, int disc,
-                             int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                             int64_t c_begin, int64_t c_end, double* out, double* last_state) {
+                             const double* bias, const double* h0, const unsigned char* reset,
+                             int softplus_on, int disc, int64_t batch, int64_t dim,
+                             int64_t dstate, int64_t seqlen, int64_t c_begin, int64_t c_end,
+                             double* out, double* last_state) {
   (void)batch;
   double complex* h = (double complex*)malloc(sizeof(double complex) * (size_t)dstate);
   for (int64_t c = c_begin; c < c_end; ++c) {
@@ -373,6 +376,8 @@ void oracle_scan_fwd_complex(const double* u, const double* delta, const double*
       double dt = step_size(delta[c * seqlen + t], bias, d, softplus_on);
       double ut = u[c * seqlen + t];
       double y = 0.0;
+      if (reset && reset[b * seqlen + t])
+        for (int64_t n = 0; n < dstate; ++n) h[n] = 0.0;
       for (int64_t n = 0; n < dstate; ++n) {
         double complex a = cload(A, d * dstate + n);
         double complex abar = cexp(dt * a);
@@ -407,10 +412,13 @@ void oracle_scan_fwd_complex(const double* u, const double* delta, const double*
  * A real variable x gets Re(conj(g_w) dw/dx); a complex one conj(dw/dx) g_w
  * (the maps are holomorphic in A).  dA, dB, dC, dh0 are complex and
  * accumulated with +=, like dD, ddelta_bias; du, ddelta, dz are written.
+ * With reset flags the state entering a flagged step is zero: its h_{t-1}
+ * counts as 0 and no adjoint passes back across the step.
  */
 void oracle_scan_bwd_complex(const double* u, const double* delta, const double* A,
                              const double* B, const double* C, const double* D, const double* z,
                              const double* bias, const double* h0, const double* dout,
+                             const unsigned char* reset,
                              int softplus_on, int disc, int64_t batch, int64_t dim, int64_t dstate,
                              int64_t seqlen, int64_t c_begin, int64_t c_end, double* du,
                              double* ddelta, double* dA, double* dB, double* dC, double* dD,
@@ -423,10 +431,12 @@ void oracle_scan_bwd_complex(const double* u, const double* delta, const double*
     for (int64_t n = 0; n < dstate; ++n) hs[n] = h0 ? cload(h0, c * dstate + n) : 0.0;
     for (int64_t t = 0; t < seqlen; ++t) {
       double dt = step_size(delta[c * seqlen + t], bias, d, softplus_on);
+      int rs = reset && reset[b * seqlen + t];
       for (int64_t n = 0; n < dstate; ++n) {
         double complex a = cload(A, d * dstate + n);
         double complex bbar = cbbar_coef(dt, a, disc) * cload(B, (b * dstate + n) * seqlen + t);
-        hs[(t + 1) * dstate + n] = cexp(dt * a) * hs[t * dstate + n] + bbar * u[c * seqlen + t];
+        double complex hprev = rs ? 0.0 : hs[t * dstate + n];
+        hs[(t + 1) * dstate + n] = cexp(dt * a) * hprev + bbar * u[c * seqlen + t];
       }
     }
     for (int64_t n = 0; n < dstate; ++n) gh[n] = 0.0;
@@ -447,13 +457,14 @@ void oracle_scan_bwd_complex(const double* u, const double* delta, const double*
       double du_t = D ? gy * D[d] : 0.0;
       if (D) dD[d] += gy * ut;
       double gdt = 0.0;
+      int rs = reset && reset[b * seqlen + t];
       for (int64_t n = 0; n < dstate; ++n) {
         int64_t k = (b * dstate + n) * seqlen + t;
         double complex a = cload(A, d * dstate + n);
         double complex abar = cexp(dt * a);
         double complex Bv = cload(B, k), Cv = cload(C, k);
         double complex E = cbbar_coef(dt, a, disc);
-        double complex hprev = hs[t * dstate + n], hcur = hs[(t + 1) * dstate + n];
+        double complex hprev = rs ? 0.0 : hs[t * dstate + n], hcur = hs[(t + 1) * dstate + n];
         gh[n] += conj(Cv) * gy;                       /* g_h_t */
         double complex gC = gy * conj(hcur);
         dC[2 * k] += creal(gC);
@@ -473,7 +484,7 @@ void oracle_scan_bwd_complex(const double* u, const double* delta, const double*
         double complex gA = conj(dt * abar) * gAbar + conj(dE_dA * Bv * ut) * gbeta;
         dA[2 * (d * dstate + n)] += creal(gA);
         dA[2 * (d * dstate + n) + 1] += cimag(gA);
-        gh[n] = conj(abar) * gh[n];                   /* carry to t-1 */
+        gh[n] = rs ? 0.0 : conj(abar) * gh[n];        /* carry to t-1 (none across a reset) */
       }
       du[c * seqlen + t] = du_t;
       double gr = softplus_on ? gdt * sigmoid(r) : gdt;
@@ -490,4 +501,4 @@ void oracle_scan_bwd_complex(const double* u, const double* delta, const double*
   free(gh);
 }
 
-int oracle_version(void) { return 5; }
+int oracle_version(void) { return 6; }

@@ -9,7 +9,9 @@ independent numpy brute-force convolution with the complex kernel
 Re(C Abar^k Bbar) when delta, B, C are constant along t; and the
 conjugate-pair identity (a pair (a, conj a) gives twice the real part of one).
 The complex backward is pinned to central differences of the forward, in
-the real and the imaginary direction of every complex input.
+the real and the imaginary direction of every complex input.  Reset flags
+(packed sequences) are pinned by splitting: a packed run equals independent
+runs of its pieces, forward and backward.
 """
 import numpy as np
 import pytest
@@ -136,3 +138,77 @@ def test_complex_backward_zero_A_limit():
     # difference step keeps the rounding of the differences small
     ref = _fd(p, "A", dout, oracle.ZOH, True, eps=1e-4)
     np.testing.assert_allclose(g["dA"], ref, rtol=1e-5, atol=1e-6 * max(1, np.abs(ref).max()))
+
+
+# ---------------------------------------------------------------------------
+# Reset flags: the state entering a flagged step is zero, so a packed run is
+# independent runs of its pieces (the first piece keeps the initial state
+# unless it is itself reset).  Outputs and per-step gradients must match piece
+# by piece; dA, dD, ddelta_bias are sums over the pieces.
+# ---------------------------------------------------------------------------
+def _pieces(row):
+    starts = [0] + [t for t in range(1, row.size) if row[t]]
+    return list(zip(starts, starts[1:] + [row.size]))
+
+
+def _packed(seed):
+    p = _inputs(seed)
+    batch, _, L = p["u"].shape
+    reset = np.zeros((batch, L), np.uint8)
+    reset[0, [0, 7, 8, 30]] = 1          # a reset at t = 0 and two adjacent flags
+    reset[1, [13, L - 1]] = 1            # a one-step final piece
+    dout = np.random.default_rng(seed + 100).standard_normal(p["u"].shape)
+    return p, reset, dout
+
+
+def _piece(p, b, s, e):
+    q = {}
+    for k, v in p.items():
+        if k in ("u", "delta", "z", "B", "C"):
+            q[k] = v[b:b + 1, :, s:e]
+        elif k == "h0":
+            q[k] = v[b:b + 1]
+        else:
+            q[k] = v
+    return q
+
+
+@pytest.mark.parametrize("disc", [oracle.ZOH, oracle.EULER])
+def test_complex_reset_forward_equals_independent_pieces(disc):
+    p, reset, _ = _packed(31)
+    out, last = oracle.scan_fwd_complex(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"],
+                                        p["z"], p["delta_bias"], p["h0"], disc=disc, reset=reset)
+    for b in range(reset.shape[0]):
+        for i, (s, e) in enumerate(_pieces(reset[b])):
+            q = _piece(p, b, s, e)
+            h0 = q["h0"] if (i == 0 and not reset[b, 0]) else None
+            o, l = oracle.scan_fwd_complex(q["u"], q["delta"], q["A"], q["B"], q["C"], q["D"],
+                                           q["z"], q["delta_bias"], h0, disc=disc)
+            np.testing.assert_array_equal(out[b, :, s:e], o[0])
+        np.testing.assert_array_equal(last[b], l[0])
+
+
+@pytest.mark.parametrize("disc", [oracle.ZOH, oracle.EULER])
+def test_complex_reset_backward_equals_independent_pieces(disc):
+    p, reset, dout = _packed(32)
+    g = oracle.scan_bwd_complex(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                                p["delta_bias"], dout, p["h0"], disc=disc, reset=reset)
+    sums = dict(dA=0.0, dD=0.0, ddelta_bias=0.0)
+    for b in range(reset.shape[0]):
+        for i, (s, e) in enumerate(_pieces(reset[b])):
+            q = _piece(p, b, s, e)
+            first = i == 0 and not reset[b, 0]
+            gs = oracle.scan_bwd_complex(q["u"], q["delta"], q["A"], q["B"], q["C"], q["D"],
+                                         q["z"], q["delta_bias"], dout[b:b + 1, :, s:e],
+                                         q["h0"] if first else None, disc=disc)
+            for k in ("du", "ddelta", "dz"):
+                np.testing.assert_array_equal(g[k][b, :, s:e], gs[k][0], err_msg=k)
+            for k in ("dB", "dC"):
+                np.testing.assert_allclose(g[k][b, :, s:e], gs[k][0], rtol=1e-12, atol=1e-13)
+            for k in sums:
+                sums[k] = sums[k] + gs[k]
+            if i == 0:
+                want = gs["dh0"][0] if first else np.zeros_like(g["dh0"][b])
+                np.testing.assert_array_equal(g["dh0"][b], want)
+    for k, v in sums.items():
+        np.testing.assert_allclose(g[k], v, rtol=1e-12, atol=1e-12, err_msg=k)
