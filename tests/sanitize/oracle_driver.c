@@ -28,13 +28,14 @@ void oracle_conv1d_silu_bwd(const double*, const double*, const double*, const u
                             double*, double*, double*);
 void oracle_scan_fwd_complex(const double*, const double*, const double*, const double*,
                              const double*, const double*, const double*, const double*,
-                             const double*, int, int, int64_t, int64_t, int64_t, int64_t, int64_t,
-                             int64_t, double*, double*);
+                             const double*, const unsigned char*, int, int, int64_t, int64_t,
+                             int64_t, int64_t, int64_t, int64_t, double*, double*);
 void oracle_scan_bwd_complex(const double*, const double*, const double*, const double*,
                              const double*, const double*, const double*, const double*,
-                             const double*, const double*, int, int, int64_t, int64_t, int64_t,
-                             int64_t, int64_t, int64_t, double*, double*, double*, double*,
-                             double*, double*, double*, double*, double*);
+                             const double*, const double*, const unsigned char*, int, int,
+                             int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, double*,
+                             double*, double*, double*, double*, double*, double*, double*,
+                             double*);
 
 static uint64_t g_state = 0x9E3779B97F4A7C15ull;
 static double rnd(void) { /* xorshift64*, uniform in [-1, 1) */
@@ -95,13 +96,14 @@ static void run(int64_t Bt, int64_t D, int64_t N, int64_t L, int full, int disc,
   for (int64_t i = 0; i < DN; ++i) cA[2 * i] = -0.5 - fabs(cA[2 * i]);
   if (full && DN > 1) { cA[2] = 0.0; cA[3] = 0.0; }   /* the A = 0 limit */
   double *cout = vec(CT), *clast = vec(2 * BDN);
-  oracle_scan_fwd_complex(u, dl, cA, cB, cC, Do, zo, bo, full ? ch0 : NULL, softplus, disc, Bt,
-                          D, N, L, 0, Bt * D, cout, full ? clast : NULL);
+  oracle_scan_fwd_complex(u, dl, cA, cB, cC, Do, zo, bo, full ? ch0 : NULL, ro, softplus, disc,
+                          Bt, D, N, L, 0, Bt * D, cout, full ? clast : NULL);
   finite(cout, CT, "cfwd out");
   double *cdA = vec(2 * DN), *cdB = vec(2 * BNL), *cdC = vec(2 * BNL), *cdh0 = vec(2 * BDN);
-  oracle_scan_bwd_complex(u, dl, cA, cB, cC, Do, zo, bo, full ? ch0 : NULL, dout, softplus, disc,
-                          Bt, D, N, L, 0, Bt * D, du, ddl, cdA, cdB, cdC, full ? dD : NULL,
-                          full ? dz : NULL, full ? db : NULL, full ? cdh0 : NULL);
+  oracle_scan_bwd_complex(u, dl, cA, cB, cC, Do, zo, bo, full ? ch0 : NULL, dout, ro, softplus,
+                          disc, Bt, D, N, L, 0, Bt * D, du, ddl, cdA, cdB, cdC,
+                          full ? dD : NULL, full ? dz : NULL, full ? db : NULL,
+                          full ? cdh0 : NULL);
   finite(cdA, 2 * DN, "cbwd dA"); finite(du, CT, "cbwd du");
   double* bufs[] = {u, dl, z, dout, A, Bm, C, Dp, bias, h0, out, last, du, ddl, dz, dA, dB, dC,
                     dD, db, dh0, st, so, cA, cB, cC, ch0, cout, clast, cdA, cdB, cdC, cdh0};
