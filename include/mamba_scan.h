@@ -410,6 +410,10 @@ size_t mamba_scan_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate, in
  *    k segments of whole chunks); explicit segments need the workspace the
  *    _ex size queries report for the same count (MAMBA_ERR_WORKSPACE
  *    otherwise).
+ *  - reset (nullable, (batch, seqlen) bytes): packed sequences, as for
+ *    mamba_scan_fwd_varlen / mamba_scan_bwd_varlen: the complex state
+ *    entering each flagged step is zero (and no gradient passes back across
+ *    it).
  */
 size_t mamba_scan_complex_checkpoint_size(int64_t batch, int64_t dim, int64_t dstate,
                                           int64_t seqlen);
@@ -423,7 +427,8 @@ size_t mamba_scan_bwd_complex_workspace_size_ex(int64_t batch, int64_t dim, int6
 mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const float* A,
                                        const float* B, const float* C, const float* D,
                                        const void* z, const float* delta_bias, const float* h0,
-                                       int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                                       const uint8_t* reset, int delta_softplus, mamba_disc disc,
+                                       mamba_dtype dt,
                                        int64_t batch, int64_t dim, int64_t dstate,
                                        int64_t seqlen, void* out, float* last_state,
                                        float* checkpoints, void* workspace,
@@ -432,7 +437,8 @@ mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const f
 mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const float* A,
                                        const float* B, const float* C, const float* D,
                                        const void* z, const float* delta_bias, const float* h0,
-                                       const void* dout, int delta_softplus, mamba_disc disc,
+                                       const void* dout, const uint8_t* reset,
+                                       int delta_softplus, mamba_disc disc,
                                        mamba_dtype dt, int64_t batch, int64_t dim,
                                        int64_t dstate, int64_t seqlen, float* du, float* ddelta,
                                        float* dA, float* dB, float* dC, float* dD, float* dz,

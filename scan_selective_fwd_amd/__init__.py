@@ -296,13 +296,14 @@ def bwd_complex_workspace_bytes(batch, dim, N, L, segments=0) -> int:
 
 def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
                      delta_softplus=True, disc="zoh", out=None, checkpoints=None, segments=0,
-                     workspace=None):
+                     workspace=None, reset=None):
     """Complex-valued forward: A (dim, N), B, C (batch, N, L), h0 (batch, dim,
     N) complex64; u, delta, z real.  Returns (out, last_state complex64) with
     y = Re(sum_n C h) + D u gated by SiLU(z).  `checkpoints`: optional
     complex64 tensor of complex_checkpoint_shape, filled with the state
     entering every chunk (for scan_bwd_complex).  `segments`: 0 = automatic,
-    1 = one pass, k = k sequence segments run in parallel."""
+    1 = one pass, k = k sequence segments run in parallel.  `reset`: optional
+    (batch, L) flags of packed sequences, as for scan_fwd."""
     L_ = lib()
     if not u.is_cuda:
         raise ValueError("u must be a GPU tensor (no CPU path exists)")
@@ -321,6 +322,7 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None
     _req(h0, "h0", torch.complex64, (batch, dim, N), dev)
     _req(checkpoints, "checkpoints", torch.complex64, complex_checkpoint_shape(batch, dim, N, L),
          dev)
+    reset = _flags(reset, (batch, L), dev)
     if out is None:
         out = torch.empty((batch, dim, L), dtype=sdt, device=dev)
     last = torch.empty((batch, dim, N), dtype=torch.complex64, device=dev)
@@ -329,7 +331,7 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if nbytes else None
     st = L_.mamba_scan_fwd_complex_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                      _ptr(z), _ptr(delta_bias), _ptr(h0),
+                                      _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(reset),
                                       int(bool(delta_softplus)), _disc_code(disc),
                                       _dtype_code(u), batch, dim, N, L, _ptr(out), _ptr(last),
                                       _ptr(checkpoints), ws_ptr, nbytes, _stream(dev),
@@ -340,12 +342,12 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None
 
 def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
                      delta_softplus=True, disc="zoh", checkpoints=None, segments=0,
-                     workspace=None):
+                     workspace=None, reset=None):
     """Backward of scan_fwd_complex.  Returns a dict: du, ddelta (and dD, dz,
     ddelta_bias when given) float32; dA, dB, dC (and dh0) complex64, the
     gradient of a complex input w being dL/dRe(w) + i dL/dIm(w).
     `checkpoints`: the buffer a scan_fwd_complex over the same inputs filled;
-    the chunk states are then not recomputed.  `segments` as for
+    the chunk states are then not recomputed.  `segments` and `reset` as for
     scan_fwd_complex."""
     L_ = lib()
     dev = u.device
@@ -363,6 +365,7 @@ def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
         _req(t, name, ty, shp, dev)
     _req(checkpoints, "checkpoints", torch.complex64, complex_checkpoint_shape(batch, dim, N, L),
          dev)
+    reset = _flags(reset, (batch, L), dev)
     f32 = dict(dtype=torch.float32, device=dev)
     c64 = dict(dtype=torch.complex64, device=dev)
     g = dict(du=torch.empty((batch, dim, L), **f32), ddelta=torch.empty((batch, dim, L), **f32),
@@ -389,7 +392,7 @@ def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     st = L_.mamba_scan_bwd_complex_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                       _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(dout),
-                                      int(bool(delta_softplus)), _disc_code(disc),
+                                      _ptr(reset), int(bool(delta_softplus)), _disc_code(disc),
                                       _dtype_code(u), batch, dim, N, L, _ptr(g["du"]),
                                       _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
                                       _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")),

@@ -116,10 +116,10 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_complex_checkpoint_size.restype = _sz
     lib.mamba_scan_complex_checkpoint_size.argtypes = [_i64] * 4
     lib.mamba_scan_fwd_complex_ex.restype = _int
-    lib.mamba_scan_fwd_complex_ex.argtypes = ([_vp] * 9 + [_int, _int, _int] + [_i64] * 4
+    lib.mamba_scan_fwd_complex_ex.argtypes = ([_vp] * 10 + [_int, _int, _int] + [_i64] * 4
                                               + [_vp] * 4 + [_sz, _vp, _int])
     lib.mamba_scan_bwd_complex_ex.restype = _int
-    lib.mamba_scan_bwd_complex_ex.argtypes = ([_vp] * 10 + [_int, _int, _int] + [_i64] * 4
+    lib.mamba_scan_bwd_complex_ex.argtypes = ([_vp] * 11 + [_int, _int, _int] + [_i64] * 4
                                               + [_vp] * 11 + [_sz, _vp, _int])
     lib.mamba_state_update_complex.restype = _int
     lib.mamba_state_update_complex.argtypes = ([_vp] * 9 + [_int, _int, _int] + [_i64] * 3

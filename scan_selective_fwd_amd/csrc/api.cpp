@@ -622,15 +622,16 @@ mamba_status mamba_scan_fwd_complex(const void* u, const void* delta, const floa
                                     int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                     void* out, float* last_state, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  return mamba_scan_fwd_complex_ex(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, disc,
-                                   dt, batch, dim, dstate, seqlen, out, last_state, nullptr,
-                                   workspace, workspace_bytes, stream, 0);
+  return mamba_scan_fwd_complex_ex(u, delta, A, B, C, D, z, delta_bias, h0, nullptr,
+                                   delta_softplus, disc, dt, batch, dim, dstate, seqlen, out,
+                                   last_state, nullptr, workspace, workspace_bytes, stream, 0);
 }
 
 mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const float* A,
                                        const float* B, const float* C, const float* D,
                                        const void* z, const float* delta_bias, const float* h0,
-                                       int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                                       const uint8_t* reset, int delta_softplus, mamba_disc disc,
+                                       mamba_dtype dt,
                                        int64_t batch, int64_t dim, int64_t dstate,
                                        int64_t seqlen, void* out, float* last_state,
                                        float* checkpoints, void* workspace,
@@ -658,6 +659,7 @@ mamba_status mamba_scan_fwd_complex_ex(const void* u, const void* delta, const f
   p.D = D; p.z = z; p.bias = delta_bias; p.h0 = reinterpret_cast<const float2*>(h0);
   p.out = out; p.last_state = reinterpret_cast<float2*>(last_state);
   p.chunk_states = reinterpret_cast<float2*>(checkpoints);
+  p.reset = reset;
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.groups = w.groups;
   p.nseg = 1;
@@ -705,7 +707,7 @@ mamba_status mamba_scan_bwd_complex(const void* u, const void* delta, const floa
                                     float* dB, float* dC, float* dD, float* dz,
                                     float* ddelta_bias, float* dh0, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  return mamba_scan_bwd_complex_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout,
+  return mamba_scan_bwd_complex_ex(u, delta, A, B, C, D, z, delta_bias, h0, dout, nullptr,
                                    delta_softplus, disc, dt, batch, dim, dstate, seqlen, du,
                                    ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, nullptr,
                                    workspace, workspace_bytes, stream, 0);
@@ -714,7 +716,8 @@ mamba_status mamba_scan_bwd_complex(const void* u, const void* delta, const floa
 mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const float* A,
                                        const float* B, const float* C, const float* D,
                                        const void* z, const float* delta_bias, const float* h0,
-                                       const void* dout, int delta_softplus, mamba_disc disc,
+                                       const void* dout, const uint8_t* reset,
+                                       int delta_softplus, mamba_disc disc,
                                        mamba_dtype dt, int64_t batch, int64_t dim,
                                        int64_t dstate, int64_t seqlen, float* du, float* ddelta,
                                        float* dA, float* dB, float* dC, float* dD, float* dz,
@@ -760,6 +763,7 @@ mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const f
   fp.B = reinterpret_cast<const float2*>(B); fp.C = reinterpret_cast<const float2*>(C);
   fp.D = D; fp.z = z; fp.bias = delta_bias; fp.h0 = reinterpret_cast<const float2*>(h0);
   fp.chunk_states = states;
+  fp.reset = reset;
   fp.batch = batch; fp.dim = dim; fp.L = seqlen; fp.nchannels = batch * dim;
   fp.groups = w.groups; fp.N = (int)dstate; fp.softplus = delta_softplus ? 1 : 0;
   fp.nseg = 1;
@@ -787,6 +791,7 @@ mamba_status mamba_scan_bwd_complex_ex(const void* u, const void* delta, const f
   p.dA = reinterpret_cast<float2*>(dA); p.dB = reinterpret_cast<float2*>(dB);
   p.dC = reinterpret_cast<float2*>(dC); p.dD = dD; p.dz = dz; p.dbias = ddelta_bias;
   p.dh0 = reinterpret_cast<float2*>(dh0); p.chunk_states = states;
+  p.reset = reset;
   p.batch = batch; p.dim = dim; p.L = seqlen; p.nchannels = batch * dim;
   p.nchunks = w.nchunks; p.groups = w.groups; p.N = (int)dstate;
   p.softplus = delta_softplus ? 1 : 0;

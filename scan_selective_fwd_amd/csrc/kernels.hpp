@@ -146,6 +146,7 @@ struct CplxParams {
   float2* seg_h0;          // (nchannels, nseg, N) state entering each segment (nullable)
   float2* seg_state;       // summary: (nchannels, nseg, N) end state from a zero start
   float2* seg_dec;         // summary: (nchannels, nseg, N) product of Abar over the segment
+  const uint8_t* reset;    // nullable (batch, L): zero the state before each flagged step
   int N;                   // <= 16
   int softplus;
 };
@@ -214,6 +215,7 @@ struct CplxBwdParams {
   float2* seg_gin;         // (nchannels, nseg, N) adjoint entering each segment (nullable: 0)
   float2* seg_gloc;        // summary: (nchannels, nseg, N)
   float2* seg_gdec;        // summary: (nchannels, nseg, N)
+  const uint8_t* reset;    // nullable (batch, L): zero the state before each flagged step
   int N;                   // <= 16
   int softplus;
 };

@@ -28,6 +28,11 @@
 // it, G being its adjoint at its start from a zero end.  The summary and
 // carry kernels at the end of this file compute those; only segment 0 writes
 // dh0.
+//
+// RST: packed sequences (p.reset flags), as in the real backward: a flagged
+// step's decay becomes 0 in the recurrence and the adjoint (Bbar, and the
+// Abar in its derivatives, keep the true value), its h_{t-1} counts as 0, and
+// no adjoint passes back across it.
 #include "complex_common.hpp"
 #include "kernels.hpp"
 #include "scan_fwd_impl.hpp"
@@ -45,7 +50,7 @@ constexpr int NT = 16;
 constexpr int G = 2;                 // state indices per dB/dC flush
 constexpr int NW = kBlock / 64;
 
-template <typename T, bool ZOH, bool VEC>
+template <typename T, bool ZOH, bool VEC, bool RST>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void scan_bwd_complex_kernel(
     const CplxBwdParams p) {
   __shared__ float4 prm[CPB][NT];            // {A, 1/A} (1/A = 0 where A ~ 0)
@@ -104,6 +109,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   const T* __restrict__ do_row = static_cast<const T*>(p.dout) + c * L;
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
+  const uint8_t* __restrict__ rst_row = RST ? p.reset + b * L : nullptr;
   float dD_acc = 0.0f, db_acc = 0.0f;
   const float* __restrict__ Bf = reinterpret_cast<const float*>(p.B) + b * N * 2 * L;
   const float* __restrict__ Cf = reinterpret_cast<const float*>(p.C) + b * N * 2 * L;
@@ -150,6 +156,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       gdt[k] = 0.0f;
       dD_acc = __builtin_fmaf(gy[k], uv[k], dD_acc);
     }
+    float keep[K];
+    float lane_keep = 1.0f;
+    if constexpr (RST) lane_keep = load_keep<K>(rst_row, tl, L, keep) ? 0.0f : 1.0f;
+    // a step's decay in the recurrence and the adjoint (0 at a flagged step)
+    auto decay = [&](int k, float2 ab) { return RST ? cscale(ab, keep[k]) : ab; };
 
 #pragma unroll 1
     for (int n = 0; n < N; ++n) {
@@ -191,8 +202,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
       float2 agg = beta[0];
 #pragma unroll
-      for (int k = 1; k < K; ++k) agg = cfma(ab[k], agg, beta[k]);
-      const float2 Alane = cexp_scaled(dsum, ps.x, ps.y);
+      for (int k = 1; k < K; ++k) agg = cfma(decay(k, ab[k]), agg, beta[k]);
+      const float2 Alane = RST ? cscale(cexp_scaled(dsum, ps.x, ps.y), lane_keep)
+                               : cexp_scaled(dsum, ps.x, ps.y);
       float2 Ag = Alane;
       if (j == 0) agg = cfma(Ag, h_in, agg);
       cplx_scan_prefix_row(Ag, agg);
@@ -202,7 +214,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         float2 h = hstart;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          h = cfma(ab[k], h, beta[k]);
+          h = cfma(decay(k, ab[k]), h, beta[k]);
           hv[k] = h;
           yv[k] = __builtin_fmaf(Cv[k].x, h.x, __builtin_fmaf(-Cv[k].y, h.y, yv[k]));
         }
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       float2 gagg = make_float2(0.0f, 0.0f);
 #pragma unroll
       for (int k = K - 1; k >= 0; --k)
-        gagg = cmul(cconj(ab[k]), cadd(cscale(cconj(Cv[k]), gy[k]), gagg));
+        gagg = cmul(cconj(decay(k, ab[k])), cadd(cscale(cconj(Cv[k]), gy[k]), gagg));
       float2 As = cconj(Alane);
       if (j == R - 1) gagg = cfma(As, gc, gagg);      // the later chunk enters lane 15
       cplx_scan_suffix_row(As, gagg);
@@ -228,8 +240,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       for (int k = K - 1; k >= 0; --k) {
         const float2 Gk = make_float2(__builtin_fmaf(Cv[k].x, gy[k], g.x),
                                       __builtin_fmaf(-Cv[k].y, gy[k], g.y));
-        const float2 gn = cmul(cconj(ab[k]), Gk);   // the adjoint passed to step t - 1
-        const float2 hprev = (k == 0) ? hstart : hv[k - 1];
+        const float2 gn = cmul(cconj(ab[k]), Gk);   // with the true Abar (also in conj(E) G)
+        float2 hprev = (k == 0) ? hstart : hv[k - 1];
+        if constexpr (RST) hprev = cscale(hprev, keep[k]);
         const float2 Bu = cscale(Bv[k], uv[k]);
         // s = conj(E) G with E = Bbar / B; du and dB both use it
         float2 sG;
@@ -265,7 +278,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             else if (k == 0) Tq[qq][0] = rs_pair32(sv[qq][0], sv[qq][1]);
           }
         }
-        g = gn;
+        g = RST ? cscale(gn, keep[k]) : gn;   // the adjoint passed to step t - 1
       }
       const int buf = (n / G) & 1;
 #pragma unroll
@@ -378,7 +391,7 @@ __global__ __launch_bounds__(256) void cplx_bwd_zero_kernel(const CplxBwdParams 
 // segment's chunks from last to first with a zero adjoint entering its end;
 // per state, G (the adjoint at the segment's first step) and prod(conj Abar)
 // over the segment.  Only delta, dout, z and C are read.
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool RST>
 __global__ __launch_bounds__(kBlock) void bwd_seg_summary_complex_kernel(const CplxBwdParams p) {
   constexpr int RW = 2 * TCH;
   __shared__ float4 tile_mem[NT * RW / 4];   // C rows
@@ -418,6 +431,7 @@ __global__ __launch_bounds__(kBlock) void bwd_seg_summary_complex_kernel(const C
   const T* __restrict__ z_row = p.z ? static_cast<const T*>(p.z) + c * L : nullptr;
   const T* __restrict__ do_row = static_cast<const T*>(p.dout) + c * L;
   const float bias = p.bias ? p.bias[d] : 0.0f;
+  const uint8_t* __restrict__ rst_row = RST ? p.reset + b * L : nullptr;
   const float* __restrict__ Cf = reinterpret_cast<const float*>(p.C) + b * N * 2 * L;
   float* tile = reinterpret_cast<float*>(tile_mem);
   TileStager<float, RW, 2 * K, NT, NT, kBlock> stage;
@@ -453,6 +467,9 @@ __global__ __launch_bounds__(kBlock) void bwd_seg_summary_complex_kernel(const C
     float dsum = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) dsum += dt[k];
+    float keep[K];
+    float lane_keep = 1.0f;
+    if constexpr (RST) lane_keep = load_keep<K>(rst_row, tl, L, keep) ? 0.0f : 1.0f;
 
     for (int n = 0; n < N; ++n) {
       const float2 ps = prs[cl][n];
@@ -462,11 +479,13 @@ __global__ __launch_bounds__(kBlock) void bwd_seg_summary_complex_kernel(const C
       float2 gagg = make_float2(0.0f, 0.0f);
 #pragma unroll
       for (int k = K - 1; k >= 0; --k) {
-        const float2 ab = cexp_scaled(dt[k], ps.x, ps.y);
+        float2 ab = cexp_scaled(dt[k], ps.x, ps.y);
+        if constexpr (RST) ab = cscale(ab, keep[k]);
         gagg = cmul(cconj(ab), make_float2(__builtin_fmaf(cf[2 * k], gy[k], gagg.x),
                                            __builtin_fmaf(-cf[2 * k + 1], gy[k], gagg.y)));
       }
       float2 As = cconj(cexp_scaled(dsum, ps.x, ps.y));
+      if constexpr (RST) As = cscale(As, lane_keep);
       const float2 gc = gcs[cl][n];
       if (j == R - 1) gagg = cfma(As, gc, gagg);       // the later chunk enters lane 15
       cplx_scan_suffix_row(As, gagg);
@@ -508,6 +527,19 @@ __global__ __launch_bounds__(256) void bwd_seg_carry_complex_kernel(const CplxBw
   }
 }
 
+template <typename T, bool RST>
+hipError_t launch_bwd_complex_main(const CplxBwdParams& p, int disc, bool vec, hipStream_t s) {
+  const dim3 grid((unsigned)(p.batch * p.groups * p.nseg)), block(kBlock);
+  if (disc == 0) {
+    if (vec) hipLaunchKernelGGL((scan_bwd_complex_kernel<T, true, true, RST>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_bwd_complex_kernel<T, true, false, RST>), grid, block, 0, s, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((scan_bwd_complex_kernel<T, false, true, RST>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_bwd_complex_kernel<T, false, false, RST>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_bwd_complex(const CplxBwdParams& p, int disc, bool vec, hipStream_t s) {
   {
@@ -518,14 +550,15 @@ hipError_t launch_bwd_complex(const CplxBwdParams& p, int disc, bool vec, hipStr
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  return p.reset ? launch_bwd_complex_main<T, true>(p, disc, vec, s)
+                 : launch_bwd_complex_main<T, false>(p, disc, vec, s);
+}
+
+template <typename T, bool RST>
+hipError_t launch_bwd_seg_summary_complex(const CplxBwdParams& p, bool vec, hipStream_t s) {
   const dim3 grid((unsigned)(p.batch * p.groups * p.nseg)), block(kBlock);
-  if (disc == 0) {
-    if (vec) hipLaunchKernelGGL((scan_bwd_complex_kernel<T, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_bwd_complex_kernel<T, true, false>), grid, block, 0, s, p);
-  } else {
-    if (vec) hipLaunchKernelGGL((scan_bwd_complex_kernel<T, false, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_bwd_complex_kernel<T, false, false>), grid, block, 0, s, p);
-  }
+  if (vec) hipLaunchKernelGGL((bwd_seg_summary_complex_kernel<T, true, RST>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((bwd_seg_summary_complex_kernel<T, false, RST>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -539,15 +572,11 @@ hipError_t dispatch_scan_bwd_complex(const CplxBwdParams& p, int dtype, int disc
 
 hipError_t dispatch_bwd_seg_summary_complex(const CplxBwdParams& p, int dtype, bool vec,
                                             hipStream_t s) {
-  const dim3 grid((unsigned)(p.batch * p.groups * p.nseg)), block(kBlock);
-  if (dtype == 0) {
-    if (vec) hipLaunchKernelGGL((bwd_seg_summary_complex_kernel<float, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((bwd_seg_summary_complex_kernel<float, false>), grid, block, 0, s, p);
-  } else {
-    if (vec) hipLaunchKernelGGL((bwd_seg_summary_complex_kernel<bf16_t, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((bwd_seg_summary_complex_kernel<bf16_t, false>), grid, block, 0, s, p);
-  }
-  return hipGetLastError();
+  if (dtype == 0)
+    return p.reset ? launch_bwd_seg_summary_complex<float, true>(p, vec, s)
+                   : launch_bwd_seg_summary_complex<float, false>(p, vec, s);
+  return p.reset ? launch_bwd_seg_summary_complex<bf16_t, true>(p, vec, s)
+                 : launch_bwd_seg_summary_complex<bf16_t, false>(p, vec, s);
 }
 
 hipError_t dispatch_bwd_seg_carry_complex(const CplxBwdParams& p, hipStream_t s) {

@@ -43,11 +43,16 @@ constexpr int NT = 16;
 // carry kernel below filled from the summaries (the associative combination
 // of trishampatil essay, Part III §2, on whole segments).
 //
+// RST: packed sequences.  Where p.reset flags a step the state entering it
+// is zero: the step's decay in the recurrence (not in Bbar) becomes 0, and so
+// does the decay of any lane summary that holds the step (the segment's
+// product of Abar then vanishes too, so the carry passes nothing across it).
+//
 // B and C (complex, shared by the block's 16 channels) are staged per chunk
 // into one LDS tile by the whole block with 16-byte loads (tile_stage.hpp:
 // a complex row of TCH steps is a float row of 2*TCH); the next chunk's
 // loads are in flight in registers while the current chunk computes.
-template <typename T, bool ZOH, bool VEC, int MODE>
+template <typename T, bool ZOH, bool VEC, int MODE, bool RST>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_fwd_complex_kernel(
     const CplxParams p) {
   constexpr bool STATES = MODE != 0;
@@ -103,6 +108,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const float* __restrict__ Cf = reinterpret_cast<const float*>(p.C) + b * N * 2 * L;
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
+  const uint8_t* __restrict__ rst_row = RST ? p.reset + b * L : nullptr;
   const int64_t nchunks = (L + TCH - 1) / TCH;
   const int64_t ch_begin = p.seg_chunks > 0 ? seg * p.seg_chunks : 0;
   const int64_t ch_end =
@@ -139,6 +145,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       dsum += dt[k];
       y[k] = Dd * uv[k];
     }
+    float keep[K];
+    float lane_keep = 1.0f;
+    if constexpr (RST) lane_keep = load_keep<K>(rst_row, tl, L, keep) ? 0.0f : 1.0f;
 
     for (int n = 0; n < N; ++n) {
       const float4 pr = prm[cl][n];
@@ -165,11 +174,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           beta[k] = tiny ? cscale(Bu, dt[k]) : cmul_minus_one(ab[k], cmul(ia, Bu));
         }
       }
+      if constexpr (RST) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) ab[k] = cscale(ab[k], keep[k]);   // the decay only
+      }
       float2 agg = beta[0];
 #pragma unroll
       for (int k = 1; k < K; ++k) agg = cfma(ab[k], agg, beta[k]);
       // the lane's decay: exp(A * sum of its steps)
       float2 Ag = cexp_scaled(dsum, ar2, air);
+      if constexpr (RST) Ag = cscale(Ag, lane_keep);
       const float2 cin = carry[cl][n];
       if (j == 0) agg = cfma(Ag, cin, agg);    // the carried state enters lane 0
       cplx_scan_prefix_row(Ag, agg);
@@ -241,17 +255,23 @@ __global__ __launch_bounds__(256) void seg_carry_complex_kernel(const CplxParams
   if (p.last_state) p.last_state[c * p.N + n] = H;
 }
 
-template <typename T, int MODE>
-hipError_t launch_complex(const CplxParams& p, int disc, bool vec, hipStream_t s) {
+template <typename T, int MODE, bool RST>
+hipError_t launch_complex_rst(const CplxParams& p, int disc, bool vec, hipStream_t s) {
   const dim3 grid((unsigned)(p.batch * p.groups * p.nseg)), block(kBlock);
   if (disc == 0) {
-    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, true, MODE>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, false, MODE>), grid, block, 0, s, p);
+    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, true, MODE, RST>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, true, false, MODE, RST>), grid, block, 0, s, p);
   } else {
-    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, true, MODE>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, false, MODE>), grid, block, 0, s, p);
+    if (vec) hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, true, MODE, RST>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_fwd_complex_kernel<T, false, false, MODE, RST>), grid, block, 0, s, p);
   }
   return hipGetLastError();
+}
+
+template <typename T, int MODE>
+hipError_t launch_complex(const CplxParams& p, int disc, bool vec, hipStream_t s) {
+  return p.reset ? launch_complex_rst<T, MODE, true>(p, disc, vec, s)
+                 : launch_complex_rst<T, MODE, false>(p, disc, vec, s);
 }
 
 }  // namespace

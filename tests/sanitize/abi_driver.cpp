@@ -75,9 +75,9 @@ void sweep(int64_t b, int64_t d, int64_t n, int64_t l) {
     for (int segs : {0, 1, 3, 1000}) {
       (void)mamba_scan_fwd_complex_workspace_size_ex(b, d, n, l, segs);
       (void)mamba_scan_bwd_complex_workspace_size_ex(b, d, n, l, segs);
-      (void)mamba_scan_fwd_complex_ex(P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d, n,
+      (void)mamba_scan_fwd_complex_ex(P, P, P, P, P, P, P, P, P, F, 1, MAMBA_DISC_ZOH, dt, b, d, n,
                                       l, P, P, P, P, BIG, nullptr, segs);
-      (void)mamba_scan_bwd_complex_ex(P, P, P, P, P, P, P, P, P, P, 1, MAMBA_DISC_ZOH, dt, b, d,
+      (void)mamba_scan_bwd_complex_ex(P, P, P, P, P, P, P, P, P, P, F, 1, MAMBA_DISC_ZOH, dt, b, d,
                                       n, l, P, P, P, P, P, P, P, P, P, nullptr, P, BIG, nullptr,
                                       segs);
     }
@@ -139,7 +139,7 @@ int main() {
            MAMBA_ERR_UNSUPPORTED);
   }
   EXPECT(mamba_scan_complex_checkpoint_size(2, 64, 17, 2049), SIZE_MAX);
-  EXPECT(mamba_scan_bwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, P, 1,
+  EXPECT(mamba_scan_bwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, P, nullptr, 1,
                                    MAMBA_DISC_ZOH, MAMBA_F32, 2, 64, 16, 2048, P, P, P, P, P,
                                    nullptr, nullptr, nullptr, nullptr, P, nullptr, 0, nullptr,
                                    0),
@@ -149,11 +149,11 @@ int main() {
     const size_t fw = mamba_scan_fwd_complex_workspace_size_ex(1, 16, 16, 65536, 8);
     const size_t bw = mamba_scan_bwd_complex_workspace_size_ex(1, 16, 16, 65536, 8);
     if (!(fw > 0 && bw > fw)) ++g_fail;
-    EXPECT(mamba_scan_fwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, 1,
+    EXPECT(mamba_scan_fwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, nullptr, 1,
                                      MAMBA_DISC_ZOH, MAMBA_F32, 1, 16, 16, 65536, P, nullptr,
                                      nullptr, P, fw - 1, nullptr, 8),
            MAMBA_ERR_WORKSPACE);
-    EXPECT(mamba_scan_fwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, 1,
+    EXPECT(mamba_scan_fwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, nullptr, 1,
                                      MAMBA_DISC_ZOH, MAMBA_F32, 1, 16, 16, 65536, P, P, nullptr,
                                      P, fw, nullptr, 8),
            MAMBA_OK);
@@ -161,12 +161,12 @@ int main() {
                                   MAMBA_DISC_ZOH, MAMBA_F32, 1, 16, 16, 65536, P, nullptr,
                                   nullptr, 0, nullptr),
            MAMBA_OK);                           // automatic without the workspace: one pass
-    EXPECT(mamba_scan_bwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, P, 1,
+    EXPECT(mamba_scan_bwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, P, nullptr, 1,
                                      MAMBA_DISC_ZOH, MAMBA_F32, 1, 16, 16, 65536, P, P, P, P, P,
                                      nullptr, nullptr, nullptr, nullptr, nullptr, P, bw - 1,
                                      nullptr, 8),
            MAMBA_ERR_WORKSPACE);
-    EXPECT(mamba_scan_bwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, P, 1,
+    EXPECT(mamba_scan_bwd_complex_ex(P, P, P, P, P, nullptr, nullptr, nullptr, nullptr, P, nullptr, 1,
                                      MAMBA_DISC_ZOH, MAMBA_F32, 1, 16, 16, 65536, P, P, P, P, P,
                                      nullptr, nullptr, nullptr, nullptr, nullptr, P, bw, nullptr,
                                      -1),

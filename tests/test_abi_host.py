@@ -193,15 +193,15 @@ def test_complex_checkpoints_size_and_workspace(lib):
     assert need == 2 * 64 * 16 * 16 * 8
 
     def bwd_ex(ws, wsb, ckpt):
-        return lib.mamba_scan_bwd_complex_ex(P, P, P, P, P, None, None, None, None, P, 1, 0, 0,
+        return lib.mamba_scan_bwd_complex_ex(P, P, P, P, P, None, None, None, None, P, None, 1, 0, 0,
                                              2, 64, 16, 2048, P, P, P, P, P, None, None, None,
                                              None, ckpt, ws, wsb, None, 1)
     assert bwd_ex(None, 0, None) == 5                # no checkpoints: the states need room
     assert bwd_ex(P, need - 1, None) == 5
     assert bwd_ex(P, need, P + 8) == 4               # misaligned checkpoints
-    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 2, 64,
+    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, None, 1, 0, 0, 2, 64,
                                          16, 2048, P, None, P + 4, None, 0, None, 1) == 4
-    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 2, 64,
+    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, None, 1, 0, 0, 2, 64,
                                          17, 2048, P, None, P, None, 0, None, 1) == 6
 
 
@@ -222,9 +222,9 @@ def test_complex_segment_workspace(lib):
     assert lib.mamba_scan_bwd_complex_workspace_size_ex(1, 16, 17, 1024, 2) == 2 ** 64 - 1
     fw = lib.mamba_scan_fwd_complex_workspace_size_ex(1, 16, 16, 1024, 4)
     assert fw > 0
-    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 1, 16,
+    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, None, 1, 0, 0, 1, 16,
                                          16, 1024, P, None, None, P, fw - 1, None, 4) == 5
-    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, 1, 0, 0, 1, 16,
+    assert lib.mamba_scan_fwd_complex_ex(P, P, P, P, P, None, None, None, None, None, 1, 0, 0, 1, 16,
                                          16, 1024, P, None, None, P, fw, None, -1) == 6
 
 

@@ -23,10 +23,11 @@ def _dev(x, dtype):
 
 
 def _case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None,
-          zero_A=False, segments=0):
+          zero_A=False, segments=0, reset=None):
     opts = opts or {}
     announce(f"complex fwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} h0={h0} "
-             f"softplus={softplus} opts={opts} segments={segments}")
+             f"softplus={softplus} opts={opts} segments={segments} "
+             f"resets={None if reset is None else int(reset.sum())}")
     inp = W.make_complex_inputs(wid, batch, dim, N, L, dtype=dtype, **opts)
     if not softplus:   # a positive raw step without the softplus
         raw = np.abs(W.as_f64(inp["delta"], dtype)) * 0.05 + 0.01
@@ -44,12 +45,14 @@ def _case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None
     out, last = ms.scan_fwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t.get("D"),
                                     t.get("z"), t.get("delta_bias"),
                                     None if h0v is None else torch.from_numpy(h0v).cuda(),
-                                    delta_softplus=softplus, disc=disc, segments=segments)
+                                    delta_softplus=softplus, disc=disc, segments=segments,
+                                    reset=None if reset is None else torch.from_numpy(reset).cuda())
     torch.cuda.synchronize()
     f = {k: (W.as_f64(v, dtype) if v.dtype == np.uint16 else v) for k, v in inp.items()}
     ref, ref_last = oracle.scan_fwd_complex(
         f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"), f.get("z"), f.get("delta_bias"),
-        h0v, delta_softplus=softplus, disc=oracle.ZOH if disc == "zoh" else oracle.EULER)
+        h0v, delta_softplus=softplus, disc=oracle.ZOH if disc == "zoh" else oracle.EULER,
+        reset=reset)
     assert_match(to_f64(out), ref, RTOL[dtype], "out")
     got_last = last.cpu().numpy().astype(np.complex128)
     assert_match(np.stack([got_last.real, got_last.imag], -1),
@@ -93,10 +96,11 @@ def _as_pairs(x):
 
 
 def _bwd_case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=None,
-              zero_A=False, segments=0):
+              zero_A=False, segments=0, reset=None):
     opts = opts or {}
     announce(f"complex bwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} h0={h0} "
-             f"softplus={softplus} opts={opts} zero_A={zero_A} segments={segments}")
+             f"softplus={softplus} opts={opts} zero_A={zero_A} segments={segments} "
+             f"resets={None if reset is None else int(reset.sum())}")
     inp = W.make_complex_inputs(wid, batch, dim, N, L, dtype=dtype, with_dout=True, **opts)
     if not softplus:
         raw = np.abs(W.as_f64(inp["delta"], dtype)) * 0.05 + 0.01
@@ -114,13 +118,15 @@ def _bwd_case(wid, batch, dim, N, L, dtype, disc, h0=False, softplus=True, opts=
     res = ms.scan_bwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t.get("D"), t.get("z"),
                               t.get("delta_bias"), t["dout"],
                               None if h0v is None else torch.from_numpy(h0v).cuda(),
-                              delta_softplus=softplus, disc=disc, segments=segments)
+                              delta_softplus=softplus, disc=disc, segments=segments,
+                              reset=None if reset is None else torch.from_numpy(reset).cuda())
     torch.cuda.synchronize()
     f = {k: (W.as_f64(v, dtype) if v.dtype == np.uint16 else v) for k, v in inp.items()}
     ref = oracle.scan_bwd_complex(f["u"], f["delta"], f["A"], f["B"], f["C"], f.get("D"),
                                   f.get("z"), f.get("delta_bias"), f["dout"], h0v,
                                   delta_softplus=softplus,
-                                  disc=oracle.ZOH if disc == "zoh" else oracle.EULER)
+                                  disc=oracle.ZOH if disc == "zoh" else oracle.EULER,
+                                  reset=reset)
     assert set(res) == set(ref), (set(res), set(ref))
     for k in ref:
         got = res[k].cpu().numpy()
@@ -160,6 +166,34 @@ def test_complex_segmented_sizes_zero_A_slow_decay():
     # carried product of Abar must hold it (A.im up to pi (N - 1))
     _case(87, 1, 16, 16, 4096, "f32", "zoh", h0=True, softplus=False, segments=32)
     _bwd_case(87, 1, 16, 16, 4096, "f32", "zoh", h0=True, softplus=False, segments=32)
+
+
+# Packed sequences: the state entering each flagged step is zero.  Flags at
+# t = 0 (the initial state is dropped), inside a lane's steps, on chunk
+# borders, and at the last step.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_complex_varlen(dtype, disc):
+    L = 700
+    rs = W.make_resets(89, 2, L, 1, 200, force=(0, 8, 128, 129, L - 1))
+    rs[1, 0] = 0
+    _case(89, 2, 19, 16, L, dtype, disc, h0=True, reset=rs, segments=1)
+    _bwd_case(89, 2, 19, 16, L, dtype, disc, h0=True, reset=rs, segments=1)
+
+
+def test_complex_varlen_segments_sizes_zero_A():
+    # resets with segments: one in a segment's first chunk, a segment free of
+    # them between two that have them
+    L = 2048
+    rs = W.make_resets(90, 2, L, 1, 700, force=(0, 1, 255, 256, 511, 1024, 1025, L - 1))
+    rs[1, 512:1024] = 0
+    _case(90, 2, 9, 16, L, "f32", "zoh", h0=True, reset=rs, segments=8)
+    _bwd_case(90, 2, 9, 16, L, "f32", "zoh", h0=True, reset=rs, segments=8)
+    _case(91, 2, 9, 5, L, "bf16", "euler", reset=rs, segments=3)
+    _bwd_case(91, 2, 9, 5, L, "bf16", "euler", reset=rs, segments=3)
+    rs2 = W.make_resets(92, 1, 1000, 20, 300, force=(0, 384))
+    _case(92, 1, 12, 4, 1000, "f32", "zoh", h0=True, zero_A=True, reset=rs2)
+    _bwd_case(92, 1, 12, 4, 1000, "f32", "zoh", h0=True, zero_A=True, reset=rs2)
 
 
 def test_complex_automatic_segmentation_long_sequence():
