@@ -105,3 +105,60 @@ def test_captured_step_replays_match_eager_and_oracle(wid, batch, dim, N, L, seg
                           f["delta_bias"], f["dout"])
     for k in ref:
         assert_match(to_f64(graph_g[k]), ref[k], RTOL["f32"], f"graph {k} vs oracle")
+
+
+@pytest.mark.parametrize("segments", [1, 4])
+def test_captured_complex_step_replays_match_eager(segments):
+    """The complex forward (saving checkpoints) and backward from them,
+    captured and replayed three times, in one pass and in 4 segments, with
+    packed-sequence flags: each replay matches the eager run and the oracle."""
+    wid, batch, dim, N, L = 86, 1, 20, 16, 1100
+    announce(f"graph capture complex wid={wid} shape=({batch},{dim},{N},{L}) "
+             f"segments={segments}")
+    inp = W.make_complex_inputs(wid, batch, dim, N, L, dtype="f32", with_dout=True)
+    reset = W.make_resets(wid, batch, L, 100, 500, force=(0, 300))
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in inp.items()}
+    rt = torch.from_numpy(reset).cuda()
+    ckpt = torch.empty(ms.complex_checkpoint_shape(batch, dim, N, L), dtype=torch.complex64,
+                       device="cuda")
+    out = torch.empty((batch, dim, L), dtype=torch.float32, device="cuda")
+    nf = ms.fwd_complex_workspace_bytes(batch, dim, N, L, segments)
+    fws = torch.empty(max(nf, 1), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(max(ms.bwd_complex_workspace_bytes(batch, dim, N, L, segments), 1),
+                      dtype=torch.uint8, device="cuda")
+
+    def run():
+        ms.scan_fwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                            t["delta_bias"], out=out, checkpoints=ckpt, segments=segments,
+                            workspace=fws, reset=rt)
+        return ms.scan_bwd_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                   t["delta_bias"], t["dout"], checkpoints=ckpt,
+                                   segments=segments, workspace=bws, reset=rt)
+
+    eager = {k: v.clone() for k, v in run().items()}
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graph_g = run()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for buf in (out, ckpt, *graph_g.values()):
+            buf.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), f"replay {r}: forward output differs"
+        for k in eager:
+            a = torch.view_as_real(graph_g[k]) if graph_g[k].is_complex() else graph_g[k]
+            e = torch.view_as_real(eager[k]) if eager[k].is_complex() else eager[k]
+            assert_match(to_f64(a), to_f64(e), 1e-5, f"replay {r} {k}")
+    ref, _ = oracle.scan_fwd_complex(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                     inp["D"], inp["z"], inp["delta_bias"], reset=reset)
+    assert_match(to_f64(out), ref, RTOL["f32"], "graph complex out vs oracle")
