@@ -288,13 +288,15 @@ def probe_rates(torch, blocks=8192, iters=2048):
 # (paper-graph-ui summary, "Speed and Memory Benchmarks", Figure 8 left;
 # context only: other hardware, and the page does not say whether forward or
 # forward + backward).
+SWEEP_COMPLEX_MAX_LOG2 = 17
 SWEEP_PAGES_MS = {32768: 2.0, 131072: 10.0}
 
 
 def sweep(torch, ms_lib, W, steps=10):
     """Forward and backward time over the sequence lengths of the pages'
     scan benchmark, inputs drawn like workload 1; each call with its default
-    (automatic) sequence segmentation."""
+    (automatic) sequence segmentation.  Up to 2^SWEEP_COMPLEX_MAX_LOG2 steps
+    the complex-valued forward and backward are timed at the same shape."""
     rows = []
     for e in range(9, 20):
         L = 1 << e
@@ -334,10 +336,41 @@ def sweep(torch, ms_lib, W, steps=10):
             t = e0.elapsed_time(e1) / steps
             row[f"{name}_ms"] = round(t, 4)
             row[f"{name}_channel_tokens_per_s"] = round(1024 * L / (t * 1e-3), 1)
+        del g, out, fws, bws
+        if e <= SWEEP_COMPLEX_MAX_LOG2:
+            # the complex-valued calls (S4D-Lin A, complex64 B and C), same shape
+            ci = W.make_complex_inputs(9, 1, 1024, 16, L, dtype="bf16", with_dout=True)
+            cg = {}
+            for k, v in ci.items():
+                if v.dtype == np.uint16:
+                    cg[k] = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(
+                        torch.bfloat16).cuda()
+                else:
+                    cg[k] = torch.from_numpy(np.ascontiguousarray(v)).cuda()
+            del ci
+
+            def cfwd():
+                ms_lib.scan_fwd_complex(cg["u"], cg["delta"], cg["A"], cg["B"], cg["C"], cg["D"],
+                                        cg["z"], cg["delta_bias"])
+
+            def cbwd():
+                ms_lib.scan_bwd_complex(cg["u"], cg["delta"], cg["A"], cg["B"], cg["C"], cg["D"],
+                                        cg["z"], cg["delta_bias"], cg["dout"])
+
+            for name, fn in (("complex_fwd", cfwd), ("complex_bwd", cbwd)):
+                fn()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                row[f"{name}_ms"] = round(e0.elapsed_time(e1) / steps, 4)
+            del cg
         if L in SWEEP_PAGES_MS:
             row["pages_a100_ms"] = SWEEP_PAGES_MS[L]
         rows.append(row)
-        del g, out, fws, bws
     return rows
 
 
