@@ -139,3 +139,46 @@ def test_long_sequence_bwd_segmented_sampled_channels():
     for k in got:
         errs[k] = assert_match(got[k], ref[k], RTOL["bf16"], k)
     print(f"long-sequence bwd rel errors {errs}", flush=True)
+
+
+def test_over_2e31_elements_sampled_channels():
+    # batch 1, D 2064, 2^20 steps: 2.16e9 elements per (B, D, L) tensor, past
+    # 2^31, so every element offset needs 64 bits.  129 channel groups split
+    # into 16 segments each.  Forward and backward on sampled channels (the
+    # last one in the last group); dout is zero elsewhere, so dB and dC come
+    # from the sampled channels alone.
+    wid, batch, dim, N, L = 93, 1, 2064, 16, 1 << 20
+    assert batch * dim * L > 2 ** 31
+    announce(f"over 2^31 elements: bf16 ({batch},{dim},{N},{L}) sampled channels")
+    inp = W.make_inputs(wid, batch, dim, N, L, dtype="bf16", bias="const", per_row=True,
+                        with_dout=True)
+    chans = [0, 1031, 2063]
+    others = np.ones(dim, bool)
+    others[chans] = False
+    inp["dout"][:, others] = 0
+    g = to_device(inp, "bf16")
+    out, last = ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                            g["delta_bias"], return_last_state=True)
+    torch.cuda.synchronize()
+    got_out = to_f64(out[:, chans])
+    got_last = to_f64(last[:, chans])
+    del out
+    res = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                      g["delta_bias"], g["dout"])
+    torch.cuda.synchronize()
+    got = {k: to_f64(v[:, chans]) for k, v in res.items() if k in ("du", "ddelta", "dz")}
+    got.update({k: to_f64(res[k][chans]) for k in ("dA", "dD", "ddelta_bias")})
+    got.update({k: to_f64(res[k]) for k in ("dB", "dC")})
+    del g, res
+    sub = {k: (v[:, chans] if k in ("u", "delta", "z", "dout") else
+               v[chans] if k in ("A", "D", "delta_bias") else v) for k, v in inp.items()}
+    del inp
+    f = W.inputs_f64(sub, "bf16")
+    ref_out, ref_last = oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"],
+                                        f["z"], f["delta_bias"])
+    e = assert_match(got_out, ref_out, RTOL["bf16"], "out")
+    e2 = assert_match(got_last, ref_last, 1e-4, "last_state")
+    ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                          f["delta_bias"], f["dout"])
+    errs = {k: assert_match(got[k], ref[k], RTOL["bf16"], k) for k in got}
+    print(f"over-2^31 rel errors out {e} state {e2} grads {errs}", flush=True)
