@@ -68,3 +68,38 @@ def test_conv_packed_sequences(dtype):
     rs[1, 0] = 0
     _case(62, 2, 9, L, 4, dtype, reset=rs)
     _case(63, 2, 9, L, 2, dtype, with_b=False, reset=rs)
+
+
+def test_conv_over_2e31_elements_sampled_channels():
+    # batch 1, D 2064, 2^20 steps: 2.16e9 elements per tensor (64-bit offsets
+    # and about a million blocks); sampled channels against the oracle, with
+    # packed-sequence flags
+    seed, batch, dim, L, width = 94, 1, 2064, 1 << 20, 4
+    announce(f"conv over 2^31 elements: bf16 ({batch},{dim},{L}) W={width} sampled channels")
+    inp = W.make_inputs(seed, batch, dim, 1, L, dtype="bf16", per_row=True, with_dout=True,
+                        with_D=False, with_z=False, with_bias=False)
+    g = np.random.default_rng([seed, 10])
+    w = (g.standard_normal((dim, width)) * 0.5).astype(np.float32)
+    b = (g.standard_normal(dim) * 0.5).astype(np.float32)
+    reset = W.make_resets(seed, batch, L, 1000, 300000, force=(0, 2048 * 300))
+    xt = torch.from_numpy(np.ascontiguousarray(inp["u"]).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    dut = torch.from_numpy(np.ascontiguousarray(inp["dout"]).view(np.int16)).view(
+        torch.bfloat16).cuda().float()               # bf16 values, exact in float32
+    wt, bt, rt = torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda(), torch.from_numpy(reset).cuda()
+    u = ms.conv1d_silu_fwd(xt, wt, bt, reset=rt)
+    grads = ms.conv1d_silu_bwd(xt, wt, bt, dut, reset=rt)
+    torch.cuda.synchronize()
+    chans = [0, 1031, 2063]
+    got_u = to_f64(u[:, chans])
+    got = {k: to_f64(grads[k][:, chans]) for k in ("dx",)}
+    got.update({k: to_f64(grads[k][chans]) for k in ("dw", "db")})
+    del xt, dut, u, grads
+    x64 = W.as_f64(inp["u"][:, chans], "bf16")
+    du64 = W.as_f64(inp["dout"][:, chans], "bf16")
+    ref_u = oracle.conv1d_silu_fwd(x64, w[chans], b[chans], reset=reset)
+    ref_g = oracle.conv1d_silu_bwd(x64, w[chans], b[chans], du64, reset=reset)
+    assert_match(got_u, ref_u, RTOL["bf16"], "u")
+    assert_match(got["dx"], ref_g["dx"], RTOL["f32"], "dx")
+    assert_match(got["dw"], ref_g["dw"], RTOL["f32"], "dw")
+    assert_match(got["db"], ref_g["dcb"], RTOL["f32"], "db")
