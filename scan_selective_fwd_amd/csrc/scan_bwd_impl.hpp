@@ -50,6 +50,16 @@
 
 namespace mscan {
 
+// Returns v, hidden from the optimizer: what is computed from the result is
+// computed again at each use instead of being kept in registers from an
+// earlier one.  Used for per-thread addresses in the chunk loop: kept, they
+// are spilled, and reloading a spill (an s_waitcnt vmcnt(0)) waits for every
+// store, atomic and prefetch load still in flight.
+__device__ __forceinline__ int opaque_int(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Lane i receives lane i+1 of its 16-lane row; lane 15 receives `last`.
 __device__ __forceinline__ float row_shift_left(float v, float last) {
   return dpp_mov<0x101 /*row_shl:1*/>(last, v);
@@ -152,10 +162,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       p.seg_chunks > 0 ? (ch_begin + p.seg_chunks < nchunks ? ch_begin + p.seg_chunks : nchunks)
                        : nchunks;
 
-  const T* __restrict__ u_row = static_cast<const T*>(p.u) + c * L;
-  const T* __restrict__ dl_row = static_cast<const T*>(p.delta) + c * L;
-  const T* __restrict__ z_row = p.z ? static_cast<const T*>(p.z) + c * L : nullptr;
-  const T* __restrict__ do_row = static_cast<const T*>(p.dout) + c * L;
+  // this lane's channel row as block-uniform base + lane part; the row
+  // addresses are formed from an opaque copy of the lane part where they are
+  // used, so that none is kept (and spilled) across the chunk loop
+  const int64_t c_blk = b * p.dim + grp * CPB;
+  const int cl_eff = (int)(d - grp * CPB);
   const T* __restrict__ B_b = static_cast<const T*>(p.B) + b * N * L;
   const T* __restrict__ C_b = static_cast<const T*>(p.C) + b * N * L;
   const float bias = p.bias ? p.bias[d] : 0.0f;
@@ -174,8 +185,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   }
 
   // chunk-start states of this lane's channel: lane j holds state 16 q + j
-  const float* __restrict__ st_row = p.chunk_states + c * nchunks * N;
   auto load_states = [&](int64_t ch, float (&dst)[NQ]) {
+    const float* __restrict__ st_row =
+        p.chunk_states + (c_blk + opaque_int(cl_eff)) * nchunks * N;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int n = 16 * q + j;
@@ -199,8 +211,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int64_t last = ch_end - 1;
     const bool full_last = VEC && last * TCH + TCH <= L;
     if constexpr (TILE) {
-      stage.load(B_b, C_b, N, L, last * TCH, full_last, tid);
-      stage.store(reinterpret_cast<float*>(tile_mem), N, tid);
+      stage.load(B_b, C_b, N, L, last * TCH, full_last, opaque_int(tid));
+      stage.store(reinterpret_cast<float*>(tile_mem), N, opaque_int(tid));
     }
     load_states(last, hreg);
   }
@@ -225,6 +237,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
     float uv[K], dt[K], gy[K], yv[K], du[K], gdt[K];
     {
+      const int64_t co = (c_blk + opaque_int(cl_eff)) * L;
+      const T* __restrict__ u_row = static_cast<const T*>(p.u) + co;
+      const T* __restrict__ dl_row = static_cast<const T*>(p.delta) + co;
+      const T* __restrict__ z_row = p.z ? static_cast<const T*>(p.z) + co : nullptr;
+      const T* __restrict__ do_row = static_cast<const T*>(p.dout) + co;
       float raw[K], dov[K];
       load_items<T, K>(u_row, tl, L, full, uv);
       load_items<T, K>(dl_row, tl, L, full, raw);
@@ -442,11 +459,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     // the earlier chunk's B/C rows and states: issued here (not at the chunk
     // start) so their registers are not live across the state-index loop
     if (ch > ch_begin) {
-      if constexpr (TILE) stage.load(B_b, C_b, N, L, t0 - TCH, VEC, tid);   // earlier chunks are full
+      if constexpr (TILE)   // earlier chunks are full
+        stage.load(B_b, C_b, N, L, t0 - TCH, VEC, opaque_int(tid));
       load_states(ch - 1, hreg);
     }
 
     // ---- per-step outputs ----
+    const int64_t co = (c_blk + opaque_int(cl_eff)) * L;
     {
       float ddl[K];
 #pragma unroll
@@ -455,21 +474,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         db_acc += ddl[k];
       }
       if (active) {
-        store_items<float, K>(p.du + c * L, tl, L, full, du);
-        store_items<float, K>(p.ddelta + c * L, tl, L, full, ddl);
+        store_items<float, K>(p.du + co, tl, L, full, du);
+        store_items<float, K>(p.ddelta + co, tl, L, full, ddl);
       }
     }
-    if (z_row) {
+    if (p.z) {
       float dzv[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) dzv[k] = yv[k] * stash[1][k][tid];
-      if (active) store_items<float, K>(p.dz + c * L, tl, L, full, dzv);
+      if (active) store_items<float, K>(p.dz + co, tl, L, full, dzv);
     }
     // every wave is past the last group barrier, so no wave still reads the
     // tile: refill it with the earlier chunk.  The barrier also keeps the
     // next chunk's slice stores behind this chunk's last flush.
     if (ch > ch_begin) {
-      if constexpr (TILE) stage.store(reinterpret_cast<float*>(tile_mem), N, tid);
+      if constexpr (TILE) stage.store(reinterpret_cast<float*>(tile_mem), N, opaque_int(tid));
       __syncthreads();
     }
   }
