@@ -159,6 +159,16 @@ __device__ __forceinline__ float rs_pair32(float x, float y) {
 // stay with it instead of being hoisted en masse.
 __device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
 
+// Returns v, hidden from the optimizer: what is computed from the result is
+// computed again at each use instead of being kept in registers from an
+// earlier one.  Used for per-thread addresses in the backward kernels' chunk
+// loops: kept, they are spilled, and reloading a spill (an s_waitcnt
+// vmcnt(0)) waits for every store, atomic and prefetch load still in flight.
+__device__ __forceinline__ int opaque_int(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Reduce-scatter over the 4 rows of a wave: v[k] (K = 8 items) of the four
 // 16-lane rows are summed so that lane (row r, j) returns out[m] = sum over
 // rows of v[4m + r] at position j (m = 0, 1).  Uses gfx950's

@@ -103,10 +103,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
   __syncthreads();
 
-  const T* __restrict__ u_row = static_cast<const T*>(p.u) + c * L;
-  const T* __restrict__ dl_row = static_cast<const T*>(p.delta) + c * L;
-  const T* __restrict__ z_row = p.z ? static_cast<const T*>(p.z) + c * L : nullptr;
-  const T* __restrict__ do_row = static_cast<const T*>(p.dout) + c * L;
+  // the channel row as block-uniform base + lane part; row addresses are
+  // formed from an opaque copy of the lane part where they are used, so that
+  // none is kept (and spilled) across the chunk loop
+  const int64_t c_blk = b * p.dim + grp * CPB;
+  const int cl_eff = (int)(d - grp * CPB);
+  auto row_off = [&]() { return (c_blk + opaque_int(cl_eff)) * L; };
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
   const uint8_t* __restrict__ rst_row = RST ? p.reset + b * L : nullptr;
@@ -115,8 +117,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   const float* __restrict__ Cf = reinterpret_cast<const float*>(p.C) + b * N * 2 * L;
   float* tile = reinterpret_cast<float*>(tile_mem);
   TileStager<float, RW, 2 * K, NT, 2 * NT, kBlock> stage;
-  stage.load(Bf, Cf, N, 2 * L, 2 * (ch_end - 1) * TCH, VEC && ch_end * TCH <= L, tid);
-  stage.store(tile, N, tid);
+  stage.load(Bf, Cf, N, 2 * L, 2 * (ch_end - 1) * TCH, VEC && ch_end * TCH <= L,
+             opaque_int(tid));
+  stage.store(tile, N, opaque_int(tid));
   __syncthreads();
 
   for (int64_t ch = ch_end - 1; ch >= ch_begin; --ch) {
@@ -127,10 +130,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
     float uv[K], dt[K], gy[K], yv[K], du[K], gdt[K];
     {
+      const int64_t co = row_off();
       float raw[K], dov[K];
-      load_items<T, K>(u_row, tl, L, full, uv);
-      load_items<T, K>(dl_row, tl, L, full, raw);
-      load_items<T, K>(do_row, tl, L, full, dov);
+      load_items<T, K>(static_cast<const T*>(p.u) + co, tl, L, full, uv);
+      load_items<T, K>(static_cast<const T*>(p.delta) + co, tl, L, full, raw);
+      load_items<T, K>(static_cast<const T*>(p.dout) + co, tl, L, full, dov);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const float r = raw[k] + bias;
@@ -138,9 +142,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         dt[k] = (k < nvalid) ? s : 0.0f;
         gy[k] = dov[k];
       }
-      if (z_row) {
+      if (p.z) {
         float zv[K];
-        load_items<T, K>(z_row, tl, L, full, zv);
+        load_items<T, K>(static_cast<const T*>(p.z) + co, tl, L, full, zv);
 #pragma unroll
         for (int k = 0; k < K; ++k) gy[k] *= silu(zv[k]);
       }
@@ -315,12 +319,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
 
     // the earlier chunk's B/C rows (every earlier chunk is whole)
-    if (ch > ch_begin) stage.load(Bf, Cf, N, 2 * L, 2 * (ch - 1) * TCH, VEC, tid);
+    if (ch > ch_begin) stage.load(Bf, Cf, N, 2 * L, 2 * (ch - 1) * TCH, VEC, opaque_int(tid));
 
     // ---- per-step outputs ----
+    const int64_t co = row_off();
     {
       float raw[K], ddl[K];
-      load_items<T, K>(dl_row, tl, L, full, raw);
+      load_items<T, K>(static_cast<const T*>(p.delta) + co, tl, L, full, raw);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const float sg = p.softplus ? sigmoid(raw[k] + bias) : 1.0f;
@@ -328,26 +333,26 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         db_acc += ddl[k];
       }
       if (active) {
-        store_items<float, K>(p.du + c * L, tl, L, full, du);
-        store_items<float, K>(p.ddelta + c * L, tl, L, full, ddl);
+        store_items<float, K>(p.du + co, tl, L, full, du);
+        store_items<float, K>(p.ddelta + co, tl, L, full, ddl);
       }
     }
-    if (z_row) {
+    if (p.z) {
       float zv[K], dov[K], dzv[K];
-      load_items<T, K>(z_row, tl, L, full, zv);
-      load_items<T, K>(do_row, tl, L, full, dov);
+      load_items<T, K>(static_cast<const T*>(p.z) + co, tl, L, full, zv);
+      load_items<T, K>(static_cast<const T*>(p.dout) + co, tl, L, full, dov);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const float sg = sigmoid(zv[k]);
         dzv[k] = dov[k] * yv[k] * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
       }
-      if (active) store_items<float, K>(p.dz + c * L, tl, L, full, dzv);
+      if (active) store_items<float, K>(p.dz + co, tl, L, full, dzv);
     }
     // keeps the next chunk's slice stores behind this chunk's flushes, and
     // every wave's tile reads behind the refill
     __syncthreads();
     if (ch > ch_begin) {
-      stage.store(tile, N, tid);
+      stage.store(tile, N, opaque_int(tid));
       __syncthreads();
     }
   }

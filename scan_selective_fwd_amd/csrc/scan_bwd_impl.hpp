@@ -50,16 +50,6 @@
 
 namespace mscan {
 
-// Returns v, hidden from the optimizer: what is computed from the result is
-// computed again at each use instead of being kept in registers from an
-// earlier one.  Used for per-thread addresses in the chunk loop: kept, they
-// are spilled, and reloading a spill (an s_waitcnt vmcnt(0)) waits for every
-// store, atomic and prefetch load still in flight.
-__device__ __forceinline__ int opaque_int(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
 // Lane i receives lane i+1 of its 16-lane row; lane 15 receives `last`.
 __device__ __forceinline__ float row_shift_left(float v, float last) {
   return dpp_mov<0x101 /*row_shl:1*/>(last, v);
