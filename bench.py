@@ -45,7 +45,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 # float32 vector peak: the chip's published 157.3 TFLOP/s (256 CUs, 2.4 GHz).
-# Plain (non-packed) FMAs reach 119 TFLOP/s on the box (`bench.py --probe`:
+# Plain (non-packed) FMAs reach 119 TFLOP/s on an MI355X (`bench.py --probe`:
 # one wave64 FMA per SIMD every ~2.2 cycles), so the published figure is the
 # honest ceiling for these kernels too, although they use no packed FP32.
 PEAK_F32_TFLOPS = 157.3
