@@ -128,6 +128,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   // conflict-free
   __shared__ float stash[2][kItemsBwd][kBlock];
 
+  // the TINY launch computes only the blocks the fast launch deferred; the
+  // others leave before loading anything
+  if constexpr (ZOH && TINY) {
+    if (p.deferred[blockIdx.x] == 0) return;   // block-uniform
+  }
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -212,8 +218,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     if constexpr (!TINY) {
       if (tid == 0) p.deferred[blockIdx.x] = any_tiny ? 1 : 0;
       if (any_tiny) return;            // block-uniform: the TINY kernel takes it
-    } else {
-      if (p.deferred[blockIdx.x] == 0) return;
     }
   }
 
@@ -545,7 +549,7 @@ static hipError_t dispatch_bwd_nt(const BwdParams& p, int disc, bool vec, hipStr
   {
     const int64_t total = 2 * p.batch * p.N * p.L + p.dim * p.N + 2 * p.dim;
     int64_t blocks = (total + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
+    if (blocks > 1024) blocks = 1024;   // grid-stride: a few elements per thread
     hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
