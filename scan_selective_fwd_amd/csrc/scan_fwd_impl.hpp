@@ -166,6 +166,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const int N = EXACT ? NT : p.N;
   const int64_t L = p.L;
 
+  // OPQ (reset flags, whose extra registers made the kernel spill most):
+  // per-thread addresses are formed again in every chunk from an opaque lane
+  // index instead of being kept across the chunk loop.  Without reset flags
+  // keeping them measured faster.
+  constexpr bool OPQ = RST;
+  const int64_t c_blk = b * p.dim + grp * CPB;
+  const int cl_eff = (int)(d - grp * CPB);
+  auto lane_row = [&]() -> int64_t {
+    return OPQ ? (c_blk + opaque_int(cl_eff)) * L : c * L;
+  };
+  auto tid_o = [&]() { return OPQ ? opaque_int(tid) : tid; };
   const T* __restrict__ u_row = static_cast<const T*>(p.u) + c * L;
   const T* __restrict__ dl_row = static_cast<const T*>(p.delta) + c * L;
   const T* __restrict__ z_row = p.z ? static_cast<const T*>(p.z) + c * L : nullptr;
@@ -257,15 +268,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       }
       const int buf = (int)((ch - ch_begin) & 1);
       const int64_t t0 = ch * TCH;
-      const int64_t tl = t0 + (int64_t)j * K;   // this lane's first step
+      const int64_t tl = t0 + (int64_t)(OPQ ? opaque_int(j) : j) * K;   // this lane's first step
       const bool full = VEC && t0 + TCH <= L;
       const bool more = ch + 1 < ch_end;
       const bool full_next = VEC && t0 + 2 * TCH <= L;
       const int64_t rem = L - tl;
       const int nvalid = rem >= K ? K : (rem < 0 ? 0 : (int)rem);
       if constexpr (TILE) {
-        if (more) stage.load(B_b, C_b, N, L, t0 + TCH, full_next, tid);
+        if (more) stage.load(B_b, C_b, N, L, t0 + TCH, full_next, tid_o());
       }
+      const T* __restrict__ u_c = OPQ ? static_cast<const T*>(p.u) + lane_row() : u_row;
+      const T* __restrict__ dl_c = OPQ ? static_cast<const T*>(p.delta) + lane_row() : dl_row;
 
       float uv[K], dt[K], y[K], zv[K];
 #pragma unroll
@@ -274,11 +287,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         dt[k] = nd[k];
       }
       if (more) {
-        load_items<T, K>(u_row, tl + TCH, L, full_next, nu);
-        load_items<T, K>(dl_row, tl + TCH, L, full_next, nd);
+        load_items<T, K>(u_c, tl + TCH, L, full_next, nu);
+        load_items<T, K>(dl_c, tl + TCH, L, full_next, nd);
       }
       if constexpr (!STATES) {
-        if (z_row) load_items<T, K>(z_row, tl, L, full, zv);
+        if constexpr (OPQ) {
+          if (p.z) load_items<T, K>(static_cast<const T*>(p.z) + lane_row(), tl, L, full, zv);
+        } else {
+          if (z_row) load_items<T, K>(z_row, tl, L, full, zv);
+        }
       }
       float dsum = 0.0f;
 #pragma unroll
@@ -376,11 +393,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
           for (int k = 0; k < K; ++k) y[k] *= silu(zv[k]);
         }
-        if (active) store_items<T, K>(out_row, tl, L, full, y);
+        if (active)
+          store_items<T, K>(OPQ ? static_cast<T*>(p.out) + lane_row() : out_row, tl, L, full, y);
       }
       if (more) store_state(ch + 1);
       if constexpr (TILE) {
-        if (more) stage.store(reinterpret_cast<float*>(tile_mem[buf ^ 1]), N, tid);
+        if (more) stage.store(reinterpret_cast<float*>(tile_mem[buf ^ 1]), N, tid_o());
         __syncthreads();
       }
     }
