@@ -45,9 +45,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 # float32 vector peak: the chip's published 157.3 TFLOP/s (256 CUs, 2.4 GHz).
-# Plain (non-packed) FMAs reach 119 TFLOP/s on an MI355X (`bench.py --probe`:
-# one wave64 FMA per SIMD every ~2.2 cycles), so the published figure is the
-# honest ceiling for these kernels too, although they use no packed FP32.
+# Plain (non-packed) FMAs issue at most one wave64 instruction per SIMD about
+# every 2.4 cycles even with many waves per SIMD (measured on an MI355X), so
+# the published figure is the honest ceiling for these kernels too, although
+# they use no packed FP32.
 PEAK_F32_TFLOPS = 157.3
 # Algorithmic float32 work per (t, n) (an exp counts as one flop):
 #   forward : dA 1, exp 1, ZOH Bbar*u 4, h update 2, y accumulate 2       = 10
@@ -239,50 +240,6 @@ def copy_bandwidth(torch, nbytes=COPY_BYTES, iters=10):
     return gbs
 
 
-PROBE_KINDS = {0: ("v_fma_f32", 2), 1: ("v_exp_f32", 1), 2: ("v_mul_f32", 1), 3: ("v_rcp_f32", 1),
-               4: ("v_fma_f32 1 chain", 2), 5: ("v_fma_f32 2 chains", 2)}
-
-
-def probe_rates(torch, blocks=8192, iters=2048):
-    """Issue rates of single VALU instruction kinds on this GPU (8 independent
-    chains per thread, a grid of many waves), from the probe library built
-    next to the scan library.  Returns {name: {"G_per_s": lane-instructions per
-    second, "vs_fma": rate / FMA rate}} plus the FMA rate in TFLOP/s."""
-    import ctypes
-    path = os.path.join(ROOT, "scan_selective_fwd_amd", "libmscan_probe.so")
-    if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: build the library first")
-    lib = ctypes.CDLL(path)
-    lib.mscan_probe_valu.restype = ctypes.c_int
-    lib.mscan_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    res = {}
-    for kind, (name, flops) in PROBE_KINDS.items():
-        best = None
-        for _ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)   # creates the events; the probe records them again
-            e1.record(stream)
-            st = lib.mscan_probe_valu(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()),
-                                      ctypes.c_void_p(stream.cuda_stream),
-                                      ctypes.c_void_p(e0.cuda_event), ctypes.c_void_p(e1.cuda_event))
-            if st != 0:
-                raise RuntimeError(f"mscan_probe_valu({kind}) failed: {st}")
-            torch.cuda.synchronize()
-            ms_ = e0.elapsed_time(e1)
-            best = ms_ if best is None else min(best, ms_)
-        n = blocks * 256 * iters * 8
-        res[name] = {"G_per_s": round(n / (best * 1e-3) / 1e9, 1), "ms": round(best, 4),
-                     "instructions": n}
-    fma = res["v_fma_f32"]["G_per_s"]
-    for v in res.values():
-        v["vs_fma"] = round(v["G_per_s"] / fma, 3)
-    res["fma_TFLOP_s"] = round(2 * fma / 1e3, 2)
-    return res
-
-
 # The pages' scan benchmark shape (batch 1, D 1024, N 16, bf16; sequence
 # lengths 2^9 .. 2^19) and the times they read for the fused scan on an A100
 # (paper-graph-ui summary, "Speed and Memory Benchmarks", Figure 8 left;
@@ -408,9 +365,6 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="time the forward and backward over sequence lengths 2^9..2^19 "
                          "at the pages' scan benchmark shape; one JSON line")
-    ap.add_argument("--probe", action="store_true",
-                    help="print the measured VALU issue rates (FMA, exp, mul, rcp) and the "
-                         "streaming-copy rate as one JSON line instead of the benchmark")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the step replayed from a captured HIP graph")
     ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="CSV")
@@ -433,15 +387,6 @@ def main():
                                    "bf16 inputs, ZOH, softplus, D and z",
                           "rows": sweep(torch, ms, W)}), flush=True)
         return
-    if args.probe:
-        # 8192 blocks: many waves per SIMD; 768 blocks: 3 waves per SIMD (the
-        # scan kernels' occupancy)
-        print(json.dumps({"probe": "valu issue rates and streaming copy, one GPU",
-                          "valu_8192_blocks": probe_rates(torch, blocks=8192),
-                          "valu_768_blocks": probe_rates(torch, blocks=768, iters=8192),
-                          "stream_copy_GBs": round(copy_bandwidth(torch), 1)}), flush=True)
-        return
-
     w = W.WORKLOADS[args.workload]
     calls = {2: ["fwd", "bwd", "step"], 3: ["fwd"], 4: ["fwd"], 5: ["bwd"]}[w.wid]
     if args.calls:

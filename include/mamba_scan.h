@@ -209,9 +209,9 @@ mamba_status mamba_scan_bwd_varlen(const void* u, const void* delta, const float
 
 /*
  * Complex-valued forward: diagonal complex A, complex B, C and state (the
- * S4D-Lin parameterization A_n = -1/2 + i*pi*n that paper-graph-ui summary,
- * section 3.4 "Real vs. Complex", and trishampatil essay, Part III, describe
- * for audio).  Abar = exp(delta A); Bbar = (Abar - 1)/A B (ZOH, delta B at
+ * S4D-Lin parameterization, printed as A_n = -1/2 + n i in the paper-graph-ui
+ * summary, section 5 (Table 8 discussion); section 3.4 "Real vs. Complex"
+ * and the trishampatil essay, Part III, name complex states for audio).  Abar = exp(delta A); Bbar = (Abar - 1)/A B (ZOH, delta B at
  * A = 0) or delta B (Euler); h_t = Abar h_{t-1} + Bbar u_t;
  * y_t = Re(sum_n C_t[n] h_t[n]) + D u_t; out = y * SiLU(z).  The pages fix no
  * output convention for a complex state: the real part is this library's

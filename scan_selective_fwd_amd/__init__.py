@@ -204,6 +204,11 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
     if h0 is not None and want_dh0:
         g["dh0"] = torch.empty((batch, dim, N), **f32)
     nbytes = bwd_workspace_bytes(batch, dim, N, L, sdt, lanes, segments)
+    if checkpoints is not None:
+        # the chunk-start states come from the checkpoints: the workspace
+        # starts at the block flags
+        states = checkpoints.numel() * 4
+        nbytes -= (states + 255) // 256 * 256
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     st = L_.mamba_scan_bwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),

@@ -18,9 +18,6 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmamba_scan.so")
-# issue-rate probes for `bench.py --probe` (not part of the scan library)
-PROBE_SRC = os.path.join(HERE, "probe", "valu_probe.hip")
-PROBE_LIB = os.path.join(HERE, "libmscan_probe.so")
 ARCH = os.environ.get("MAMBA_SCAN_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -74,11 +71,6 @@ def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> st
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
-    pcmd = [HIPCC] + COMMON + ["-shared", PROBE_SRC, "-o", PROBE_LIB + ".tmp"]
-    if verbose:
-        print(" ".join(pcmd), flush=True)
-    subprocess.run(pcmd, check=True)
-    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 

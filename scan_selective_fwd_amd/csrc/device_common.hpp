@@ -124,6 +124,34 @@ __device__ __forceinline__ void affine_suffix_scan_row_fused(float& A, float& B)
       : "+v"(A), "+v"(B));
 }
 
+// A prefix scan of (A1, B1) (row_shr sources, as affine_scan_inclusive_fused
+// with R = 16) and a suffix scan of (A2, B2) (row_shl sources, as
+// affine_suffix_scan_row_fused), interleaved.  The two are independent, so
+// every DPP read finds its source register written three instructions
+// earlier and only the first step needs wait states.  The final products
+// A1, A2 of the last step are not formed: the callers use only B1, B2 (on
+// return A1, A2 hold the products over the first 8 lanes' spans).
+__device__ __forceinline__ void dual_scan_row_fused(float& A1, float& B1, float& A2, float& B2) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %2 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %2, %2, %2 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %2 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %2, %2, %2 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %2 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %2, %2, %2 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %2 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      : "+v"(A1), "+v"(B1), "+v"(A2), "+v"(B2));
+}
+
 // Sum over each 16-lane row, result in the row's lane 15 (the other lanes
 // hold partial sums): an inclusive DPP add-scan with row_shr sources.
 __device__ __forceinline__ float row_sum_to_last(float v) {
@@ -308,6 +336,52 @@ __device__ __forceinline__ float softplus(float x) {
 }
 
 __device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + fast_exp(-x)); }
+// ---------------------------------------------------------------------------
+// The ZOH coefficient without cancellation.  Bbar = (e^x - 1)/A B with
+// x = delta A (chapterpal.com page, Knowl 1 "Selective State Space Layer
+// (S6)", step 3).  With Abar = e^x rounded, Abar - 1 keeps only the bits of
+// Abar below 1: for |x| = 1e-4 the relative error is about 1e-3, and at a
+// constant step it does not average out along the recurrence.
+//
+// expm1 from two lower bounds of e^x - 1, both valid for every real x:
+//   * the cubic Taylor polynomial x + x^2/2 + x^3/6 (its remainder
+//     e^xi x^4/24, Lagrange form, is never negative);
+//   * Abar - (1 + 2^-23): v_exp_f32 is within 0.78 ulp, at most 9e-8 for
+//     results in [0.5, 2) (measured on gfx950 against float64 over 16M
+//     arguments), below 2^-23.
+// Their maximum is within about 5e-6 of e^x - 1 relative: the polynomial
+// wins for |x| below about 0.05, the hardware exponential above.  The
+// arguments are in exp2 units: z = x log2(e), so x = z ln 2.
+// ---------------------------------------------------------------------------
+constexpr float kExpm1C2 = 0.24022650695910071f;   // ln(2)^2 / 2
+constexpr float kExpm1C3 = 0.05550410866482158f;   // ln(2)^3 / 6
+constexpr float kExpBound = 1.00000011920928955f;  // 1 + 2^-23
+
+// e^x - 1 for x = z ln 2, given abar = exp2(z) from the hardware.
+__device__ __forceinline__ float expm1_zoh(float z, float abar) {
+  const float poly = z * __builtin_fmaf(z, __builtin_fmaf(z, kExpm1C3, kExpm1C2), kLn2);
+  return __builtin_fmaxf(poly, abar - kExpBound);
+}
+
+// d/dA of the ZOH coefficient (e^x - 1)/A at fixed delta: delta^2 psi(x),
+// psi(x) = (x e^x - e^x + 1)/x^2 = 1/2 + x/3 + x^2/8 + x^3/30 + ...  The
+// closed form cancels to second order for small x, so below |x| = 0.11 the
+// series is used (its first omitted term, x^4/144, is below 1e-6 of psi
+// there); above, the closed form is within 1.2e-7/x^2 (relative), since
+// abar carries at most 9e-8 of absolute error.  In the closed form delta^2
+// cancels: delta^2 psi = (abar (x - 1) + 1) / A^2, so A = 0 needs no
+// special case (the series branch is taken).  dt2 = delta^2, iA2 = 1/A^2.
+constexpr float kPsiZ = 0.15869619f;               // 0.11 / ln 2: |x| < 0.11 in z units
+constexpr float kPsiC1 = 0.23104906018664844f;     // ln(2) / 3
+constexpr float kPsiC2 = 0.06005662673977518f;     // ln(2)^2 / 8
+constexpr float kPsiC3 = 0.01110082173296432f;     // ln(2)^3 / 30
+__device__ __forceinline__ float dcoef_dA(float z, float abar, float dt2, float iA2) {
+  const float series =
+      dt2 * __builtin_fmaf(z, __builtin_fmaf(z, __builtin_fmaf(z, kPsiC3, kPsiC2), kPsiC1), 0.5f);
+  const float closed = __builtin_fmaf(abar, __builtin_fmaf(z, kLn2, -1.0f), 1.0f) * iA2;
+  return __builtin_fabsf(z) < kPsiZ ? series : closed;
+}
+
 __device__ __forceinline__ float silu(float x) { return x * sigmoid(x); }
 
 // ---------------------------------------------------------------------------

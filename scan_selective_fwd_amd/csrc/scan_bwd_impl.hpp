@@ -11,6 +11,9 @@
 //   du_t    = D gy_t + sum_n gh_t Bbar_t
 //   ddelta  = softplus'(r_t) * sum_n gh_t (h_{t-1} A Abar_t + u_t dBbar/ddelta)
 //   dA[d,n] = sum_{b,t} gh_t (h_{t-1} delta_t Abar_t + u_t dBbar/dA)
+// with the ZOH coefficient (Abar - 1)/A and its A-derivative
+// dBbar/dA = B delta^2 psi(delta A) formed without cancellation
+// (expm1_zoh, dcoef_dA in device_common.hpp).
 //   dB_t[n] = sum_d gh_t u_t Bbar_t/B_t,  dC_t[n] = sum_d gy_t h_t[n]
 //   dz_t    = dout_t y_t SiLU'(z_t),  dD = sum gy u,  ddelta_bias = sum ddelta
 // With g_t = Abar_t gh_t the reverse recurrence is g_t = Abar_t (g_{t+1} + e_t),
@@ -28,7 +31,7 @@
 // terms.  The B/C chunk and the chunk-start states are staged in LDS once per
 // block.  dB/dC are summed over the wave's 4 channels with gfx950 permlane
 // swaps, over the block's waves through per-wave LDS slices (plain stores,
-// summed after a barrier every 4 state indices), and into global memory with
+// summed after a barrier every 2 state indices), and into global memory with
 // one float atomic per (n, t) per block.  dA, dD, ddelta_bias are summed over the
 // channel's lanes and atomically over batch rows.  Atomics make the result
 // deterministic only up to float32 rounding order.
@@ -112,8 +115,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   constexpr int NQ = NT / 16;
   // single-buffered: refilled between the two barriers that close a chunk
   __shared__ float4 tile_mem[TILE ? 2 * NT * TCH / 4 : 1];   // B, C rows of the chunk
-  __shared__ float4 prm[CPB][NT];       // {A log2(e), 1/A (0 where A ~ 0), A, 0}
-  // dB, dC partial sums of each wave for a group of 4 state indices, double
+  __shared__ float4 prm[CPB][NT];       // {A log2(e), 1/A (0 where A ~ 0), A, 1/A^2}
+  // dB, dC partial sums of each wave for a group of G state indices, double
   // buffered: written with plain stores, summed over the waves and flushed
   // to global memory after the group's barrier.  (LDS float atomics are far
   // slower than stores on this chip.)  Step tt of the chunk sits at
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const float a = real ? p.A[dd * N + n] : -1.0f;
     const bool tiny = __builtin_fabsf(a) < 1e-30f;
     my_tiny |= real && tiny;
-    prm[ci][n] = make_float4(a * kLog2e, tiny ? 0.0f : 1.0f / a, a, 0.0f);
+    prm[ci][n] = make_float4(a * kLog2e, tiny ? 0.0f : 1.0f / a, a, tiny ? 0.0f : 1.0f / (a * a));
   }
 
   // chunk-start states of this lane's channel: lane j holds state 16 q + j
@@ -287,126 +290,122 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       const float4 pr = pr_next;
       if (n + 1 < NT) pr_next = prm[cl][n + 1];
       if (n < N) {
-        const float a2 = pr.x, ia = pr.y, An = pr.z;
+        const float a2 = pr.x, ia = pr.y, An = pr.z, iA2 = pr.w;
         const float h_in = row_lane_to_first<nl>(hq);   // state n, in lane 0
         const float gc = row_lane_to_last<nl>(gq);      // carry n, in lane 15
         float Bv[K], Cv[K];
-        if constexpr (TILE) {
-          tile_read<K>(tB + n * TCH, j, Bv);
-          tile_read<K>(tB + (NT + n) * TCH, j, Cv);
-        } else {
-          load_items<T, K>(B_b + (int64_t)n * L, tl, L, full, Bv);
-          load_items<T, K>(C_b + (int64_t)n * L, tl, L, full, Cv);
-        }
+        auto read_bc = [&]() {
+          if constexpr (TILE) {
+            tile_read<K>(tB + n * TCH, j, Bv);
+            tile_read<K>(tB + (NT + n) * TCH, j, Cv);
+          } else {
+            load_items<T, K>(B_b + (int64_t)n * L, tl, L, full, Bv);
+            load_items<T, K>(C_b + (int64_t)n * L, tl, L, full, Cv);
+          }
+        };
+        read_bc();
         // TINY: where A ~ 0 (1/A stored as 0) the ZOH coefficient
         // (e^{dA}-1)/A takes its limit delta
         const bool tiny = TINY && ia == 0.0f;
 
-        // ---- forward replay of this chunk for state index n ----
-        float a[K], beta[K], hv[K];
+        // ---- replay, pass 1: each lane's steps folded into its summary ----
+        // coef[k] is the ZOH coefficient (Abar - 1)/A (its limit delta at
+        // A = 0; delta under Euler); Bbar u = coef B u is formed again where
+        // it is used, which keeps one array fewer live across the scans
+        float a[K], coef[K], ghv[K];
         float agg;
+        // a step's decay in the recurrence and the adjoint (0 at a flagged step)
+        auto decay = [&](int k) { return RST ? a[k] * keep[k] : a[k]; };
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          a[k] = fast_exp2(dt[k] * a2);
+          const float z = dt[k] * a2;
+          a[k] = fast_exp2(z);
           if constexpr (ZOH && !TINY) {
-            const float qv = Bv[k] * (uv[k] * ia);
-            beta[k] = __builtin_fmaf(a[k], qv, -qv);
+            coef[k] = expm1_zoh(z, a[k]) * ia;
           } else if constexpr (ZOH) {
-            const float coef = tiny ? dt[k] : (a[k] - 1.0f) * ia;
-            beta[k] = coef * Bv[k] * uv[k];
+            coef[k] = tiny ? dt[k] : expm1_zoh(z, a[k]) * ia;
           } else {
-            beta[k] = dt[k] * Bv[k] * uv[k];
+            coef[k] = dt[k];
           }
-          agg = k == 0 ? beta[0] : __builtin_fmaf(RST ? a[k] * keep[k] : a[k], agg, beta[k]);
+          const float beta = coef[k] * (Bv[k] * uv[k]);
+          agg = k == 0 ? beta : __builtin_fmaf(decay(k), agg, beta);
         }
         const float Alane = RST ? fast_exp2(a2 * dsum) * lane_keep : fast_exp2(a2 * dsum);
         float Ag = Alane;
         agg = (j == 0) ? __builtin_fmaf(Ag, h_in, agg) : agg;   // chunk-start state enters lane 0
-        affine_scan_inclusive_fused<R>(Ag, agg);
-        const float hstart = group_shift_right<R>(agg, h_in);
-        {
-          float h = hstart;
-#pragma unroll
-          for (int k = 0; k < K; ++k) {
-            h = __builtin_fmaf(RST ? a[k] * keep[k] : a[k], h, beta[k]);
-            hv[k] = h;
-            yv[k] = __builtin_fmaf(Cv[k], h, yv[k]);
-          }
-        }
 
-        // ---- reverse adjoint: g_t = Abar_t (g_{t+1} + C_t gy_t) ----
+        // ---- adjoint, pass 1: g_t = Abar_t (g_{t+1} + C_t gy_t) folded ----
         float gagg = 0.0f;
 #pragma unroll
-        for (int k = K - 1; k >= 0; --k)
-          gagg = (RST ? a[k] * keep[k] : a[k]) * __builtin_fmaf(Cv[k], gy[k], gagg);
+        for (int k = K - 1; k >= 0; --k) gagg = decay(k) * __builtin_fmaf(Cv[k], gy[k], gagg);
         float As = Alane;
         gagg = (j == R - 1) ? __builtin_fmaf(As, gc, gagg) : gagg;   // later chunk enters lane 15
-        affine_suffix_scan_row_fused(As, gagg);
+
+        // the replay's prefix scan and the adjoint's suffix scan together
+        dual_scan_row_fused(Ag, agg, As, gagg);
+        const float hstart = group_shift_right<R>(agg, h_in);   // state before this lane's steps
         float g = row_shift_left(gagg, gc);                 // adjoint entering each lane from the right
         const float gc_new = row_first_to_lane<nl>(gagg);   // leaving lane 0, now in lane n
         gq = (j == nl) ? gc_new : gq;
 
-        // ---- gradient terms, with dB/dC summed over the wave's 4 channels
-        //      as soon as each pair of steps is done ----
-        float dAp = 0.0f, dA2 = 0.0f;
-        float pB = 0.0f, pC = 0.0f, sB[4], sC[4], TB[2], TC[2];
+        // ---- adjoint, pass 2: dL/dh_t of each step ----
 #pragma unroll
         for (int k = K - 1; k >= 0; --k) {
-          const float gh = __builtin_fmaf(Cv[k], gy[k], g);   // dL/dh_t
-          const float hprev = ((k == 0) ? hstart : hv[k - 1]) * (RST ? keep[k] : 1.0f);
+          ghv[k] = __builtin_fmaf(Cv[k], gy[k], g);
+          g = decay(k) * ghv[k];
+        }
+
+        // B and C again from the tile (LDS): kept from the first reads, their
+        // registers would be live across the scans (the fence keeps the
+        // compiler from reusing those reads)
+        if constexpr (TILE) {
+          mem_fence_compiler();
+          read_bc();
+        }
+        // ---- replay, pass 2, with the gradient terms: dB/dC are summed
+        //      over the wave's 4 channels as soon as each pair of steps is
+        //      done; dA collects delta P h_{t-1} (the Abar path) and, under
+        //      ZOH, dcoef/dA gh B u (the Bbar path), with no division by A ----
+        float dAp = 0.0f;
+        float pB = 0.0f, pC = 0.0f, sB[4], sC[4], TB[2], TC[2];
+        float h = hstart;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const float Bu = Bv[k] * uv[k];
+          const float hprev = RST ? h * keep[k] : h;
+          const float hk = __builtin_fmaf(decay(k), h, coef[k] * Bu);
+          yv[k] = __builtin_fmaf(Cv[k], hk, yv[k]);
+          const float gh = ghv[k];                           // dL/dh_t
           const float P = gh * a[k];
-          float coef;
-          if constexpr (ZOH && !TINY) {
-            // with Y = A h_{t-1} + B u:  ddelta += gh Abar Y;
-            // dA += (delta gh Abar Y - gh Bbar u) / A  (1/A applied once below)
-            const float Y = __builtin_fmaf(An, hprev, Bv[k] * uv[k]);
-            gdt[k] = __builtin_fmaf(P, Y, gdt[k]);
-            dAp = __builtin_fmaf(dt[k] * P, Y, dAp);
-            dA2 = __builtin_fmaf(gh, beta[k], dA2);
-            coef = __builtin_fmaf(a[k], ia, -ia);           // (Abar - 1)/A
+          if constexpr (ZOH) {
+            // ddelta: gh Abar (A h_{t-1} + B u), since dBbar/ddelta = Abar B
+            gdt[k] = __builtin_fmaf(P, __builtin_fmaf(An, hprev, Bu), gdt[k]);
+            const float zeta = dcoef_dA(dt[k] * a2, a[k], dt[k] * dt[k], iA2);
+            dAp = __builtin_fmaf(dt[k] * P, hprev, __builtin_fmaf(zeta, gh * Bu, dAp));
           } else {
-            const float gu = gh * uv[k];
-            float dbdd;
-            if constexpr (ZOH) {
-              coef = __builtin_fmaf(a[k], ia, -ia);
-              coef = tiny ? dt[k] : coef;
-              dbdd = a[k] * Bv[k];                          // dBbar/ddelta
-            } else {
-              coef = dt[k];
-              dbdd = Bv[k];
-            }
-            const float Ph = P * hprev;
-            // ddelta: gh * (hprev * A * Abar + u * dBbar/ddelta)
-            gdt[k] = __builtin_fmaf(Ph, An, __builtin_fmaf(gu, dbdd, gdt[k]));
-            // dA: gh * hprev * delta * Abar + gh * u * dBbar/dA with the ZOH
-            // dBbar/dA = (delta*Abar*B - Bbar)/A, limit delta^2 B / 2 at A = 0
-            // (1/A = 0 there drops the other terms)
-            dAp = __builtin_fmaf(dt[k], Ph, dAp);
-            if constexpr (ZOH) {
-              const float t = tiny ? 0.5f * dt[k] * Bv[k] : dbdd * ia;
-              dAp = __builtin_fmaf(gu * dt[k], t, dAp);
-              dA2 = __builtin_fmaf(gh, beta[k], dA2);
-            }
+            // Euler: Bbar = delta B, no A dependence
+            gdt[k] = __builtin_fmaf(P * An, hprev, __builtin_fmaf(gh, Bu, gdt[k]));
+            dAp = __builtin_fmaf(dt[k] * P, hprev, dAp);
           }
-          const float s = gh * coef;
+          const float s = gh * coef[k];
           du[k] = __builtin_fmaf(s, Bv[k], du[k]);
           const float vB = s * uv[k];
-          const float vC = gy[k] * hv[k];
-          if (k & 1) {
+          const float vC = gy[k] * hk;
+          if (!(k & 1)) {
             pB = vB;
             pC = vC;
           } else {
-            sB[k / 2] = rs_pair16(vB, pB);
-            sC[k / 2] = rs_pair16(vC, pC);
-            if (k == 4) {
-              TB[1] = rs_pair32(sB[2], sB[3]);
-              TC[1] = rs_pair32(sC[2], sC[3]);
-            } else if (k == 0) {
+            sB[k / 2] = rs_pair16(pB, vB);
+            sC[k / 2] = rs_pair16(pC, vC);
+            if (k == 3) {
               TB[0] = rs_pair32(sB[0], sB[1]);
               TC[0] = rs_pair32(sC[0], sC[1]);
+            } else if (k == 7) {
+              TB[1] = rs_pair32(sB[2], sB[3]);
+              TC[1] = rs_pair32(sC[2], sC[3]);
             }
           }
-          g = RST ? P * keep[k] : P;
+          h = hk;
         }
         const int buf = (n / G) & 1;
 #pragma unroll
@@ -415,8 +414,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           red[buf][wave][0][n % G][pos] = TB[m];
           red[buf][wave][1][n % G][pos] = TC[m];
         }
-        if constexpr (ZOH && !TINY) dAp = (dAp - dA2) * ia;
-        else if constexpr (ZOH) dAp = __builtin_fmaf(-dA2, ia, dAp);
         const float dAn = row_last_to_lane<nl>(row_sum_to_last(dAp));
         dq += (j == nl) ? dAn : 0.0f;
       }

@@ -347,10 +347,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           if constexpr (!TP) {
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-              a[k] = fast_exp2(dt[k] * a2);
+              const float z = dt[k] * a2;
+              a[k] = fast_exp2(z);
               if constexpr (ZOH) {
                 const float q = Bv[k] * (uv[k] * ia);
-                beta[k] = __builtin_fmaf(a[k], q, -q);     // (Abar - 1)/A * B * u
+                beta[k] = expm1_zoh(z, a[k]) * q;          // (Abar - 1)/A * B * u
               } else {
                 beta[k] = Bv[k] * uv[k];
               }
@@ -362,8 +363,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             // (e^{dA}-1)/A -> delta there
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-              a[k] = fast_exp2(dt[k] * a2);
-              const float coef = ia == 0.0f ? dt[k] : (a[k] - 1.0f) * ia;
+              const float z = dt[k] * a2;
+              a[k] = fast_exp2(z);
+              const float coef = ia == 0.0f ? dt[k] : expm1_zoh(z, a[k]) * ia;
               beta[k] = coef * Bv[k] * uv[k];
               if constexpr (RST) a[k] *= keep[k];
               agg = k == 0 ? beta[0] : __builtin_fmaf(a[k], agg, beta[k]);

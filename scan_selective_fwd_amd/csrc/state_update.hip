@@ -35,9 +35,10 @@ __global__ __launch_bounds__(256) void state_update_kernel(const StepParams p) {
     const float An = p.A[d * N + n];
     const float Bn = Elem<T>::load1(static_cast<const T*>(p.B) + b * N + n);
     const float Cn = Elem<T>::load1(static_cast<const T*>(p.C) + b * N + n);
-    const float a = fast_exp2(dt * (An * kLog2e));
+    const float z = dt * (An * kLog2e);
+    const float a = fast_exp2(z);
     float coef;
-    if constexpr (ZOH) coef = (__builtin_fabsf(An) < 1e-30f) ? dt : (a - 1.0f) * fast_rcp(An);
+    if constexpr (ZOH) coef = (__builtin_fabsf(An) < 1e-30f) ? dt : expm1_zoh(z, a) / An;
     else coef = dt;
     float* hp = p.state + c * N + n;
     const float h = __builtin_fmaf(a, *hp, coef * Bn * uv);

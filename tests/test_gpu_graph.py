@@ -21,9 +21,11 @@ from parity_utils import RTOL, announce, assert_match, to_device, to_f64
 pytestmark = pytest.mark.gpu
 
 
-# (wid, batch, dim, N, L, segments, checkpoints): one pass; short segments (a
-# summary pass); long segments (zero-start pass and correction), with the
-# backward from the forward's checkpoints and recomputing its states
+# (wid, batch, dim, N, L, segments, checkpoints): segments = 0 is the
+# automatic choice (for these few channels the backward splits the sequence
+# by itself; the forward runs in one pass); short segments (a summary pass);
+# long segments (zero-start pass and correction), with the backward from the
+# forward's checkpoints and recomputing its states
 CASES = [(82, 2, 20, 16, 700, 0, True),
          (83, 1, 20, 16, 1189, 4, False),
          (84, 1, 20, 16, 4173, 2, True),

@@ -1,7 +1,8 @@
 """Pins of the float64 oracle's complex-valued forward (diagonal complex A,
-B, C and state; the S4D-Lin parameterization A_n = -1/2 + i*pi*n that the
-paper-graph-ui summary, section 3.4 "Real vs. Complex", and the
-trishampatil essay, Part III, describe for audio), with the reading
+B, C and state, as in the S4D-Lin parameterization that the paper-graph-ui
+summary prints as A_n = -1/2 + n i (section 5, Table 8 discussion) and
+names for audio in section 3.4 "Real vs. Complex"; the pins below draw
+imaginary parts of several scales), with the reading
 y = Re(sum_n C h) + D u.
 
 Pinned against: the real oracle when every imaginary part is zero; an

@@ -206,7 +206,8 @@ def make_resets(wid: int, batch: int, seqlen: int, min_len: int = 1, max_len: in
 def make_complex_inputs(wid: int, batch: int, dim: int, dstate: int, seqlen: int, *,
                         dtype: str = "f32", bias: str = "const", **kw) -> dict:
     """Inputs of the complex-valued scan: u, delta, z, D, delta_bias as in
-    make_inputs; A = S4D-Lin, A[d, n] = -1/2 + i*pi*n; B and C complex64 with
+    make_inputs; A = S4D-Lin as the paper-graph-ui summary prints it (section 5,
+    Table 8 discussion), A[d, n] = -1/2 + i*n; B and C complex64 with
     real and imaginary parts ~ N(0, 1) (imaginary parts from tensor ids 11
     and 12, float32 in both dtypes)."""
     inp = make_inputs(wid, batch, dim, dstate, seqlen, dtype="f32", bias=bias, **kw)
@@ -217,6 +218,6 @@ def make_complex_inputs(wid: int, batch: int, dim: int, dstate: int, seqlen: int
         im[name] = np.stack([_normal([wid, tid, b], (dstate, seqlen)) for b in range(batch)])
     out["B"] = (re_B + 1j * im["B"]).astype(np.complex64)
     out["C"] = (re_C + 1j * im["C"]).astype(np.complex64)
-    A = -0.5 + 1j * np.pi * np.arange(dstate, dtype=np.float64)
+    A = -0.5 + 1j * np.arange(dstate, dtype=np.float64)
     out["A"] = np.broadcast_to(A, (dim, dstate)).astype(np.complex64).copy()
     return out
