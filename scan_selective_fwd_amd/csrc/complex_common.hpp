@@ -31,6 +31,50 @@ __device__ __forceinline__ float2 cexp_scaled(float dt, float ar2, float air) {
   return make_float2(mag * __builtin_amdgcn_cosf(rev), mag * __builtin_amdgcn_sinf(rev));
 }
 
+// exp(dt * a) as cexp_scaled, and also exp(dt * a) - 1 without cancellation
+// (the ZOH coefficient (Abar - 1)/A of a complex A; chapterpal.com page,
+// Knowl 1, step 3).  With x = dt a = xr + i xi:
+//   Abar - 1 = (expm1(xr) cos(xi) + (cos(xi) - 1)) + i e^xr sin(xi).
+// The imaginary part has no cancellation (v_sin_f32 is relative-accurate
+// near 0: within 9e-7, measured on gfx950).  expm1(xr) is expm1_zoh; cos(xi)
+// - 1 is the larger of two lower bounds, its alternating Taylor series cut
+// after the y^6 term (-y^2/2 + y^4/24 - y^6/720 <= cos y - 1 for every real
+// y) and the hardware cosine minus 1 + 2^-22 (v_cos_f32 measured within
+// 1.3e-7 near 1), so its relative error stays below about 3e-6.
+constexpr float kCos2 = 19.739208802178716f;    // (2 pi)^2 / 2
+constexpr float kCos4 = 64.939394022668291f;    // (2 pi)^4 / 24
+constexpr float kCos6 = 85.456817206693722f;    // (2 pi)^6 / 720
+constexpr float kCosBound = 1.00000023841857910f;   // 1 + 2^-22
+__device__ __forceinline__ float2 cexp_expm1_scaled(float dt, float ar2, float air, float2& em1) {
+  const float zr = dt * ar2;
+  const float mag = fast_exp2(zr);
+  const float rev = dt * air;            // xi in revolutions
+  const float co = __builtin_amdgcn_cosf(rev), si = __builtin_amdgcn_sinf(rev);
+  const float w = rev * rev;
+  const float cm1 = __builtin_fmaxf(w * __builtin_fmaf(w, __builtin_fmaf(w, -kCos6, kCos4), -kCos2),
+                                    co - kCosBound);
+  em1 = make_float2(__builtin_fmaf(expm1_zoh(zr, mag), co, cm1), mag * si);
+  return make_float2(mag * co, mag * si);
+}
+
+// d/dA of the ZOH coefficient (e^x - 1)/A of a complex A at fixed dt:
+// dt^2 psi(x), psi(x) = (x e^x - e^x + 1)/x^2 = 1/2 + x/3 + x^2/8 + x^3/30 +
+// ... with x = dt a.  As dcoef_dA for real A: below |x| = 0.11 the series
+// (first omitted term x^4/144), above the closed form (ab (x - 1) + 1)/A^2,
+// whose abar carries at most about 2e-7 of absolute error.  ia2 = (1/A)^2.
+__device__ __forceinline__ float2 cdcoef_dA(float dt, float2 a, float2 ab, float2 ia2) {
+  const float2 x = cscale(a, dt);
+  float2 w = make_float2(__builtin_fmaf(x.x, 1.0f / 30.0f, 0.125f), x.y * (1.0f / 30.0f));
+  w = cmul(x, w);
+  w.x += 1.0f / 3.0f;
+  w = cmul(x, w);
+  w.x += 0.5f;
+  const float2 series = cscale(w, dt * dt);
+  const float2 closed = cmul(cfma(ab, make_float2(x.x - 1.0f, x.y), make_float2(1.0f, 0.0f)), ia2);
+  const bool small = __builtin_fmaf(x.x, x.x, x.y * x.y) < 0.0121f;   // |x| < 0.11
+  return small ? series : closed;
+}
+
 // (ab - 1) q, with q = (1/A) B u computed once per step: the ZOH term
 // Bbar u = (Abar - 1)/A B u.
 __device__ __forceinline__ float2 cmul_minus_one(float2 ab, float2 q) {

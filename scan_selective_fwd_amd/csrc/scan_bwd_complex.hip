@@ -174,8 +174,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       const bool tiny = ZOH && ia.x == 0.0f && ia.y == 0.0f;
       const float2 h_in = p.chunk_states[(c * nchunks + ch) * N + n];
       const float2 gc = gcs[cl][n];
-      float2 Bv[K], Cv[K], ab[K], beta[K], hv[K];
-      {
+      // coef[k] = (Abar - 1)/A (its limit dt at A = 0; dt under Euler);
+      // Bbar u = coef B u is formed where it is used
+      float2 Bv[K], Cv[K], ab[K], coef[K], hv[K];
+      auto read_bc = [&]() {
         float bf[2 * K], cf[2 * K];   // steps past L were staged as 0
         tile_read<2 * K>(tile + n * RW, j, bf);
         tile_read<2 * K>(tile + (NT + n) * RW, j, cf);
@@ -184,29 +186,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
           Bv[k] = make_float2(bf[2 * k], bf[2 * k + 1]);
           Cv[k] = make_float2(cf[2 * k], cf[2 * k + 1]);
         }
-      }
+      };
+      read_bc();
 
       // ---- forward replay ----
-      if (!ZOH || __builtin_amdgcn_ballot_w64(tiny) == 0) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
+      for (int k = 0; k < K; ++k) {
+        if constexpr (ZOH) {
+          float2 em1;
+          ab[k] = cexp_expm1_scaled(dt[k], ps.x, ps.y, em1);
+          coef[k] = tiny ? make_float2(dt[k], 0.0f) : cmul(em1, ia);
+        } else {
           ab[k] = cexp_scaled(dt[k], ps.x, ps.y);
-          const float2 Bu = cscale(Bv[k], uv[k]);
-          if constexpr (ZOH) beta[k] = cmul_minus_one(ab[k], cmul(ia, Bu));
-          else beta[k] = cscale(Bu, dt[k]);
-        }
-      } else {
-        // a channel of this wave has A ~ 0 (1/A stored as 0): delta B u there
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          ab[k] = cexp_scaled(dt[k], ps.x, ps.y);
-          const float2 Bu = cscale(Bv[k], uv[k]);
-          beta[k] = tiny ? cscale(Bu, dt[k]) : cmul_minus_one(ab[k], cmul(ia, Bu));
+          coef[k] = make_float2(dt[k], 0.0f);
         }
       }
-      float2 agg = beta[0];
+      auto bbar_u = [&](int k) { return cmul(coef[k], cscale(Bv[k], uv[k])); };
+      float2 agg = bbar_u(0);
 #pragma unroll
-      for (int k = 1; k < K; ++k) agg = cfma(decay(k, ab[k]), agg, beta[k]);
+      for (int k = 1; k < K; ++k) agg = cfma(decay(k, ab[k]), agg, bbar_u(k));
       const float2 Alane = RST ? cscale(cexp_scaled(dsum, ps.x, ps.y), lane_keep)
                                : cexp_scaled(dsum, ps.x, ps.y);
       float2 Ag = Alane;
@@ -218,7 +216,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         float2 h = hstart;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          h = cfma(decay(k, ab[k]), h, beta[k]);
+          h = cfma(decay(k, ab[k]), h, bbar_u(k));
           hv[k] = h;
           yv[k] = __builtin_fmaf(Cv[k].x, h.x, __builtin_fmaf(-Cv[k].y, h.y, yv[k]));
         }
@@ -236,36 +234,38 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       float2 g = make_float2(dpp_mov<0x101>(gc.x, gagg.x), dpp_mov<0x101>(gc.y, gagg.y));
       if (j == 0) gcs[cl][n] = gagg;                   // leaves the chunk at lane 0
 
+      // B and C again from the tile (LDS): kept from the first reads, their
+      // registers would be live across the scans (the fence keeps the
+      // compiler from reusing those reads)
+      mem_fence_compiler();
+      read_bc();
       // ---- gradient terms ----
-      float2 dAc = make_float2(0.0f, 0.0f);   // ZOH: times conj(1/A) below
-      float2 dAl = make_float2(0.0f, 0.0f);   // Euler and the A = 0 limit
+      // dA collects conj(dt Abar h_{t-1} + dcoef/dA B u) G: the Abar path and
+      // (ZOH) the Bbar path, whose coefficient is formed without cancellation
+      float2 dAc = make_float2(0.0f, 0.0f);
+      const float2 ia2 = cmul(ia, ia);
       float pv[4], sv[4][4], Tq[4][2];
 #pragma unroll
       for (int k = K - 1; k >= 0; --k) {
         const float2 Gk = make_float2(__builtin_fmaf(Cv[k].x, gy[k], g.x),
                                       __builtin_fmaf(-Cv[k].y, gy[k], g.y));
-        const float2 gn = cmul(cconj(ab[k]), Gk);   // with the true Abar (also in conj(E) G)
+        const float2 gn = cmul(cconj(ab[k]), Gk);   // with the true Abar
         float2 hprev = (k == 0) ? hstart : hv[k - 1];
         if constexpr (RST) hprev = cscale(hprev, keep[k]);
         const float2 Bu = cscale(Bv[k], uv[k]);
-        // s = conj(E) G with E = Bbar / B; du and dB both use it
-        float2 sG;
-        if (ZOH && !tiny) {
-          const float2 W = cmul(ab[k], cfma(a, hprev, Bu));       // Abar (A h_{t-1} + B u)
+        const float2 Ah = cmul(ab[k], hprev);        // Abar h_{t-1}
+        if constexpr (ZOH) {
+          // ddelta: Re(conj(G) Abar (A h_{t-1} + B u)), dBbar/ddelta = Abar B
+          const float2 W = cfma(a, Ah, cmul(ab[k], Bu));
           gdt[k] = __builtin_fmaf(Gk.x, W.x, __builtin_fmaf(Gk.y, W.y, gdt[k]));
-          const float2 q = make_float2(__builtin_fmaf(dt[k], W.x, -beta[k].x),
-                                       __builtin_fmaf(dt[k], W.y, -beta[k].y));
-          dAc = cfma(cconj(q), Gk, dAc);
-          // conj(E) G = conj(1/A) (conj(Abar) G - G)
-          sG = cmul(cconj(ia), make_float2(gn.x - Gk.x, gn.y - Gk.y));
+          const float2 zeta = cdcoef_dA(dt[k], a, ab[k], ia2);
+          dAc = cfma(cconj(cfma(zeta, Bu, cscale(Ah, dt[k]))), Gk, dAc);
         } else {
-          const float2 Ah = cmul(ab[k], hprev);
-          const float2 dEdt = ZOH ? ab[k] : make_float2(1.0f, 0.0f);
-          gdt[k] += cdot(Gk, cmul(a, Ah)) + cdot(Gk, cmul(dEdt, Bu));
-          dAl = cfma(cconj(cscale(Ah, dt[k])), Gk, dAl);
-          if (ZOH) dAl = cfma(cconj(cscale(Bu, 0.5f * dt[k] * dt[k])), Gk, dAl);
-          sG = cscale(Gk, dt[k]);                    // E = delta
+          gdt[k] += cdot(Gk, cmul(a, Ah)) + cdot(Gk, Bu);   // Euler: Bbar = dt B
+          dAc = cfma(cconj(cscale(Ah, dt[k])), Gk, dAc);
         }
+        // s = conj(E) G with E = Bbar / B; du and dB both use it
+        const float2 sG = cmul(cconj(coef[k]), Gk);
         // Re(conj(G) E B) = Re(conj(s) B)
         du[k] = __builtin_fmaf(sG.x, Bv[k].x, __builtin_fmaf(sG.y, Bv[k].y, du[k]));
         const float2 vB = cscale(sG, uv[k]);
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) red[buf][wave][qq][n % G][pos] = Tq[qq][m];
       }
-      const float2 dAn = cadd(cmul(dAc, cconj(ia)), dAl);
+      const float2 dAn = dAc;
       const float sx = row_sum_to_last(dAn.x);
       const float sy = row_sum_to_last(dAn.y);
       if (j == R - 1) dAs[cl][n] = cadd(dAs[cl][n], make_float2(sx, sy));

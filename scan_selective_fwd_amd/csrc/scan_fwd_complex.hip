@@ -160,18 +160,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       if (!ZOH || __builtin_amdgcn_ballot_w64(tiny) == 0) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          ab[k] = cexp_scaled(dt[k], ar2, air);
           const float2 Bu = make_float2(bf[2 * k] * uv[k], bf[2 * k + 1] * uv[k]);
-          if constexpr (ZOH) beta[k] = cmul_minus_one(ab[k], cmul(ia, Bu));
-          else beta[k] = cscale(Bu, dt[k]);
+          if constexpr (ZOH) {
+            float2 em1;
+            ab[k] = cexp_expm1_scaled(dt[k], ar2, air, em1);
+            beta[k] = cmul(em1, cmul(ia, Bu));      // (Abar - 1)/A B u
+          } else {
+            ab[k] = cexp_scaled(dt[k], ar2, air);
+            beta[k] = cscale(Bu, dt[k]);
+          }
         }
       } else {
         // a channel of this wave has A ~ 0 (1/A stored as 0): delta B u there
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          ab[k] = cexp_scaled(dt[k], ar2, air);
+          float2 em1;
+          ab[k] = cexp_expm1_scaled(dt[k], ar2, air, em1);
           const float2 Bu = make_float2(bf[2 * k] * uv[k], bf[2 * k + 1] * uv[k]);
-          beta[k] = tiny ? cscale(Bu, dt[k]) : cmul_minus_one(ab[k], cmul(ia, Bu));
+          beta[k] = tiny ? cscale(Bu, dt[k]) : cmul(em1, cmul(ia, Bu));
         }
       }
       if constexpr (RST) {

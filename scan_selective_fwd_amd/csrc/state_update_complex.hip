@@ -42,14 +42,15 @@ __global__ __launch_bounds__(256) void state_update_complex_kernel(const CplxSte
     const float2 a = p.A[d * N + n];
     const float2 Bn = p.B[b * N + n];
     const float2 Cn = p.C[b * N + n];
-    const float2 ab = cexp_scaled(dt, a.x * kLog2e, a.y * kInv2Pi);
+    float2 em1;
+    const float2 ab = cexp_expm1_scaled(dt, a.x * kLog2e, a.y * kInv2Pi, em1);
     const float2 Bu = cscale(Bn, uv);
     float2 bu;   // Ebar B u
     const bool tiny = __builtin_fabsf(a.x) < 1e-30f && __builtin_fabsf(a.y) < 1e-30f;
     if (ZOH && !tiny) {
       const float m2 = a.x * a.x + a.y * a.y;
       const float2 ia = make_float2(a.x / m2, -a.y / m2);
-      bu = cmul_minus_one(ab, cmul(ia, Bu));
+      bu = cmul(em1, cmul(ia, Bu));
     } else {
       bu = cscale(Bu, dt);
     }

