@@ -87,7 +87,9 @@ typedef enum {
   MAMBA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required    */
   MAMBA_ERR_UNSUPPORTED = 6,  /* sizes outside the supported limits         */
   MAMBA_ERR_HIP = 7,          /* a HIP runtime call or launch failed        */
-  MAMBA_ERR_INVALID = 8       /* inconsistent optional arguments            */
+  MAMBA_ERR_INVALID = 8,      /* inconsistent optional arguments            */
+  MAMBA_ERR_SCRATCH_LIMIT = 9 /* more scratch than mamba_scan_bwd_noalloc's
+                                 fixed device array holds                   */
 } mamba_status;
 
 typedef enum { MAMBA_F32 = 0, MAMBA_BF16 = 1 } mamba_dtype;
@@ -160,6 +162,37 @@ mamba_status mamba_scan_bwd(const void* u, const void* delta, const float* A, co
                             float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz,
                             float* ddelta_bias, float* dh0, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * mamba_scan_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It calls no hipMalloc, hipFree or other
+ * allocating routine.  The buffers mamba_scan_bwd keeps in its workspace (the
+ * state at every 128-step chunk start, one flag per workgroup, and for long
+ * sequences the segment summaries) live instead in a file-scope device array
+ * of MAMBA_NOALLOC_SCRATCH_BYTES (32 MiB), one per GPU, held from the
+ * library's first use on that GPU until the process ends.  Its address is
+ * looked up once per device, on the first call made with that device
+ * current; `stream` must belong to the current device.
+ *
+ * Arguments, layouts, results and errors are those of mamba_scan_bwd (the
+ * automatic segment choice included); additionally MAMBA_ERR_SCRATCH_LIMIT
+ * when the problem needs more than the array holds even in one pass, checked
+ * before anything is enqueued.  The array is shared by every call on a GPU
+ * and keeps the last call's contents (every value the kernels read from it
+ * is written earlier in the same call): calls that overlap on one GPU, from
+ * several streams or host threads, race and must be serialized by the
+ * caller.
+ */
+#define MAMBA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+mamba_status mamba_scan_bwd_noalloc(const void* u, const void* delta, const float* A,
+                                    const void* B, const void* C, const float* D, const void* z,
+                                    const float* delta_bias, const float* h0, const void* dout,
+                                    int delta_softplus, mamba_disc disc, mamba_dtype dt,
+                                    int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                    float* du, float* ddelta, float* dA, float* dB, float* dC,
+                                    float* dD, float* dz, float* ddelta_bias, float* dh0,
+                                    void* stream);
 
 /*
  * One recurrent (decode) step for every (b, d): state (batch, dim, dstate)

@@ -224,6 +224,52 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
     return g
 
 
+def scan_bwd_noalloc(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
+                     delta_softplus=True, disc="zoh", grads=None):
+    """scan_bwd through mamba_scan_bwd_noalloc: no workspace, the library's
+    fixed per-GPU scratch array instead (calls that overlap on one GPU race).
+    `grads`: optional dict of preallocated float32 outputs with the keys and
+    shapes scan_bwd returns (allocated here when absent).  Returns them."""
+    L_ = lib()
+    dev = u.device
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    sdt = u.dtype
+    dt = _dtype_code(u)
+    for t, name, shp, ty in ((u, "u", (batch, dim, L), sdt), (delta, "delta", (batch, dim, L), sdt),
+                             (A, "A", (dim, N), torch.float32), (B, "B", (batch, N, L), sdt),
+                             (C, "C", (batch, N, L), sdt), (D, "D", (dim,), torch.float32),
+                             (z, "z", (batch, dim, L), sdt),
+                             (delta_bias, "delta_bias", (dim,), torch.float32),
+                             (h0, "h0", (batch, dim, N), torch.float32),
+                             (dout, "dout", (batch, dim, L), sdt)):
+        _req(t, name, ty, shp, dev)
+    shapes = dict(du=(batch, dim, L), ddelta=(batch, dim, L), dA=(dim, N), dB=(batch, N, L),
+                  dC=(batch, N, L))
+    if D is not None:
+        shapes["dD"] = (dim,)
+    if z is not None:
+        shapes["dz"] = (batch, dim, L)
+    if delta_bias is not None:
+        shapes["ddelta_bias"] = (dim,)
+    if h0 is not None:
+        shapes["dh0"] = (batch, dim, N)
+    g = dict(grads or {})
+    for k, shp in shapes.items():
+        if k not in g:
+            g[k] = torch.empty(shp, dtype=torch.float32, device=dev)
+        _req(g[k], k, torch.float32, shp, dev)
+    st = L_.mamba_scan_bwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                   _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(dout),
+                                   int(bool(delta_softplus)), _disc_code(disc), dt, batch, dim,
+                                   N, L, _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                   _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
+                                   _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
+                                   _ptr(g.get("dh0")), _stream(dev))
+    _lib.check(st, "mamba_scan_bwd_noalloc")
+    return {k: g[k] for k in shapes}
+
+
 def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
                  delta_softplus=True, disc="zoh", out=None):
     """One recurrent step; `state` (batch, dim, N) float32 is updated in place.

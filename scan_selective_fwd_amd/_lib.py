@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libmamba_scan.so")
 STATUS = {
     0: "MAMBA_OK", 1: "MAMBA_ERR_NULL_PTR", 2: "MAMBA_ERR_SHAPE", 3: "MAMBA_ERR_DTYPE",
     4: "MAMBA_ERR_ALIGNMENT", 5: "MAMBA_ERR_WORKSPACE", 6: "MAMBA_ERR_UNSUPPORTED",
-    7: "MAMBA_ERR_HIP", 8: "MAMBA_ERR_INVALID",
+    7: "MAMBA_ERR_HIP", 8: "MAMBA_ERR_INVALID", 9: "MAMBA_ERR_SCRATCH_LIMIT",
 }
 F32, BF16 = 0, 1
 ZOH, EULER = 0, 1
@@ -33,7 +33,7 @@ EXPORTS = (
     "mamba_scan_complex_checkpoint_size", "mamba_scan_fwd_complex_ex",
     "mamba_scan_bwd_complex_ex", "mamba_state_update_complex",
     "mamba_scan_fwd_complex_workspace_size", "mamba_scan_fwd_complex_workspace_size_ex",
-    "mamba_scan_bwd_complex_workspace_size_ex",
+    "mamba_scan_bwd_complex_workspace_size_ex", "mamba_scan_bwd_noalloc",
 )
 
 
@@ -94,6 +94,8 @@ def load(path: str = LIB_PATH):
     lib.mamba_scan_bwd_varlen.argtypes = bwd_rst
     lib.mamba_scan_bwd_ex.restype = _int
     lib.mamba_scan_bwd_ex.argtypes = bwd_rst + [_int, _int, _vp, _vp, _vp]
+    lib.mamba_scan_bwd_noalloc.restype = _int
+    lib.mamba_scan_bwd_noalloc.argtypes = [_vp] * 10 + [_int, _int, _int] + [_i64] * 4 + [_vp] * 10
     lib.mamba_scan_checkpoint_size.restype = _sz
     lib.mamba_scan_checkpoint_size.argtypes = [_i64] * 4
     lib.mamba_conv1d_silu_fwd.restype = _int

@@ -245,6 +245,9 @@ const char* mamba_status_string(mamba_status s) {
     case MAMBA_ERR_UNSUPPORTED: return "sizes outside the supported limits";
     case MAMBA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case MAMBA_ERR_INVALID: return "inconsistent optional arguments";
+    case MAMBA_ERR_SCRATCH_LIMIT:
+      return "the problem needs more scratch than the allocation-free entry point's fixed "
+             "device array holds";
   }
   return "unknown status";
 }

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.mamba_abi_version() == 2
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = lib.mamba_status_string(code)
         assert s and isinstance(s, bytes)
     assert lib.mamba_status_string(0) == b"ok"
@@ -348,3 +348,17 @@ def test_conv_fwd_rejects_bad_arguments(lib, kw, code):
 ])
 def test_conv_bwd_rejects_bad_arguments(lib, kw, code):
     assert conv_bwd(lib, **kw) == code
+
+
+def test_noalloc_refuses_problems_beyond_its_scratch(lib):
+    """The allocation-free backward checks its fixed scratch size before any
+    device call: a problem whose one-pass workspace exceeds it is refused
+    (no GPU needed for the check; the pointers are never used)."""
+    assert lib.mamba_scan_bwd_workspace_size_ex(64, 5120, 16, 2048, 0, 0, 1) > 32 << 20
+    fake = 1 << 20   # 16-byte aligned, never dereferenced
+    args = [fake] * 10 + [1, 0, 0, 64, 5120, 16, 2048] + [fake] * 9 + [None]
+    assert lib.mamba_scan_bwd_noalloc(*args) == 9   # MAMBA_ERR_SCRATCH_LIMIT
+    assert b"scratch" in lib.mamba_status_string(9)
+    # invalid sizes are named by the regular checks
+    bad = [fake] * 10 + [1, 0, 0, 0, 5120, 16, 2048] + [fake] * 9 + [None]
+    assert lib.mamba_scan_bwd_noalloc(*bad) == 2    # MAMBA_ERR_SHAPE
