@@ -363,6 +363,24 @@ __device__ __forceinline__ float expm1_zoh(float z, float abar) {
   return __builtin_fmaxf(poly, abar - kExpBound);
 }
 
+// The coefficient itself, (e^x - 1)/A, for A < 0 strictly (the usual case;
+// the kernels send blocks with any other A to their general path).  Dividing
+// the two lower bounds of expm1_zoh by A < 0 turns them into upper bounds of
+// the coefficient, so their minimum is taken:
+//   * delta (1 + x/2 + x^2/6), the cubic bound over x = delta A (written in z);
+//   * (abar - (1 + 2^-22)) / A, formed as fma(abar, 1/A, -(1 + 2^-22)/A); the
+//     bound's margin (2^-22 - 9e-8 relative to 1/A) covers the rounding of the
+//     constant -(1 + 2^-22)/A and of the fma.
+// Relative error below about 8e-6; one multiply fewer than expm1_zoh(z, abar)
+// times 1/A.  mb = -(1 + 2^-22)/A.
+constexpr float kCoefC2 = 0.34657359027997264f;    // ln(2) / 2
+constexpr float kCoefC3 = 0.08007550231970023f;    // ln(2)^2 / 6
+constexpr float kCoefBound = 1.00000023841857910f; // 1 + 2^-22
+__device__ __forceinline__ float zoh_coef_neg(float dt, float z, float abar, float ia, float mb) {
+  const float poly = dt * __builtin_fmaf(z, __builtin_fmaf(z, kCoefC3, kCoefC2), 1.0f);
+  return __builtin_fminf(poly, __builtin_fmaf(abar, ia, mb));
+}
+
 // d/dA of the ZOH coefficient (e^x - 1)/A at fixed delta: delta^2 psi(x),
 // psi(x) = (x e^x - e^x + 1)/x^2 = 1/2 + x/3 + x^2/8 + x^3/30 + ...  The
 // closed form cancels to second order for small x, so below |x| = 0.11 the

@@ -88,10 +88,11 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// TINY = false: the fast kernel.  A block in which some channel has A ~ 0
-// (ZOH only) sets its flag in p.deferred and exits without computing; the
-// TINY = true kernel, launched right after on the same stream, computes
-// exactly the flagged blocks with the A = 0 limits of the ZOH coefficients.
+// TINY = false: the fast kernel, for blocks whose A are all negative.  A block
+// in which some channel has A ~ 0 or A > 0 (ZOH only) sets its flag in
+// p.deferred and exits without computing; the TINY = true kernel, launched
+// right after on the same stream, computes exactly the flagged blocks, with
+// the sign-agnostic ZOH coefficient and its A = 0 limit.
 //
 // Per-state values that live across state indices (the chunk-start state,
 // the adjoint carried from the later chunk, the dA sum) are kept in
@@ -101,7 +102,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // RST: packed sequences (p.reset flags).  The state entering a flagged step
 // is zero: the step's decay factor in the recurrence and in the adjoint
 // becomes 0 (Bbar keeps the true one), and its h_{t-1} counts as 0.
-template <typename T, int NT, bool ZOH, bool VEC, bool TINY, bool RST = false>
+// EXACT: N == NT at compile time (the usual N = 16): the state loop then has
+// no per-index branch, so the scheduler can overlap neighbouring states.
+template <typename T, int NT, bool ZOH, bool VEC, bool TINY, bool RST = false, bool EXACT = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(
     const BwdParams p) {
   constexpr int R = 16;
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const bool active = d_raw < p.dim;
   const int64_t d = active ? d_raw : p.dim - 1;
   const int64_t c = b * p.dim + d;
-  const int N = p.N;
+  const int N = EXACT ? NT : p.N;
   const int64_t L = p.L;
   const int64_t nchunks = p.nchunks;
   const int64_t ch_begin = p.seg_chunks > 0 ? seg * p.seg_chunks : 0;
@@ -179,7 +182,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const bool real = dd < p.dim && n < N;
     const float a = real ? p.A[dd * N + n] : -1.0f;
     const bool tiny = __builtin_fabsf(a) < 1e-30f;
-    my_tiny |= real && tiny;
+    // blocks with any A that is not strictly negative (A ~ 0, A > 0) are
+    // deferred to the TINY launch, which forms the coefficient generally
+    my_tiny |= real && !(a < -1e-30f);
     prm[ci][n] = make_float4(a * kLog2e, tiny ? 0.0f : 1.0f / a, a, tiny ? 0.0f : 1.0f / (a * a));
   }
 
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           const float z = dt[k] * a2;
           a[k] = fast_exp2(z);
           if constexpr (ZOH && !TINY) {
-            coef[k] = expm1_zoh(z, a[k]) * ia;
+            coef[k] = zoh_coef_neg(dt[k], z, a[k], ia, ia * -kCoefBound);   // A < 0 here
           } else if constexpr (ZOH) {
             coef[k] = tiny ? dt[k] : expm1_zoh(z, a[k]) * ia;
           } else {
@@ -520,21 +525,31 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(const BwdParams p)
   }
 }
 
-template <typename T, int NT, bool ZOH, bool VEC, bool RST>
-static hipError_t launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin,
-                             hipEvent_t ev_end) {
+template <typename T, int NT, bool ZOH, bool VEC, bool RST, bool EXACT>
+static hipError_t launch_bwd_x(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin,
+                               hipEvent_t ev_end) {
   const int64_t nblocks = p.batch * p.groups * p.nseg;
   hipError_t e;
   if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, false, RST>), dim3((unsigned)nblocks),
-                     dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, false, RST, EXACT>),
+                     dim3((unsigned)nblocks), dim3(kBlock), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
   if (!ZOH) return e;
-  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, true, RST>), dim3((unsigned)nblocks),
-                     dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, true, RST, EXACT>),
+                     dim3((unsigned)nblocks), dim3(kBlock), 0, s, p);
   return hipGetLastError();
+}
+
+// N == 16 exactly takes the EXACT kernel of the N <= 16 variant.
+template <typename T, int NT, bool ZOH, bool VEC, bool RST>
+static hipError_t launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin,
+                             hipEvent_t ev_end) {
+  if constexpr (NT == 16) {
+    if (p.N == 16) return launch_bwd_x<T, NT, ZOH, VEC, RST, true>(p, s, ev_begin, ev_end);
+  }
+  return launch_bwd_x<T, NT, ZOH, VEC, RST, false>(p, s, ev_begin, ev_end);
 }
 
 // The backward for one state-size variant (NT = 16: N <= 16; NT = 64: N <= 64):

@@ -195,7 +195,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const bool real = dd < p.dim && n < N;
     const float a = real ? p.A[dd * N + n] : -1.0f;
     const bool tiny = __builtin_fabsf(a) < 1e-30f;
-    my_tiny |= real && tiny;
+    // blocks with any A that is not strictly negative (A ~ 0, A > 0) take
+    // the general copy of the chunk loop
+    my_tiny |= real && !(a < -1e-30f);
     a2s[ci][n] = a * kLog2e;
     ias[ci][n] = tiny ? 0.0f : 1.0f / a;
   }
@@ -345,13 +347,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           float a[K], beta[K];
           float agg = 0.0f;
           if constexpr (!TP) {
+            // every A of the block is negative here
+            const float mb = ia * -kCoefBound;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
               const float z = dt[k] * a2;
               a[k] = fast_exp2(z);
               if constexpr (ZOH) {
-                const float q = Bv[k] * (uv[k] * ia);
-                beta[k] = expm1_zoh(z, a[k]) * q;          // (Abar - 1)/A * B * u
+                // (Abar - 1)/A * B * u
+                beta[k] = zoh_coef_neg(dt[k], z, a[k], ia, mb) * (Bv[k] * uv[k]);
               } else {
                 beta[k] = Bv[k] * uv[k];
               }
@@ -359,8 +363,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
               agg = k == 0 ? beta[0] : __builtin_fmaf(a[k], agg, beta[k]);
             }
           } else {
-            // a channel of this wave has A ~ 0 (stored as 1/A = 0):
-            // (e^{dA}-1)/A -> delta there
+            // a channel of this block has A ~ 0 (stored as 1/A = 0; the
+            // coefficient (e^{dA}-1)/A -> delta there) or A > 0
 #pragma unroll
             for (int k = 0; k < K; ++k) {
               const float z = dt[k] * a2;
