@@ -21,11 +21,14 @@ caches flushed before every launch (a 1 GiB buffer is written first, more
 than the L2s and the 256 MB last-level cache hold): median, p10 and p90 of
 --cold-iters launches.  `ms_per_step_graph` is the same step captured once
 into a HIP graph and replayed (context: the launch gaps between the calls
-removed; `value` stays the plain calls).
+removed; `value` stays the plain calls).  `per_config` times the other
+specified configurations once each (the Mamba-1.4B layer forward in bf16,
+ZOH and Euler; the 2^20-step forward; the bf16 backward as a plain call,
+whose state-recompute pass is included), with inputs drawn on the device.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4|5]
                        [--disc zoh|euler] [--calls fwd,bwd,step] [--no-cpu-baseline]
-                       [--copy-calibration] [--cold-iters N]
+                       [--copy-calibration] [--cold-iters N] [--no-per-config]
        python bench.py --summarize-counters counter_collection.csv [...]
 """
 from __future__ import annotations
@@ -55,6 +58,13 @@ PEAK_F32_TFLOPS = 157.3
 #   backward: forward replay incl. y 10, adjoint 3, ddelta 6, dA 5, du 5,
 #             dB 2, dC 2                                                  = 33 (+1 exp)
 FLOPS_PER_TN = {"fwd": 10, "bwd": 34}
+# Euler Bbar u = delta B u: 2 flops instead of the ZOH coefficient's 4 in the
+# forward; the backward loses the coefficient's A-derivative (about 5).
+FLOPS_PER_TN_EULER = {"fwd": 8, "bwd": 30}
+
+
+def flops_per_tn(call: str, disc: str) -> int:
+    return (FLOPS_PER_TN if disc == "zoh" else FLOPS_PER_TN_EULER)[call]
 CSRC = os.path.join(ROOT, "scan_selective_fwd_amd", "csrc")
 # Sources each timed kernel is compiled from (its counter summary is void
 # once any of them changes).
@@ -331,6 +341,75 @@ def sweep(torch, ms_lib, W, steps=10):
     return rows
 
 
+# The other specified configurations, timed after the headline step with
+# inputs drawn on the device: (tag, workload id, discretization, call).
+PER_CONFIG = [("w3_zoh", 3, "zoh", "fwd"), ("w3_euler", 3, "euler", "fwd"),
+              ("w4_zoh", 4, "zoh", "fwd"), ("w5_zoh", 5, "zoh", "bwd")]
+
+
+def per_config(torch, ms_lib, W, iters=10):
+    """Each of PER_CONFIG on its own: `iters` timed calls after two untimed
+    ones, events around every call and around its main kernel (the output
+    kernel of the forward, the reverse-scan kernel of the backward).  The
+    backward is the plain call: no checkpoints, so it includes the pass that
+    recomputes the chunk-start states.  Returns {tag: {...}}."""
+    res = {}
+    for tag, wid, disc, call in PER_CONFIG:
+        w = W.WORKLOADS[wid]
+        g = W.device_inputs(w, torch, with_dout=call == "bwd")
+        sdt = g["u"].dtype
+        if call == "fwd":
+            nws = ms_lib.fwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen, sdt)
+            ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+            out = torch.empty_like(g["u"])
+            last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device="cuda")
+
+            def fn(timing=None):
+                ms_lib.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                                g["delta_bias"], disc=disc, out=out, last_state=last,
+                                return_last_state=True, workspace=ws, timing=timing)
+        else:
+            ws = torch.empty(ms_lib.bwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen, sdt),
+                             dtype=torch.uint8, device="cuda")
+
+            def fn(timing=None):
+                ms_lib.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                                g["delta_bias"], g["dout"], disc=disc, workspace=ws,
+                                timing=timing)
+        n = max(3, iters if w.seqlen <= 65536 else iters // 2)
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            fn(kev[i])
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        kern_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
+        nbytes = algorithmic_bytes(w, call)
+        flops = flops_per_tn(call, disc) * w.batch * w.dim * w.seqlen * w.dstate
+        res[tag] = {"workload": w.name, "call": f"mamba_scan_{call}", "disc": disc,
+                    "batch": w.batch, "dim": w.dim, "dstate": w.dstate, "seqlen": w.seqlen,
+                    "dtype": w.dtype, "iters": n,
+                    "ms": round(call_ms, 5), "kernel_ms": round(kern_ms, 5),
+                    "algorithmic_MB": round(nbytes / 1e6, 3),
+                    "GB/s": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nbytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "alu_frac": round(flops / (call_ms * 1e-3) / 1e12 / PEAK_F32_TFLOPS, 4),
+                    "channel_tokens_per_s": round(w.batch * w.dim * w.seqlen / (call_ms * 1e-3),
+                                                  1)}
+        del g, ws, fn
+        if call == "fwd":
+            del out, last
+        torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(torch):
     """A plain device copy of known size, so that counter runs over this
     process can scale FETCH_SIZE / WRITE_SIZE to bytes."""
@@ -367,6 +446,8 @@ def main():
                          "at the pages' scan benchmark shape; one JSON line")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the step replayed from a captured HIP graph")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip timing the other specified configurations (per_config)")
     ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="CSV")
     args = ap.parse_args()
     if args.summarize_counters:
@@ -585,7 +666,7 @@ def main():
         dom = max(kern_ms, key=lambda c: kern_ms[c])
         kname = kernel_names[dom]
         dom_bytes = algorithmic_bytes(w, dom)
-        dom_flops = FLOPS_PER_TN[dom] * w.batch * w.dim * w.seqlen * w.dstate
+        dom_flops = flops_per_tn(dom, args.disc) * w.batch * w.dim * w.seqlen * w.dstate
         secs = kern_ms[dom] * 1e-3
         tflops = dom_flops / secs / 1e12
         gbs = dom_bytes / secs / 1e9
@@ -595,12 +676,14 @@ def main():
                            "traffic": committed_traffic(kname, wl_tag),
                            "kernel": kname, "call": f"mamba_scan_{dom}",
                            "algorithmic_flops_per_launch": int(dom_flops),
-                           "flops_per_state_step": FLOPS_PER_TN[dom],
+                           "flops_per_state_step": flops_per_tn(dom, args.disc),
                            "hbm": {"achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS,
                                    "frac": round(gbs / PEAK_HBM_GBS, 4),
                                    "algorithmic_bytes_per_launch": int(dom_bytes)},
                            "avg_launch_ms": round(kern_ms[dom], 5),
                            "kernel_source_sha256": kernel_source_hash(kname)}
+    if not args.no_per_config and args.workload == 2 and not args.calls and not args.varlen:
+        res["per_config"] = per_config(torch, ms, W)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, calls, args.disc)
     print(json.dumps(res), flush=True)

@@ -331,6 +331,10 @@ inline hipError_t dispatch_chunk_states(const FwdParams& p, int dtype, int disc,
 }
 // The backward always spreads a channel over 16 lanes (kBwdLanes).
 constexpr int kBwdLanes = 16;
+// Without reset flags and with N <= 16 the backward takes 12-wave blocks (48
+// channels) when they number at least this many (one per CU), else 4-wave
+// blocks (16 channels).
+constexpr int64_t kBwdWideMinBlocks = 256;
 // Backward launchers, one per (dtype, reset flags, state-size variant):
 // NT = 16 for N <= 16, NT = 64 for N <= 64.  ev_begin / ev_end (nullable) are
 // recorded on the stream right before and after the main backward kernel,

@@ -22,8 +22,8 @@
 //
 // Launches (api.cpp): a zero fill of the accumulated gradients; the forward
 // kernel in states-only mode (the state at every chunk start, into the
-// workspace); then this kernel.  Here a block serves 16 channels of one batch
-// row (4 per wave, 16 lanes each, 8 steps per lane: 128-step chunks) and walks
+// workspace); then this kernel.  Here a block serves 16 or 48 channels of one
+// batch row (4 per wave, 16 lanes each, 8 steps per lane: 128-step chunks) and walks
 // the chunks from last to first.  Per chunk and state index n it replays the
 // forward from the stored chunk-start state (pass 1, DPP prefix scan, pass 2
 // keeping h in registers), then the adjoint (reverse pass 1, DPP suffix scan
@@ -102,17 +102,19 @@ __device__ __forceinline__ void static_for(F&& f) {
 // RST: packed sequences (p.reset flags).  The state entering a flagged step
 // is zero: the step's decay factor in the recurrence and in the adjoint
 // becomes 0 (Bbar keeps the true one), and its h_{t-1} counts as 0.
-// EXACT: N == NT at compile time (the usual N = 16): the state loop then has
-// no per-index branch, so the scheduler can overlap neighbouring states.
-template <typename T, int NT, bool ZOH, bool VEC, bool TINY, bool RST = false, bool EXACT = false>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(
+// NW: waves per block (4: 16 channels; 12: 48 channels, a whole CU at three
+// waves per SIMD, whose dB/dC flushes sum three times as many channels before
+// the global atomics).
+template <typename T, int NT, bool ZOH, bool VEC, bool TINY, bool RST = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(
     const BwdParams p) {
   constexpr int R = 16;
   constexpr int K = kItemsBwd;
   static_assert(K == 8, "the row reduce-scatter assumes 8 steps per lane");
   static_assert(NT % 16 == 0, "states are spread over the 16 lanes of a channel");
+  constexpr int NTH = 64 * NW;   // threads per block
   constexpr int CPW = 64 / R;
-  constexpr int CPB = (kBlock / 64) * CPW;
+  constexpr int CPB = NW * CPW;
   constexpr int TCH = R * K;
   constexpr bool TILE = (NT == 16);
   constexpr int NQ = NT / 16;
@@ -126,13 +128,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   // position (tt % 8) * 16 + tt / 8, which makes each wave's 64 stores hit
   // 64 consecutive words.
   constexpr int G = 2;
-  constexpr int NW = kBlock / 64;
   __shared__ float red[2][NW][2][G][TCH];
   // per-step factors of the epilogue, made when the inputs are first read
   // (softplus'(r) for ddelta and dout*SiLU'(z) for dz), so that the inputs
   // are not read from memory a second time; [k][tid] keeps accesses
   // conflict-free
-  __shared__ float stash[2][kItemsBwd][kBlock];
+  __shared__ float stash[2][kItemsBwd][NTH];
 
   // the TINY launch computes only the blocks the fast launch deferred; the
   // others leave before loading anything
@@ -148,15 +149,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const int cl = wave * CPW + row;
   // block order (b, segment, group) with the group fastest, as in the forward
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t per_b = p.groups * p.nseg;
+  const int64_t ngrp = (p.dim + CPB - 1) / CPB;   // this kernel's channel groups per batch row
+  const int64_t per_b = ngrp * p.nseg;
   const int64_t b = blk / per_b;
-  const int64_t seg = (blk - b * per_b) / p.groups;
-  const int64_t grp = blk - b * per_b - seg * p.groups;
+  const int64_t seg = (blk - b * per_b) / ngrp;
+  const int64_t grp = blk - b * per_b - seg * ngrp;
   const int64_t d_raw = grp * CPB + cl;
   const bool active = d_raw < p.dim;
   const int64_t d = active ? d_raw : p.dim - 1;
   const int64_t c = b * p.dim + d;
-  const int N = EXACT ? NT : p.N;
+  const int N = p.N;
   const int64_t L = p.L;
   const int64_t nchunks = p.nchunks;
   const int64_t ch_begin = p.seg_chunks > 0 ? seg * p.seg_chunks : 0;
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const uint8_t* __restrict__ rst_row = RST ? p.reset + b * L : nullptr;
 
   bool my_tiny = false;
-  for (int i = tid; i < CPB * NT; i += kBlock) {
+  for (int i = tid; i < CPB * NT; i += NTH) {
     const int ci = i / NT, n = i - ci * NT;
     const int64_t dd = grp * CPB + ci;
     const bool real = dd < p.dim && n < N;
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     }
   };
 
-  TileStager<T, TCH, K, NT, TILE ? 2 * NT : 1, kBlock> stage;
+  TileStager<T, TCH, K, NT, TILE ? 2 * NT : 1, NTH> stage;
   float hreg[NQ], gcreg[NQ], dAreg[NQ];
   // the adjoint entering the block's last chunk from the right: zero at the
   // end of the sequence (no gradient flows into the final state), else the
@@ -430,8 +432,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         if (n0 < N) {
           __syncthreads();
 #pragma unroll 1
-          for (int s = 0; s < 2 * G * TCH / kBlock; ++s) {
-            const int i = s * kBlock + tid;
+          for (int i = tid; i < 2 * G * TCH; i += NTH) {
             const int which = i / (G * TCH);
             const int nn = (i / TCH) % G;
             // consecutive threads take consecutive steps, so that each wave's
@@ -525,31 +526,36 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(const BwdParams p)
   }
 }
 
-template <typename T, int NT, bool ZOH, bool VEC, bool RST, bool EXACT>
+template <typename T, int NT, bool ZOH, bool VEC, bool RST, int NW>
 static hipError_t launch_bwd_x(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin,
                                hipEvent_t ev_end) {
-  const int64_t nblocks = p.batch * p.groups * p.nseg;
+  const int64_t nblocks = p.batch * ((p.dim + 4 * NW - 1) / (4 * NW)) * p.nseg;
   hipError_t e;
   if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, false, RST, EXACT>),
-                     dim3((unsigned)nblocks), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, false, RST, NW>),
+                     dim3((unsigned)nblocks), dim3(64 * NW), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
   if (!ZOH) return e;
-  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, true, RST, EXACT>),
-                     dim3((unsigned)nblocks), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NT, ZOH, VEC, true, RST, NW>),
+                     dim3((unsigned)nblocks), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
-// N == 16 exactly takes the EXACT kernel of the N <= 16 variant.
+// N <= 16 without reset flags takes 12-wave blocks when they number at least
+// kBwdWideMinBlocks (every CU gets one), else 4-wave blocks.  At batch 8,
+// D 1536, L 2048 (256 wide blocks) the kernel measured 0.663 ms against
+// 0.673 ms, and the dB/dC atomics fall to a third; at batch 2, D 5120 (214
+// wide blocks, 640 narrow) narrow blocks measured 0.663 ms against 0.678 ms.
 template <typename T, int NT, bool ZOH, bool VEC, bool RST>
 static hipError_t launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin,
                              hipEvent_t ev_end) {
-  if constexpr (NT == 16) {
-    if (p.N == 16) return launch_bwd_x<T, NT, ZOH, VEC, RST, true>(p, s, ev_begin, ev_end);
+  if constexpr (NT == 16 && !RST) {
+    if (p.batch * ((p.dim + 47) / 48) * p.nseg >= kBwdWideMinBlocks)
+      return launch_bwd_x<T, NT, ZOH, VEC, RST, 12>(p, s, ev_begin, ev_end);
   }
-  return launch_bwd_x<T, NT, ZOH, VEC, RST, false>(p, s, ev_begin, ev_end);
+  return launch_bwd_x<T, NT, ZOH, VEC, RST, 4>(p, s, ev_begin, ev_end);
 }
 
 // The backward for one state-size variant (NT = 16: N <= 16; NT = 64: N <= 64):

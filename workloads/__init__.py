@@ -168,6 +168,40 @@ def workload_inputs(wid: int, **kw):
     return make_inputs(wid, w.batch, w.dim, w.dstate, w.seqlen, **args)
 
 
+def device_inputs(w: Workload, torch, *, with_dout=False, device="cuda"):
+    """The workload's distributions drawn directly on the device with torch's
+    generator (seeded with the workload id): for timing runs whose inputs are
+    too large to draw on the host (the 2^20-step workload), not for parity
+    (the values differ from make_inputs').  Sequence tensors are float32 or
+    bfloat16 (rounded by torch), A, D, delta_bias float32."""
+    g = torch.Generator(device=device)
+    g.manual_seed(1000 + w.wid)
+    sdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+    def seq(rows):
+        out = torch.empty((w.batch, rows, w.seqlen), dtype=sdt, device=device)
+        for b in range(w.batch):            # one batch row at a time bounds the float32 temporary
+            for r0 in range(0, rows, 256):
+                r1 = min(rows, r0 + 256)
+                out[b, r0:r1] = torch.randn((r1 - r0, w.seqlen), generator=g, device=device,
+                                            dtype=torch.float32).to(sdt)
+        return out
+
+    res = {"u": seq(w.dim), "delta": seq(w.dim), "B": seq(w.dstate), "C": seq(w.dstate),
+           "z": seq(w.dim)}
+    if with_dout:
+        res["dout"] = seq(w.dim)
+    res["A"] = -torch.arange(1, w.dstate + 1, dtype=torch.float32, device=device).expand(
+        w.dim, w.dstate).contiguous()
+    res["D"] = torch.randn(w.dim, generator=g, device=device, dtype=torch.float32)
+    if w.bias == "const":
+        res["delta_bias"] = torch.full((w.dim,), -2.0, dtype=torch.float32, device=device)
+    else:
+        res["delta_bias"] = torch.rand(w.dim, generator=g, device=device,
+                                       dtype=torch.float32) * (BIAS_HI - BIAS_LO) + BIAS_LO
+    return res
+
+
 def as_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
     """The exact float64 values of a generated array (bf16 bits widened)."""
     if dtype == "bf16" and arr.dtype == np.uint16:
