@@ -150,6 +150,54 @@ def summarize_counters(paths):
               f"min={np.min(v):16.1f} max={np.max(v):16.1f}  {name}")
 
 
+def traffic_summary(kernel, workload, fetch_csv, write_csv):
+    """Prints the HBM traffic summary of `kernel` (scan_fwd_kernel or
+    scan_bwd_kernel) from two rocprofv3 counter runs of the same bench
+    command with --copy-calibration, one with FETCH_SIZE and one with
+    WRITE_SIZE.  The 1 GiB device copy the process starts with gives the
+    scale from counter KiB to bytes; the kernel's figures are the mean per
+    dispatch of its most expensive template instance (the TINY copy of the
+    backward exits at once)."""
+    def per_dispatch(path, counter):
+        acc = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                d = acc.setdefault(row["Kernel_Name"], {})
+                d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+        return acc
+
+    fetch, write = per_dispatch(fetch_csv, "FETCH_SIZE"), per_dispatch(write_csv, "WRITE_SIZE")
+
+    def pick(acc):
+        mine = {n: v for n, v in acc.items() if f"mscan::{kernel}<" in n}
+        name = max(mine, key=lambda n: np.mean(list(mine[n].values())))
+        return name, list(mine[name].values())
+
+    def copy_kib(acc):
+        return max(max(v.values()) for n, v in acc.items() if "copyBuffer" in n)
+
+    name, fv = pick(fetch)
+    _, wv = pick(write)
+    cf, cw = copy_kib(fetch), copy_kib(write)
+    fscale, wscale = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    rd = float(np.mean(fv)) * 1024 * fscale
+    wr = float(np.mean(wv)) * 1024 * wscale
+    import workloads as W
+    wid = int(workload[1:].split("_")[0])
+    call = {"scan_fwd_kernel": "fwd", "scan_bwd_kernel": "bwd"}[kernel]
+    alg = algorithmic_bytes(W.WORKLOADS[wid], call)
+    print(f"kernel: {kernel}\ninstance: {name.split('(')[0]}\nworkload: {workload}\n"
+          f"source_sha256: {kernel_source_hash(kernel)}\ndispatches: {len(fv)}\n"
+          f"fetch_kib_per_dispatch: {np.mean(fv):.1f}\nwrite_kib_per_dispatch: {np.mean(wv):.1f}\n"
+          f"copy_1GiB_fetch_kib: {cf:.1f}\ncopy_1GiB_write_kib: {cw:.1f}\n"
+          f"fetch_scale: {fscale:.4f}\nwrite_scale: {wscale:.4f}\n"
+          f"read_bytes_per_launch: {rd:.0f}\nwritten_bytes_per_launch: {wr:.0f}\n"
+          f"traffic_bytes_per_launch: {rd + wr:.0f}\nalgorithmic_bytes_per_launch: {alg:.0f}\n"
+          f"traffic_over_algorithmic: {(rd + wr) / alg:.3f}")
+
+
 def gpu_inputs(w, torch, with_dout):
     import workloads as W
     inp = W.workload_inputs(w.wid, with_dout=with_dout)
@@ -449,9 +497,16 @@ def main():
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip timing the other specified configurations (per_config)")
     ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="CSV")
+    ap.add_argument("--traffic-summary", nargs=4, default=None,
+                    metavar=("KERNEL", "WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic summary of a kernel from FETCH_SIZE and "
+                         "WRITE_SIZE counter runs (workload tag as w2_zoh)")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every (batch, channel) recurrence is "

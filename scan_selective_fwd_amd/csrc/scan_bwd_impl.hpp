@@ -431,8 +431,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         const int buf = (n / G) & 1;
         if (n0 < N) {
           __syncthreads();
+          // (the thread index is hidden from the optimizer: the atomics'
+          // addresses derived from it were otherwise formed once, before the
+          // chunk loop, and spilled -- their reloads read scratch from HBM)
 #pragma unroll 1
-          for (int i = tid; i < 2 * G * TCH; i += NTH) {
+          for (int i = opaque_int(tid); i < 2 * G * TCH; i += NTH) {
             const int which = i / (G * TCH);
             const int nn = (i / TCH) % G;
             // consecutive threads take consecutive steps, so that each wave's
