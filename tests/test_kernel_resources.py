@@ -41,9 +41,10 @@ CPLX_BWD = re.compile(r"^_ZN5mscan12_GLOBAL__N_123scan_bwd_complex_kernelI([ft])
 # Scratch caps (bytes per lane).  The Euler backward has none.  The ZOH
 # backward forms the ZOH coefficient and its A-derivative without
 # cancellation (a cubic expm1 bound, the psi series and closed form), whose
-# temporaries spill a few dwords per lane outside the state loop; the caps
-# keep that from growing unnoticed.
-BWD_ZOH_SCRATCH_CAP = {"16": 112, "64": 96}
+# temporaries spill a few dwords per lane outside the chunk loop (N <= 16)
+# or outside the state loop (N <= 64, 64 carried states per channel); the
+# caps keep that from growing unnoticed.
+BWD_ZOH_SCRATCH_CAP = {"16": 32, "64": 104}
 
 
 def test_real_backward_main_variants_scratch(res):
