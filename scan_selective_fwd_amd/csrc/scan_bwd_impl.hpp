@@ -547,10 +547,10 @@ static hipError_t launch_bwd_x(const BwdParams& p, hipStream_t s, hipEvent_t ev_
 }
 
 // N <= 16 without reset flags takes 12-wave blocks when they number at least
-// kBwdWideMinBlocks (every CU gets one), else 4-wave blocks.  At batch 8,
-// D 1536, L 2048 (256 wide blocks) the kernel measured 0.663 ms against
-// 0.673 ms, and the dB/dC atomics fall to a third; at batch 2, D 5120 (214
-// wide blocks, 640 narrow) narrow blocks measured 0.663 ms against 0.678 ms.
+// kBwdWideMinBlocks, else 4-wave blocks.  Measured (f32 batch 8, D 1536,
+// L 2048: 256 wide blocks): 0.652-0.662 ms against 0.682 ms, with a third of
+// the dB/dC atomics; bf16 batch 2, D 5120 (214 wide blocks, 640 narrow):
+// 0.622-0.629 ms against 0.682-0.685 ms.
 template <typename T, int NT, bool ZOH, bool VEC, bool RST>
 static hipError_t launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin,
                              hipEvent_t ev_end) {
