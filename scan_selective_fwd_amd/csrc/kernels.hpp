@@ -331,12 +331,13 @@ inline hipError_t dispatch_chunk_states(const FwdParams& p, int dtype, int disc,
 }
 // The backward always spreads a channel over 16 lanes (kBwdLanes).
 constexpr int kBwdLanes = 16;
-// Without reset flags and with N <= 16 the backward takes 12-wave blocks (48
-// channels, one per CU) when they number at least this many, else 4-wave
-// blocks (16 channels, three per CU).  From 171 wide blocks on, the narrow
-// ones would put a third block on some CU, so both take a full CU's turn
-// and the wide blocks' fewer atomics and barriers-per-channel win; below,
-// the narrow ones finish in two thirds of that.
+// Without reset flags, with N <= 16 and in one pass (no sequence segments)
+// the backward takes 12-wave blocks (48 channels, one per CU) when they number
+// at least this many, else 4-wave blocks (16 channels, three per CU).  From
+// 171 wide blocks on, the narrow ones would put a third block on some CU, so
+// both take a full CU's turn and the wide blocks' fewer atomics win; below,
+// the narrow ones finish in two thirds of that.  Segmented runs (many short
+// blocks per channel group) measured faster with narrow blocks.
 constexpr int64_t kBwdWideMinBlocks = 171;
 // Backward launchers, one per (dtype, reset flags, state-size variant):
 // NT = 16 for N <= 16, NT = 64 for N <= 64.  ev_begin / ev_end (nullable) are

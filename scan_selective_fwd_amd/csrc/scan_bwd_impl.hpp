@@ -546,16 +546,17 @@ static hipError_t launch_bwd_x(const BwdParams& p, hipStream_t s, hipEvent_t ev_
   return hipGetLastError();
 }
 
-// N <= 16 without reset flags takes 12-wave blocks when they number at least
-// kBwdWideMinBlocks, else 4-wave blocks.  Measured (f32 batch 8, D 1536,
-// L 2048: 256 wide blocks): 0.652-0.662 ms against 0.682 ms, with a third of
-// the dB/dC atomics; bf16 batch 2, D 5120 (214 wide blocks, 640 narrow):
-// 0.622-0.629 ms against 0.682-0.685 ms.
+// N <= 16 without reset flags, in one pass, takes 12-wave blocks when they
+// number at least kBwdWideMinBlocks, else 4-wave blocks.  Measured (f32
+// batch 8, D 1536, L 2048: 256 wide blocks): 0.652-0.662 ms against 0.682 ms,
+// with a third of the dB/dC atomics; bf16 batch 2, D 5120 (214 wide blocks,
+// 640 narrow): 0.622-0.629 ms against 0.682-0.685 ms.  Segmented (bf16
+// batch 1, D 1024, 32 segments from L = 4096): narrow blocks 7-12 % faster.
 template <typename T, int NT, bool ZOH, bool VEC, bool RST>
 static hipError_t launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin,
                              hipEvent_t ev_end) {
   if constexpr (NT == 16 && !RST) {
-    if (p.batch * ((p.dim + 47) / 48) * p.nseg >= kBwdWideMinBlocks)
+    if (p.nseg == 1 && p.batch * ((p.dim + 47) / 48) >= kBwdWideMinBlocks)
       return launch_bwd_x<T, NT, ZOH, VEC, RST, 12>(p, s, ev_begin, ev_end);
   }
   return launch_bwd_x<T, NT, ZOH, VEC, RST, 4>(p, s, ev_begin, ev_end);

@@ -414,15 +414,15 @@ def test_bwd_segmented(segments, dtype, disc):
     run_bwd_case(51, 1, 20, 16, 1189, dtype, disc, h0=True, segments=segments)
 
 
-# Wide backward blocks (12 waves, 48 channels) run when batch * ceil(D/48) *
-# segments reaches 171 (N <= 16, no reset flags).  These shapes reach it
-# with a partial last channel group (2050 = 42 * 48 + 34), ragged sequences
-# and, in the segmented case, 22 groups over 17 automatic segments.
+# Wide backward blocks (12 waves, 48 channels) run when batch * ceil(D/48)
+# reaches 171 in a one-pass backward (N <= 16, no reset flags).  These shapes
+# reach it with a partial last channel group (2050 = 42 * 48 + 34) and
+# ragged sequences.
 WIDE_MIN_BLOCKS = 171
 
 
-def _wide_blocks(batch, dim, nseg=1):
-    return batch * -(-dim // 48) * nseg
+def _wide_blocks(batch, dim):
+    return batch * -(-dim // 48)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -432,16 +432,15 @@ def test_bwd_wide_blocks(dtype, disc):
     run_bwd_case(54, 4, 2050, 16, 300, dtype, disc, h0=True)
 
 
-def test_bwd_wide_blocks_zero_A_checkpoints_and_segments():
+def test_bwd_wide_blocks_zero_A_and_checkpoints():
     # A = 0 in every fourth channel: the wide blocks holding one are deferred
     # to the launch with the A = 0 limit
     assert _wide_blocks(4, 2050) >= WIDE_MIN_BLOCKS
     run_bwd_case(55, 4, 2050, 16, 300, "f32", "zoh", zero_A=True, h0=True)
     _ckpt_case(56, 4, 2050, 16, 300, "f32", "zoh", h0=True)
-    # batch 1, D 1030: 65 narrow blocks, so the sequence (16 chunks and a
-    # ragged one) is split into 17 segments automatically: 22 * 17 wide blocks
-    assert _wide_blocks(1, 1030, 17) >= WIDE_MIN_BLOCKS
-    run_bwd_case(57, 1, 1030, 16, 2125, "f32", "zoh", h0=True)
+    # one channel group fewer: narrow blocks (4 * 42 = 168 wide ones)
+    assert _wide_blocks(4, 2016) < WIDE_MIN_BLOCKS
+    run_bwd_case(57, 4, 2016, 16, 300, "f32", "zoh", h0=True)
 
 
 def test_bwd_segmented_state_sizes_optionals_zero_A():
