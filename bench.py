@@ -13,8 +13,10 @@ Prints ONE JSON line.  `value` is the achieved algorithmic HBM throughput of
 the step (bytes every call must move at least once, divided by the step
 time), in GB/s.  `roofline` is for the kernel that takes most of the step,
 timed alone with HIP events that the library records around it on the
-stream it runs on; its `traffic` comes from the committed counter summary of
-that kernel when the kernel's sources are unchanged since it was taken.
+stream it runs on; its `traffic` (HBM bytes per launch) and `issue` (vector
+instructions per (t, n) and the issue rate against the FMA rate reachable at
+3 waves per SIMD) come from the committed counter summaries of that kernel
+when the kernel's sources are unchanged since they were taken.
 `cpu_baseline` is the float64 CPU oracle on a bounded sample of the same
 workload.  `per_call.<call>.cold` times each scan kernel again with the
 caches flushed before every launch (a 1 GiB buffer is written first, more
@@ -128,6 +130,34 @@ def committed_traffic(kernel: str, workload: str):
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def committed_issue(kernel: str, workload: str):
+    """The kernel's vector-issue figures from profiles/valu_scan_kernels_<workload>.txt
+    (VALU instructions and transcendentals per (t, n), and the issue rate as a
+    fraction of what independent FMAs reach at the kernels' 3 waves per SIMD,
+    transcendentals at their issue cost), or None when the kernel changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"valu_scan_kernels_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields, cur = {}, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("kernel:"):
+                cur = line.split()[1]
+            elif cur == kernel and ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    try:
+        return {"valu_per_state_step": float(fields["valu_per_state_step"]),
+                "trans_per_state_step": float(fields["trans_per_state_step"]),
+                "issue_frac_vs_fma_3_waves": float(fields["fma_equivalent_vs_3_waves"]),
+                "waves_per_simd": 3}
     except (KeyError, ValueError):
         return None
 
@@ -729,6 +759,7 @@ def main():
         res["roofline"] = {"bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_F32_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / PEAK_F32_TFLOPS, 4),
                            "traffic": committed_traffic(kname, wl_tag),
+                           "issue": committed_issue(kname, wl_tag),
                            "kernel": kname, "call": f"mamba_scan_{dom}",
                            "algorithmic_flops_per_launch": int(dom_flops),
                            "flops_per_state_step": flops_per_tn(dom, args.disc),

@@ -343,12 +343,14 @@ __device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + fast_
 // Abar below 1: for |x| = 1e-4 the relative error is about 1e-3, and at a
 // constant step it does not average out along the recurrence.
 //
-// expm1 from two lower bounds of e^x - 1, both valid for every real x:
-//   * the cubic Taylor polynomial x + x^2/2 + x^3/6 (its remainder
-//     e^xi x^4/24, Lagrange form, is never negative);
-//   * Abar - (1 + 2^-23): v_exp_f32 is within 0.78 ulp, at most 9e-8 for
-//     results in [0.5, 2) (measured on gfx950 against float64 over 16M
-//     arguments), below 2^-23.
+// expm1 from two lower bounds of e^x - 1:
+//   * the cubic Taylor polynomial x + x^2/2 + x^3/6, for every real x (its
+//     remainder e^xi x^4/24, Lagrange form, is never negative);
+//   * Abar - (1 + 2^-23), for x < ln 2: v_exp_f32 is within 0.78 ulp, at
+//     most 9e-8 for results in [0.5, 2) (measured on gfx950 against float64
+//     over 16M arguments), below 2^-23.  Above ln 2 Abar's error may exceed
+//     2^-23, but it stays below 1e-7 relative to e^x - 1 >= 1 there, where
+//     this term is the larger one: the maximum stays accurate.
 // Their maximum is within about 5e-6 of e^x - 1 relative: the polynomial
 // wins for |x| below about 0.05, the hardware exponential above.  The
 // arguments are in exp2 units: z = x log2(e), so x = z ln 2.
@@ -384,9 +386,9 @@ __device__ __forceinline__ float zoh_coef_neg(float dt, float z, float abar, flo
 // d/dA of the ZOH coefficient (e^x - 1)/A at fixed delta: delta^2 psi(x),
 // psi(x) = (x e^x - e^x + 1)/x^2 = 1/2 + x/3 + x^2/8 + x^3/30 + ...  The
 // closed form cancels to second order for small x, so below |x| = 0.11 the
-// series is used (its first omitted term, x^4/144, is below 1e-6 of psi
-// there); above, the closed form is within 1.2e-7/x^2 (relative), since
-// abar carries at most 9e-8 of absolute error.  In the closed form delta^2
+// series is used (its first omitted term, x^4/144, is about 2e-6 of psi
+// there); above, the closed form is within about 2e-7/x^2 (relative: abar
+// carries at most 9e-8 of absolute error, the numerator is about x^2/2).  In the closed form delta^2
 // cancels: delta^2 psi = (abar (x - 1) + 1) / A^2, so A = 0 needs no
 // special case (the series branch is taken).  dt2 = delta^2, iA2 = 1/A^2.
 constexpr float kPsiZ = 0.15869619f;               // 0.11 / ln 2: |x| < 0.11 in z units
