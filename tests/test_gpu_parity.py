@@ -37,9 +37,17 @@ def _positive_steps(inp, dtype):
     return inp, W.inputs_f64(inp, dtype)
 
 
+def _positive_A(inp):
+    """Some A > 0 (a state that grows): +0.05 in every fifth channel's state 2
+    and +1e-3 in the next channel's state 5 (small x = delta A > 0)."""
+    inp["A"][1::5, 2] = 0.05
+    inp["A"][2::5, min(5, inp["A"].shape[1] - 1)] = 1e-3
+    return inp["A"].astype(np.float64)
+
+
 def run_fwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=False, opts=None,
                  zero_A=False, A_mode="s4d_real", rtol=None, segments=0, reset=None,
-                 h0_scale=1.0):
+                 h0_scale=1.0, pos_A=False):
     opts = opts or {}
     announce(f"fwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} lanes={lanes} "
              f"softplus={softplus} h0={h0}x{h0_scale} opts={opts} zero_A={zero_A} "
@@ -50,6 +58,8 @@ def run_fwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=
     if zero_A:
         inp["A"][::3, 0] = 0.0
         f["A"] = inp["A"].astype(np.float64)
+    if pos_A:
+        f["A"] = _positive_A(inp)
     h0v = None
     if h0:
         h0v = (np.random.default_rng(wid).standard_normal((batch, dim, N))
@@ -114,6 +124,15 @@ def test_fwd_initial_state(dtype):
 def test_fwd_zero_A_limit():
     run_fwd_case(17, 2, 12, 16, 400, "f32", "zoh", zero_A=True)
     run_fwd_case(17, 2, 12, 16, 400, "f32", "zoh", zero_A=True, lanes=64)
+
+
+def test_fwd_positive_A():
+    # A > 0 takes the kernels' general copy (the sign-agnostic expm1); the
+    # state grows, and the segment carry multiplies by exp(A sum(delta)) > 1
+    run_fwd_case(18, 2, 12, 16, 700, "f32", "zoh", pos_A=True, h0=True)
+    run_fwd_case(18, 2, 12, 16, 700, "f32", "zoh", pos_A=True, segments=3)
+    run_fwd_case(18, 2, 12, 16, 700, "f32", "zoh", pos_A=True, lanes=32)
+    run_fwd_case(18, 2, 12, 16, 700, "bf16", "euler", pos_A=True)
 
 
 @pytest.mark.parametrize("segments", [2, 3, 10])
@@ -291,7 +310,8 @@ def test_state_update_without_optionals():
 # backward
 # --------------------------------------------------------------------------
 def run_bwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=False,
-                 opts=None, zero_A=False, A_mode="s4d_real", rtol=None, reset=None, segments=0):
+                 opts=None, zero_A=False, A_mode="s4d_real", rtol=None, reset=None, segments=0,
+                 pos_A=False):
     opts = opts or {}
     announce(f"bwd wid={wid} shape=({batch},{dim},{N},{L}) {dtype} {disc} lanes={lanes} "
              f"h0={h0} opts={opts} zero_A={zero_A} segments={segments} "
@@ -302,6 +322,8 @@ def run_bwd_case(wid, batch, dim, N, L, dtype, disc, lanes=0, softplus=True, h0=
     if zero_A:
         inp["A"][::4, 1] = 0.0
         f["A"] = inp["A"].astype(np.float64)
+    if pos_A:
+        f["A"] = _positive_A(inp)
     h0v = np.random.default_rng(wid).standard_normal((batch, dim, N)).astype(np.float32) \
         if h0 else None
     g = to_device(inp, dtype)
@@ -430,6 +452,14 @@ def _wide_blocks(batch, dim):
 def test_bwd_wide_blocks(dtype, disc):
     assert _wide_blocks(4, 2050) >= WIDE_MIN_BLOCKS
     run_bwd_case(54, 4, 2050, 16, 300, dtype, disc, h0=True)
+
+
+def test_bwd_positive_A():
+    # A > 0: the blocks holding one are deferred to the general launch; one
+    # pass, segmented, and in wide blocks
+    run_bwd_case(58, 2, 19, 16, 700, "f32", "zoh", pos_A=True, h0=True)
+    run_bwd_case(58, 1, 20, 16, 1189, "f32", "zoh", pos_A=True, segments=3)
+    run_bwd_case(58, 4, 2050, 16, 300, "f32", "zoh", pos_A=True)
 
 
 def test_bwd_wide_blocks_zero_A_and_checkpoints():
