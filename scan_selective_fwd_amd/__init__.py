@@ -151,11 +151,18 @@ def checkpoint_shape(batch, dim, N, L):
     return (batch, dim, (L + 127) // 128, N)
 
 
+def _size_status(*sizes) -> int:
+    """The status the library gives sizes its workspace query refuses (the
+    query itself returns SIZE_MAX): MAMBA_ERR_SHAPE for an empty or negative
+    size, else MAMBA_ERR_UNSUPPORTED."""
+    return 2 if min(int(x) for x in sizes) <= 0 else 6
+
+
 def fwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0, segments=0) -> int:
     code = F32 if dtype == torch.float32 else BF16
     n = lib().mamba_scan_fwd_workspace_size_ex(batch, dim, N, L, code, int(lanes), int(segments))
     if n >= 2 ** 63:
-        raise MambaScanError(6, "mamba_scan_fwd_workspace_size")
+        raise MambaScanError(_size_status(batch, dim, N, L), "mamba_scan_fwd_workspace_size")
     return int(n)
 
 
@@ -163,7 +170,7 @@ def bwd_workspace_bytes(batch, dim, N, L, dtype=torch.float32, lanes=0, segments
     code = F32 if dtype == torch.float32 else BF16
     n = lib().mamba_scan_bwd_workspace_size_ex(batch, dim, N, L, code, int(lanes), int(segments))
     if n >= 2 ** 63:
-        raise MambaScanError(6, "mamba_scan_bwd_workspace_size")
+        raise MambaScanError(_size_status(batch, dim, N, L), "mamba_scan_bwd_workspace_size")
     return int(n)
 
 
@@ -334,14 +341,16 @@ def complex_checkpoint_shape(batch, dim, N, L):
 def fwd_complex_workspace_bytes(batch, dim, N, L, segments=0) -> int:
     n = lib().mamba_scan_fwd_complex_workspace_size_ex(batch, dim, N, L, int(segments))
     if n >= 2 ** 63:
-        raise MambaScanError(6, "mamba_scan_fwd_complex_workspace_size")
+        raise MambaScanError(_size_status(batch, dim, N, L),
+                             "mamba_scan_fwd_complex_workspace_size")
     return int(n)
 
 
 def bwd_complex_workspace_bytes(batch, dim, N, L, segments=0) -> int:
     n = lib().mamba_scan_bwd_complex_workspace_size_ex(batch, dim, N, L, int(segments))
     if n >= 2 ** 63:
-        raise MambaScanError(6, "mamba_scan_bwd_complex_workspace_size")
+        raise MambaScanError(_size_status(batch, dim, N, L),
+                             "mamba_scan_bwd_complex_workspace_size")
     return int(n)
 
 

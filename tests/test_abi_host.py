@@ -362,3 +362,21 @@ def test_noalloc_refuses_problems_beyond_its_scratch(lib):
     # invalid sizes are named by the regular checks
     bad = [fake] * 10 + [1, 0, 0, 0, 5120, 16, 2048] + [fake] * 9 + [None]
     assert lib.mamba_scan_bwd_noalloc(*bad) == 2    # MAMBA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("sizes,status", [
+    ((0, 4, 16, 64), 2), ((1, 0, 16, 64), 2), ((1, 4, 0, 64), 2), ((1, 4, 16, 0), 2),
+    ((1, 4, 16, -1), 2), ((1, 4, 65, 64), 6)])
+def test_binding_size_errors_match_the_abi(lib, sizes, status):
+    # the workspace queries answer SIZE_MAX for every refused size; the binding
+    # reports the status the entry points themselves give: MAMBA_ERR_SHAPE for
+    # an empty or negative size, MAMBA_ERR_UNSUPPORTED beyond the limits
+    import scan_selective_fwd_amd as ms
+    for query in (ms.fwd_workspace_bytes, ms.bwd_workspace_bytes,
+                  ms.fwd_complex_workspace_bytes, ms.bwd_complex_workspace_bytes):
+        with pytest.raises(ms.MambaScanError) as e:
+            query(*sizes)
+        assert e.value.status == status, (query.__name__, sizes)
+    batch, dim, N, L = sizes
+    assert fwd(lib, batch=batch, dim=dim, N=N, L=L) == status
+    assert bwd(lib, batch=batch, dim=dim, N=N, L=L) == status

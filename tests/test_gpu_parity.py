@@ -580,3 +580,33 @@ def test_fwd_split_sequence_resumes_exactly(split):
     assert_match(to_f64(full), ref, RTOL["f32"], "full out")
     # the two GPU runs agree more closely with each other than with the oracle
     assert_match(to_f64(joined), to_f64(full), 1e-5, "split vs full")
+
+
+@pytest.mark.parametrize("shape", [(0, 4, 8, 64), (2, 0, 8, 64), (2, 4, 0, 64), (2, 4, 8, 0)])
+def test_empty_inputs_are_refused_without_launching(shape):
+    """Empty tensors reach the library, which refuses them with
+    MAMBA_ERR_SHAPE before enqueuing anything (the forward and backward
+    through their workspace queries, the decode step through its entry point);
+    caller buffers are left as they were."""
+    batch, dim, N, L = shape
+    announce(f"empty inputs {shape}")
+    dev = "cuda"
+    u = torch.zeros((batch, dim, L), device=dev)
+    A = -torch.ones((dim, N), device=dev)
+    B = torch.zeros((batch, N, L), device=dev)
+    out = torch.full((batch, dim, L), 7.0, device=dev)
+    with pytest.raises(ms.MambaScanError) as e:
+        ms.scan_fwd(u, u, A, B, B, out=out)
+    assert e.value.status == 2
+    with pytest.raises(ms.MambaScanError) as e:
+        ms.scan_bwd(u, u, A, B, B, None, None, None, u)
+    assert e.value.status == 2
+    state = torch.full((batch, dim, N), 3.0, device=dev)
+    x = torch.zeros((batch, dim), device=dev)
+    Bs = torch.zeros((batch, N), device=dev)
+    if batch == 0 or dim == 0 or N == 0:
+        with pytest.raises(ms.MambaScanError) as e:
+            ms.state_update(state, x, x, A, Bs, Bs)
+        assert e.value.status == 2
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((state == 3.0).all())
