@@ -67,7 +67,7 @@ def test_coef_for_negative_A_within_bound():
         coef = np.minimum(poly, fma(abar, ia, mb))
         rel = np.abs(np.float64(coef) - ref) / np.abs(ref)
         worst = max(worst, rel.max())
-    assert worst < 1e-5, worst
+    assert worst < 8e-6, worst          # zoh_coef_neg's comment: below about 8e-6
 
 
 def test_expm1_any_sign_within_bound():
@@ -81,7 +81,7 @@ def test_expm1_any_sign_within_bound():
         ref = np.expm1(np.float64(z) * 0.6931471805599453)
         rel = np.abs(np.float64(em1) - ref) / np.abs(ref)
         worst = max(worst, rel.max())
-    assert worst < 1e-5, worst
+    assert worst < 5e-6, worst          # expm1_zoh's comment: within about 5e-6
 
 
 def test_coef_derivative_within_bound():
@@ -107,4 +107,6 @@ def test_coef_derivative_within_bound():
         ref = np.float64(dt) ** 2 * psi
         rel = np.abs(np.float64(zeta) - ref) / np.abs(ref)
         worst = max(worst, rel.max())
-    assert worst < 5e-5, worst
+    # dcoef_dA's comment: the series within about 2e-6 below |x| = 0.11, the
+    # closed form within about 2e-7/x^2 above (1.65e-5 at 0.11)
+    assert worst < 1.7e-5, worst
