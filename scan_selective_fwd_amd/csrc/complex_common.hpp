@@ -59,10 +59,16 @@ __device__ __forceinline__ float2 cexp_expm1_scaled(float dt, float ar2, float a
 
 // d/dA of the ZOH coefficient (e^x - 1)/A of a complex A at fixed dt:
 // dt^2 psi(x), psi(x) = (x e^x - e^x + 1)/x^2 = 1/2 + x/3 + x^2/8 + x^3/30 +
-// ... with x = dt a.  As dcoef_dA for real A: below |x| = 0.11 the series
-// (first omitted term x^4/144), above the closed form (ab (x - 1) + 1)/A^2,
-// whose abar carries at most about 2e-7 of absolute error.  ia2 = (1/A)^2.
-__device__ __forceinline__ float2 cdcoef_dA(float dt, float2 a, float2 ab, float2 ia2) {
+// ... with x = dt a.  Below |x| = 0.17 the series (its first omitted term,
+// x^4/144, is at most 1.2e-5 of psi there).  Above, (dt Abar - coef)/A,
+// from the exact identity A d(coef)/dA = dt Abar - coef, with coef = (Abar -
+// 1)/A the accurate coefficient the replay formed: the difference cancels
+// only to O(|x|) of its terms, so coef's and Abar's errors grow by at most
+// about 2/|x| (12 at the threshold), where the closed form (Abar (x - 1) +
+// 1)/A^2 divides Abar's absolute error by |x|^2 / 2.  Worst relative error
+// about 1.5e-5 (float32 emulation with the hardware exp, sin and cos off by
+// their measured errors).  At A = 0 (ia = 0, coef = dt) the series is taken.
+__device__ __forceinline__ float2 cdcoef_dA(float dt, float2 a, float2 ab, float2 coef, float2 ia) {
   const float2 x = cscale(a, dt);
   float2 w = make_float2(__builtin_fmaf(x.x, 1.0f / 30.0f, 0.125f), x.y * (1.0f / 30.0f));
   w = cmul(x, w);
@@ -70,8 +76,9 @@ __device__ __forceinline__ float2 cdcoef_dA(float dt, float2 a, float2 ab, float
   w = cmul(x, w);
   w.x += 0.5f;
   const float2 series = cscale(w, dt * dt);
-  const float2 closed = cmul(cfma(ab, make_float2(x.x - 1.0f, x.y), make_float2(1.0f, 0.0f)), ia2);
-  const bool small = __builtin_fmaf(x.x, x.x, x.y * x.y) < 0.0121f;   // |x| < 0.11
+  const float2 closed =
+      cmul(make_float2(__builtin_fmaf(dt, ab.x, -coef.x), __builtin_fmaf(dt, ab.y, -coef.y)), ia);
+  const bool small = __builtin_fmaf(x.x, x.x, x.y * x.y) < 0.0289f;   // |x| < 0.17
   return small ? series : closed;
 }
 

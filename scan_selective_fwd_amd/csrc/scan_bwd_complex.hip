@@ -243,7 +243,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       // dA collects conj(dt Abar h_{t-1} + dcoef/dA B u) G: the Abar path and
       // (ZOH) the Bbar path, whose coefficient is formed without cancellation
       float2 dAc = make_float2(0.0f, 0.0f);
-      const float2 ia2 = cmul(ia, ia);
       float pv[4], sv[4][4], Tq[4][2];
 #pragma unroll
       for (int k = K - 1; k >= 0; --k) {
@@ -258,7 +257,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
           // ddelta: Re(conj(G) Abar (A h_{t-1} + B u)), dBbar/ddelta = Abar B
           const float2 W = cfma(a, Ah, cmul(ab[k], Bu));
           gdt[k] = __builtin_fmaf(Gk.x, W.x, __builtin_fmaf(Gk.y, W.y, gdt[k]));
-          const float2 zeta = cdcoef_dA(dt[k], a, ab[k], ia2);
+          const float2 zeta = cdcoef_dA(dt[k], a, ab[k], coef[k], ia);
           dAc = cfma(cconj(cfma(zeta, Bu, cscale(Ah, dt[k]))), Gk, dAc);
         } else {
           gdt[k] += cdot(Gk, cmul(a, Ah)) + cdot(Gk, Bu);   // Euler: Bbar = dt B

@@ -112,8 +112,12 @@ def test_complex_coef_derivative_within_bound():
     for se in (-1.0, 1.0):
         for ss in (-1.0, 1.0):
             for sc in (-1.0, 1.0):
-                _, _, _, mag, co, si = emulated_expm1(dt, ar, ai, se, ss, sc)
+                re, im, _, mag, co, si = emulated_expm1(dt, ar, ai, se, ss, sc)
                 abr, abi = mul(mag, co), mul(mag, si)
+                ia = 1.0 / (np.float64(ar) + 1j * np.float64(ai))
+                iar, iai = ia.real.astype(F), ia.imag.astype(F)
+                # the replay's coefficient, coef = (e^x - 1) / A
+                cr, ci = fma(re, iar, -mul(im, iai)), fma(re, iai, mul(im, iar))
                 # cdcoef_dA, with x = dt A formed in float32
                 xr, xi = mul(ar, dt), mul(ai, dt)
                 wr = fma(xr, F(1.0 / 30.0), F(0.125))
@@ -124,21 +128,17 @@ def test_complex_coef_derivative_within_bound():
                 wr = (np.float64(wr) + 0.5).astype(F)
                 d2 = mul(dt, dt)
                 sr, si_ = mul(wr, d2), mul(wi, d2)
-                # closed: (ab (x - 1) + 1) / A^2, ia2 = (1/A)^2 in float32
-                ia = 1.0 / (np.float64(ar) + 1j * np.float64(ai))
-                ia2 = ia * ia
-                i2r, i2i = ia2.real.astype(F), ia2.imag.astype(F)
-                x1r = (np.float64(xr) - 1.0).astype(F)
-                tr = fma(abr, x1r, fma(-abi, xi, F(1.0)))
-                ti = fma(abr, xi, fma(abi, x1r, F(0.0)))
-                cr, ci = fma(tr, i2r, -mul(ti, i2i)), fma(tr, i2i, mul(ti, i2r))
-                small = fma(xr, xr, mul(xi, xi)) < F(0.0121)
-                zr = np.where(small, sr, cr)
-                zi = np.where(small, si_, ci)
+                # above the threshold: (dt Abar - coef) / A
+                tr, ti = fma(dt, abr, -cr), fma(dt, abi, -ci)
+                kr, ki = fma(tr, iar, -mul(ti, iai)), fma(tr, iai, mul(ti, iar))
+                small = fma(xr, xr, mul(xi, xi)) < F(0.0289)
+                zr = np.where(small, sr, kr)
+                zi = np.where(small, si_, ki)
                 x = np.float64(dt) * (np.float64(ar) + 1j * np.float64(ai))   # exact dt A
                 ref = np.float64(dt) ** 2 * psi_ref(x)
                 got = np.float64(zr) + 1j * np.float64(zi)
                 worst = max(worst, (np.abs(got - ref) / np.abs(ref)).max())
-    # the comment: the series within x^4/144 of psi below |x| = 0.11, the
-    # closed form within about 2e-7 absolute in abar over |x|^2 / 2 above it
-    assert worst < 5e-5, worst
+    # cdcoef_dA's comment: about 1.5e-5 (the series' truncation, at most
+    # 1.2e-5 of psi below |x| = 0.17; above, the coefficient's error grown
+    # by at most about 2/|x|)
+    assert worst < 1.6e-5, worst
