@@ -454,6 +454,15 @@ def test_bwd_wide_blocks(dtype, disc):
     run_bwd_case(54, 4, 2050, 16, 300, dtype, disc, h0=True)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_wide_blocks_small_state_unaligned(dtype):
+    # wide blocks with N < 16 (state rows past N are neither read nor
+    # flushed) and a length whose rows are not 16-byte aligned (the guarded
+    # loads and stores, a ragged last chunk)
+    assert _wide_blocks(4, 2050) >= WIDE_MIN_BLOCKS
+    run_bwd_case(59, 4, 2050, 5, 301, dtype, "zoh", h0=True)
+
+
 def test_bwd_positive_A():
     # A > 0: the blocks holding one are deferred to the general launch; one
     # pass, segmented, and in wide blocks
