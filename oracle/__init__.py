@@ -108,6 +108,22 @@ def _split(n_items: int, threads: int):
     return [(i, min(i + step, n_items)) for i in range(0, n_items, step)]
 
 
+def _check_shapes(batch, dim, N, L, **arrays):
+    """Raises ValueError unless every given array has its documented shape
+    (the C code reads through the pointers with these sizes).  A required
+    array is passed as (array, True); None is allowed only for optional ones."""
+    shapes = dict(u=(batch, dim, L), delta=(batch, dim, L), z=(batch, dim, L),
+                  dout=(batch, dim, L), A=(dim, N), B=(batch, N, L), C=(batch, N, L),
+                  D=(dim,), delta_bias=(dim,), h0=(batch, dim, N))
+    for name, (arr, required) in arrays.items():
+        if arr is None:
+            if required:
+                raise ValueError(f"{name} is required")
+            continue
+        if tuple(arr.shape) != shapes[name]:
+            raise ValueError(f"{name} has shape {tuple(arr.shape)}, expected {shapes[name]}")
+
+
 def default_threads() -> int:
     """Host cores available to this process, capped by OMP_NUM_THREADS when
     the environment sets it (a machine's share of cores may be smaller than
@@ -135,8 +151,9 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
     D, z, delta_bias, h0 = (_f64(t) for t in (D, z, delta_bias, h0))
     batch, dim, L = u.shape
     N = A.shape[1]
-    assert delta.shape == u.shape and A.shape == (dim, N)
-    assert B.shape == (batch, N, L) and C.shape == (batch, N, L)
+    _check_shapes(batch, dim, N, L, delta=(delta, True), A=(A, True), B=(B, True),
+                  C=(C, True), D=(D, False), z=(z, False), delta_bias=(delta_bias, False),
+                  h0=(h0, False))
     out = np.zeros((batch, dim, L), np.float64)
     last = np.zeros((batch, dim, N), np.float64) if return_last_state else None
     nthreads = threads or default_threads()
@@ -187,6 +204,9 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *, delta_softpl
     D, z, delta_bias, h0 = (_f64(t) for t in (D, z, delta_bias, h0))
     batch, dim, L = u.shape
     N = A.shape[1]
+    _check_shapes(batch, dim, N, L, delta=(delta, True), A=(A, True), B=(B, True),
+                  C=(C, True), dout=(dout, True), D=(D, False), z=(z, False),
+                  delta_bias=(delta_bias, False), h0=(h0, False))
     du = np.zeros_like(u)
     ddelta = np.zeros_like(u)
     dz = np.zeros_like(u) if z is not None else None
@@ -279,6 +299,10 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None
     y_t = Re(sum_n C_t[n] h_t[n]) + D u_t gated by SiLU(z).  reset (batch,
     L) flags as in scan_fwd."""
     lib = _load()
+    _b, _d, _l = np.shape(u)
+    _check_shapes(_b, _d, np.shape(A)[1], _l, delta=(delta, True), A=(A, True), B=(B, True),
+                  C=(C, True), D=(D, False), z=(z, False), delta_bias=(delta_bias, False),
+                  h0=(h0, False))
     u, delta, D, z, delta_bias = (_f64(t) for t in (u, delta, D, z, delta_bias))
     A, B, C, h0 = (_c128(t) for t in (A, B, C, h0))
     batch, dim, L = u.shape
@@ -309,6 +333,10 @@ def scan_bwd_complex(u, delta, A, B, C, D, z, delta_bias, dout, h0=None, *,
     dL/dRe(w) + i dL/dIm(w)); the others real.  Returns a dict like scan_bwd.
     reset (batch, L) flags as in scan_bwd."""
     lib = _load()
+    _b, _d, _l = np.shape(u)
+    _check_shapes(_b, _d, np.shape(A)[1], _l, delta=(delta, True), A=(A, True), B=(B, True),
+                  C=(C, True), dout=(dout, True), D=(D, False), z=(z, False),
+                  delta_bias=(delta_bias, False), h0=(h0, False))
     u, delta, D, z, delta_bias, dout = (_f64(t) for t in (u, delta, D, z, delta_bias, dout))
     A, B, C, h0 = (_c128(t) for t in (A, B, C, h0))
     batch, dim, L = u.shape

@@ -431,3 +431,21 @@ def test_reset_backward_equals_independent_segments(disc):
                 np.testing.assert_array_equal(g["dh0"][b], want)
     for k, v in sums.items():
         np.testing.assert_allclose(g[k], v, rtol=1e-12, atol=1e-12, err_msg=k)
+
+
+def test_oracle_rejects_missing_or_misshaped_arguments():
+    # the C code reads through the pointers with the documented sizes: a
+    # missing required array or a wrong shape is refused before the call
+    inp = W.make_inputs(62, 1, 4, 8, 64, dtype="f32", with_dout=True)
+    f = W.inputs_f64(inp, "f32")
+    args = [f[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
+    with pytest.raises(ValueError, match="dout is required"):
+        oracle.scan_bwd(*args, None)
+    with pytest.raises(ValueError, match="h0 has shape"):
+        oracle.scan_fwd(*args, f["dout"])            # (batch, dim, L) where h0 goes
+    with pytest.raises(ValueError, match="B has shape"):
+        oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"][:, :4], f["C"])
+    ci = W.make_complex_inputs(62, 1, 4, 8, 64, dtype="f32", with_dout=True)
+    cargs = [ci[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
+    with pytest.raises(ValueError, match="dout is required"):
+        oracle.scan_bwd_complex(*cargs, None)
