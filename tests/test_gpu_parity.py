@@ -619,3 +619,41 @@ def test_empty_inputs_are_refused_without_launching(shape):
         assert e.value.status == 2
     torch.cuda.synchronize()
     assert bool((out == 7.0).all()) and bool((state == 3.0).all())
+
+
+def test_nan_and_infinite_step_inputs_propagate():
+    """Non-finite inputs never stall a call, and they stay where the
+    recurrence carries them.  A NaN in u at one step makes that channel's
+    outputs NaN from that step on; a step of +inf (delta_raw = +inf) resets
+    the state, the limit the pages give for a large step, and the outputs
+    stay finite.  Every other channel matches the oracle as usual (rows are
+    independent; the shared B and C are finite)."""
+    batch, dim, N, L = 2, 20, 16, 700
+    announce(f"non-finite inputs shape=({batch},{dim},{N},{L})")
+    inp, _ = _make(63, batch, dim, N, L, "f32", with_dout=True)
+    inp["u"][0, 3, 100] = np.nan
+    inp["delta"][1, 5, 50] = np.inf
+    f = W.inputs_f64(inp, "f32")
+    g = to_device(inp, "f32")
+    out, last = ms.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                            g["delta_bias"], return_last_state=True)
+    res = ms.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                      g["delta_bias"], g["dout"])
+    torch.cuda.synchronize()
+    ref, ref_last = _oracle_fwd(f, "zoh")
+    gref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"],
+                           f["delta_bias"], f["dout"])
+    o = to_f64(out)
+    # the NaN channel: finite and exact before the step, NaN from it on
+    assert np.isnan(o[0, 3, 100:]).all() and np.isnan(ref[0, 3, 100:]).all()
+    assert_match(o[0, 3, :100], ref[0, 3, :100], RTOL_F32, "out before the NaN")
+    # the infinite step's channel: finite everywhere (the state is reset)
+    assert np.isfinite(ref[1, 5]).all()
+    assert_match(o[1, 5], ref[1, 5], RTOL_F32, "out across the infinite step")
+    # every other channel, forward and per-channel gradients
+    keep = np.ones((batch, dim), bool)
+    keep[0, 3] = keep[1, 5] = False
+    assert_match(o[keep], ref[keep], RTOL_F32, "out, other channels")
+    assert_match(to_f64(last)[keep], ref_last[keep], RTOL_F32, "last_state, other channels")
+    for k in ("du", "ddelta", "dz"):
+        assert_match(to_f64(res[k])[keep], gref[k][keep], RTOL_F32, f"{k}, other channels")
